@@ -1,0 +1,239 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) sparse token-choice MoE layer.
+ *
+ * One process, one GPU.  Every entry point validates its arguments on the
+ * host, enqueues hand-written HIP kernels on the given stream and returns; no
+ * call synchronises the device and no call allocates or frees device memory.
+ * The caller owns every buffer; the library keeps no pointer after a call
+ * returns.  Layer outputs that later calls need (logits, top-K, rows, saved
+ * activations) are plain caller buffers passed back in.
+ *
+ * Sources (web pages on the method, cited by title and section):
+ *  [P1] "Wrong router gradient with experts_implementation=batched_mm under
+ *       expert parallelism": cause section (sentinel slots, proj_out mask).
+ *  [P2] MiniMind issue "[Bug] num_experts_per_tok=1: the MoE router receives
+ *       no gradient": sections 2 and 3 (renormalised top-1 has a constant
+ *       weight).
+ *  [P3] "MoE" tutorial chapter (8-MoE): Router/Gating Network, KeepTopK,
+ *       Expert Capacity, GShard pseudo-code, Switch Transformers, ST-MoE
+ *       (router z-loss), efficient inference (grouping and permutation).
+ *  [P4] "MoE training: routing and communication behind sparse compute":
+ *       forward data path, load balance, capacity.
+ *  [P5] course notes "08 MoE: capacity, routing, gradients, balance and
+ *       system implementation": sections 8.1-8.8.
+ *
+ * Conventions shared by all entry points
+ *  - Layouts are row-major.  x, y, dx, dy: [T][D].  logits: [T][E] fp32.
+ *    topk_idx, topk_w: [T][K].  Router weight W_r: [E][D] fp32 (s = x W_r^T).
+ *    Expert weights (GShard orientation, [P3] GShard pseudo-code):
+ *      w_gate, w_up: [G][D][F];  w_down: [G][F][D]
+ *    where G = (expert_hi - expert_lo) + n_shared: local routed experts first,
+ *    then the shared expert.
+ *  - dtype MOE_BF16: x, dy, dx, expert weights and their gradients, x_perm,
+ *    act, h, o_perm, y are bf16 (fp32 accumulation everywhere); the router
+ *    (logits, W_r, dW_r) stays fp32 ([P3] Switch Transformers: the router is
+ *    kept in full precision).  dtype MOE_F32: all of those are fp32.
+ *  - "rows": routed rows are expert-major (local expert lo..hi-1), in token
+ *    order within an expert; the shared expert's rows follow, one per token.
+ *    rows_max = T*K + n_shared*T bounds every row buffer.
+ *  - Pointers must be 16-byte aligned device pointers (MOE_EALIGN).
+ *  - Requirements: T >= 0; D and F positive multiples of 64; 1 <= K <= E;
+ *    K <= 64; E <= 1024; 0 <= expert_lo <= expert_hi <= E; n_shared in {0,1}
+ *    (MOE_EINVAL).  T == 0 is a successful no-op.
+ *  - Inputs are assumed finite; no entry point checks for NaN or Inf.
+ *  - Return value: MOE_OK or a negative MOE_E* code; moe_error_string() gives
+ *    text (for MOE_ELAUNCH it includes the HIP error of the failed launch).
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  MOE_OK = 0,
+  MOE_EINVAL = -1,     /* a size, range or enum is out of bounds, or NULL    */
+  MOE_EALIGN = -2,     /* a pointer is not 16-byte aligned                   */
+  MOE_EDTYPE = -3,     /* dtype not supported for this operation             */
+  MOE_ELAUNCH = -4,    /* a HIP launch or runtime call failed                */
+  MOE_EWORKSPACE = -5  /* workspace smaller than moe_workspace_size()        */
+};
+
+enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 };
+enum { MOE_GATE_TRUNCATED = 0, /* gating A: g = p over all E, not renormalised */
+       MOE_GATE_RENORM = 1 };  /* gating B: renormalised over the top-K        */
+enum { MOE_F32 = 0, MOE_BF16 = 1 };
+enum { MOE_ROUTE_LOGITS_GIVEN = 1 }; /* moe_route flag: logits is an input   */
+
+/* Plain configuration record, read during the call and never retained. */
+typedef struct moe_config {
+  int32_t T, D, E, K, F;         /* tokens, model dim, global experts, top-k, FFN width */
+  int32_t expert_lo, expert_hi;  /* local experts [lo,hi); slots routed elsewhere are sentinels */
+  int32_t n_shared;              /* 0 or 1 always-on shared expert of width F, weight 1 */
+  int32_t score_fn;              /* MOE_SCORE_* */
+  int32_t gating;                /* MOE_GATE_* */
+  int32_t dtype;                 /* MOE_F32 or MOE_BF16 */
+  double capacity_factor;        /* <= 0: no capacity (dropless); C = ceil(c*T*K/E) in double */
+} moe_config;
+
+/* A hipStream_t (NULL: the null stream). */
+typedef void* moe_stream_t;
+
+/* Capacity per expert, C = ceil(c*T*K/E) with the global E, evaluated in
+ * double ([P5] 8.5; [P3] Switch Transformers capacity factor).  Writes -1
+ * when capacity_factor <= 0.  Host-only. */
+int moe_capacity(const moe_config* cfg, int32_t* capacity);
+
+/* rows_max = T*K + n_shared*T.  Host-only. */
+int moe_rows_max(const moe_config* cfg, int64_t* rows);
+
+/* Bytes of device workspace needed by moe_permute, aux_balance_loss and
+ * moe_backward for this configuration.  Host-only. */
+int moe_workspace_size(const moe_config* cfg, size_t* bytes);
+
+/*
+ * moe_route -- router GEMM, score, top-K and gate weights.
+ * [P3] Router/Gating Network (s = x W_g then a score function); [P5] 8.2
+ * (token-choice top-K, gating A vs B), 8.6 (sigmoid scores with selection
+ * bias b_e used only to select); [P3] KeepTopK.
+ *   x        [T][D] (dtype)            in
+ *   w_r      [E][D] fp32               in
+ *   r_bias   [E] fp32 or NULL          in   router bias, added to the logits
+ *   sel_bias [E] fp32 or NULL          in   selection bias (sigmoid only)
+ *   logits   [T][E] fp32               out (in with MOE_ROUTE_LOGITS_GIVEN;
+ *                                            then x, w_r, r_bias are unused)
+ *   topk_idx [T][K] int32              out  in pick order: descending key,
+ *                                            equal keys -> lower index first
+ *   topk_w   [T][K] fp32               out  gate weights (A or B)
+ *   lse      [T] fp32                  out  log-sum-exp of the logits
+ * The logits are the binary32 rounding of a double-precision accumulation of
+ * the products, so a top-K decision on them does not depend on the summation
+ * order.  Selection key: softmax -> the logit; sigmoid -> sig32(s) + b, a
+ * fixed binary32 sequence (range reduction by ln2 split in two parts, degree-7
+ * Taylor polynomial with fma, scaling by 2^n, IEEE division).
+ */
+int moe_route(const moe_config* cfg, const void* x, const float* w_r, const float* r_bias,
+              const float* sel_bias, float* logits, int32_t* topk_idx, float* topk_w, float* lse,
+              int32_t flags, moe_stream_t stream);
+
+/*
+ * moe_permute -- expert histogram, prefix scan, stable in-expert rank,
+ * capacity drops, row maps and the gather of token rows.
+ * [P3] efficient inference (sort tokens by expert, gather), GShard
+ * pseudo-code (expert buffers filled in token order; overflow dropped),
+ * Expert Capacity; [P5] 8.5 (C = ceil(c*T*K/E)), 8.8 (group by expert);
+ * [P1] cause section (slots of experts outside [lo,hi) are sentinels).
+ *   topk_idx   [T][K] int32  in
+ *   x          [T][D] dtype  in
+ *   counts_all [E] int32     out  slots per expert over all E, before capacity
+ *   offsets    [G+1] int32   out  row offsets of the groups (shared last)
+ *   slot_row   [T*K] int32   out  row of slot t*K+k; -1 dropped; -2 sentinel
+ *   row_token  [rows_max]    out  token of each row (valid for rows < offsets[G])
+ *   row_slot   [rows_max]    out  slot t*K+k of each routed row; -1 for shared rows
+ *   n_dropped  [1] int32     out  local assignments dropped by capacity
+ *   x_perm     [rows_max][D] out  x rows of the routed rows (shared rows are
+ *                                 not copied: the shared expert reads x)
+ *   ws, ws_bytes             workspace of moe_workspace_size() bytes
+ * Deterministic: the rank inside an expert comes from counts and scans, not
+ * from atomic slot grabbing.
+ */
+int moe_permute(const moe_config* cfg, const int32_t* topk_idx, const void* x,
+                int32_t* counts_all, int32_t* offsets, int32_t* slot_row, int32_t* row_token,
+                int32_t* row_slot, int32_t* n_dropped, void* x_perm, void* ws, size_t ws_bytes,
+                moe_stream_t stream);
+
+/*
+ * moe_expert_ffn -- grouped SwiGLU experts on the permuted rows.
+ * [P5] 8.1 (SwiGLU expert, ~3DF parameters), 8.7 (shared expert, weight 1),
+ * 8.8 (grouped GEMM instead of a per-expert loop); [P3] efficient inference.
+ *   x, x_perm            in   (the shared group reads x directly)
+ *   offsets [G+1]        in   from moe_permute
+ *   w_gate, w_up, w_down in   expert weights (layouts above)
+ *   act   [rows_max][2F] out  saved pre-activations: a = x W_gate in columns
+ *                             [0,F), b = x W_up in [F,2F)
+ *   h     [rows_max][F]  out  silu(a) * b
+ *   o_perm[rows_max][D]  out  expert output h W_down, unweighted (proj_out)
+ * Only rows < offsets[G] are written.  No host synchronisation: the grid is
+ * sized from rows_max and surplus workgroups exit.
+ */
+int moe_expert_ffn(const moe_config* cfg, const void* x, const void* x_perm, const int32_t* offsets,
+                   const void* w_gate, const void* w_up, const void* w_down, void* act, void* h,
+                   void* o_perm, moe_stream_t stream);
+
+/*
+ * moe_combine -- weighted scatter-add back to token order.
+ * [P5] 8.8 (a token appears K times: accumulate, do not overwrite), 8.7
+ * (shared expert added with weight 1); [P3] GShard combine.
+ *   y[t] = sum_k [slot_row >= 0] topk_w[t,k] * o_perm[slot_row[t,k]]
+ *          + o_perm[offsets[G-1] + t] (shared)          fp32 accumulation
+ * Sentinel and dropped slots contribute nothing; a token with all slots
+ * dropped gets y = 0 (the residual path is outside the layer).
+ */
+int moe_combine(const moe_config* cfg, const void* o_perm, const int32_t* offsets,
+                const int32_t* slot_row, const float* topk_w, void* y, moe_stream_t stream);
+
+/*
+ * aux_balance_loss -- Switch load-balance loss and router z-loss.  Defined
+ * for softmax scoring only (MOE_EINVAL for sigmoid).
+ * [P5] 8.5 (L = alpha*E*sum_e f_e P_e with f held constant), [P4] load
+ * balance section; [P3] ST-MoE and [P5] 8.6 (z-loss on log-sum-exp).
+ *   f_e = counts_all[e]/(T*K), P_e = mean_t softmax(s_t)_e
+ *   losses[0] = alpha*E*sum_e f_e P_e;  losses[1] = z_lambda*mean_t lse_t^2;
+ *   losses[2] = mean_t lse_t^2 (raw)                         [3] fp32, device
+ *   d_logits [T][E] fp32 (NULL: not written) = d(losses[0]+losses[1])/ds
+ */
+int aux_balance_loss(const moe_config* cfg, const float* logits, const int32_t* counts_all,
+                     float alpha, float z_lambda, float* losses, float* d_logits, void* ws,
+                     size_t ws_bytes, moe_stream_t stream);
+
+/*
+ * moe_backward -- full backward of the layer given dy.
+ * [P1] cause section: the gradient of a gate weight is that slot's proj_out,
+ * so sentinel (and dropped) slots have proj_out = 0 and dg = 0; [P5] 8.3 and
+ * [P2] section 2: gradients reach the router only through the continuous
+ * gate weights (top-K indices are piecewise constant).
+ *   saved forward tensors: x, w_r, logits, topk_idx, topk_w, offsets,
+ *   slot_row, x_perm, act, h, o_perm; weights w_gate, w_up, w_down.
+ *   dy [T][D]               in
+ *   d_logits_extra [T][E]   in, NULL = none (e.g. from aux_balance_loss)
+ *   dx [T][D]               out  through the experts and the router
+ *   dw_r [E][D] fp32        out
+ *   d_rbias [E] fp32        out, may be NULL
+ *   dw_gate, dw_up [G][D][F], dw_down [G][F][D]   out (experts with no rows
+ *                                                     get zeros)
+ *   d_logits_out [T][E]     out, may be NULL: the logit gradient ds
+ * Gating backward (centred forms, G = sum_k g_k dg_k): softmax A:
+ * ds_i = p_i(sum_{k:i_k=i} dg_k - G); softmax B: ds_{i_k} = g_k(dg_k - G),
+ * other ds = 0; sigmoid A: ds = dg sig(1-sig); sigmoid B:
+ * ds = ((dg - G)/sum sig) sig(1-sig).  With K = 1 and B the result is exactly 0.
+ */
+int moe_backward(const moe_config* cfg, const void* x, const float* w_r, const float* logits,
+                 const int32_t* topk_idx, const float* topk_w, const int32_t* offsets,
+                 const int32_t* slot_row, const void* x_perm, const void* act, const void* h,
+                 const void* o_perm, const void* w_gate, const void* w_up, const void* w_down,
+                 const void* dy, const float* d_logits_extra, void* dx, float* dw_r,
+                 float* d_rbias, void* dw_gate, void* dw_up, void* dw_down, float* d_logits_out,
+                 void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/* Text for an error code (thread-local detail for MOE_ELAUNCH). */
+const char* moe_error_string(int code);
+
+/*
+ * Kernel timing for measurement: while enabled, every kernel the library
+ * launches is bracketed by HIP events recorded on its own stream.
+ * moe_timing_report() waits for those events and writes one line per kernel
+ * name, "name<TAB>launches<TAB>total_ms\n", into buf (NUL-terminated,
+ * truncated to len), then clears the records.  Not for concurrent use from
+ * several host threads.
+ */
+int moe_timing_enable(int32_t on);
+int moe_timing_report(char* buf, size_t len);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

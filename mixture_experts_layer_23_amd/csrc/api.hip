@@ -1,0 +1,272 @@
+// api.hip -- the C ABI: argument validation, workspace layout, launch order,
+// error reporting and optional per-kernel timing.  Host code only.
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <string>
+#include <vector>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+static thread_local char g_err[512] = "";
+
+void set_error(const char* where, hipError_t e) {
+  snprintf(g_err, sizeof g_err, "%s: %s (%d)", where, hipGetErrorString(e), (int)e);
+}
+
+// --- timing ----------------------------------------------------------------
+struct TimedLaunch {
+  std::string name;
+  hipEvent_t a, b;
+};
+static bool g_timing = false;
+static std::vector<TimedLaunch> g_records;
+
+bool timing_on() { return g_timing; }
+
+void timing_before(const char* name, hipStream_t s) {
+  TimedLaunch r;
+  r.name = name;
+  if (hipEventCreate(&r.a) != hipSuccess || hipEventCreate(&r.b) != hipSuccess) return;
+  (void)hipEventRecord(r.a, s);
+  g_records.push_back(r);
+}
+
+void timing_after(hipStream_t s) {
+  if (!g_records.empty()) (void)hipEventRecord(g_records.back().b, s);
+}
+
+// --- configuration ----------------------------------------------------------
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+static int check_cfg(const moe_config* c) {
+  if (!c) return MOE_EINVAL;
+  if (c->T < 0 || c->D <= 0 || c->F <= 0 || c->E < 1 || c->E > 1024) return MOE_EINVAL;
+  if (c->D % 64 || c->F % 64) return MOE_EINVAL;
+  if (c->K < 1 || c->K > c->E || c->K > 64) return MOE_EINVAL;
+  if (c->expert_lo < 0 || c->expert_lo > c->expert_hi || c->expert_hi > c->E) return MOE_EINVAL;
+  if (c->n_shared < 0 || c->n_shared > 1) return MOE_EINVAL;
+  if (c->score_fn != MOE_SCORE_SOFTMAX && c->score_fn != MOE_SCORE_SIGMOID) return MOE_EINVAL;
+  if (c->gating != MOE_GATE_TRUNCATED && c->gating != MOE_GATE_RENORM) return MOE_EINVAL;
+  if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return MOE_EDTYPE;
+  if (!std::isfinite(c->capacity_factor)) return MOE_EINVAL;
+  // row indices and element offsets of row buffers fit the kernels' int32 /
+  // int64 arithmetic
+  const int64_t rows = (int64_t)c->T * c->K + (int64_t)c->n_shared * c->T;
+  if (rows > INT32_MAX / 2) return MOE_EINVAL;
+  return MOE_OK;
+}
+
+static int capacity_of(const moe_config& c) {
+  if (!(c.capacity_factor > 0.0)) return -1;
+  const double v = std::ceil((c.capacity_factor * (double)c.T * (double)c.K) / (double)c.E);
+  return v > (double)INT32_MAX ? INT32_MAX : (int)v;
+}
+
+static size_t al(size_t b) { return (b + 255) & ~(size_t)255; }
+
+static int groups(const moe_config& c) { return (c.expert_hi - c.expert_lo) + c.n_shared; }
+
+Workspace workspace_layout(const moe_config& c) {
+  Workspace L = {};
+  const int64_t TK = (int64_t)c.T * c.K;
+  const int64_t rows = TK + (int64_t)c.n_shared * c.T;
+  const size_t esz = c.dtype == MOE_BF16 ? 2 : 4;
+  L.ntiles = (int)std::max<int64_t>(1, cdiv(TK, kSlotTile));
+  L.aux_blocks = (int)std::max<int64_t>(1, cdiv(c.T, kAuxTokens));
+  if (c.E <= 16) {
+    L.dwr_splits = (int)std::max<int64_t>(1, cdiv(c.T, 256));
+  } else {
+    const int64_t tiles = cdiv(c.E, 64) * cdiv(c.D, 64);
+    int64_t s = cdiv(1024, tiles);
+    s = std::min<int64_t>(s, std::max<int64_t>(1, c.T / 256));
+    L.dwr_splits = (int)std::max<int64_t>(1, s);
+  }
+  size_t o = 0;
+  L.tile_counts = o; o += al((size_t)L.ntiles * c.E * 4);
+  L.tile_base = o;   o += al((size_t)L.ntiles * c.E * 4);
+  L.aux_part = o;    o += al((size_t)L.aux_blocks * (c.E + 1) * 4);
+  L.d_o = o;         o += al((size_t)rows * c.D * esz);
+  L.dact = o;        o += al((size_t)rows * 2 * c.F * esz);
+  L.dx_perm = o;     o += al((size_t)rows * c.D * esz);
+  L.dg = o;          o += al((size_t)TK * 4);
+  L.ds = o;          o += al((size_t)c.T * c.E * 4);
+  L.dxr = o;         o += (c.E > 16) ? al((size_t)c.T * c.D * 4) : 0;
+  L.dwr_part = o;    o += al((size_t)L.dwr_splits * ((size_t)c.E * c.D + c.E) * 4);
+  L.total = o;
+  return L;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+#define REQ(p) \
+  do { if (!(p)) return MOE_EINVAL; if (!aligned16(p)) return MOE_EALIGN; } while (0)
+#define OPT(p) \
+  do { if ((p) && !aligned16(p)) return MOE_EALIGN; } while (0)
+
+extern "C" {
+
+int moe_capacity(const moe_config* cfg, int32_t* capacity) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (!capacity) return MOE_EINVAL;
+  *capacity = capacity_of(*cfg);
+  return MOE_OK;
+}
+
+int moe_rows_max(const moe_config* cfg, int64_t* rows) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (!rows) return MOE_EINVAL;
+  *rows = (int64_t)cfg->T * cfg->K + (int64_t)cfg->n_shared * cfg->T;
+  return MOE_OK;
+}
+
+int moe_workspace_size(const moe_config* cfg, size_t* bytes) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (!bytes) return MOE_EINVAL;
+  *bytes = workspace_layout(*cfg).total;
+  return MOE_OK;
+}
+
+int moe_route(const moe_config* cfg, const void* x, const float* w_r, const float* r_bias,
+              const float* sel_bias, float* logits, int32_t* topk_idx, float* topk_w, float* lse,
+              int32_t flags, moe_stream_t stream) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (flags & ~MOE_ROUTE_LOGITS_GIVEN) return MOE_EINVAL;
+  const bool given = (flags & MOE_ROUTE_LOGITS_GIVEN) != 0;
+  if (!given) { REQ(x); REQ(w_r); OPT(r_bias); }
+  OPT(sel_bias);
+  REQ(logits); REQ(topk_idx); REQ(topk_w); OPT(lse);
+  if (cfg->T == 0) return MOE_OK;
+  return launch_route(*cfg, x, w_r, r_bias, sel_bias, logits, topk_idx, topk_w, lse, given,
+                      (hipStream_t)stream);
+}
+
+int moe_permute(const moe_config* cfg, const int32_t* topk_idx, const void* x,
+                int32_t* counts_all, int32_t* offsets, int32_t* slot_row, int32_t* row_token,
+                int32_t* row_slot, int32_t* n_dropped, void* x_perm, void* ws, size_t ws_bytes,
+                moe_stream_t stream) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  REQ(topk_idx); REQ(x); REQ(counts_all); REQ(offsets); REQ(slot_row); REQ(row_token);
+  REQ(row_slot); REQ(n_dropped); REQ(x_perm); REQ(ws);
+  const Workspace L = workspace_layout(*cfg);
+  if (ws_bytes < L.total) return MOE_EWORKSPACE;
+  if (cfg->T == 0) return MOE_OK;
+  return launch_permute(*cfg, capacity_of(*cfg), topk_idx, x, counts_all, offsets, slot_row,
+                        row_token, row_slot, n_dropped, x_perm, (char*)ws, L, (hipStream_t)stream);
+}
+
+int moe_expert_ffn(const moe_config* cfg, const void* x, const void* x_perm, const int32_t* offsets,
+                   const void* w_gate, const void* w_up, const void* w_down, void* act, void* h,
+                   void* o_perm, moe_stream_t stream) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  REQ(x); REQ(x_perm); REQ(offsets); REQ(act); REQ(h); REQ(o_perm);
+  if (groups(*cfg) > 0) { REQ(w_gate); REQ(w_up); REQ(w_down); }
+  if (cfg->T == 0 || groups(*cfg) == 0) return MOE_OK;
+  hipStream_t st = (hipStream_t)stream;
+  if ((rc = gemm_swiglu_fwd(*cfg, x, x_perm, offsets, w_gate, w_up, act, h, st))) return rc;
+  return gemm_down_fwd(*cfg, offsets, h, w_down, o_perm, st);
+}
+
+int moe_combine(const moe_config* cfg, const void* o_perm, const int32_t* offsets,
+                const int32_t* slot_row, const float* topk_w, void* y, moe_stream_t stream) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  REQ(o_perm); REQ(offsets); REQ(slot_row); REQ(topk_w); REQ(y);
+  if (cfg->T == 0) return MOE_OK;
+  return launch_combine(*cfg, o_perm, offsets, slot_row, topk_w, y, (hipStream_t)stream);
+}
+
+int aux_balance_loss(const moe_config* cfg, const float* logits, const int32_t* counts_all,
+                     float alpha, float z_lambda, float* losses, float* d_logits, void* ws,
+                     size_t ws_bytes, moe_stream_t stream) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (cfg->score_fn != MOE_SCORE_SOFTMAX) return MOE_EINVAL;
+  if (!std::isfinite(alpha) || !std::isfinite(z_lambda)) return MOE_EINVAL;
+  REQ(logits); REQ(counts_all); REQ(losses); OPT(d_logits); REQ(ws);
+  const Workspace L = workspace_layout(*cfg);
+  if (ws_bytes < L.total) return MOE_EWORKSPACE;
+  if (cfg->T == 0) return MOE_OK;
+  return launch_aux(*cfg, logits, counts_all, alpha, z_lambda, losses, d_logits, (char*)ws, L,
+                    (hipStream_t)stream);
+}
+
+int moe_backward(const moe_config* cfg, const void* x, const float* w_r, const float* logits,
+                 const int32_t* topk_idx, const float* topk_w, const int32_t* offsets,
+                 const int32_t* slot_row, const void* x_perm, const void* act, const void* h,
+                 const void* o_perm, const void* w_gate, const void* w_up, const void* w_down,
+                 const void* dy, const float* d_logits_extra, void* dx, float* dw_r,
+                 float* d_rbias, void* dw_gate, void* dw_up, void* dw_down, float* d_logits_out,
+                 void* ws, size_t ws_bytes, moe_stream_t stream) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  REQ(x); REQ(w_r); REQ(logits); REQ(topk_idx); REQ(topk_w); REQ(offsets); REQ(slot_row);
+  REQ(x_perm); REQ(act); REQ(h); REQ(o_perm); REQ(dy);
+  OPT(d_logits_extra); REQ(dx); REQ(dw_r); OPT(d_rbias); OPT(d_logits_out); REQ(ws);
+  if (groups(*cfg) > 0) {
+    REQ(w_gate); REQ(w_up); REQ(w_down); REQ(dw_gate); REQ(dw_up); REQ(dw_down);
+  }
+  const Workspace L = workspace_layout(*cfg);
+  if (ws_bytes < L.total) return MOE_EWORKSPACE;
+  if (cfg->T == 0) return MOE_OK;
+  return launch_backward(*cfg, x, w_r, logits, topk_idx, topk_w, offsets, slot_row, x_perm, act,
+                         h, o_perm, w_gate, w_up, w_down, dy, d_logits_extra, dx, dw_r, d_rbias,
+                         dw_gate, dw_up, dw_down, d_logits_out, (char*)ws, L, (hipStream_t)stream);
+}
+
+const char* moe_error_string(int code) {
+  switch (code) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument (size, range, enum or NULL pointer)";
+    case MOE_EALIGN: return "pointer not 16-byte aligned";
+    case MOE_EDTYPE: return "unsupported dtype";
+    case MOE_ELAUNCH: return g_err[0] ? g_err : "HIP launch failed";
+    case MOE_EWORKSPACE: return "workspace smaller than moe_workspace_size()";
+    default: return "unknown error code";
+  }
+}
+
+int moe_timing_enable(int32_t on) {
+  g_timing = on != 0;
+  return MOE_OK;
+}
+
+int moe_timing_report(char* buf, size_t len) {
+  if (!buf || len == 0) return MOE_EINVAL;
+  std::map<std::string, std::pair<int, double>> agg;
+  std::vector<std::string> order;
+  for (auto& r : g_records) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) == hipSuccess && hipEventElapsedTime(&ms, r.a, r.b) == hipSuccess) {
+      if (!agg.count(r.name)) order.push_back(r.name);
+      agg[r.name].first += 1;
+      agg[r.name].second += ms;
+    }
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  g_records.clear();
+  std::string out;
+  for (auto& n : order) {
+    char line[256];
+    snprintf(line, sizeof line, "%s\t%d\t%.6f\n", n.c_str(), agg[n].first, agg[n].second);
+    out += line;
+  }
+  strncpy(buf, out.c_str(), len - 1);
+  buf[len - 1] = 0;
+  return MOE_OK;
+}
+
+}  // extern "C"

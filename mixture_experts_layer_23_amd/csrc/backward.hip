@@ -1,0 +1,378 @@
+// backward.hip -- gating backward, router backward and the order of the
+// backward kernels.
+//
+// [P5] course notes 8.3: the top-K indices are piecewise constant, so the
+// router learns only through the continuous gate weights g; with gating B and
+// K = 1 the single weight is identically 1 and the router gets no gradient
+// from the layer output.  [P2] section 2 states the same for MiniMind's
+// renormalised top-1.  [P1] cause section: sentinel slots must carry a zero
+// expert output so that their gate weights receive no gradient.
+//
+// Gating backward in centred form (G = sum_k g_k dg_k):
+//   softmax A: ds_i = p_i (sum_{k: i_k = i} dg_k - G)
+//   softmax B: ds_{i_k} = g_k (dg_k - G); every other ds_i = 0
+//   sigmoid A: ds_{i_k} = dg_k sig(1 - sig)
+//   sigmoid B: ds_{i_k} = ((dg_k - G) / sum_j sig_{i_j}) sig(1 - sig)
+// The centred form keeps the exact zeros: K = 1 with B gives 1*(dg - dg) = 0.
+// Router backward: dx += ds W_r; dW_r = ds^T x; d r_b = sum_t ds_t.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+int launch_combine_bwd(const moe_config& c, const void* o_perm, const void* dy,
+                       const int32_t* slot_row, const float* topk_w, float* dg, void* d_o,
+                       hipStream_t st);
+int launch_unpermute(const moe_config& c, const void* dxp, const int32_t* slot_row,
+                     const int32_t* offsets, const float* ds, const float* wr, const float* dxr,
+                     void* dx, hipStream_t st);
+
+// L lanes per token (L = min(64, pow2ceil(E))), EPL experts per lane
+template <int L, int EPL>
+__global__ __launch_bounds__(256) void gating_bwd_kernel(
+    const float* __restrict__ logits, const int32_t* __restrict__ idx,
+    const float* __restrict__ gw, const float* __restrict__ dg, const float* __restrict__ dlx,
+    int T_, int E, int K, int score, int gating, float* __restrict__ ds,
+    float* __restrict__ ds_copy) {
+  const int gid = blockIdx.x * blockDim.x + threadIdx.x;
+  const int t = gid / L, sub = gid % L;
+  if (t >= T_) return;
+  const float* s = logits + (size_t)t * E;
+  const int32_t* it = idx + (size_t)t * K;
+  const float* g = gw + (size_t)t * K;
+  const float* d = dg + (size_t)t * K;
+  float G = 0.f;
+  for (int k = 0; k < K; ++k) G = fmaf(g[k], d[k], G);
+  float out[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) out[j] = 0.f;
+  if (score == 0 && gating == 0) {
+    float sv[EPL], m = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const int e = sub + L * j;
+      sv[j] = (e < E) ? s[e] : -INFINITY;
+      m = fmaxf(m, sv[j]);
+    }
+#pragma unroll
+    for (int o = L / 2; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    float z = 0.f;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j)
+      if (sub + L * j < E) z += expf(sv[j] - m);
+#pragma unroll
+    for (int o = L / 2; o >= 1; o >>= 1) z += __shfl_xor(z, o, 64);
+    float dp[EPL];
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) dp[j] = 0.f;
+    for (int k = 0; k < K; ++k) {
+      const int e = it[k];
+      if ((e % L) == sub) {
+        const int jj = e / L;
+#pragma unroll
+        for (int j = 0; j < EPL; ++j)
+          if (j == jj) dp[j] += d[k];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < EPL; ++j)
+      if (sub + L * j < E) out[j] = (expf(sv[j] - m) / z) * (dp[j] - G);
+  } else {
+    float S = 0.f;
+    if (score == 1 && gating == 1)
+      for (int k = 0; k < K; ++k) S += 1.0f / (1.0f + expf(-s[it[k]]));
+    for (int k = 0; k < K; ++k) {
+      const int e = it[k];
+      if ((e % L) != sub) continue;
+      float v;
+      if (score == 0) {
+        v = g[k] * (d[k] - G);
+      } else {
+        const float sg = 1.0f / (1.0f + expf(-s[e]));
+        const float dsig = sg * (1.0f - sg);
+        v = (gating == 0) ? d[k] * dsig : ((d[k] - G) / S) * dsig;
+      }
+      const int jj = e / L;
+#pragma unroll
+      for (int j = 0; j < EPL; ++j)
+        if (j == jj) out[j] = v;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const int e = sub + L * j;
+    if (e >= E) continue;
+    float v = out[j];
+    if (dlx) v += dlx[(size_t)t * E + e];
+    ds[(size_t)t * E + e] = v;
+    if (ds_copy) ds_copy[(size_t)t * E + e] = v;
+  }
+}
+
+template <int L, int EPL>
+static int launch_gating_bwd_t(const moe_config& c, const float* lg, const int32_t* idx,
+                               const float* gw, const float* dg, const float* dlx, float* ds,
+                               float* ds_copy, hipStream_t st) {
+  const int grid = (int)cdiv((int64_t)c.T * L, 256);
+  MOE_LAUNCH("gating_bwd", (gating_bwd_kernel<L, EPL>), dim3(grid), dim3(256), 0, st, lg, idx,
+             gw, dg, dlx, c.T, c.E, c.K, c.score_fn, c.gating, ds, ds_copy);
+  return MOE_OK;
+}
+
+static int launch_gating_bwd(const moe_config& c, const float* lg, const int32_t* idx,
+                             const float* gw, const float* dg, const float* dlx, float* ds,
+                             float* ds_copy, hipStream_t st) {
+  const int E = c.E;
+#define GB(Lv, Ev) return launch_gating_bwd_t<Lv, Ev>(c, lg, idx, gw, dg, dlx, ds, ds_copy, st)
+  if (E <= 1) GB(1, 1);
+  if (E <= 2) GB(2, 1);
+  if (E <= 4) GB(4, 1);
+  if (E <= 8) GB(8, 1);
+  if (E <= 16) GB(16, 1);
+  if (E <= 32) GB(32, 1);
+  if (E <= 64) GB(64, 1);
+  if (E <= 128) GB(64, 2);
+  if (E <= 256) GB(64, 4);
+  if (E <= 512) GB(64, 8);
+  GB(64, 16);
+#undef GB
+}
+
+// ---------------------------------------------------------------------------
+// router weight gradient, few experts (E <= 16): each thread owns 4
+// consecutive model dims and sums ds[t,e] * x[t,d] over a chunk of
+// kRouterChunk tokens (ds rows of the chunk staged in LDS); per-chunk partials
+// are reduced in a fixed order afterwards.  Chunk 0's d-block 0 also sums the
+// router-bias gradient partial.
+// ---------------------------------------------------------------------------
+constexpr int kRouterChunk = 256;
+
+template <typename T, int EM>
+__global__ __launch_bounds__(256) void router_wgrad_skinny_kernel(
+    const float* __restrict__ ds, const T* __restrict__ x, int T_, int D, int E,
+    float* __restrict__ part) {
+  __shared__ float sds[kRouterChunk * EM];
+  const int chunk = blockIdx.y;
+  const int t0 = chunk * kRouterChunk;
+  const int nt = min(kRouterChunk, T_ - t0);
+  for (int i = threadIdx.x; i < nt * E; i += blockDim.x) sds[i] = ds[(size_t)t0 * E + i];
+  __syncthreads();
+  const int d0 = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  float acc[EM][4];
+  float accb[EM];
+#pragma unroll
+  for (int e = 0; e < EM; ++e) {
+    accb[e] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[e][i] = 0.f;
+  }
+  if (d0 < D) {
+    for (int t = 0; t < nt; ++t) {
+      float xv[4];
+      const T* xp = x + (size_t)(t0 + t) * D + d0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xv[i] = Elem<T>::to_f32(xp[i]);
+#pragma unroll
+      for (int e = 0; e < EM; ++e) {
+        if (e < E) {
+          const float s = sds[t * E + e];
+          accb[e] += s;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[e][i] = fmaf(s, xv[i], acc[e][i]);
+        }
+      }
+    }
+    float* p = part + (size_t)chunk * (E * D + E);
+#pragma unroll
+    for (int e = 0; e < EM; ++e)
+      if (e < E)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[(size_t)e * D + d0 + i] = acc[e][i];
+    if (d0 == 0)
+#pragma unroll
+      for (int e = 0; e < EM; ++e)
+        if (e < E) p[(size_t)E * D + e] = accb[e];
+  }
+}
+
+// fixed-order sum of the split partials: out[i] = sum_s part[s][i]
+__global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restrict__ part,
+                                                            int nsplit, int64_t n,
+                                                            int64_t stride, float* __restrict__ out,
+                                                            float* __restrict__ out2,
+                                                            int64_t n_first) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  float s = 0.f;
+  for (int k = 0; k < nsplit; ++k) s += part[(size_t)k * stride + i];
+  if (i < n_first) out[i] = s;
+  else if (out2) out2[i - n_first] = s;
+}
+
+// ---------------------------------------------------------------------------
+// router GEMMs for many experts: SIMT fp32 tiles of 64 x 64, k-slabs of 16 in
+// LDS, 4 x 4 register micro-tile, optional split over k (partials).
+//   C[split][m][n] = sum_{k in split} A(m,k) B(k,n)
+//   A(m,k) = AKC ? A[m*lda + k] : A[k*lda + m];  B(k,n) = B[k*ldb + n]
+// ---------------------------------------------------------------------------
+template <typename TA, typename TB, bool AKC>
+__global__ __launch_bounds__(256) void simt_gemm_kernel(const TA* __restrict__ A, int64_t lda,
+                                                        const TB* __restrict__ B, int64_t ldb,
+                                                        int M, int N, int Kd, int kper,
+                                                        float* __restrict__ C, int64_t ldc,
+                                                        int64_t split_stride) {
+  __shared__ float sa[16][65];
+  __shared__ float sb[16][65];
+  const int m0 = blockIdx.x * 64, n0 = blockIdx.y * 64, split = blockIdx.z;
+  const int kb = split * kper, ke = min(Kd, kb + kper);
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  float acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+  for (int k0 = kb; k0 < ke; k0 += 16) {
+    float av[4], bv[4];
+    if (AKC) {  // thread -> (m = tid/4, k = (tid%4)*4 + i)
+      const int m = m0 + (threadIdx.x >> 2), kk = (threadIdx.x & 3) * 4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int k = k0 + kk + i;
+        av[i] = (m < M && k < ke) ? Elem<TA>::to_f32(A[(int64_t)m * lda + k]) : 0.f;
+      }
+    } else {  // thread -> (k = tid/16, m = (tid%16)*4 + i)
+      const int k = k0 + (threadIdx.x >> 4), mm = (threadIdx.x & 15) * 4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + mm + i;
+        av[i] = (m < M && k < ke) ? Elem<TA>::to_f32(A[(int64_t)k * lda + m]) : 0.f;
+      }
+    }
+    {
+      const int k = k0 + (threadIdx.x >> 4), nn = (threadIdx.x & 15) * 4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int n = n0 + nn + i;
+        bv[i] = (n < N && k < ke) ? Elem<TB>::to_f32(B[(int64_t)k * ldb + n]) : 0.f;
+      }
+    }
+    __syncthreads();
+    if (AKC) {
+      const int mm = threadIdx.x >> 2, kk = (threadIdx.x & 3) * 4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sa[kk + i][mm] = av[i];
+    } else {
+      const int kk = threadIdx.x >> 4, mm = (threadIdx.x & 15) * 4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sa[kk][mm + i] = av[i];
+    }
+    {
+      const int kk = threadIdx.x >> 4, nn = (threadIdx.x & 15) * 4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sb[kk][nn + i] = bv[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { a[i] = sa[k][ty + 16 * i]; b[i] = sb[k][tx + 16 * i]; }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+  }
+  float* Cs = C + (int64_t)split * split_stride;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + ty + 16 * i;
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + tx + 16 * j;
+      if (n < N) Cs[(int64_t)m * ldc + n] = acc[i][j];
+    }
+  }
+}
+
+// d r_b[e] = sum_t ds[t,e] (fixed order), one thread per expert
+__global__ void rbias_grad_kernel(const float* __restrict__ ds, int T_, int E,
+                                  float* __restrict__ drb) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= E) return;
+  float s = 0.f;
+  for (int t = 0; t < T_; ++t) s += ds[(size_t)t * E + e];
+  drb[e] = s;
+}
+
+template <typename T>
+static int router_bwd_t(const moe_config& c, const void* x, const float* wr, const float* ds,
+                        float* dxr, float* dwr, float* drb, char* ws, const Workspace& L,
+                        hipStream_t st) {
+  const int E = c.E, D = c.D, T_ = c.T;
+  float* part = reinterpret_cast<float*>(ws + L.dwr_part);
+  if (E <= 16) {
+    const int nchunk = (int)cdiv(T_, kRouterChunk);
+    dim3 grid((unsigned)cdiv(D / 4, 256), (unsigned)nchunk);
+#define RW(EMV)                                                                               \
+  MOE_LAUNCH("router_wgrad", (router_wgrad_skinny_kernel<T, EMV>), grid, dim3(256), 0, st, ds, \
+             (const T*)x, T_, D, E, part)
+    if (E <= 4) RW(4);
+    else if (E <= 8) RW(8);
+    else RW(16);
+#undef RW
+    const int64_t n = (int64_t)E * D + E;
+    MOE_LAUNCH("router_wgrad_reduce", reduce_splits_kernel, dim3((unsigned)cdiv(n, 256)),
+               dim3(256), 0, st, part, nchunk, n, n, dwr, drb, (int64_t)E * D);
+  } else {
+    // dxr[T,D] = ds[T,E] W_r[E,D]
+    dim3 g1((unsigned)cdiv(T_, 64), (unsigned)cdiv(D, 64), 1);
+    MOE_LAUNCH("router_dgrad", (simt_gemm_kernel<float, float, true>), g1, dim3(256), 0, st, ds,
+               (int64_t)E, wr, (int64_t)D, T_, D, E, E, dxr, (int64_t)D, (int64_t)0);
+    // dW_r[E,D] = ds^T x, split over tokens
+    const int splits = L.dwr_splits;
+    const int kper = (int)(cdiv(cdiv(T_, splits), 16) * 16);
+    dim3 g2((unsigned)cdiv(E, 64), (unsigned)cdiv(D, 64), (unsigned)splits);
+    MOE_LAUNCH("router_wgrad", (simt_gemm_kernel<float, T, false>), g2, dim3(256), 0, st, ds,
+               (int64_t)E, (const T*)x, (int64_t)D, E, D, T_, kper, part, (int64_t)D,
+               (int64_t)E * D);
+    const int64_t n = (int64_t)E * D;
+    MOE_LAUNCH("router_wgrad_reduce", reduce_splits_kernel, dim3((unsigned)cdiv(n, 256)),
+               dim3(256), 0, st, part, splits, n, n, dwr, (float*)nullptr, n);
+    if (drb)
+      MOE_LAUNCH("router_bias_grad", rbias_grad_kernel, dim3((unsigned)cdiv(E, 256)), dim3(256),
+                 0, st, ds, T_, E, drb);
+  }
+  return MOE_OK;
+}
+
+int launch_backward(const moe_config& c, const void* x, const float* wr, const float* logits,
+                    const int32_t* idx, const float* topk_w, const int32_t* offsets,
+                    const int32_t* slot_row, const void* x_perm, const void* act, const void* h,
+                    const void* o_perm, const void* wg, const void* wu, const void* wd,
+                    const void* dy, const float* dlx, void* dx, float* dwr, float* drb,
+                    void* dwg, void* dwu, void* dwd, float* d_logits_out, char* ws,
+                    const Workspace& L, hipStream_t st) {
+  void* d_o = ws + L.d_o;
+  void* dact = ws + L.dact;
+  void* dxp = ws + L.dx_perm;
+  float* dg = reinterpret_cast<float*>(ws + L.dg);
+  float* ds = reinterpret_cast<float*>(ws + L.ds);
+  float* dxr = (c.E > 16) ? reinterpret_cast<float*>(ws + L.dxr) : nullptr;
+  int rc;
+  if ((rc = launch_combine_bwd(c, o_perm, dy, slot_row, topk_w, dg, d_o, st))) return rc;
+  if ((rc = launch_gating_bwd(c, logits, idx, topk_w, dg, dlx, ds, d_logits_out, st))) return rc;
+  if ((rc = gemm_down_dgrad(c, offsets, d_o, dy, wd, act, dact, st))) return rc;
+  if ((rc = gemm_down_wgrad(c, offsets, h, d_o, dy, dwd, st))) return rc;
+  if ((rc = gemm_up_dgrad(c, offsets, dact, wg, wu, dxp, st))) return rc;
+  if ((rc = gemm_up_wgrad(c, offsets, x, x_perm, dact, dwg, dwu, st))) return rc;
+  if (c.dtype == MOE_BF16) {
+    if ((rc = router_bwd_t<bf16_t>(c, x, wr, ds, dxr, dwr, drb, ws, L, st))) return rc;
+  } else {
+    if ((rc = router_bwd_t<float>(c, x, wr, ds, dxr, dwr, drb, ws, L, st))) return rc;
+  }
+  return launch_unpermute(c, dxp, slot_row, offsets, ds, wr, dxr, dx, st);
+}
+
+}  // namespace moe

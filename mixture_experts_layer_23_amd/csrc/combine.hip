@@ -1,0 +1,232 @@
+// combine.hip -- weighted combine back to token order, its backward, and the
+// un-permute reduction of the row gradients.
+//
+// [P5] course notes 8.8: after the expert matmuls the outputs are multiplied
+// by their gate weights and scattered back with index_add -- a token appears
+// once per selected expert, so its contributions accumulate; 8.7: the shared
+// expert is added with weight 1.  [P1] cause section: the gradient of a gate
+// weight is the expert output (proj_out) of that slot, which is zero for a
+// slot this device does not serve (sentinel) -- and, by the same rule, for a
+// dropped slot.
+//
+// All three kernels are HBM-bound row streams: 16-byte vector loads, fp32
+// accumulation in a fixed k order (no atomics, deterministic).
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+// y[t] = sum_k [row>=0] g[t,k] * o[row] + o[shared row of t]
+template <typename T>
+__global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ o,
+                                                      const int32_t* __restrict__ slot_row,
+                                                      const float* __restrict__ topk_w,
+                                                      const int32_t* __restrict__ offsets,
+                                                      int EL, int n_shared, int T_, int K, int D,
+                                                      int nv, T* __restrict__ y) {
+  constexpr int VEC = Elem<T>::VEC;
+  const int64_t total = (int64_t)T_ * nv;
+  const int64_t b0 = (int64_t)blockIdx.x * 1024 + threadIdx.x;
+  const int shared0 = n_shared ? offsets[EL] : 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t it = b0 + u * 256;
+    if (it >= total) break;
+    const int t = (int)(it / nv);
+    const int c = (int)(it - (int64_t)t * nv);
+    float acc[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
+    for (int k = 0; k < K; ++k) {
+      const int row = slot_row[(size_t)t * K + k];
+      if (row < 0) continue;
+      const float g = topk_w[(size_t)t * K + k];
+      Vec16<T> v;
+      v.load(o + (size_t)row * D + (size_t)c * VEC);
+      float f[VEC];
+      v.to_f32(f);
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) acc[i] = fmaf(g, f[i], acc[i]);
+    }
+    if (n_shared) {
+      Vec16<T> v;
+      v.load(o + (size_t)(shared0 + t) * D + (size_t)c * VEC);
+      float f[VEC];
+      v.to_f32(f);
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) acc[i] += f[i];
+    }
+    Vec16<T> out;
+    out.from_f32(acc);
+    out.store(y + (size_t)t * D + (size_t)c * VEC);
+  }
+}
+
+// one wave per token: dg[t,k] = dy_t . o[row] (0 for sentinel / dropped),
+// d_o[row] = g[t,k] * dy_t
+template <typename T>
+__global__ __launch_bounds__(256) void combine_bwd_kernel(const T* __restrict__ o,
+                                                          const T* __restrict__ dy,
+                                                          const int32_t* __restrict__ slot_row,
+                                                          const float* __restrict__ topk_w,
+                                                          int T_, int K, int D,
+                                                          float* __restrict__ dg,
+                                                          T* __restrict__ d_o) {
+  constexpr int VEC = Elem<T>::VEC;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= T_) return;
+  for (int k = 0; k < K; ++k) {
+    const int row = slot_row[(size_t)t * K + k];
+    if (row < 0) {  // uniform across the wave
+      if (lane == 0) dg[(size_t)t * K + k] = 0.f;
+      continue;
+    }
+    const float g = topk_w[(size_t)t * K + k];
+    float dot = 0.f;
+    for (int d0 = lane * VEC; d0 < D; d0 += 64 * VEC) {
+      Vec16<T> vy, vo;
+      vy.load(dy + (size_t)t * D + d0);
+      vo.load(o + (size_t)row * D + d0);
+      float fy[VEC], fo[VEC], fd[VEC];
+      vy.to_f32(fy);
+      vo.to_f32(fo);
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) {
+        dot = fmaf(fy[i], fo[i], dot);
+        fd[i] = g * fy[i];
+      }
+      Vec16<T> vd;
+      vd.from_f32(fd);
+      vd.store(d_o + (size_t)row * D + d0);
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) dot += __shfl_xor(dot, m, 64);
+    if (lane == 0) dg[(size_t)t * K + k] = dot;
+  }
+}
+
+// dx[t] = sum_k [row>=0] dx_perm[row] + dx_perm[shared row of t]
+//         + router part: sum_e ds[t,e] W_r[e,:] (inline for E <= EM) or dxr[t]
+template <typename T, int EM>
+__global__ __launch_bounds__(256) void unpermute_kernel(
+    const T* __restrict__ dxp, const int32_t* __restrict__ slot_row,
+    const int32_t* __restrict__ offsets, int EL, int n_shared, const float* __restrict__ ds,
+    const float* __restrict__ wr, int E, const float* __restrict__ dxr, int T_, int K, int D,
+    int nv, T* __restrict__ dx) {
+  constexpr int VEC = Elem<T>::VEC;
+  const int64_t total = (int64_t)T_ * nv;
+  const int64_t b0 = (int64_t)blockIdx.x * 1024 + threadIdx.x;
+  const int shared0 = n_shared ? offsets[EL] : 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t it = b0 + u * 256;
+    if (it >= total) break;
+    const int t = (int)(it / nv);
+    const int c = (int)(it - (int64_t)t * nv);
+    const int d0 = c * VEC;
+    float acc[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
+    for (int k = 0; k < K; ++k) {
+      const int row = slot_row[(size_t)t * K + k];
+      if (row < 0) continue;
+      Vec16<T> v;
+      v.load(dxp + (size_t)row * D + d0);
+      float f[VEC];
+      v.to_f32(f);
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) acc[i] += f[i];
+    }
+    if (n_shared) {
+      Vec16<T> v;
+      v.load(dxp + (size_t)(shared0 + t) * D + d0);
+      float f[VEC];
+      v.to_f32(f);
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) acc[i] += f[i];
+    }
+    if constexpr (EM > 0) {
+#pragma unroll
+      for (int e = 0; e < EM; ++e) {
+        if (e < E) {
+          const float s = ds[(size_t)t * E + e];
+          const float* w = wr + (size_t)e * D + d0;
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) acc[i] = fmaf(s, w[i], acc[i]);
+        }
+      }
+    } else {
+      const float* r = dxr + (size_t)t * D + d0;
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) acc[i] += r[i];
+    }
+    Vec16<T> out;
+    out.from_f32(acc);
+    out.store(dx + (size_t)t * D + d0);
+  }
+}
+
+int launch_combine(const moe_config& c, const void* o_perm, const int32_t* offsets,
+                   const int32_t* slot_row, const float* topk_w, void* y, hipStream_t st) {
+  const int EL = c.expert_hi - c.expert_lo;
+  if (c.dtype == MOE_BF16) {
+    const int nv = c.D / 8;
+    const int grid = (int)cdiv((int64_t)c.T * nv, 1024);
+    MOE_LAUNCH("combine", combine_kernel<bf16_t>, dim3(grid), dim3(256), 0, st,
+               (const bf16_t*)o_perm, slot_row, topk_w, offsets, EL, c.n_shared, c.T, c.K, c.D,
+               nv, (bf16_t*)y);
+  } else {
+    const int nv = c.D / 4;
+    const int grid = (int)cdiv((int64_t)c.T * nv, 1024);
+    MOE_LAUNCH("combine", combine_kernel<float>, dim3(grid), dim3(256), 0, st,
+               (const float*)o_perm, slot_row, topk_w, offsets, EL, c.n_shared, c.T, c.K, c.D,
+               nv, (float*)y);
+  }
+  return MOE_OK;
+}
+
+int launch_combine_bwd(const moe_config& c, const void* o_perm, const void* dy,
+                       const int32_t* slot_row, const float* topk_w, float* dg, void* d_o,
+                       hipStream_t st) {
+  const int grid = (int)cdiv(c.T, 4);
+  if (c.dtype == MOE_BF16)
+    MOE_LAUNCH("combine_bwd", combine_bwd_kernel<bf16_t>, dim3(grid), dim3(256), 0, st,
+               (const bf16_t*)o_perm, (const bf16_t*)dy, slot_row, topk_w, c.T, c.K, c.D, dg,
+               (bf16_t*)d_o);
+  else
+    MOE_LAUNCH("combine_bwd", combine_bwd_kernel<float>, dim3(grid), dim3(256), 0, st,
+               (const float*)o_perm, (const float*)dy, slot_row, topk_w, c.T, c.K, c.D, dg,
+               (float*)d_o);
+  return MOE_OK;
+}
+
+template <typename T>
+static int unpermute_t(const moe_config& c, const void* dxp, const int32_t* slot_row,
+                       const int32_t* offsets, const float* ds, const float* wr,
+                       const float* dxr, void* dx, hipStream_t st) {
+  const int EL = c.expert_hi - c.expert_lo;
+  const int nv = c.D / Elem<T>::VEC;
+  const int grid = (int)cdiv((int64_t)c.T * nv, 1024);
+  const int E = c.E;
+#define UNPERM(EMV)                                                                          \
+  MOE_LAUNCH("unpermute_dx", (unpermute_kernel<T, EMV>), dim3(grid), dim3(256), 0, st,        \
+             (const T*)dxp, slot_row, offsets, EL, c.n_shared, ds, wr, E, dxr, c.T, c.K, c.D, \
+             nv, (T*)dx)
+  if (dxr) UNPERM(0);
+  else if (E <= 4) UNPERM(4);
+  else if (E <= 8) UNPERM(8);
+  else UNPERM(16);
+#undef UNPERM
+  return MOE_OK;
+}
+
+int launch_unpermute(const moe_config& c, const void* dxp, const int32_t* slot_row,
+                     const int32_t* offsets, const float* ds, const float* wr, const float* dxr,
+                     void* dx, hipStream_t st) {
+  if (c.dtype == MOE_BF16)
+    return unpermute_t<bf16_t>(c, dxp, slot_row, offsets, ds, wr, dxr, dx, st);
+  return unpermute_t<float>(c, dxp, slot_row, offsets, ds, wr, dxr, dx, st);
+}
+
+}  // namespace moe

@@ -1,0 +1,587 @@
+// gemm.hip -- grouped GEMMs of the expert FFNs (forward and backward) on
+// CDNA4 matrix cores.
+//
+// [P5] course notes 8.1 (SwiGLU expert: a = x W_gate, b = x W_up,
+// h = silu(a) * b, o = h W_down), 8.8 (the production form is a grouped GEMM
+// over the per-expert row blocks instead of a Python loop); [P3] efficient
+// inference (after grouping, each expert sees one dense batch).
+//
+// One kernel template covers the six GEMMs of the layer:
+//   forward  GEMM1: [a|b] = X_g W_{gate|up}[g]    + SwiGLU epilogue (h, a, b)
+//            GEMM2: o = h W_down[g]
+//   backward dgrad2: dh = d_o W_down[g]^T          + SwiGLU-backward epilogue
+//            wgrad2: dW_down[g] = h^T d_o           (reduction over the rows)
+//            dgrad1: dx_perm = da W_gate^T + db W_up^T
+//            wgrad1: dW_gate|up[g] = X^T [da|db]
+// Groups are the local experts (row ranges from the permutation offsets,
+// read on the device: no host synchronisation) plus the shared expert, whose
+// rows are the tokens themselves (it reads x / dy directly).
+//
+// Tile: 128 x 128 outputs, 256 threads = 4 waves (2 x 2), each wave 64 x 64
+// as 2 x 2 blocks of v_mfma_f32_32x32x16_bf16 (fp32: 4 x v_mfma_f32_32x32x2f32
+// per 16-byte fragment).  K-slabs of 128 bytes per row (64 bf16 / 32 fp32)
+// are double-buffered in LDS; the k-chunks of 16 bytes are XOR-swizzled by
+// row so that both the transposing stores and the fragment reads are free of
+// bank conflicts.  Operands stored with K contiguous are copied as 16-byte
+// vectors; operands stored with M/N contiguous are loaded as coalesced
+// 16-byte row vectors and transposed in registers (4 k x VEC) before the LDS
+// store.  Workgroup ids are remapped so that consecutive tiles (same rows,
+// same expert weights) land on the same XCD and share its L2.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kBM = 128, kBN = 128, kThreads = 256;
+
+enum OpMode { KC = 0, MC = 1 };  // K contiguous / M (or N) contiguous in memory
+enum Grouping { GROUP_M = 0, GROUP_K = 1 };
+enum Epi { EPI_STORE = 0, EPI_SWIGLU_FWD = 1, EPI_SWIGLU_BWD = 2 };
+enum BSplit { BS_NONE = 0, BS_N = 1, BS_K = 2 };
+
+struct GemmParams {
+  int G;              // groups (local experts + shared)
+  int EL_A, EL_B;     // groups >= EL_A (EL_B) read A (B) from the shared pointer
+  const int32_t* offsets;
+  int N;              // output columns (for BS_N: 2 * width of each half)
+  int Kdim;           // reduction length for GROUP_M
+  int Mfix;           // output rows for GROUP_K
+  int ntn, ntm;       // tiles along N (and M for GROUP_K)
+  int64_t nblocks;
+  // A operand: routed pointer (rows at offsets[g]) and shared pointer (row 0)
+  const void* A;
+  const void* A_sh;
+  int64_t lda;
+  // B operand: group g at B + g * strideB (two halves for BS_N / BS_K)
+  const void* B0;
+  const void* B1;
+  int64_t ldb, strideB;
+  int bsplit;         // BS_N: columns per half; BS_K: k where B1 starts
+  // outputs
+  void* C0;
+  void* C1;           // second half (wgrad1 dW_up) or SwiGLU h
+  int64_t ldc;
+  int csplit;         // columns of C0 before C1 (wgrad1)
+  int64_t strideC;    // per-group stride of C (GROUP_K)
+  const void* act;    // SwiGLU-backward input [rows][2F]
+  void* act_out;      // SwiGLU forward a|b output [rows][2F]
+  int F;
+};
+
+MOE_DEV int swz(int row) { return (row ^ (row >> 3)) & 7; }
+
+// XCD-aware remap: hardware places workgroup b on XCD b % 8; give each XCD a
+// contiguous range of logical tiles.
+MOE_DEV int64_t remap_xcd(int64_t b, int64_t n) {
+  const int64_t q = n / 8, r = n % 8;
+  const int64_t x = b % 8, i = b / 8;
+  return (x < r) ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
+}
+
+// wave-parallel search of the group holding global m-tile mt (GROUP_M)
+MOE_DEV bool find_group(const int32_t* offsets, int G, int mt, int& g_out, int& mt_local) {
+  const int lane = threadIdx.x & 63;
+  const int gpl = (G + 63) / 64;
+  int mine = 0;
+  for (int j = 0; j < gpl; ++j) {
+    const int g = lane * gpl + j;
+    if (g < G) mine += (offsets[g + 1] - offsets[g] + kBM - 1) / kBM;
+  }
+  int incl = mine;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
+  }
+  const int excl = incl - mine;
+  const uint64_t hit = __ballot(mt >= excl && mt < incl);
+  if (hit == 0) return false;
+  const int owner = __ffsll((unsigned long long)hit) - 1;
+  int gsel = 0, base = 0;
+  if (lane == owner) {
+    int run = excl;
+    for (int j = 0; j < gpl; ++j) {
+      const int g = lane * gpl + j;
+      if (g >= G) break;
+      const int n = (offsets[g + 1] - offsets[g] + kBM - 1) / kBM;
+      if (mt < run + n) { gsel = g; base = run; break; }
+      run += n;
+    }
+  }
+  g_out = __shfl(gsel, owner, 64);
+  mt_local = mt - __shfl(base, owner, 64);
+  return true;
+}
+
+template <typename T>
+struct Frag;
+template <>
+struct Frag<bf16_t> {
+  static constexpr int BK = 64, KSTEP = 16, VEC = 8;
+};
+template <>
+struct Frag<float> {
+  static constexpr int BK = 32, KSTEP = 8, VEC = 4;
+};
+
+// One operand tile (128 rows x BK) : global -> registers -> LDS.
+// Element (r, k) of the tile (r = output row for A / output column for B).
+template <typename T, int MODE>
+struct TileLoader {
+  static constexpr int VEC = Frag<T>::VEC, BK = Frag<T>::BK;
+  uint4 reg[4];
+  // KC: element (r,k) at p[r*ld + k]; thread loads vectors v = tid + 256*i:
+  //     row v / 8, chunk v % 8.
+  // MC: element (r,k) at p[k*ld + r]; thread loads rows k = kg*4 + j of the
+  //     VEC columns mg*VEC.., kg = tid / MG, mg = tid % MG, MG = 128 / VEC.
+  MOE_DEV void load(const T* p, int64_t ld, int r_valid, int k0, int k_valid) {
+    const int tid = threadIdx.x;
+    if constexpr (MODE == KC) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int v = tid + 256 * i, r = v >> 3, ch = v & 7;
+        const int k = k0 + ch * VEC;
+        if (r < r_valid && k < k_valid)
+          reg[i] = *reinterpret_cast<const uint4*>(p + (int64_t)r * ld + k);
+        else
+          reg[i] = make_uint4(0, 0, 0, 0);
+      }
+    } else {
+      constexpr int MG = 128 / VEC;
+      const int kg = tid / MG, mg = tid % MG;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int k = k0 + kg * 4 + j, r = mg * VEC;
+        if (k < k_valid && r < r_valid)
+          reg[j] = *reinterpret_cast<const uint4*>(p + (int64_t)k * ld + r);
+        else
+          reg[j] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  }
+  // for BS_N (SwiGLU forward): rows [0,64) from p0, rows [64,128) from p1
+  MOE_DEV void load_split_n(const T* p0, const T* p1, int64_t ld, int col0, int k0) {
+    static_assert(MODE == MC, "split-N operand is N-contiguous");
+    constexpr int MG = 128 / VEC;
+    const int tid = threadIdx.x;
+    const int kg = tid / MG, mg = tid % MG;
+    const int r = mg * VEC;
+    const T* p = (r < 64) ? p0 + col0 + r : p1 + col0 + (r - 64);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int k = k0 + kg * 4 + j;
+      reg[j] = *reinterpret_cast<const uint4*>(p + (int64_t)k * ld);
+    }
+  }
+  MOE_DEV void store(char* lds) const {
+    const int tid = threadIdx.x;
+    if constexpr (MODE == KC) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int v = tid + 256 * i, r = v >> 3, ch = v & 7;
+        *reinterpret_cast<uint4*>(lds + r * 128 + ((ch ^ swz(r)) << 4)) = reg[i];
+      }
+    } else {
+      constexpr int MG = 128 / VEC;
+      const int kg = tid / MG, mg = tid % MG;
+      if constexpr (sizeof(T) == 2) {
+        // 4 rows (k) x 8 bf16 columns -> 8 rows of 4 consecutive k (8 bytes)
+        const uint32_t w0[4] = {reg[0].x, reg[0].y, reg[0].z, reg[0].w};
+        const uint32_t w1[4] = {reg[1].x, reg[1].y, reg[1].z, reg[1].w};
+        const uint32_t w2[4] = {reg[2].x, reg[2].y, reg[2].z, reg[2].w};
+        const uint32_t w3[4] = {reg[3].x, reg[3].y, reg[3].z, reg[3].w};
+        const int ch = kg >> 1, half = kg & 1;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const int wi = c >> 1;
+          uint32_t lo, hi;
+          if (c & 1) {
+            lo = (w0[wi] >> 16) | (w1[wi] & 0xFFFF0000u);
+            hi = (w2[wi] >> 16) | (w3[wi] & 0xFFFF0000u);
+          } else {
+            lo = (w0[wi] & 0xFFFFu) | (w1[wi] << 16);
+            hi = (w2[wi] & 0xFFFFu) | (w3[wi] << 16);
+          }
+          const int r = mg * 8 + c;
+          *reinterpret_cast<uint2*>(lds + r * 128 + ((ch ^ swz(r)) << 4) + (half << 3)) =
+              make_uint2(lo, hi);
+        }
+      } else {
+        // 4 rows (k) x 4 fp32 columns -> 4 rows of 4 consecutive k (a chunk)
+        const float* f0 = reinterpret_cast<const float*>(&reg[0]);
+        const float* f1 = reinterpret_cast<const float*>(&reg[1]);
+        const float* f2 = reinterpret_cast<const float*>(&reg[2]);
+        const float* f3 = reinterpret_cast<const float*>(&reg[3]);
+        const int ch = kg;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int r = mg * 4 + c;
+          *reinterpret_cast<float4*>(lds + r * 128 + ((ch ^ swz(r)) << 4)) =
+              make_float4(f0[c], f1[c], f2[c], f3[c]);
+        }
+      }
+    }
+  }
+};
+
+// MFMA on one LDS slab: acc[i][j] += A[rows ra_i..] * B[rows rb_j..]^T
+template <typename T>
+MOE_DEV void mma_slab(const char* la, const char* lb, const int ra[2], const int rb[2],
+                      f32x16_t acc[2][2]) {
+  const int lane = threadIdx.x & 63;
+  const int l32 = lane & 31, hi = lane >> 5;
+  constexpr int NSTEP = Frag<T>::BK / Frag<T>::KSTEP;  // 4
+#pragma unroll
+  for (int ks = 0; ks < NSTEP; ++ks) {
+    const int ch = ks * 2 + hi;
+    uint4 fa[2], fb[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = ra[i] + l32;
+      fa[i] = *reinterpret_cast<const uint4*>(la + r * 128 + ((ch ^ swz(r)) << 4));
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int r = rb[j] + l32;
+      fb[j] = *reinterpret_cast<const uint4*>(lb + r * 128 + ((ch ^ swz(r)) << 4));
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        if constexpr (sizeof(T) == 2) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8_t, fa[i]), __builtin_bit_cast(bf16x8_t, fb[j]), acc[i][j],
+              0, 0, 0);
+        } else {
+          const float* a = reinterpret_cast<const float*>(&fa[i]);
+          const float* b = reinterpret_cast<const float*>(&fb[j]);
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[q], b[q], acc[i][j], 0, 0, 0);
+        }
+      }
+  }
+}
+
+MOE_DEV float silu_f(float a) { return a / (1.0f + expf(-a)); }
+
+template <typename T, int AMODE, int BMODE, int GROUPING, int EPI, int BSPL>
+__global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmParams P) {
+  __shared__ __attribute__((aligned(16))) char smem[2][2][kBM * 128];  // [buf][A/B]
+  constexpr int BK = Frag<T>::BK;
+  const int64_t lin = remap_xcd(blockIdx.x, P.nblocks);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  int g, m0, n0, rows_valid, kdim;
+  int64_t arow0;  // first row of this group's rows in the output/row buffers
+  const T* Ap;
+  const T* Bp0;
+  const T* Bp1 = nullptr;
+  if constexpr (GROUPING == GROUP_M) {
+    const int mt = (int)(lin / P.ntn), nt = (int)(lin % P.ntn);
+    int mtl;
+    if (!find_group(P.offsets, P.G, mt, g, mtl)) return;
+    const int nrows = P.offsets[g + 1] - P.offsets[g];
+    m0 = mtl * kBM;
+    n0 = nt * kBN;
+    rows_valid = min(kBM, nrows - m0);
+    kdim = P.Kdim;
+    arow0 = P.offsets[g];
+    if (g < P.EL_A)
+      Ap = reinterpret_cast<const T*>(P.A) + (arow0 + m0) * P.lda;
+    else
+      Ap = reinterpret_cast<const T*>(P.A_sh) + (int64_t)m0 * P.lda;
+  } else {
+    const int per = P.ntm * P.ntn;
+    g = (int)(lin / per);
+    const int rem = (int)(lin % per);
+    m0 = (rem / P.ntn) * kBM;
+    n0 = (rem % P.ntn) * kBN;
+    rows_valid = min(kBM, P.Mfix - m0);
+    kdim = P.offsets[g + 1] - P.offsets[g];
+    arow0 = P.offsets[g];
+    if (g < P.EL_A)
+      Ap = reinterpret_cast<const T*>(P.A) + arow0 * P.lda + m0;
+    else
+      Ap = reinterpret_cast<const T*>(P.A_sh) + m0;
+  }
+  Bp0 = reinterpret_cast<const T*>(P.B0) + (int64_t)g * P.strideB;
+  if constexpr (BSPL != BS_NONE) Bp1 = reinterpret_cast<const T*>(P.B1) + (int64_t)g * P.strideB;
+  // B row/col origin of this tile
+  int cols_valid;
+  const T* Bt;  // tile origin for the unsplit cases
+  if constexpr (GROUPING == GROUP_M) {
+    cols_valid = min(kBN, P.N - n0);
+    if constexpr (BMODE == KC) Bt = Bp0 + (int64_t)n0 * P.ldb;
+    else Bt = Bp0 + n0;
+  } else {
+    cols_valid = min(kBN, P.N - n0);
+    // B(k = row r, n) at (g < EL ? B0 + arow0*ldb : B1 (shared)) + r*ldb + n
+    if (g < P.EL_B) Bt = reinterpret_cast<const T*>(P.B0) + arow0 * P.ldb + n0;
+    else Bt = reinterpret_cast<const T*>(P.B1) + n0;
+  }
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  TileLoader<T, AMODE> la;
+  TileLoader<T, BMODE> lb;
+  const int nk = (kdim + BK - 1) / BK;
+
+  auto load_k = [&](int kt) {
+    const int k0 = kt * BK;
+    if constexpr (GROUPING == GROUP_M) {
+      la.load(Ap, P.lda, rows_valid, k0, kdim);
+      if constexpr (BSPL == BS_N) {
+        lb.load_split_n(Bp0, Bp1, P.ldb, n0 / 2, k0);
+      } else if constexpr (BSPL == BS_K) {
+        if (k0 < P.bsplit) lb.load(Bp0 + (int64_t)n0 * P.ldb, P.ldb, cols_valid, k0, P.bsplit);
+        else lb.load(Bp1 + (int64_t)n0 * P.ldb - P.bsplit, P.ldb, cols_valid, k0, kdim);
+      } else {
+        lb.load(Bt, P.ldb, cols_valid, k0, kdim);
+      }
+    } else {
+      la.load(Ap, P.lda, rows_valid, k0, kdim);
+      lb.load(Bt, P.ldb, cols_valid, k0, kdim);
+    }
+  };
+
+  int ra[2], rb[2];
+  ra[0] = wm * 64;
+  ra[1] = wm * 64 + 32;
+  if constexpr (EPI == EPI_SWIGLU_FWD) {
+    rb[0] = wn * 32;        // gate columns
+    rb[1] = 64 + wn * 32;   // matching up columns
+  } else {
+    rb[0] = wn * 64;
+    rb[1] = wn * 64 + 32;
+  }
+
+  if (nk > 0) {
+    load_k(0);
+    la.store(smem[0][0]);
+    lb.store(smem[0][1]);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      if (kt + 1 < nk) load_k(kt + 1);
+      mma_slab<T>(smem[cur][0], smem[cur][1], ra, rb, acc);
+      if (kt + 1 < nk) {
+        la.store(smem[cur ^ 1][0]);
+        lb.store(smem[cur ^ 1][1]);
+      }
+      __syncthreads();
+    }
+  }
+
+  // epilogue.  Output element (i, j, r): row = ra[i] + (r/4)*8 + (lane/32)*4 +
+  // r%4, column = rb[j] + lane%32 (32x32 MFMA accumulator layout).
+  const int l32 = lane & 31, hi4 = (lane >> 5) * 4;
+  if constexpr (EPI == EPI_SWIGLU_FWD) {
+    T* hout = reinterpret_cast<T*>(P.C1);
+    T* aout = reinterpret_cast<T*>(P.act_out);
+    const int f = n0 / 2 + wn * 32 + l32;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = ra[i] + (r >> 2) * 8 + hi4 + (r & 3);
+        if (row >= rows_valid) continue;
+        const int64_t grow = arow0 + m0 + row;
+        const float a = acc[i][0][r], b = acc[i][1][r];
+        aout[grow * 2 * P.F + f] = Elem<T>::from_f32(a);
+        aout[grow * 2 * P.F + P.F + f] = Elem<T>::from_f32(b);
+        hout[grow * P.F + f] = Elem<T>::from_f32(silu_f(a) * b);
+      }
+  } else if constexpr (EPI == EPI_SWIGLU_BWD) {
+    const T* act = reinterpret_cast<const T*>(P.act);
+    T* dact = reinterpret_cast<T*>(P.C0);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = ra[i] + (r >> 2) * 8 + hi4 + (r & 3);
+          const int col = rb[j] + l32;
+          if (row >= rows_valid || col >= cols_valid) continue;
+          const int64_t grow = arow0 + m0 + row;
+          const int f = n0 + col;
+          const float dh = acc[i][j][r];
+          const float a = Elem<T>::to_f32(act[grow * 2 * P.F + f]);
+          const float b = Elem<T>::to_f32(act[grow * 2 * P.F + P.F + f]);
+          const float sg = 1.0f / (1.0f + expf(-a));
+          const float da = dh * b * sg * (1.0f + a * (1.0f - sg));
+          const float db = dh * a * sg;
+          dact[grow * 2 * P.F + f] = Elem<T>::from_f32(da);
+          dact[grow * 2 * P.F + P.F + f] = Elem<T>::from_f32(db);
+        }
+  } else {
+    // plain store; GROUP_M: C rows at arow0 + m0 + row; GROUP_K: C per group
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = ra[i] + (r >> 2) * 8 + hi4 + (r & 3);
+          const int col = rb[j] + l32;
+          if (row >= rows_valid || col >= cols_valid) continue;
+          const T v = Elem<T>::from_f32(acc[i][j][r]);
+          if constexpr (GROUPING == GROUP_M) {
+            T* C = reinterpret_cast<T*>(P.C0);
+            C[(arow0 + m0 + row) * P.ldc + n0 + col] = v;
+          } else {
+            const int n = n0 + col;
+            if (n < P.csplit) {
+              T* C = reinterpret_cast<T*>(P.C0) + (int64_t)g * P.strideC;
+              C[(int64_t)(m0 + row) * P.ldc + n] = v;
+            } else {
+              T* C = reinterpret_cast<T*>(P.C1) + (int64_t)g * P.strideC;
+              C[(int64_t)(m0 + row) * P.ldc + (n - P.csplit)] = v;
+            }
+          }
+        }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+static int groups_of(const moe_config& c) { return (c.expert_hi - c.expert_lo) + c.n_shared; }
+
+// upper bound of m-tiles over all groups: sum ceil(n_g/BM) <= rows/BM + G
+static int64_t mtiles_bound(const moe_config& c) {
+  const int64_t routed = (int64_t)c.T * c.K;
+  const int EL = c.expert_hi - c.expert_lo;
+  int64_t b = (EL > 0) ? cdiv(routed, kBM) + EL : 0;
+  if (c.n_shared) b += cdiv(c.T, kBM) * c.n_shared;
+  return b;
+}
+
+template <typename T, int AM, int BM_, int GR, int EPI, int BS>
+static int run_gemm(const char* name, GemmParams& P, hipStream_t st) {
+  if (P.nblocks <= 0) return MOE_OK;
+  MOE_LAUNCH(name, (grouped_gemm_kernel<T, AM, BM_, GR, EPI, BS>), dim3((unsigned)P.nblocks),
+             dim3(kThreads), 0, st, P);
+  return MOE_OK;
+}
+
+static GemmParams base_params(const moe_config& c, const int32_t* offsets) {
+  GemmParams P = {};
+  P.G = groups_of(c);
+  P.EL_A = P.EL_B = c.expert_hi - c.expert_lo;
+  P.offsets = offsets;
+  P.F = c.F;
+  P.csplit = 1 << 30;
+  return P;
+}
+
+int gemm_swiglu_fwd(const moe_config& c, const void* x, const void* x_perm,
+                    const int32_t* offsets, const void* wg, const void* wu, void* act, void* h,
+                    hipStream_t st) {
+  GemmParams P = base_params(c, offsets);
+  P.N = 2 * c.F;
+  P.Kdim = c.D;
+  P.ntn = (int)cdiv(P.N, kBN);
+  P.nblocks = mtiles_bound(c) * P.ntn;
+  P.A = x_perm; P.A_sh = x; P.lda = c.D;
+  P.B0 = wg; P.B1 = wu; P.ldb = c.F; P.strideB = (int64_t)c.D * c.F;
+  P.C1 = h; P.act_out = act;
+  if (c.dtype == MOE_BF16) return run_gemm<bf16_t, KC, MC, GROUP_M, EPI_SWIGLU_FWD, BS_N>("gemm_gate_up_fwd", P, st);
+  return run_gemm<float, KC, MC, GROUP_M, EPI_SWIGLU_FWD, BS_N>("gemm_gate_up_fwd", P, st);
+}
+
+int gemm_down_fwd(const moe_config& c, const int32_t* offsets, const void* h, const void* wd,
+                  void* o_perm, hipStream_t st) {
+  GemmParams P = base_params(c, offsets);
+  P.N = c.D;
+  P.Kdim = c.F;
+  P.ntn = (int)cdiv(P.N, kBN);
+  P.nblocks = mtiles_bound(c) * P.ntn;
+  // shared rows of h live in the same row buffer: every group reads its rows
+  P.EL_A = P.G;
+  P.A = h; P.A_sh = h; P.lda = c.F;
+  P.B0 = wd; P.ldb = c.D; P.strideB = (int64_t)c.F * c.D;
+  P.C0 = o_perm; P.ldc = c.D;
+  if (c.dtype == MOE_BF16) return run_gemm<bf16_t, KC, MC, GROUP_M, EPI_STORE, BS_NONE>("gemm_down_fwd", P, st);
+  return run_gemm<float, KC, MC, GROUP_M, EPI_STORE, BS_NONE>("gemm_down_fwd", P, st);
+}
+
+int gemm_down_dgrad(const moe_config& c, const int32_t* offsets, const void* d_o, const void* dy,
+                    const void* wd, const void* act, void* dact, hipStream_t st) {
+  GemmParams P = base_params(c, offsets);
+  P.N = c.F;
+  P.Kdim = c.D;
+  P.ntn = (int)cdiv(P.N, kBN);
+  P.nblocks = mtiles_bound(c) * P.ntn;
+  P.A = d_o; P.A_sh = dy; P.lda = c.D;
+  // B(k = d, n = f) = W_down[f][d]: row n, K contiguous
+  P.B0 = wd; P.ldb = c.D; P.strideB = (int64_t)c.F * c.D;
+  P.C0 = dact; P.act = act;
+  if (c.dtype == MOE_BF16) return run_gemm<bf16_t, KC, KC, GROUP_M, EPI_SWIGLU_BWD, BS_NONE>("gemm_down_dgrad", P, st);
+  return run_gemm<float, KC, KC, GROUP_M, EPI_SWIGLU_BWD, BS_NONE>("gemm_down_dgrad", P, st);
+}
+
+int gemm_up_dgrad(const moe_config& c, const int32_t* offsets, const void* dact, const void* wg,
+                  const void* wu, void* dx_perm, hipStream_t st) {
+  GemmParams P = base_params(c, offsets);
+  P.N = c.D;
+  P.Kdim = 2 * c.F;
+  P.ntn = (int)cdiv(P.N, kBN);
+  P.nblocks = mtiles_bound(c) * P.ntn;
+  P.EL_A = P.G;  // dact holds the shared rows too
+  P.A = dact; P.A_sh = dact; P.lda = 2 * c.F;
+  // B(k = f, n = d) = W_gate[d][f] for f < F, W_up[d][f - F] above
+  P.B0 = wg; P.B1 = wu; P.ldb = c.F; P.strideB = (int64_t)c.D * c.F; P.bsplit = c.F;
+  P.C0 = dx_perm; P.ldc = c.D;
+  if (c.dtype == MOE_BF16) return run_gemm<bf16_t, KC, KC, GROUP_M, EPI_STORE, BS_K>("gemm_gate_up_dgrad", P, st);
+  return run_gemm<float, KC, KC, GROUP_M, EPI_STORE, BS_K>("gemm_gate_up_dgrad", P, st);
+}
+
+int gemm_down_wgrad(const moe_config& c, const int32_t* offsets, const void* h, const void* d_o,
+                    const void* dy, void* dwd, hipStream_t st) {
+  GemmParams P = base_params(c, offsets);
+  P.Mfix = c.F;
+  P.N = c.D;
+  P.ntm = (int)cdiv(P.Mfix, kBM);
+  P.ntn = (int)cdiv(P.N, kBN);
+  P.nblocks = (int64_t)P.G * P.ntm * P.ntn;
+  // A(m = f, k = row) = h[row][f]: every group (shared too) reads its h rows;
+  // B(k = row, n = d) = d_o[row][d] for routed groups, dy[token][d] for shared
+  P.EL_A = P.G;
+  P.A = h; P.A_sh = h; P.lda = c.F;
+  P.B0 = d_o; P.B1 = dy; P.ldb = c.D;
+  P.C0 = dwd; P.ldc = c.D; P.strideC = (int64_t)c.F * c.D;
+  if (c.dtype == MOE_BF16) return run_gemm<bf16_t, MC, MC, GROUP_K, EPI_STORE, BS_NONE>("gemm_down_wgrad", P, st);
+  return run_gemm<float, MC, MC, GROUP_K, EPI_STORE, BS_NONE>("gemm_down_wgrad", P, st);
+}
+
+int gemm_up_wgrad(const moe_config& c, const int32_t* offsets, const void* x, const void* x_perm,
+                  const void* dact, void* dwg, void* dwu, hipStream_t st) {
+  GemmParams P = base_params(c, offsets);
+  P.Mfix = c.D;
+  P.N = 2 * c.F;
+  P.ntm = (int)cdiv(P.Mfix, kBM);
+  P.ntn = (int)cdiv(P.N, kBN);
+  P.nblocks = (int64_t)P.G * P.ntm * P.ntn;
+  P.A = x_perm; P.A_sh = x; P.lda = c.D;
+  // B(k = row, n) = dact[row][n], n in [0, 2F): every group reads dact rows
+  P.EL_B = P.G;
+  P.B0 = dact; P.B1 = dact; P.ldb = 2 * c.F;
+  P.C0 = dwg; P.C1 = dwu; P.ldc = c.F; P.csplit = c.F; P.strideC = (int64_t)c.D * c.F;
+  if (c.dtype == MOE_BF16) return run_gemm<bf16_t, MC, MC, GROUP_K, EPI_STORE, BS_NONE>("gemm_gate_up_wgrad", P, st);
+  return run_gemm<float, MC, MC, GROUP_K, EPI_STORE, BS_NONE>("gemm_gate_up_wgrad", P, st);
+}
+
+}  // namespace moe

@@ -1,0 +1,70 @@
+// kernels.h -- host-side launchers of the HIP kernels (internal).
+#pragma once
+
+#include <algorithm>
+#include <cstddef>
+
+#include "common.h"
+
+namespace moe {
+
+// workspace carve-up (all sub-buffers 256-byte aligned)
+struct Workspace {
+  size_t tile_counts, tile_base;   // int32 [ntiles][E]
+  size_t aux_part;                 // float [aux_blocks][E + 1]
+  size_t d_o, dact, dx_perm;       // dtype rows buffers
+  size_t dg, ds;                   // float [T][K], [T][E]
+  size_t dxr;                      // float [T][D] (router dgrad, large E)
+  size_t dwr_part;                 // float [splits][E][D] (+ [splits][E] bias)
+  size_t total;
+  int ntiles, aux_blocks, dwr_splits;
+};
+Workspace workspace_layout(const moe_config& c);
+
+constexpr int kSlotTile = 256;  // slots per histogram / rank tile
+constexpr int kAuxTokens = 256; // tokens per aux-loss partial
+
+int launch_route(const moe_config& c, const void* x, const float* wr, const float* rb,
+                 const float* selb, float* logits, int32_t* idx, float* w, float* lse,
+                 bool logits_given, hipStream_t st);
+
+int launch_permute(const moe_config& c, int capacity, const int32_t* idx, const void* x,
+                   int32_t* counts_all, int32_t* offsets, int32_t* slot_row, int32_t* row_token,
+                   int32_t* row_slot, int32_t* n_dropped, void* x_perm, char* ws,
+                   const Workspace& L, hipStream_t st);
+
+int launch_expert_ffn(const moe_config& c, const void* x, const void* x_perm,
+                      const int32_t* offsets, const void* wg, const void* wu, const void* wd,
+                      void* act, void* h, void* o_perm, hipStream_t st);
+
+int launch_combine(const moe_config& c, const void* o_perm, const int32_t* offsets,
+                   const int32_t* slot_row, const float* topk_w, void* y, hipStream_t st);
+
+int launch_aux(const moe_config& c, const float* logits, const int32_t* counts_all, float alpha,
+               float zlam, float* losses, float* d_logits, char* ws, const Workspace& L,
+               hipStream_t st);
+
+int launch_backward(const moe_config& c, const void* x, const float* wr, const float* logits,
+                    const int32_t* idx, const float* topk_w, const int32_t* offsets,
+                    const int32_t* slot_row, const void* x_perm, const void* act, const void* h,
+                    const void* o_perm, const void* wg, const void* wu, const void* wd,
+                    const void* dy, const float* dlx, void* dx, float* dwr, float* drb,
+                    void* dwg, void* dwu, void* dwd, float* d_logits_out, char* ws,
+                    const Workspace& L, hipStream_t st);
+
+// grouped GEMM launchers (gemm.hip)
+int gemm_swiglu_fwd(const moe_config& c, const void* x, const void* x_perm,
+                    const int32_t* offsets, const void* wg, const void* wu, void* act, void* h,
+                    hipStream_t st);
+int gemm_down_fwd(const moe_config& c, const int32_t* offsets, const void* h, const void* wd,
+                  void* o_perm, hipStream_t st);
+int gemm_down_dgrad(const moe_config& c, const int32_t* offsets, const void* d_o, const void* dy,
+                    const void* wd, const void* act, void* dact, hipStream_t st);
+int gemm_down_wgrad(const moe_config& c, const int32_t* offsets, const void* h, const void* d_o,
+                    const void* dy, void* dwd, hipStream_t st);
+int gemm_up_dgrad(const moe_config& c, const int32_t* offsets, const void* dact, const void* wg,
+                  const void* wu, void* dx_perm, hipStream_t st);
+int gemm_up_wgrad(const moe_config& c, const int32_t* offsets, const void* x, const void* x_perm,
+                  const void* dact, void* dwg, void* dwu, hipStream_t st);
+
+}  // namespace moe

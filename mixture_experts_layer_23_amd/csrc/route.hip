@@ -1,0 +1,334 @@
+// route.hip -- router logits, selection key, top-K and gate weights.
+//
+// [P3] "MoE" tutorial, Router/Gating Network: the router is a linear layer
+// s = x W_g followed by a score function; KeepTopK keeps the K largest.
+// [P5] course notes 8.2: token-choice top-K with gating A (truncated softmax)
+// or B (softmax renormalised over the selected set); 8.6: sigmoid scores with a
+// selection bias b_e that only selects, the weights use the raw scores.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// Router logits.  Products of a bf16/fp32 activation and an fp32 weight are
+// exact in double, the sum is accumulated in double and rounded once to
+// binary32, so the result is (up to a ~1e-12 relative accumulation error) the
+// correctly rounded dot product whatever the summation order.  A top-K taken
+// on these logits is therefore reproducible by any other double-accumulating
+// implementation.
+// ---------------------------------------------------------------------------
+
+// Skinny router (E <= 16): W_r (E*D fp32, at most 128 KB) staged in LDS once
+// per workgroup; each wave takes two tokens at a time, lanes stride over D in
+// 16-byte vectors (coalesced), fp64 partials are reduced across the wave.
+template <typename T, int EM>
+__global__ __launch_bounds__(256) void router_skinny_kernel(const T* __restrict__ x,
+                                                            const float* __restrict__ wr,
+                                                            const float* __restrict__ rb,
+                                                            float* __restrict__ logits, int T_,
+                                                            int D, int E) {
+  extern __shared__ float4 sw4[];
+  float* sw = reinterpret_cast<float*>(sw4);
+  const int n4 = (E * D) >> 2;
+  for (int i = threadIdx.x; i < n4; i += blockDim.x) sw4[i] = reinterpret_cast<const float4*>(wr)[i];
+  __syncthreads();
+  constexpr int VEC = Elem<T>::VEC;
+  const int lane = threadIdx.x & 63;
+  const int wave = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int nwave = gridDim.x * (blockDim.x >> 6);
+  for (int t0 = wave * 2; t0 < T_; t0 += nwave * 2) {
+    const bool two = (t0 + 1) < T_;
+    double acc0[EM], acc1[EM];
+#pragma unroll
+    for (int e = 0; e < EM; ++e) { acc0[e] = 0.0; acc1[e] = 0.0; }
+    for (int d0 = lane * VEC; d0 < D; d0 += 64 * VEC) {
+      float xa[VEC], xb[VEC];
+      Vec16<T> va, vb;
+      va.load(x + (size_t)t0 * D + d0);
+      va.to_f32(xa);
+      if (two) {
+        vb.load(x + (size_t)(t0 + 1) * D + d0);
+        vb.to_f32(xb);
+      } else {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) xb[i] = 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < EM; ++e) {
+        if (e < E) {
+          const float* w = sw + e * D + d0;
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) {
+            acc0[e] = fma((double)xa[i], (double)w[i], acc0[e]);
+            acc1[e] = fma((double)xb[i], (double)w[i], acc1[e]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < EM; ++e) {
+      if (e < E) {
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) {
+          acc0[e] += shfl_xor_d(acc0[e], m);
+          acc1[e] += shfl_xor_d(acc1[e], m);
+        }
+      }
+    }
+    if (lane < E) {
+      double a0 = 0.0, a1 = 0.0;
+#pragma unroll
+      for (int e = 0; e < EM; ++e)
+        if (e == lane) { a0 = acc0[e]; a1 = acc1[e]; }
+      const double b = rb ? (double)rb[lane] : 0.0;
+      logits[(size_t)t0 * E + lane] = (float)(a0 + b);
+      if (two) logits[(size_t)(t0 + 1) * E + lane] = (float)(a1 + b);
+    }
+  }
+}
+
+// Tiled router (E > 16): 64 tokens x 64 experts per workgroup, k-slabs of 16
+// staged in LDS as double, 4x4 register micro-tile per thread.
+template <typename T>
+__global__ __launch_bounds__(256) void router_tiled_kernel(const T* __restrict__ x,
+                                                           const float* __restrict__ wr,
+                                                           const float* __restrict__ rb,
+                                                           float* __restrict__ logits, int T_,
+                                                           int D, int E) {
+  __shared__ double sx[16][65];
+  __shared__ double sw[16][65];
+  const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int lr = threadIdx.x >> 2, lk = (threadIdx.x & 3) * 4;  // loader: row, 4 k's
+  double acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
+  for (int k0 = 0; k0 < D; k0 += 16) {
+    double xv[4], wv[4];
+    const int t = t0 + lr, e = e0 + lr;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      xv[i] = (t < T_) ? (double)Elem<T>::to_f32(x[(size_t)t * D + k0 + lk + i]) : 0.0;
+      wv[i] = (e < E) ? (double)wr[(size_t)e * D + k0 + lk + i] : 0.0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sx[lk + i][lr] = xv[i];
+      sw[lk + i][lr] = wv[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      double a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { a[i] = sx[k][ty + 16 * i]; b[i] = sw[k][tx + 16 * i]; }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = t0 + ty + 16 * i;
+    if (t >= T_) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = e0 + tx + 16 * j;
+      if (e < E) logits[(size_t)t * E + e] = (float)(acc[i][j] + (rb ? (double)rb[e] : 0.0));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// sig32: the fixed binary32 sigmoid of the selection key (no contraction; the
+// only fma are the explicit ones).  exp32(z): clamp to [-87, 87];
+// n = rint(z * log2e); r = (z - n*L1) then fma(-n, L2, r) with L1 + L2 = ln 2
+// and n*L1 exact (L1 has 15 significant bits); Taylor degree 7 of e^r with
+// coefficients 1/k! in binary32, Horner with fma; times 2^n from exponent
+// bits.  sig32(z) = 1 / (1 + exp32(-z)) with IEEE division.
+// ---------------------------------------------------------------------------
+MOE_DEV float sig32(float z) {
+#pragma clang fp contract(off)
+  const float LOG2E = 1.44269502162933349609375f;
+  const float L1 = 0.693145751953125f;
+  const float L2 = 1.428606765330187045037746429443359375e-06f;
+  float u = -z;
+  u = u > 87.0f ? 87.0f : u;
+  u = u < -87.0f ? -87.0f : u;
+  const float t = u * LOG2E;
+  const float n = __builtin_rintf(t);
+  const float nl1 = n * L1;
+  float r = u - nl1;
+  r = __builtin_fmaf(-n, L2, r);
+  float p = (float)(1.0 / 5040.0);
+  p = __builtin_fmaf(p, r, (float)(1.0 / 720.0));
+  p = __builtin_fmaf(p, r, (float)(1.0 / 120.0));
+  p = __builtin_fmaf(p, r, (float)(1.0 / 24.0));
+  p = __builtin_fmaf(p, r, (float)(1.0 / 6.0));
+  p = __builtin_fmaf(p, r, 0.5f);
+  p = __builtin_fmaf(p, r, 1.0f);
+  p = __builtin_fmaf(p, r, 1.0f);
+  const float s = __uint_as_float((uint32_t)((int)n + 127) << 23);
+  const float e = p * s;
+  const float d = 1.0f + e;
+  return 1.0f / d;
+}
+
+// ---------------------------------------------------------------------------
+// Selection and gate weights: L lanes per token (L = min(64, pow2ceil(E))),
+// EPL experts per lane (expert e = sub + L*j).  K rounds of a group-wide
+// arg-max on (key, index) with equal keys going to the lower index.
+// ---------------------------------------------------------------------------
+MOE_DEV bool better(float ka, int ia, float kb, int ib) {
+  return (ka > kb) || (ka == kb && ia < ib);
+}
+
+template <int L, int EPL>
+__global__ __launch_bounds__(256) void route_select_kernel(
+    const float* __restrict__ logits, const float* __restrict__ selb, int T_, int E, int K,
+    int score, int gating, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+    float* __restrict__ lse_out) {
+  const int gid = blockIdx.x * blockDim.x + threadIdx.x;
+  const int t = gid / L, sub = gid % L;
+  const bool active = t < T_;  // whole L-groups are (in)active together
+  if (!active) return;
+  const float* s = logits + (size_t)t * E;
+  float sv[EPL], key[EPL];
+  bool used[EPL];
+  float m = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const int e = sub + L * j;
+    const bool ok = e < E;
+    sv[j] = ok ? s[e] : -INFINITY;
+    if (score == 0) key[j] = sv[j];
+    else key[j] = ok ? (sig32(sv[j]) + (selb ? selb[e] : 0.0f)) : -INFINITY;
+    used[j] = !ok;
+    m = fmaxf(m, sv[j]);
+  }
+#pragma unroll
+  for (int o = L / 2; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  float z = 0.f;
+#pragma unroll
+  for (int j = 0; j < EPL; ++j)
+    if (sub + L * j < E) z += expf(sv[j] - m);
+#pragma unroll
+  for (int o = L / 2; o >= 1; o >>= 1) z += __shfl_xor(z, o, 64);
+  if (sub == 0 && lse_out) lse_out[t] = m + logf(z);
+
+  // K rounds of arg-max; the chosen raw scores are kept by lane sub==k%L
+  float gsum = 0.f;
+  for (int k = 0; k < K; ++k) {
+    float bk = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const int e = sub + L * j;
+      if (!used[j] && better(key[j], e, bk, bi)) { bk = key[j]; bi = e; }
+    }
+#pragma unroll
+    for (int o = L / 2; o >= 1; o >>= 1) {
+      const float ok_ = __shfl_xor(bk, o, 64);
+      const int oi = __shfl_xor(bi, o, 64);
+      if (better(ok_, oi, bk, bi)) { bk = ok_; bi = oi; }
+    }
+    bi = bi < E ? bi : 0;  // only reachable with non-finite logits (outside the contract)
+    // the owner marks it used
+#pragma unroll
+    for (int j = 0; j < EPL; ++j)
+      if (sub + L * j == bi) used[j] = true;
+    const float sc = s[bi];
+    float g;
+    if (score == 0) g = expf(sc - m);                 // unnormalised softmax term
+    else g = 1.0f / (1.0f + expf(-sc));               // raw sigmoid score
+    gsum += g;
+    if (sub == 0) {
+      topk_idx[(size_t)t * K + k] = bi;
+      topk_w[(size_t)t * K + k] = g;
+    }
+  }
+  if (sub == 0) {
+    // normalise: softmax A divides by the full sum z; B by the selected sum;
+    // sigmoid A keeps the raw score; sigmoid B divides by the selected sum.
+    float den = 1.f;
+    if (score == 0) den = (gating == 0) ? z : gsum;
+    else den = (gating == 0) ? 1.f : gsum;
+    if (!(score == 1 && gating == 0))
+      for (int k = 0; k < K; ++k) topk_w[(size_t)t * K + k] = topk_w[(size_t)t * K + k] / den;
+  }
+}
+
+template <int L, int EPL>
+static int launch_select(const float* lg, const float* selb, int T_, int E, int K, int score,
+                         int gating, int32_t* idx, float* w, float* lse, hipStream_t st) {
+  const int64_t threads = (int64_t)T_ * L;
+  const int grid = (int)cdiv(threads, 256);
+  MOE_LAUNCH("route_select", (route_select_kernel<L, EPL>), dim3(grid), dim3(256), 0, st, lg, selb,
+             T_, E, K, score, gating, idx, w, lse);
+  return MOE_OK;
+}
+
+int launch_route(const moe_config& c, const void* x, const float* wr, const float* rb,
+                 const float* selb, float* logits, int32_t* idx, float* w, float* lse,
+                 bool logits_given, hipStream_t st) {
+  const int T_ = c.T, D = c.D, E = c.E;
+  if (!logits_given) {
+    if (E <= 16 && (size_t)E * D * 4 <= 128 * 1024) {
+      const int waves_needed = (int)cdiv(T_, 2);
+      int grid = (int)std::min<int64_t>(cdiv(waves_needed, 4), 2048);
+      const size_t shm = (size_t)E * D * 4;
+      if (shm > 64 * 1024) {
+        // W_r tiles above 64 KB need the kernel's dynamic-LDS limit raised
+        hipError_t e1 = hipFuncSetAttribute((const void*)router_skinny_kernel<bf16_t, 8>,
+                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+        hipError_t e2 = hipFuncSetAttribute((const void*)router_skinny_kernel<float, 8>,
+                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+        hipError_t e3 = hipFuncSetAttribute((const void*)router_skinny_kernel<bf16_t, 16>,
+                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+        hipError_t e4 = hipFuncSetAttribute((const void*)router_skinny_kernel<float, 16>,
+                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+        hipError_t e5 = hipFuncSetAttribute((const void*)router_skinny_kernel<bf16_t, 4>,
+                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+        hipError_t e6 = hipFuncSetAttribute((const void*)router_skinny_kernel<float, 4>,
+                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+        for (hipError_t e : {e1, e2, e3, e4, e5, e6})
+          if (e != hipSuccess) { set_error("router_logits (LDS limit)", e); return MOE_ELAUNCH; }
+      }
+      if (c.dtype == MOE_BF16) {
+        if (E <= 4) MOE_LAUNCH("router_logits", (router_skinny_kernel<bf16_t, 4>), dim3(grid), dim3(256), shm, st, (const bf16_t*)x, wr, rb, logits, T_, D, E);
+        else if (E <= 8) MOE_LAUNCH("router_logits", (router_skinny_kernel<bf16_t, 8>), dim3(grid), dim3(256), shm, st, (const bf16_t*)x, wr, rb, logits, T_, D, E);
+        else MOE_LAUNCH("router_logits", (router_skinny_kernel<bf16_t, 16>), dim3(grid), dim3(256), shm, st, (const bf16_t*)x, wr, rb, logits, T_, D, E);
+      } else {
+        if (E <= 4) MOE_LAUNCH("router_logits", (router_skinny_kernel<float, 4>), dim3(grid), dim3(256), shm, st, (const float*)x, wr, rb, logits, T_, D, E);
+        else if (E <= 8) MOE_LAUNCH("router_logits", (router_skinny_kernel<float, 8>), dim3(grid), dim3(256), shm, st, (const float*)x, wr, rb, logits, T_, D, E);
+        else MOE_LAUNCH("router_logits", (router_skinny_kernel<float, 16>), dim3(grid), dim3(256), shm, st, (const float*)x, wr, rb, logits, T_, D, E);
+      }
+    } else {
+      dim3 grid((unsigned)cdiv(T_, 64), (unsigned)cdiv(E, 64));
+      if (c.dtype == MOE_BF16)
+        MOE_LAUNCH("router_logits", (router_tiled_kernel<bf16_t>), grid, dim3(256), 0, st, (const bf16_t*)x, wr, rb, logits, T_, D, E);
+      else
+        MOE_LAUNCH("router_logits", (router_tiled_kernel<float>), grid, dim3(256), 0, st, (const float*)x, wr, rb, logits, T_, D, E);
+    }
+  }
+  const int K = c.K, sc = c.score_fn, ga = c.gating;
+  const float* sb = (sc == MOE_SCORE_SIGMOID) ? selb : nullptr;
+  if (E <= 1) return launch_select<1, 1>(logits, sb, T_, E, K, sc, ga, idx, w, lse, st);
+  if (E <= 2) return launch_select<2, 1>(logits, sb, T_, E, K, sc, ga, idx, w, lse, st);
+  if (E <= 4) return launch_select<4, 1>(logits, sb, T_, E, K, sc, ga, idx, w, lse, st);
+  if (E <= 8) return launch_select<8, 1>(logits, sb, T_, E, K, sc, ga, idx, w, lse, st);
+  if (E <= 16) return launch_select<16, 1>(logits, sb, T_, E, K, sc, ga, idx, w, lse, st);
+  if (E <= 32) return launch_select<32, 1>(logits, sb, T_, E, K, sc, ga, idx, w, lse, st);
+  if (E <= 64) return launch_select<64, 1>(logits, sb, T_, E, K, sc, ga, idx, w, lse, st);
+  if (E <= 128) return launch_select<64, 2>(logits, sb, T_, E, K, sc, ga, idx, w, lse, st);
+  if (E <= 256) return launch_select<64, 4>(logits, sb, T_, E, K, sc, ga, idx, w, lse, st);
+  if (E <= 512) return launch_select<64, 8>(logits, sb, T_, E, K, sc, ga, idx, w, lse, st);
+  return launch_select<64, 16>(logits, sb, T_, E, K, sc, ga, idx, w, lse, st);
+}
+
+}  // namespace moe

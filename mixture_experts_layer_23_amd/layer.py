@@ -1,0 +1,124 @@
+"""A MoE layer driven through the C ABI: buffers come from torch (device memory
+only), every computation is a call into ``libmoe_mi355x.so``.
+
+Forward:  moe_route -> moe_permute -> moe_expert_ffn -> moe_combine
+          (+ aux_balance_loss when a balance or z-loss coefficient is set)
+Backward: moe_backward (with the aux-loss logit gradient as d_logits_extra)
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib as L
+
+
+@dataclass
+class LayerSpec:
+    T: int
+    D: int
+    E: int
+    K: int
+    F: int
+    lo: int = 0
+    hi: int = -1
+    n_shared: int = 0
+    score: int = L.MOE_SCORE_SOFTMAX
+    gating: int = L.MOE_GATE_RENORM
+    dtype: int = L.MOE_BF16
+    cap: float = 0.0
+    alpha: float = 0.0
+    zlam: float = 0.0
+
+    def config(self) -> L.MoeConfig:
+        return L.make_config(self.T, self.D, self.E, self.K, self.F, self.lo,
+                             self.E if self.hi < 0 else self.hi, self.n_shared, self.score,
+                             self.gating, self.dtype, self.cap)
+
+    @property
+    def groups(self) -> int:
+        return (self.E if self.hi < 0 else self.hi) - self.lo + self.n_shared
+
+    @staticmethod
+    def from_workload(wl, **over) -> "LayerSpec":
+        kw = dict(T=wl.T, D=wl.D, E=wl.E, K=wl.K, F=wl.F, lo=wl.lo, hi=wl.hi,
+                  n_shared=wl.n_shared, score=wl.score, gating=wl.gating, dtype=wl.dtype,
+                  cap=wl.cap, alpha=wl.alpha, zlam=wl.zlam)
+        kw.update(over)
+        return LayerSpec(**kw)
+
+
+class MoELayer:
+    def __init__(self, spec: LayerSpec, w_r, w_gate, w_up, w_down, r_bias=None, sel_bias=None,
+                 device="cuda"):
+        self.spec = spec
+        self.cfg = spec.config()
+        self.dev = torch.device(device)
+        s = spec
+        tdt = torch.bfloat16 if s.dtype == L.MOE_BF16 else torch.float32
+        self.tdt = tdt
+        self.w_r, self.w_gate, self.w_up, self.w_down = w_r, w_gate, w_up, w_down
+        self.r_bias, self.sel_bias = r_bias, sel_bias
+        rows = max(L.rows_max(self.cfg), 1)
+        T1 = max(s.T, 1)
+        G = s.groups
+        f32, i32 = torch.float32, torch.int32
+        z = lambda *shape, dt: torch.empty(*shape, dtype=dt, device=self.dev)
+        self.logits = z(T1, s.E, dt=f32)
+        self.topk_idx = z(T1, s.K, dt=i32)
+        self.topk_w = z(T1, s.K, dt=f32)
+        self.lse = z(T1, dt=f32)
+        self.counts = z(s.E, dt=i32)
+        self.offsets = z(G + 1, dt=i32)
+        self.slot_row = z(T1 * s.K, dt=i32)
+        self.row_token = z(rows, dt=i32)
+        self.row_slot = z(rows, dt=i32)
+        self.n_dropped = z(4, dt=i32)
+        self.x_perm = z(rows, s.D, dt=tdt)
+        self.act = z(rows, 2 * s.F, dt=tdt)
+        self.h = z(rows, s.F, dt=tdt)
+        self.o_perm = z(rows, s.D, dt=tdt)
+        self.y = z(T1, s.D, dt=tdt)
+        self.losses = z(4, dt=f32)
+        self.dlogits_aux = z(T1, s.E, dt=f32)
+        self.ws = torch.empty(max(L.workspace_size(self.cfg), 256), dtype=torch.uint8,
+                              device=self.dev)
+        self.dx = z(T1, s.D, dt=tdt)
+        self.dw_r = z(s.E, s.D, dt=f32)
+        self.d_rbias = z(s.E, dt=f32)
+        self.dw_gate = torch.empty_like(w_gate)
+        self.dw_up = torch.empty_like(w_up)
+        self.dw_down = torch.empty_like(w_down)
+        self.d_logits = z(T1, s.E, dt=f32)
+        self.x = None
+
+    @property
+    def use_aux(self) -> bool:
+        return self.spec.score == L.MOE_SCORE_SOFTMAX and (self.spec.alpha != 0 or self.spec.zlam != 0)
+
+    def route(self, x, logits_given: bool = False):
+        L.moe_route(self.cfg, x, self.w_r, self.r_bias, self.sel_bias, self.logits, self.topk_idx,
+                    self.topk_w, self.lse, L.MOE_ROUTE_LOGITS_GIVEN if logits_given else 0)
+
+    def forward(self, x, logits_given: bool = False):
+        self.x = x
+        self.route(x, logits_given)
+        L.moe_permute(self.cfg, self.topk_idx, x, self.counts, self.offsets, self.slot_row,
+                      self.row_token, self.row_slot, self.n_dropped, self.x_perm, self.ws)
+        L.moe_expert_ffn(self.cfg, x, self.x_perm, self.offsets, self.w_gate, self.w_up,
+                         self.w_down, self.act, self.h, self.o_perm)
+        L.moe_combine(self.cfg, self.o_perm, self.offsets, self.slot_row, self.topk_w, self.y)
+        if self.use_aux:
+            L.aux_balance_loss(self.cfg, self.logits, self.counts, self.spec.alpha,
+                               self.spec.zlam, self.losses, self.dlogits_aux, self.ws)
+        return self.y
+
+    def backward(self, dy, with_aux: bool | None = None):
+        use = self.use_aux if with_aux is None else with_aux
+        L.moe_backward(self.cfg, self.x, self.w_r, self.logits, self.topk_idx, self.topk_w,
+                       self.offsets, self.slot_row, self.x_perm, self.act, self.h, self.o_perm,
+                       self.w_gate, self.w_up, self.w_down, dy,
+                       self.dlogits_aux if use else None, self.dx, self.dw_r, self.d_rbias,
+                       self.dw_gate, self.dw_up, self.dw_down, self.d_logits, self.ws)
+        return self.dx

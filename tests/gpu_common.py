@@ -1,0 +1,78 @@
+"""Helpers shared by the GPU parity tests: move seeded host inputs to the
+device, run the layer through the C ABI, run the oracle on the same inputs
+and compare with the norm-wise relative error
+
+    err(a, r) = max|a - r| / max|r|      (a reference that is all zeros
+                                          demands exact zeros)
+
+against 1e-5 (fp32 layers) or 2e-2 (bf16 layers, fp32 accumulation)."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+from mixture_experts_layer_23_amd import synthetic as S
+
+TOL = {S.F32: 1e-5, S.BF16: 2e-2}
+
+
+def note(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def rel_err(a, r) -> float:
+    a = np.asarray(a, np.float64)
+    r = np.asarray(r, np.float64)
+    assert a.shape == r.shape, (a.shape, r.shape)
+    den = np.max(np.abs(r)) if r.size else 0.0
+    num = np.max(np.abs(a - r)) if r.size else 0.0
+    if den == 0.0:
+        return 0.0 if num == 0.0 else float("inf")
+    return float(num / den)
+
+
+def assert_close(name, a, r, tol):
+    e = rel_err(a, r)
+    assert e <= tol, f"{name}: rel err {e:.3e} > {tol:.1e}"
+    return e
+
+
+def to_dev(arr, torch, dtype_code=None):
+    """numpy (bf16 as uint16 bits / fp32) -> torch cuda tensor"""
+    if arr is None:
+        return None
+    if arr.dtype == np.uint16:
+        t = torch.from_numpy(arr.view(np.int16).copy()).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(arr))
+    return t.cuda()
+
+
+def to_host(t):
+    """torch tensor -> numpy (bf16 -> uint16 bits, others as is)"""
+    import torch
+    t = t.detach()
+    if t.dtype == torch.bfloat16:
+        return t.cpu().view(torch.int16).numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def as_f64(a):
+    if a.dtype == np.uint16:
+        return S.bf16_to_f32(a).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def ocfg(wl):
+    from oracle import oracle as O
+    return O.Cfg(T=wl.T, D=wl.D, E=wl.E, K=wl.K, F=wl.F, lo=wl.lo, hi=wl.local_hi,
+                 n_shared=wl.n_shared, score=wl.score, gating=wl.gating, cap=wl.cap)
+
+
+def build_layer(wl, hin, torch):
+    from mixture_experts_layer_23_amd.layer import LayerSpec, MoELayer
+    spec = LayerSpec.from_workload(wl)
+    return MoELayer(spec, to_dev(hin.wr, torch), to_dev(hin.wg, torch), to_dev(hin.wu, torch),
+                    to_dev(hin.wd, torch), to_dev(hin.rb, torch), to_dev(hin.selb, torch))
