@@ -1,0 +1,243 @@
+"""Benchmark of the MoE layer (forward + backward) on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--k K] [--gating A|B]
+
+A step is one pass of the whole layer over one batch of synthetic tokens:
+router GEMM, top-K gating, histogram/scan/permute, grouped SwiGLU expert
+GEMMs, weighted combine, Switch/z losses and the full backward (expert dgrad
+and wgrad, gating and router gradients).  Inputs and weights are resident in
+HBM before the timed region.  Prints one JSON line.
+
+The default workload is the MiniMind-like layer (T = 4096 tokens, D = 768,
+E = 4 experts, top-2, SwiGLU F = 2048, bf16 with an fp32 router, gating B,
+balance-loss coefficient 5e-4).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
+F32_PEAK_TFLOPS = 157.3        # MI355X fp32 MFMA
+
+GEMM_FLOPS_PER_ROW = {          # in units of D*F per row
+    "gemm_gate_up_fwd": 4, "gemm_down_fwd": 2, "gemm_down_dgrad": 2, "gemm_down_wgrad": 2,
+    "gemm_gate_up_dgrad": 4, "gemm_gate_up_wgrad": 4,
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="minimind")
+    ap.add_argument("--k", type=int, default=None, help="override top-K")
+    ap.add_argument("--gating", choices=["A", "B"], default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=None)
+    ap.add_argument("--json-out", default=None)
+    return ap.parse_args()
+
+
+def workload(args):
+    from mixture_experts_layer_23_amd import synthetic as S
+    wl = S.WORKLOADS[args.workload]
+    if args.k is not None:
+        wl = wl.with_(K=args.k)
+    if args.gating is not None:
+        wl = wl.with_(gating=S.GATE_A if args.gating == "A" else S.GATE_B)
+    return wl
+
+
+def wl_name(wl):
+    g = "A" if wl.gating == 0 else "B"
+    sc = "softmax" if wl.score == 0 else "sigmoid"
+    s = (f"{wl.name}: T={wl.T} D={wl.D} E={wl.E} K={wl.K} F={wl.F} {sc}/{g}"
+         f" local=[{wl.lo},{wl.local_hi}) shared={wl.n_shared}")
+    if wl.cap > 0:
+        s += f" cap={wl.cap}"
+    if wl.alpha:
+        s += f" alpha={wl.alpha}"
+    if wl.zlam:
+        s += f" zloss={wl.zlam}"
+    if wl.hot_bias:
+        s += f" hot_bias={wl.hot_bias}"
+    return s
+
+
+def cpu_baseline(wl, host, n_tok):
+    """The oracle as it stands, on a bounded sample of the same workload:
+    routing of all T tokens (logits, top-K, dispatch), then forward and the
+    full backward (dx, dW_r and every expert-weight gradient contribution) of
+    the first n_tok tokens.  Reported in tokens/s."""
+    import numpy as np
+    from oracle import oracle as O
+
+    oc = O.Cfg(T=wl.T, D=wl.D, E=wl.E, K=wl.K, F=wl.F, lo=wl.lo, hi=wl.local_hi,
+               n_shared=wl.n_shared, score=wl.score, gating=wl.gating, cap=wl.cap)
+    x, wr, rb, selb, wg, wu, wd, dy = host
+    tok = np.arange(n_tok, dtype=np.int32)
+    t0 = time.perf_counter()
+    lg = O.logits(oc, x, wr, rb)
+    idx, w, lse, _ = O.route(oc, lg, selb)
+    d = O.dispatch(oc, idx)
+    O.forward(oc, x, wg, wu, wd, idx, w, d["slot_row"], tok=tok)
+    dl = None
+    if wl.score == 0 and (wl.alpha or wl.zlam):
+        _, dl = O.aux(oc, lg, d["counts_all"], wl.alpha, wl.zlam)
+    dyt = dy[tok].astype(np.float64) if dy.dtype != np.uint16 else \
+        ((dy[tok].astype(np.uint32) << 16).view(np.float32).astype(np.float64))
+    O.backward(oc, x, wr, wg, wu, wd, lg, idx, w, d["slot_row"], dyt, tok=tok, dlx=dl)
+    dt = time.perf_counter() - t0
+    return dict(value=n_tok / dt, unit="tokens/s", cores=O.threads(), kind="oracle",
+                sample=(f"routing of all {wl.T} tokens + forward and backward (dx, dW_r, all "
+                        f"expert-weight gradient rows) of {n_tok} of them; {dt:.1f} s on "
+                        f"{O.threads()} threads ({platform.processor() or platform.machine()})"))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from mixture_experts_layer_23_amd import _lib as L
+    from mixture_experts_layer_23_amd import synthetic as S
+    from mixture_experts_layer_23_amd.layer import LayerSpec, MoELayer
+
+    assert torch.cuda.is_available(), "needs a GPU"
+    L.lib()
+    wl = workload(args)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = S.device_inputs(wl, device="cuda")
+    spec = LayerSpec.from_workload(wl)
+    layer = MoELayer(spec, inp["wr"], inp["wg"], inp["wu"], inp["wd"], inp["rb"], inp["selb"])
+    x, dy = inp["x"], inp["dy"]
+    torch.cuda.synchronize()
+
+    def step():
+        layer.forward(x)
+        layer.backward(dy)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = elapsed * 1000.0 / max(args.steps, 1)
+
+    # second pass: per-kernel durations from HIP events recorded by the
+    # library on the stream each kernel runs on
+    L.timing_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    L.timing_enable(False)
+    kt = L.timing_report()
+
+    offsets = layer.offsets.cpu().numpy()
+    counts = layer.counts.cpu().numpy()
+    n_rows_local = int(offsets[wl.n_local]) if wl.n_local > 0 else 0
+    rows = n_rows_local + wl.n_shared * wl.T
+    n_dropped = int(layer.n_dropped.cpu().numpy()[0])
+    esz = 2 if wl.dtype == S.BF16 else 4
+    kernels = {}
+    gemm_flops = gemm_ms = 0.0
+    for name, (n, tot) in kt.items():
+        avg = tot / n
+        e = dict(launches_per_step=n / max(args.steps, 1), avg_ms=avg)
+        if name in GEMM_FLOPS_PER_ROW:
+            fl = GEMM_FLOPS_PER_ROW[name] * wl.D * wl.F * rows
+            e["tflops"] = fl / (avg * 1e-3) / 1e12
+            gemm_flops += fl * n
+            gemm_ms += tot
+        kernels[name] = e
+    # algorithmic bytes of the HBM-bound stages (per launch)
+    Dsz = wl.D * esz
+    stage_bytes = {
+        "permute_gather": n_rows_local * Dsz * 2,
+        "combine": rows * Dsz + wl.T * Dsz + wl.T * wl.K * 8,
+        "combine_bwd": n_rows_local * Dsz * 2 + wl.T * Dsz + wl.T * wl.K * 8,
+        "unpermute_dx": rows * Dsz + wl.T * Dsz + wl.T * wl.K * 4,
+        "route_select": wl.T * wl.E * 4 + wl.T * wl.K * 8 + wl.T * 4,
+        "router_logits": wl.T * Dsz + wl.E * wl.D * 4 + wl.T * wl.E * 4,
+    }
+    for name, b in stage_bytes.items():
+        if name in kernels:
+            kernels[name]["gbs"] = b / (kernels[name]["avg_ms"] * 1e-3) / 1e9
+            kernels[name]["hbm_frac"] = kernels[name]["gbs"] / HBM_PEAK_GBS
+    dom = max(kt.items(), key=lambda kv: kv[1][1])[0]
+    dom_avg = kernels[dom]["avg_ms"]
+    peak_t = BF16_PEAK_TFLOPS if wl.dtype == S.BF16 else F32_PEAK_TFLOPS
+    if dom in GEMM_FLOPS_PER_ROW:
+        ach = GEMM_FLOPS_PER_ROW[dom] * wl.D * wl.F * rows / (dom_avg * 1e-3) / 1e12
+        roof = dict(kernel=dom, bound="mfma", achieved=ach, peak=peak_t, unit="TFLOP/s",
+                    frac=ach / peak_t, traffic=None,
+                    per_launch=f"{GEMM_FLOPS_PER_ROW[dom]}*D*F flop x {rows} rows")
+    else:
+        b = stage_bytes.get(dom, 0)
+        ach = b / (dom_avg * 1e-3) / 1e9
+        roof = dict(kernel=dom, bound="hbm", achieved=ach, peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=ach / HBM_PEAK_GBS, traffic=None)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        host = (S.bf16_bits(inp["x"].float().cpu().numpy()) if wl.dtype == S.BF16
+                else inp["x"].cpu().numpy(),
+                inp["wr"].cpu().numpy(),
+                None if inp["rb"] is None else inp["rb"].cpu().numpy(),
+                None if inp["selb"] is None else inp["selb"].cpu().numpy(),
+                *[t.cpu().view(torch.int16).numpy().view(np.uint16) if wl.dtype == S.BF16
+                  else t.cpu().numpy() for t in (inp["wg"], inp["wu"], inp["wd"], inp["dy"])])
+        n_tok = args.cpu_sample_tokens or min(wl.T, 1024)
+        cpu = cpu_baseline(wl, host, n_tok)
+
+    out = {
+        "metric": "MoE layer fwd+bwd tokens/s",
+        "value": wl.T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == S.BF16 else "f32",
+        "data": "synthetic (seeded, on-device Philox normals)",
+        "config": {"workload": wl_name(wl), "tokens": wl.T, "local_rows": n_rows_local,
+                   "shared_rows": wl.n_shared * wl.T, "dropped": n_dropped,
+                   "expert_load": counts.tolist() if wl.E <= 16 else None},
+        "grouped_gemm": {"tflops": gemm_flops / (gemm_ms * 1e-3) / 1e12 if gemm_ms else None,
+                         "frac_of_peak": (gemm_flops / (gemm_ms * 1e-3) / 1e12 / peak_t)
+                         if gemm_ms else None,
+                         "ms_per_step": gemm_ms / max(args.steps, 1)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+    }
+    line = json.dumps(out)
+    print(line, flush=True)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(line + "\n")
+
+
+if __name__ == "__main__":
+    main()
