@@ -177,6 +177,8 @@ def main():
         "unpermute_dx": rows * Dsz + wl.T * Dsz + wl.T * wl.K * 4,
         "route_select": wl.T * wl.E * 4 + wl.T * wl.K * 8 + wl.T * 4,
         "router_logits": wl.T * Dsz + wl.E * wl.D * 4 + wl.T * wl.E * 4,
+        "router_wgrad": wl.T * Dsz + wl.T * wl.E * 4,
+        "aux_partial": wl.T * wl.E * 4 * (2 if wl.alpha or wl.zlam else 1),
     }
     for name, b in stage_bytes.items():
         if name in kernels:
@@ -205,7 +207,7 @@ def main():
                 None if inp["selb"] is None else inp["selb"].cpu().numpy(),
                 *[t.cpu().view(torch.int16).numpy().view(np.uint16) if wl.dtype == S.BF16
                   else t.cpu().numpy() for t in (inp["wg"], inp["wu"], inp["wd"], inp["dy"])])
-        n_tok = args.cpu_sample_tokens or min(wl.T, 1024)
+        n_tok = args.cpu_sample_tokens or min(wl.T, 4096)
         cpu = cpu_baseline(wl, host, n_tok)
 
     out = {

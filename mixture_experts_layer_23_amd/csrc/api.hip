@@ -77,9 +77,17 @@ Workspace workspace_layout(const moe_config& c) {
   const int64_t rows = TK + (int64_t)c.n_shared * c.T;
   const size_t esz = c.dtype == MOE_BF16 ? 2 : 4;
   L.ntiles = (int)std::max<int64_t>(1, cdiv(TK, kSlotTile));
-  L.aux_blocks = (int)std::max<int64_t>(1, cdiv(c.T, kAuxTokens));
+  L.aux_blocks = (int)std::max<int64_t>(1, cdiv(c.T, aux_tokens_per_block(c.E)));
   if (c.E <= 16) {
-    L.dwr_splits = (int)std::max<int64_t>(1, cdiv(c.T, 256));
+    // token chunks of the few-expert router weight gradient: about 256
+    // workgroups, chunks of at most 256 tokens
+    const int64_t dblk = cdiv(c.D, 256);
+    int64_t nchunk = std::max<int64_t>(1, cdiv(256, dblk));
+    nchunk = std::min<int64_t>(nchunk, std::max<int64_t>(1, cdiv(c.T, 8)));
+    nchunk = std::max<int64_t>(nchunk, cdiv(c.T, 256));
+    // every chunk must be non-empty: re-derive the count from the chunk length
+    const int64_t len = cdiv(std::max<int64_t>(c.T, 1), nchunk);
+    L.dwr_splits = (int)std::max<int64_t>(1, cdiv(std::max<int64_t>(c.T, 1), len));
   } else {
     const int64_t tiles = cdiv(c.E, 64) * cdiv(c.D, 64);
     int64_t s = cdiv(1024, tiles);
@@ -96,7 +104,7 @@ Workspace workspace_layout(const moe_config& c) {
   L.dg = o;          o += al((size_t)TK * 4);
   L.ds = o;          o += al((size_t)c.T * c.E * 4);
   L.dxr = o;         o += (c.E > 16) ? al((size_t)c.T * c.D * 4) : 0;
-  L.dwr_part = o;    o += al((size_t)L.dwr_splits * ((size_t)c.E * c.D + c.E) * 4);
+  L.dwr_part = o;    o += al((size_t)L.dwr_splits * (((size_t)c.E * c.D + c.E + 3) & ~(size_t)3) * 4);
   L.total = o;
   return L;
 }

@@ -7,56 +7,87 @@
 // [P4] load-balance section: the same E sum_e f_e p_e form.  [P3] ST-MoE and
 // [P5] 8.6: z-loss = lambda * mean_t (log sum_e exp s_te)^2.
 //
-// Two passes, deterministic: per block of kAuxTokens tokens, (1) per token
-// max, normaliser, lse and sum_e p_e u_e (u_e = alpha E f_e / T), (2) per
-// expert the block's sum of p_e in token order and, if asked, the logit
-// gradient p (u - sum p u) + lambda (2/T) lse p.  A final single-workgroup
-// kernel sums the block partials in block order.
+// Deterministic two-level reduction: each workgroup takes TB tokens and
+// computes per token the max, normaliser and lse, then every probability
+// (kept in LDS), sum_e p_e u_e (u_e = alpha E f_e / T) and, if asked, the
+// logit gradient p (u - sum p u) + lambda (2/T) lse p; then per expert the
+// workgroup's sum of p_e in token order.  A final single-workgroup kernel
+// sums the partials in workgroup order.
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 
+// TB tokens per workgroup, four threads per token for the per-token
+// reductions, all threads over (token, expert) pairs for the probabilities.
 __global__ __launch_bounds__(256) void aux_partial_kernel(const float* __restrict__ logits,
                                                           const int32_t* __restrict__ counts,
-                                                          int T_, int E, int K, float alpha,
-                                                          float zlam, float* __restrict__ part,
+                                                          int T_, int E, int K, int TB,
+                                                          float alpha, float zlam,
+                                                          float* __restrict__ part,
                                                           float* __restrict__ dlog) {
-  __shared__ float sm[kAuxTokens], sz[kAuxTokens], slse[kAuxTokens], spu[kAuxTokens];
-  const int t0 = blockIdx.x * kAuxTokens;
-  const int nt = min(kAuxTokens, T_ - t0);
-  const float inv_tk = 1.0f / ((float)T_ * (float)K);
-  const float ucoef = alpha * (float)E * inv_tk / (float)T_;
-  for (int i = threadIdx.x; i < nt; i += blockDim.x) {
-    const float* s = logits + (size_t)(t0 + i) * E;
-    float m = -INFINITY;
-    for (int e = 0; e < E; ++e) m = fmaxf(m, s[e]);
-    float z = 0.f;
-    for (int e = 0; e < E; ++e) z += expf(s[e] - m);
-    float pu = 0.f;
-    if (dlog)
-      for (int e = 0; e < E; ++e) pu += (expf(s[e] - m) / z) * (ucoef * (float)counts[e]);
-    sm[i] = m;
-    sz[i] = z;
-    slse[i] = m + logf(z);
-    spu[i] = pu;
+  extern __shared__ float sh[];
+  float* sp = sh;                  // [TB][E] probabilities
+  float* sm = sh + (size_t)TB * E; // [TB] max
+  float* sz = sm + TB;             // [TB] normaliser
+  float* slse = sz + TB;           // [TB] log-sum-exp
+  float* spu = slse + TB;          // [TB] sum_e p_e u_e
+  const int t0 = blockIdx.x * TB;
+  const int nt = min(TB, T_ - t0);
+  const float ucoef = alpha * (float)E / ((float)T_ * (float)K) / (float)T_;
+  const int tq = threadIdx.x >> 2, q = threadIdx.x & 3;  // token, quarter
+  // per token max and normaliser (4 lanes per token, fixed combine order)
+  if (tq < TB) {
+    float m = -INFINITY, z = 0.f;
+    if (tq < nt) {
+      const float* s = logits + (size_t)(t0 + tq) * E;
+      for (int e = q; e < E; e += 4) m = fmaxf(m, s[e]);
+    }
+    m = fmaxf(m, __shfl_xor(m, 1, 64));
+    m = fmaxf(m, __shfl_xor(m, 2, 64));
+    if (tq < nt) {
+      const float* s = logits + (size_t)(t0 + tq) * E;
+      for (int e = q; e < E; e += 4) z += expf(s[e] - m);
+    }
+    z += __shfl_xor(z, 1, 64);
+    z += __shfl_xor(z, 2, 64);
+    if (q == 0 && tq < nt) {
+      sm[tq] = m;
+      sz[tq] = z;
+      slse[tq] = m + logf(z);
+    }
   }
   __syncthreads();
+  for (int i = threadIdx.x; i < nt * E; i += blockDim.x) {
+    const int t = i / E, e = i - t * E;
+    sp[i] = expf(logits[(size_t)(t0 + t) * E + e] - sm[t]) / sz[t];
+  }
+  __syncthreads();
+  if (dlog) {
+    if (tq < nt) {
+      float pu = 0.f;
+      for (int e = q; e < E; e += 4) pu += sp[tq * E + e] * (ucoef * (float)counts[e]);
+      pu += __shfl_xor(pu, 1, 64);
+      pu += __shfl_xor(pu, 2, 64);
+      if (q == 0) spu[tq] = pu;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < nt * E; i += blockDim.x) {
+      const int t = i / E, e = i - t * E;
+      const float p = sp[i];
+      const float u = ucoef * (float)counts[e];
+      dlog[(size_t)(t0 + t) * E + e] = p * (u - spu[t]) + zlam * (2.0f / (float)T_) * slse[t] * p;
+    }
+  }
   float* pb = part + (size_t)blockIdx.x * (E + 1);
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    const float u = ucoef * (float)counts[e];
     float P = 0.f;
-    for (int i = 0; i < nt; ++i) {
-      const float p = expf(logits[(size_t)(t0 + i) * E + e] - sm[i]) / sz[i];
-      P += p;
-      if (dlog)
-        dlog[(size_t)(t0 + i) * E + e] = p * (u - spu[i]) + zlam * (2.0f / (float)T_) * slse[i] * p;
-    }
+    for (int t = 0; t < nt; ++t) P += sp[t * E + e];
     pb[e] = P;
   }
   if (threadIdx.x == 0) {
     float z2 = 0.f;
-    for (int i = 0; i < nt; ++i) z2 += slse[i] * slse[i];
+    for (int t = 0; t < nt; ++t) z2 += slse[t] * slse[t];
     pb[E] = z2;
   }
 }
@@ -93,8 +124,10 @@ int launch_aux(const moe_config& c, const float* logits, const int32_t* counts_a
                float zlam, float* losses, float* d_logits, char* ws, const Workspace& L,
                hipStream_t st) {
   float* part = reinterpret_cast<float*>(ws + L.aux_part);
-  MOE_LAUNCH("aux_partial", aux_partial_kernel, dim3(L.aux_blocks), dim3(256), 0, st, logits,
-             counts_all, c.T, c.E, c.K, alpha, zlam, part, d_logits);
+  const int TB = aux_tokens_per_block(c.E);
+  const size_t shm = ((size_t)TB * c.E + 4 * (size_t)TB) * sizeof(float);
+  MOE_LAUNCH("aux_partial", aux_partial_kernel, dim3(L.aux_blocks), dim3(256), shm, st, logits,
+             counts_all, c.T, c.E, c.K, TB, alpha, zlam, part, d_logits);
   MOE_LAUNCH("aux_final", aux_final_kernel, dim3(1), dim3(1024), 0, st, part, L.aux_blocks,
              counts_all, c.T, c.E, c.K, alpha, zlam, losses);
   return MOE_OK;

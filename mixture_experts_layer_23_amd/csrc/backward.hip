@@ -139,74 +139,76 @@ static int launch_gating_bwd(const moe_config& c, const float* lg, const int32_t
 }
 
 // ---------------------------------------------------------------------------
-// router weight gradient, few experts (E <= 16): each thread owns 4
-// consecutive model dims and sums ds[t,e] * x[t,d] over a chunk of
-// kRouterChunk tokens (ds rows of the chunk staged in LDS); per-chunk partials
-// are reduced in a fixed order afterwards.  Chunk 0's d-block 0 also sums the
-// router-bias gradient partial.
+// router weight gradient, few experts (E <= 16): each thread owns one model
+// dim and sums ds[t,e] * x[t,d] over a chunk of tokens
+// (the chunk's ds rows staged in LDS); chunk partials are reduced in a fixed
+// order afterwards.  The d-block 0 threads also sum the router-bias partial.
+// The chunk length is chosen on the host so that about 256 workgroups run.
 // ---------------------------------------------------------------------------
-constexpr int kRouterChunk = 256;
+constexpr int kRouterChunkMax = 256;
 
 template <typename T, int EM>
 __global__ __launch_bounds__(256) void router_wgrad_skinny_kernel(
-    const float* __restrict__ ds, const T* __restrict__ x, int T_, int D, int E,
+    const float* __restrict__ ds, const T* __restrict__ x, int T_, int D, int E, int chunk_len,
     float* __restrict__ part) {
-  __shared__ float sds[kRouterChunk * EM];
+  __shared__ float sds[kRouterChunkMax * EM];
   const int chunk = blockIdx.y;
-  const int t0 = chunk * kRouterChunk;
-  const int nt = min(kRouterChunk, T_ - t0);
+  const int t0 = chunk * chunk_len;
+  const int nt = min(chunk_len, T_ - t0);
   for (int i = threadIdx.x; i < nt * E; i += blockDim.x) sds[i] = ds[(size_t)t0 * E + i];
   __syncthreads();
-  const int d0 = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
-  float acc[EM][4];
-  float accb[EM];
+  const int d = blockIdx.x * blockDim.x + threadIdx.x;
+  if (d >= D) return;
+  float acc[EM], accb[EM];
 #pragma unroll
-  for (int e = 0; e < EM; ++e) {
-    accb[e] = 0.f;
+  for (int e = 0; e < EM; ++e) { acc[e] = 0.f; accb[e] = 0.f; }
+  const T* xp = x + (size_t)t0 * D + d;
+  for (int t = 0; t < nt; ++t) {
+    const float xv = Elem<T>::to_f32(xp[(size_t)t * D]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[e][i] = 0.f;
-  }
-  if (d0 < D) {
-    for (int t = 0; t < nt; ++t) {
-      float xv[4];
-      const T* xp = x + (size_t)(t0 + t) * D + d0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) xv[i] = Elem<T>::to_f32(xp[i]);
-#pragma unroll
-      for (int e = 0; e < EM; ++e) {
-        if (e < E) {
-          const float s = sds[t * E + e];
-          accb[e] += s;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[e][i] = fmaf(s, xv[i], acc[e][i]);
-        }
+    for (int e = 0; e < EM; ++e) {
+      if (e < E) {
+        const float s = sds[t * E + e];
+        accb[e] += s;
+        acc[e] = fmaf(s, xv, acc[e]);
       }
     }
-    float* p = part + (size_t)chunk * (E * D + E);
+  }
+  // partial row stride rounded up to 4 floats (shared with the workspace layout)
+  float* p = part + (size_t)chunk * (((size_t)E * D + E + 3) & ~(size_t)3);
+#pragma unroll
+  for (int e = 0; e < EM; ++e)
+    if (e < E) p[(size_t)e * D + d] = acc[e];
+  if (d == 0)
 #pragma unroll
     for (int e = 0; e < EM; ++e)
-      if (e < E)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) p[(size_t)e * D + d0 + i] = acc[e][i];
-    if (d0 == 0)
-#pragma unroll
-      for (int e = 0; e < EM; ++e)
-        if (e < E) p[(size_t)E * D + e] = accb[e];
-  }
+      if (e < E) p[(size_t)E * D + e] = accb[e];
 }
 
-// fixed-order sum of the split partials: out[i] = sum_s part[s][i]
+// fixed-order sum of the split partials: out[i] = sum_s part[s * stride + i].
+// 16 columns x 16 split lanes per workgroup; lane ty sums splits ty, ty+16, ...
+// and the 16 lane sums are added in lane order, so the result does not depend
+// on scheduling.
 __global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restrict__ part,
                                                             int nsplit, int64_t n,
                                                             int64_t stride, float* __restrict__ out,
                                                             float* __restrict__ out2,
                                                             int64_t n_first) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n) return;
+  __shared__ float red[16][17];
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int64_t i = (int64_t)blockIdx.x * 16 + tx;
   float s = 0.f;
-  for (int k = 0; k < nsplit; ++k) s += part[(size_t)k * stride + i];
-  if (i < n_first) out[i] = s;
-  else if (out2) out2[i - n_first] = s;
+  if (i < n)
+    for (int k = ty; k < nsplit; k += 16) s += part[(size_t)k * stride + i];
+  red[ty][tx] = s;
+  __syncthreads();
+  if (ty == 0 && i < n) {
+    float t = 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) t += red[k][tx];
+    if (i < n_first) out[i] = t;
+    else if (out2) out2[i - n_first] = t;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -313,18 +315,20 @@ static int router_bwd_t(const moe_config& c, const void* x, const float* wr, con
   const int E = c.E, D = c.D, T_ = c.T;
   float* part = reinterpret_cast<float*>(ws + L.dwr_part);
   if (E <= 16) {
-    const int nchunk = (int)cdiv(T_, kRouterChunk);
-    dim3 grid((unsigned)cdiv(D / 4, 256), (unsigned)nchunk);
+    const int nchunk = L.dwr_splits;
+    const int chunk_len = (int)cdiv(T_, nchunk);
+    dim3 grid((unsigned)cdiv(D, 256), (unsigned)nchunk);
 #define RW(EMV)                                                                               \
   MOE_LAUNCH("router_wgrad", (router_wgrad_skinny_kernel<T, EMV>), grid, dim3(256), 0, st, ds, \
-             (const T*)x, T_, D, E, part)
+             (const T*)x, T_, D, E, chunk_len, part)
     if (E <= 4) RW(4);
     else if (E <= 8) RW(8);
     else RW(16);
 #undef RW
     const int64_t n = (int64_t)E * D + E;
-    MOE_LAUNCH("router_wgrad_reduce", reduce_splits_kernel, dim3((unsigned)cdiv(n, 256)),
-               dim3(256), 0, st, part, nchunk, n, n, dwr, drb, (int64_t)E * D);
+    const int64_t stride = (n + 3) & ~(int64_t)3;
+    MOE_LAUNCH("router_wgrad_reduce", reduce_splits_kernel, dim3((unsigned)cdiv(n, 16)),
+               dim3(256), 0, st, part, nchunk, n, stride, dwr, drb, (int64_t)E * D);
   } else {
     // dxr[T,D] = ds[T,E] W_r[E,D]
     dim3 g1((unsigned)cdiv(T_, 64), (unsigned)cdiv(D, 64), 1);
@@ -338,7 +342,7 @@ static int router_bwd_t(const moe_config& c, const void* x, const float* wr, con
                (int64_t)E, (const T*)x, (int64_t)D, E, D, T_, kper, part, (int64_t)D,
                (int64_t)E * D);
     const int64_t n = (int64_t)E * D;
-    MOE_LAUNCH("router_wgrad_reduce", reduce_splits_kernel, dim3((unsigned)cdiv(n, 256)),
+    MOE_LAUNCH("router_wgrad_reduce", reduce_splits_kernel, dim3((unsigned)cdiv(n, 16)),
                dim3(256), 0, st, part, splits, n, n, dwr, (float*)nullptr, n);
     if (drb)
       MOE_LAUNCH("router_bias_grad", rbias_grad_kernel, dim3((unsigned)cdiv(E, 256)), dim3(256),

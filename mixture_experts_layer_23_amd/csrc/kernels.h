@@ -22,7 +22,9 @@ struct Workspace {
 Workspace workspace_layout(const moe_config& c);
 
 constexpr int kSlotTile = 256;  // slots per histogram / rank tile
-constexpr int kAuxTokens = 256; // tokens per aux-loss partial
+// tokens per aux-loss workgroup: up to 64, with the [TB][E] probability tile
+// plus four [TB] vectors kept within 64 KB of LDS
+inline int aux_tokens_per_block(int E) { return std::max(1, std::min(64, (16384 - 256) / E)); }
 
 int launch_route(const moe_config& c, const void* x, const float* wr, const float* rb,
                  const float* selb, float* logits, int32_t* idx, float* w, float* lse,
