@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=None)
     ap.add_argument("--json-out", default=None)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (for HBM counter scaling)")
     return ap.parse_args()
 
 
@@ -119,6 +121,13 @@ def main():
 
     assert torch.cuda.is_available(), "needs a GPU"
     L.lib()
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     wl = workload(args)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

@@ -27,6 +27,8 @@
 // 16-byte row vectors and transposed in registers (4 k x VEC) before the LDS
 // store.  Workgroup ids are remapped so that consecutive tiles (same rows,
 // same expert weights) land on the same XCD and share its L2.
+#include <cstdlib>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -133,21 +135,26 @@ template <typename T, int MODE>
 struct TileLoader {
   static constexpr int VEC = Frag<T>::VEC, BK = Frag<T>::BK;
   uint4 reg[4];
+  uint32_t ok;  // bit i: vector i is in range (out-of-range vectors store as zeros)
   // KC: element (r,k) at p[r*ld + k]; thread loads vectors v = tid + 256*i:
   //     row v / 8, chunk v % 8.
   // MC: element (r,k) at p[k*ld + r]; thread loads rows k = kg*4 + j of the
   //     VEC columns mg*VEC.., kg = tid / MG, mg = tid % MG, MG = 128 / VEC.
+  // Every load is issued (out-of-range lanes read element (0, k0) of the
+  // slab, which is always in bounds) so that no branch forces an early wait on
+  // the loads in flight; the mask is applied when the registers go to LDS.
   MOE_DEV void load(const T* p, int64_t ld, int r_valid, int k0, int k_valid) {
     const int tid = threadIdx.x;
+    ok = 0;
     if constexpr (MODE == KC) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int v = tid + 256 * i, r = v >> 3, ch = v & 7;
         const int k = k0 + ch * VEC;
-        if (r < r_valid && k < k_valid)
-          reg[i] = *reinterpret_cast<const uint4*>(p + (int64_t)r * ld + k);
-        else
-          reg[i] = make_uint4(0, 0, 0, 0);
+        const bool in = (r < r_valid) && (k < k_valid);
+        const T* q = in ? p + (int64_t)r * ld + k : p + k0;
+        reg[i] = *reinterpret_cast<const uint4*>(q);
+        ok |= (uint32_t)in << i;
       }
     } else {
       constexpr int MG = 128 / VEC;
@@ -155,10 +162,10 @@ struct TileLoader {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int k = k0 + kg * 4 + j, r = mg * VEC;
-        if (k < k_valid && r < r_valid)
-          reg[j] = *reinterpret_cast<const uint4*>(p + (int64_t)k * ld + r);
-        else
-          reg[j] = make_uint4(0, 0, 0, 0);
+        const bool in = (k < k_valid) && (r < r_valid);
+        const T* q = in ? p + (int64_t)k * ld + r : p + (int64_t)k0 * ld;
+        reg[j] = *reinterpret_cast<const uint4*>(q);
+        ok |= (uint32_t)in << j;
       }
     }
   }
@@ -175,9 +182,13 @@ struct TileLoader {
       const int k = k0 + kg * 4 + j;
       reg[j] = *reinterpret_cast<const uint4*>(p + (int64_t)k * ld);
     }
+    ok = 0xF;
   }
-  MOE_DEV void store(char* lds) const {
+  MOE_DEV void store(char* lds) {
     const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (!((ok >> i) & 1)) reg[i] = make_uint4(0, 0, 0, 0);
     if constexpr (MODE == KC) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -269,12 +280,131 @@ MOE_DEV void mma_slab(const char* la, const char* lb, const int ra[2], const int
 
 MOE_DEV float silu_f(float a) { return a / (1.0f + expf(-a)); }
 
+// Epilogue shared by both GEMM kernels: each wave's 64 x 64 fp32 tile goes
+// through its own 16 KB of LDS (r0..r3, one per wave; chunks of 4 floats
+// XOR-swizzled by row) and is read back as rows of 8 consecutive columns, so
+// global loads and stores are 16-byte vectors.
+template <typename T, int GROUPING, int EPI>
+MOE_DEV void gemm_epilogue(const GemmParams& P, f32x16_t (&acc)[2][2], char* r0, char* r1,
+                           char* r2, char* r3, int m0, int n0, int rows_valid, int cols_valid,
+                           int64_t arow0, int g) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  char* region = wave == 0 ? r0 : wave == 1 ? r1 : wave == 2 ? r2 : r3;  // 16 KB each
+  const int l32 = lane & 31, hi4 = (lane >> 5) * 4;
+  float* ep = reinterpret_cast<float*>(region);
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = i * 32 + (r >> 2) * 8 + hi4 + (r & 3);
+        const int col = j * 32 + l32;
+        ep[row * 64 + (((col >> 2) ^ (row & 15)) << 2) + (col & 3)] = acc[i][j][r];
+      }
+  __syncthreads();
+  auto read8 = [&](int row, int col0, float* v) {
+    const float4 a = *reinterpret_cast<const float4*>(ep + row * 64 + (((col0 >> 2) ^ (row & 15)) << 2));
+    const float4 b = *reinterpret_cast<const float4*>(ep + row * 64 + ((((col0 >> 2) + 1) ^ (row & 15)) << 2));
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  };
+  auto store8 = [&](T* dst, const float* v) {
+    if constexpr (sizeof(T) == 2) {
+      Vec16<T> o;
+      o.from_f32(v);
+      o.store(dst);
+    } else {
+      Vec16<T> o0, o1;
+      o0.from_f32(v);
+      o1.from_f32(v + 4);
+      o0.store(dst);
+      o1.store(dst + 4);
+    }
+  };
+  auto load8 = [&](const T* src, float* v) {
+    if constexpr (sizeof(T) == 2) {
+      Vec16<T> o;
+      o.load(src);
+      o.to_f32(v);
+    } else {
+      Vec16<T> o0, o1;
+      o0.load(src);
+      o1.load(src + 4);
+      o0.to_f32(v);
+      o1.to_f32(v + 4);
+    }
+  };
+  const int row_base = wm * 64;  // tile-relative first row of this wave
+
+  if constexpr (EPI == EPI_SWIGLU_FWD) {
+    // LDS columns [0,32) hold a (gate), [32,64) hold b (up) of the same f's
+    T* hout = reinterpret_cast<T*>(P.C1);
+    T* aout = reinterpret_cast<T*>(P.act_out);
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int item = lane + 64 * it;
+      const int row = item >> 2, fg = (item & 3) * 8;
+      if (row_base + row >= rows_valid) continue;
+      float a[8], b[8], h[8];
+      read8(row, fg, a);
+      read8(row, 32 + fg, b);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) h[q] = silu_f(a[q]) * b[q];
+      const int64_t grow = arow0 + m0 + row_base + row;
+      const int f = n0 / 2 + wn * 32 + fg;
+      store8(aout + grow * 2 * P.F + f, a);
+      store8(aout + grow * 2 * P.F + P.F + f, b);
+      store8(hout + grow * P.F + f, h);
+    }
+  } else {
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int item = lane + 64 * it;
+      const int row = item >> 3, cg = (item & 7) * 8;
+      const int col = wn * 64 + cg;  // tile-relative column
+      if (row_base + row >= rows_valid || col >= cols_valid) continue;
+      float v[8];
+      read8(row, cg, v);
+      if constexpr (EPI == EPI_SWIGLU_BWD) {
+        const T* act = reinterpret_cast<const T*>(P.act);
+        T* dact = reinterpret_cast<T*>(P.C0);
+        const int64_t grow = arow0 + m0 + row_base + row;
+        const int f = n0 + col;
+        float a[8], b[8], da[8], db[8];
+        load8(act + grow * 2 * P.F + f, a);
+        load8(act + grow * 2 * P.F + P.F + f, b);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const float sg = 1.0f / (1.0f + expf(-a[q]));
+          da[q] = v[q] * b[q] * sg * (1.0f + a[q] * (1.0f - sg));
+          db[q] = v[q] * a[q] * sg;
+        }
+        store8(dact + grow * 2 * P.F + f, da);
+        store8(dact + grow * 2 * P.F + P.F + f, db);
+      } else if constexpr (GROUPING == GROUP_M) {
+        T* C = reinterpret_cast<T*>(P.C0);
+        store8(C + (arow0 + m0 + row_base + row) * P.ldc + n0 + col, v);
+      } else {
+        const int n = n0 + col;
+        const int64_t mrow = m0 + row_base + row;
+        if (n < P.csplit)
+          store8(reinterpret_cast<T*>(P.C0) + (int64_t)g * P.strideC + mrow * P.ldc + n, v);
+        else
+          store8(reinterpret_cast<T*>(P.C1) + (int64_t)g * P.strideC + mrow * P.ldc +
+                     (n - P.csplit), v);
+      }
+    }
+  }
+}
+
 template <typename T, int AMODE, int BMODE, int GROUPING, int EPI, int BSPL>
 __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmParams P) {
   __shared__ __attribute__((aligned(16))) char smem[2][2][kBM * 128];  // [buf][A/B]
   constexpr int BK = Frag<T>::BK;
   const int64_t lin = remap_xcd(blockIdx.x, P.nblocks);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
   int g, m0, n0, rows_valid, kdim;
@@ -334,11 +464,14 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmParams P) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  TileLoader<T, AMODE> la;
-  TileLoader<T, BMODE> lb;
+  // Two register sets, prefetch distance two: while slab kt is multiplied
+  // from LDS, slab kt+1 is in registers (or arriving) and slab kt+2 is being
+  // loaded.  The loop is unrolled by two so that the sets are static.
+  TileLoader<T, AMODE> la0, la1;
+  TileLoader<T, BMODE> lb0, lb1;
   const int nk = (kdim + BK - 1) / BK;
 
-  auto load_k = [&](int kt) {
+  auto load_k = [&](TileLoader<T, AMODE>& la, TileLoader<T, BMODE>& lb, int kt) {
     const int k0 = kt * BK;
     if constexpr (GROUPING == GROUP_M) {
       la.load(Ap, P.lda, rows_valid, k0, kdim);
@@ -368,91 +501,326 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmParams P) {
   }
 
   if (nk > 0) {
-    load_k(0);
-    la.store(smem[0][0]);
-    lb.store(smem[0][1]);
+    load_k(la0, lb0, 0);
+    if (nk > 1) load_k(la1, lb1, 1);
+    la0.store(smem[0][0]);
+    lb0.store(smem[0][1]);
     __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      if (kt + 1 < nk) load_k(kt + 1);
-      mma_slab<T>(smem[cur][0], smem[cur][1], ra, rb, acc);
-      if (kt + 1 < nk) {
-        la.store(smem[cur ^ 1][0]);
-        lb.store(smem[cur ^ 1][1]);
+    // pairs of slabs: buffer 0 holds the even slab, buffer 1 the odd one
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+      if (kt + 2 < nk) load_k(la0, lb0, kt + 2);
+      mma_slab<T>(smem[0][0], smem[0][1], ra, rb, acc);
+      la1.store(smem[1][0]);
+      lb1.store(smem[1][1]);
+      __syncthreads();
+      if (kt + 3 < nk) load_k(la1, lb1, kt + 3);
+      mma_slab<T>(smem[1][0], smem[1][1], ra, rb, acc);
+      if (kt + 2 < nk) {
+        la0.store(smem[0][0]);
+        lb0.store(smem[0][1]);
       }
+      __syncthreads();
+    }
+    if (kt < nk) {  // odd slab count: the last slab is in buffer 0
+      mma_slab<T>(smem[0][0], smem[0][1], ra, rb, acc);
       __syncthreads();
     }
   }
 
-  // epilogue.  Output element (i, j, r): row = ra[i] + (r/4)*8 + (lane/32)*4 +
-  // r%4, column = rb[j] + lane%32 (32x32 MFMA accumulator layout).
-  const int l32 = lane & 31, hi4 = (lane >> 5) * 4;
-  if constexpr (EPI == EPI_SWIGLU_FWD) {
-    T* hout = reinterpret_cast<T*>(P.C1);
-    T* aout = reinterpret_cast<T*>(P.act_out);
-    const int f = n0 / 2 + wn * 32 + l32;
+  gemm_epilogue<T, GROUPING, EPI>(P, acc, &smem[0][0][0], &smem[0][0][0] + 16384,
+                                   &smem[0][0][0] + 32768, &smem[0][0][0] + 49152, m0, n0,
+                                   rows_valid, cols_valid, arow0, g);
+}
+
+
+// ===========================================================================
+// CDNA4 path (bf16, full 128-column tiles): operand slabs are copied global ->
+// LDS by the LDS-DMA loads (no register staging), through a ring of S stages.
+//  * K-contiguous operand: LDS tile [128 rows][64 k] (128-byte rows, 16-byte
+//    chunks XOR-swizzled by swz(row)); MFMA fragments by ds_read_b128.
+//  * M/N-contiguous operand: LDS tile [64 k][128 m|n] as stored in memory
+//    (256-byte rows, chunk swizzle (k & 3) << 2); MFMA fragments by
+//    ds_read_b64_tr_b16, which hands lane l of each 16-lane group element l%4
+//    of the 8-byte chunk addressed by lane 4j + l/4 (j = 0..3): with lane
+//    4j + q pointing at (k0 + j, n0 + 4q), lane l receives column n0 + l for
+//    k0..k0+3 -- the transposed fragment.
+// Activation rows are read with buffer loads whose range ends at the group's
+// last row, so rows past a ragged group end (or past a group's k extent in
+// the weight-gradient GEMMs) arrive as zeros; full weight tiles use per-lane
+// global addresses.
+// ===========================================================================
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s_t lds_v4s_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+constexpr int kBufDword3 = 0x00020000;  // raw buffer descriptor word 3 (CDNA)
+
+MOE_DEV __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int nb = bytes > 0x7fffffffLL ? 0x7fffffff : (int)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nb, kBufDword3);
+}
+
+MOE_DEV lds_void_t* to_lds(char* p) {
+  return (lds_void_t*)(__attribute__((address_space(3))) char*)(p);
+}
+
+// vmcnt wait with expcnt / lgkmcnt left open (gfx9 s_waitcnt encoding)
+template <int N>
+MOE_DEV void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// per-lane source of one DMA instruction (u = 0..3) of this wave
+// KC tile: chunk P = 64*t + lane, row = P/8, logical chunk = (P%8) ^ swz(row)
+MOE_DEV void kc_slot(int t, int lane, int& row, int& lc) {
+  const int P = 64 * t + lane;
+  row = P >> 3;
+  lc = (P & 7) ^ swz(row);
+}
+// MC tile: chunk P = 64*t + lane, k row = P/16, logical chunk = (P%16) ^ ((k&3)<<2)
+MOE_DEV void mc_slot(int t, int lane, int& krow, int& lc) {
+  const int P = 64 * t + lane;
+  krow = P >> 4;
+  lc = (P & 15) ^ ((krow & 3) << 2);
+}
+
+// fragment reads: 8 bf16 of one 32x32x16 MFMA operand for block rows rbase
+MOE_DEV uint4 frag_kc(const char* tile, int rbase, int ks, int lane) {
+  const int r = rbase + (lane & 31);
+  const int ch = ks * 2 + (lane >> 5);
+  return *reinterpret_cast<const uint4*>(tile + r * 128 + ((ch ^ swz(r)) << 4));
+}
+MOE_DEV uint4 frag_mc(char* tile, int rbase, int ks, int lane) {
+  const int gi = lane >> 4, a = lane & 15, j = a >> 2, q = a & 3;
+  const int col = rbase + (gi & 1) * 16 + 4 * q;
+  const int lc = col >> 3, half = (col >> 2) & 1;
+  uint32_t w[4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = ra[i] + (r >> 2) * 8 + hi4 + (r & 3);
-        if (row >= rows_valid) continue;
-        const int64_t grow = arow0 + m0 + row;
-        const float a = acc[i][0][r], b = acc[i][1][r];
-        aout[grow * 2 * P.F + f] = Elem<T>::from_f32(a);
-        aout[grow * 2 * P.F + P.F + f] = Elem<T>::from_f32(b);
-        hout[grow * P.F + f] = Elem<T>::from_f32(silu_f(a) * b);
-      }
-  } else if constexpr (EPI == EPI_SWIGLU_BWD) {
-    const T* act = reinterpret_cast<const T*>(P.act);
-    T* dact = reinterpret_cast<T*>(P.C0);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = ra[i] + (r >> 2) * 8 + hi4 + (r & 3);
-          const int col = rb[j] + l32;
-          if (row >= rows_valid || col >= cols_valid) continue;
-          const int64_t grow = arow0 + m0 + row;
-          const int f = n0 + col;
-          const float dh = acc[i][j][r];
-          const float a = Elem<T>::to_f32(act[grow * 2 * P.F + f]);
-          const float b = Elem<T>::to_f32(act[grow * 2 * P.F + P.F + f]);
-          const float sg = 1.0f / (1.0f + expf(-a));
-          const float da = dh * b * sg * (1.0f + a * (1.0f - sg));
-          const float db = dh * a * sg;
-          dact[grow * 2 * P.F + f] = Elem<T>::from_f32(da);
-          dact[grow * 2 * P.F + P.F + f] = Elem<T>::from_f32(db);
-        }
-  } else {
-    // plain store; GROUP_M: C rows at arow0 + m0 + row; GROUP_K: C per group
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = ra[i] + (r >> 2) * 8 + hi4 + (r & 3);
-          const int col = rb[j] + l32;
-          if (row >= rows_valid || col >= cols_valid) continue;
-          const T v = Elem<T>::from_f32(acc[i][j][r]);
-          if constexpr (GROUPING == GROUP_M) {
-            T* C = reinterpret_cast<T*>(P.C0);
-            C[(arow0 + m0 + row) * P.ldc + n0 + col] = v;
-          } else {
-            const int n = n0 + col;
-            if (n < P.csplit) {
-              T* C = reinterpret_cast<T*>(P.C0) + (int64_t)g * P.strideC;
-              C[(int64_t)(m0 + row) * P.ldc + n] = v;
-            } else {
-              T* C = reinterpret_cast<T*>(P.C1) + (int64_t)g * P.strideC;
-              C[(int64_t)(m0 + row) * P.ldc + (n - P.csplit)] = v;
-            }
-          }
-        }
+  for (int h = 0; h < 2; ++h) {
+    const int krow = ks * 16 + (gi >> 1) * 8 + 4 * h + j;
+    char* p = tile + krow * 256 + ((lc ^ ((krow & 3) << 2)) << 4) + (half << 3);
+    const v4s_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)(__attribute__((address_space(3))) char*)p);
+    w[2 * h] = (uint32_t)(uint16_t)v[0] | ((uint32_t)(uint16_t)v[1] << 16);
+    w[2 * h + 1] = (uint32_t)(uint16_t)v[2] | ((uint32_t)(uint16_t)v[3] << 16);
   }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+template <int AMODE, int BMODE, int GROUPING, int EPI, int BSPL, int S>
+__global__ __launch_bounds__(256) void grouped_gemm_dma_kernel(GemmParams P) {
+  typedef bf16_t T;
+  constexpr int BK = 64;
+  constexpr int TILE = 16384;  // bytes of one operand slab
+  // one LDS array per stage and operand: distinct objects let the compiler
+  // see that the DMA into one stage does not alias the reads of another, so
+  // it inserts no blanket wait for the loads in flight
+  __shared__ __attribute__((aligned(1024))) char sA0[TILE];
+  __shared__ __attribute__((aligned(1024))) char sB0[TILE];
+  __shared__ __attribute__((aligned(1024))) char sA1[TILE];
+  __shared__ __attribute__((aligned(1024))) char sB1[TILE];
+  __shared__ __attribute__((aligned(1024))) char sA2[S == 3 ? TILE : 16];
+  __shared__ __attribute__((aligned(1024))) char sB2[S == 3 ? TILE : 16];
+  static_assert(S == 2 || S == 3, "two or three stages");
+  const int64_t lin = remap_xcd(blockIdx.x, P.nblocks);
+  // wave index as a scalar: the LDS destinations of the DMA loads must be
+  // wave-uniform
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  int g, m0, n0, rows_valid, kdim;
+  int64_t arow0;
+  int nrows_g = 0;
+  if constexpr (GROUPING == GROUP_M) {
+    const int mt = (int)(lin / P.ntn), nt = (int)(lin % P.ntn);
+    int mtl;
+    if (!find_group(P.offsets, P.G, mt, g, mtl)) return;
+    g = __builtin_amdgcn_readfirstlane(g);
+    mtl = __builtin_amdgcn_readfirstlane(mtl);
+    nrows_g = P.offsets[g + 1] - P.offsets[g];
+    m0 = mtl * kBM;
+    n0 = nt * kBN;
+    rows_valid = min(kBM, nrows_g - m0);
+    kdim = P.Kdim;
+    arow0 = P.offsets[g];
+  } else {
+    const int per = P.ntm * P.ntn;
+    g = (int)(lin / per);
+    const int rem = (int)(lin % per);
+    m0 = (rem / P.ntn) * kBM;
+    n0 = (rem % P.ntn) * kBN;
+    rows_valid = kBM;
+    kdim = P.offsets[g + 1] - P.offsets[g];
+    arow0 = P.offsets[g];
+  }
+  const int cols_valid = kBN;
+
+  // ---- A source: buffer over this group's rows
+  const T* a_base = (g < P.EL_A) ? reinterpret_cast<const T*>(P.A) + arow0 * P.lda
+                                 : reinterpret_cast<const T*>(P.A_sh);
+  const int64_t a_rows = (GROUPING == GROUP_M) ? nrows_g : kdim;
+  const __amdgpu_buffer_rsrc_t a_rs = make_rsrc(a_base, a_rows * P.lda * 2);
+  // per-lane byte offsets of this wave's 4 A instructions at k0 = 0
+  uint32_t a_off[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int t = wave * 4 + u;
+    int r, lc;
+    if constexpr (AMODE == KC) {
+      kc_slot(t, lane, r, lc);
+      a_off[u] = (uint32_t)(((int64_t)(m0 + r) * P.lda + 8 * lc) * 2);
+    } else {
+      mc_slot(t, lane, r, lc);
+      a_off[u] = (uint32_t)(((int64_t)r * P.lda + m0 + 8 * lc) * 2);
+    }
+  }
+  // ---- B source
+  // GROUP_M: weights, full tiles, per-lane global addresses
+  // GROUP_K: activations (k = rows of the group), buffer over the group rows
+  const T* b_ptr[4];
+  uint32_t b_off[4];
+  __amdgpu_buffer_rsrc_t b_rs;
+  const T* Bw0 = reinterpret_cast<const T*>(P.B0) + (int64_t)g * P.strideB;
+  const T* Bw1 = (BSPL != BS_NONE) ? reinterpret_cast<const T*>(P.B1) + (int64_t)g * P.strideB
+                                   : nullptr;
+  if constexpr (GROUPING == GROUP_M) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = wave * 4 + u;
+      int r, lc;
+      if constexpr (BMODE == KC) {
+        kc_slot(t, lane, r, lc);
+        b_ptr[u] = Bw0 + (int64_t)(n0 + r) * P.ldb + 8 * lc;   // k0 added per slab
+      } else if constexpr (BSPL == BS_N) {
+        mc_slot(t, lane, r, lc);
+        const int col0 = n0 / 2;
+        b_ptr[u] = (lc < 8) ? Bw0 + (int64_t)r * P.ldb + col0 + 8 * lc
+                            : Bw1 + (int64_t)r * P.ldb + col0 + 8 * (lc - 8);
+      } else {
+        mc_slot(t, lane, r, lc);
+        b_ptr[u] = Bw0 + (int64_t)r * P.ldb + n0 + 8 * lc;
+      }
+    }
+    b_rs = make_rsrc(Bw0, 16);
+  } else {
+    const T* b_base = (g < P.EL_B) ? reinterpret_cast<const T*>(P.B0) + arow0 * P.ldb
+                                   : reinterpret_cast<const T*>(P.B1);
+    b_rs = make_rsrc(b_base, (int64_t)kdim * P.ldb * 2);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = wave * 4 + u;
+      int r, lc;
+      mc_slot(t, lane, r, lc);
+      b_off[u] = (uint32_t)(((int64_t)r * P.ldb + n0 + 8 * lc) * 2);
+    }
+  }
+
+  // issue the 8 DMA instructions of this wave for slab kt into (la, lb)
+  auto issue = [&](int kt, char* la, char* lb) {
+    const int k0 = kt * BK;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = wave * 4 + u;
+      const uint32_t kadd = (AMODE == KC) ? (uint32_t)(k0 * 2) : (uint32_t)((int64_t)k0 * P.lda * 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rs, to_lds(la + t * 1024), 16, a_off[u] + kadd, 0,
+                                               0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = wave * 4 + u;
+      if constexpr (GROUPING == GROUP_M) {
+        const T* src;
+        if constexpr (BMODE == KC) {
+          if constexpr (BSPL == BS_K) {
+            // k < bsplit from W_gate, above from W_up (the same row layout)
+            src = (k0 < P.bsplit) ? b_ptr[u] + k0 : (b_ptr[u] - Bw0) + Bw1 + (k0 - P.bsplit);
+          } else {
+            src = b_ptr[u] + k0;
+          }
+        } else {
+          src = b_ptr[u] + (int64_t)k0 * P.ldb;
+        }
+        __builtin_amdgcn_global_load_lds(src, to_lds(lb + t * 1024), 16, 0, 0);
+      } else {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rs, to_lds(lb + t * 1024), 16,
+                                                 b_off[u] + (uint32_t)((int64_t)k0 * P.ldb * 2),
+                                                 0, 0, 0);
+      }
+    }
+  };
+
+  int ra[2], rb[2];
+  ra[0] = wm * 64;
+  ra[1] = wm * 64 + 32;
+  if constexpr (EPI == EPI_SWIGLU_FWD) {
+    rb[0] = wn * 32;
+    rb[1] = 64 + wn * 32;
+  } else {
+    rb[0] = wn * 64;
+    rb[1] = wn * 64 + 32;
+  }
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // one pipeline step: slab kt is in (la, lb); slab kt + S - 1 goes to (na, nb)
+  auto mma = [&](char* la, char* lb) {
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      uint4 fa[2], fb[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        fa[i] = (AMODE == KC) ? frag_kc(la, ra[i], ks, lane) : frag_mc(la, ra[i], ks, lane);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        fb[j] = (BMODE == KC) ? frag_kc(lb, rb[j], ks, lane) : frag_mc(lb, rb[j], ks, lane);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8_t, fa[i]), __builtin_bit_cast(bf16x8_t, fb[j]),
+              acc[i][j], 0, 0, 0);
+    }
+  };
+  const int nk = (kdim + BK - 1) / BK;
+  auto step = [&](int kt, char* la, char* lb, char* na, char* nb) {
+    // slab kt has landed once at most the next slab's loads are outstanding
+    if (S == 3 && kt + 1 < nk) wait_vmcnt<8>();
+    else wait_vmcnt<0>();
+    __syncthreads();
+    if (kt + S - 1 < nk) issue(kt + S - 1, na, nb);
+    mma(la, lb);
+  };
+  if (nk > 0) issue(0, sA0, sB0);
+  if (S == 3 && nk > 1) issue(1, sA1, sB1);
+  if constexpr (S == 2) {
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+      step(kt, sA0, sB0, sA1, sB1);
+      step(kt + 1, sA1, sB1, sA0, sB0);
+    }
+    if (kt < nk) step(kt, sA0, sB0, sA1, sB1);
+  } else {
+    int kt = 0;
+    for (; kt + 2 < nk; kt += 3) {
+      step(kt, sA0, sB0, sA2, sB2);
+      step(kt + 1, sA1, sB1, sA0, sB0);
+      step(kt + 2, sA2, sB2, sA1, sB1);
+    }
+    if (kt < nk) step(kt, sA0, sB0, sA2, sB2);
+    if (kt + 1 < nk) step(kt + 1, sA1, sB1, sA0, sB0);
+  }
+  __syncthreads();
+  gemm_epilogue<T, GROUPING, EPI>(P, acc, sA0, sB0, sA1, sB1, m0, n0, rows_valid, cols_valid,
+                                  arow0, g);
 }
 
 // ---------------------------------------------------------------------------
@@ -469,9 +837,33 @@ static int64_t mtiles_bound(const moe_config& c) {
   return b;
 }
 
+static int dma_stages() {
+  static int s = [] {
+    const char* e = getenv("MOE_GEMM_STAGES");
+    const int v = e ? atoi(e) : 2;
+    return (v == 3) ? 3 : (v == 0 ? 0 : 2);
+  }();
+  return s;
+}
+
+// bf16 with whole 128-column (and, for the weight gradients, 128-row) tiles
+// runs on the LDS-DMA kernel; fp32 and ragged shapes on the register-staged one
 template <typename T, int AM, int BM_, int GR, int EPI, int BS>
 static int run_gemm(const char* name, GemmParams& P, hipStream_t st) {
   if (P.nblocks <= 0) return MOE_OK;
+  const bool full = (P.N % kBN == 0) && (GR == GROUP_M ? P.Kdim % 64 == 0 : P.Mfix % kBM == 0);
+  if constexpr (sizeof(T) == 2) {
+    if (full && dma_stages() == 3) {
+      MOE_LAUNCH(name, (grouped_gemm_dma_kernel<AM, BM_, GR, EPI, BS, 3>),
+                 dim3((unsigned)P.nblocks), dim3(kThreads), 0, st, P);
+      return MOE_OK;
+    }
+    if (full && dma_stages() == 2) {
+      MOE_LAUNCH(name, (grouped_gemm_dma_kernel<AM, BM_, GR, EPI, BS, 2>),
+                 dim3((unsigned)P.nblocks), dim3(kThreads), 0, st, P);
+      return MOE_OK;
+    }
+  }
   MOE_LAUNCH(name, (grouped_gemm_kernel<T, AM, BM_, GR, EPI, BS>), dim3((unsigned)P.nblocks),
              dim3(kThreads), 0, st, P);
   return MOE_OK;
