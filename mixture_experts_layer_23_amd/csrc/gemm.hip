@@ -52,7 +52,11 @@ struct GemmParams {
   int Kdim;           // reduction length for GROUP_M
   int Mfix;           // output rows for GROUP_K
   int ntn, ntm;       // tiles along N (and M for GROUP_K)
+  int mt_total;       // m-tiles in the tile space (GROUP_M: an upper bound)
   int64_t nblocks;
+  int64_t routed_rows_max;  // T*K when the local experts exist, else 0
+  int64_t shared_rows;      // n_shared*T
+  int n_routed;             // local routed groups
   // A operand: routed pointer (rows at offsets[g]) and shared pointer (row 0)
   const void* A;
   const void* A_sh;
@@ -83,14 +87,16 @@ MOE_DEV int64_t remap_xcd(int64_t b, int64_t n) {
   return (x < r) ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
 }
 
-// wave-parallel search of the group holding global m-tile mt (GROUP_M)
-MOE_DEV bool find_group(const int32_t* offsets, int G, int mt, int& g_out, int& mt_local) {
+// wave-parallel search of the group holding global m-tile mt (GROUP_M) for
+// tiles of bm rows
+MOE_DEV bool find_group(const int32_t* offsets, int G, int mt, int& g_out, int& mt_local,
+                        int bm = kBM) {
   const int lane = threadIdx.x & 63;
   const int gpl = (G + 63) / 64;
   int mine = 0;
   for (int j = 0; j < gpl; ++j) {
     const int g = lane * gpl + j;
-    if (g < G) mine += (offsets[g + 1] - offsets[g] + kBM - 1) / kBM;
+    if (g < G) mine += (offsets[g + 1] - offsets[g] + bm - 1) / bm;
   }
   int incl = mine;
 #pragma unroll
@@ -108,7 +114,7 @@ MOE_DEV bool find_group(const int32_t* offsets, int G, int mt, int& g_out, int& 
     for (int j = 0; j < gpl; ++j) {
       const int g = lane * gpl + j;
       if (g >= G) break;
-      const int n = (offsets[g + 1] - offsets[g] + kBM - 1) / kBM;
+      const int n = (offsets[g + 1] - offsets[g] + bm - 1) / bm;
       if (mt < run + n) { gsel = g; base = run; break; }
       run += n;
     }
@@ -281,16 +287,14 @@ MOE_DEV void mma_slab(const char* la, const char* lb, const int ra[2], const int
 MOE_DEV float silu_f(float a) { return a / (1.0f + expf(-a)); }
 
 // Epilogue shared by both GEMM kernels: each wave's 64 x 64 fp32 tile goes
-// through its own 16 KB of LDS (r0..r3, one per wave; chunks of 4 floats
+// through its own 16 KB region of LDS (chunks of 4 floats
 // XOR-swizzled by row) and is read back as rows of 8 consecutive columns, so
 // global loads and stores are 16-byte vectors.
 template <typename T, int GROUPING, int EPI>
-MOE_DEV void gemm_epilogue(const GemmParams& P, f32x16_t (&acc)[2][2], char* r0, char* r1,
-                           char* r2, char* r3, int m0, int n0, int rows_valid, int cols_valid,
-                           int64_t arow0, int g) {
+MOE_DEV void gemm_epilogue(const GemmParams& P, f32x16_t (&acc)[2][2], char* region, int m0,
+                           int n0, int rows_valid, int cols_valid, int64_t arow0, int g) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wm = wave >> 1, wn = wave & 1;
-  char* region = wave == 0 ? r0 : wave == 1 ? r1 : wave == 2 ? r2 : r3;  // 16 KB each
   const int l32 = lane & 31, hi4 = (lane >> 5) * 4;
   float* ep = reinterpret_cast<float*>(region);
 #pragma unroll
@@ -528,8 +532,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmParams P) {
     }
   }
 
-  gemm_epilogue<T, GROUPING, EPI>(P, acc, &smem[0][0][0], &smem[0][0][0] + 16384,
-                                   &smem[0][0][0] + 32768, &smem[0][0][0] + 49152, m0, n0,
+  gemm_epilogue<T, GROUPING, EPI>(P, acc, &smem[0][0][0] + (threadIdx.x >> 6) * 16384, m0, n0,
                                    rows_valid, cols_valid, arow0, g);
 }
 
@@ -565,6 +568,15 @@ MOE_DEV lds_void_t* to_lds(char* p) {
   return (lds_void_t*)(__attribute__((address_space(3))) char*)(p);
 }
 
+// 16-byte LDS-DMA loads.  Plain (non-template) device functions: the host
+// pass does not check the gfx950-only operand size inside them.
+MOE_DEV void dma16_global(const void* src, lds_void_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+}
+MOE_DEV void dma16_buffer(__amdgpu_buffer_rsrc_t rs, lds_void_t* dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, voff, 0, 0, 0);
+}
+
 // vmcnt wait with expcnt / lgkmcnt left open (gfx9 s_waitcnt encoding)
 template <int N>
 MOE_DEV void wait_vmcnt() {
@@ -592,7 +604,7 @@ MOE_DEV uint4 frag_kc(const char* tile, int rbase, int ks, int lane) {
   const int ch = ks * 2 + (lane >> 5);
   return *reinterpret_cast<const uint4*>(tile + r * 128 + ((ch ^ swz(r)) << 4));
 }
-MOE_DEV uint4 frag_mc(char* tile, int rbase, int ks, int lane) {
+MOE_DEV uint4 frag_mc(char* tile, int rbase, int ks, int lane, int pitch) {
   const int gi = lane >> 4, a = lane & 15, j = a >> 2, q = a & 3;
   const int col = rbase + (gi & 1) * 16 + 4 * q;
   const int lc = col >> 3, half = (col >> 2) & 1;
@@ -600,7 +612,7 @@ MOE_DEV uint4 frag_mc(char* tile, int rbase, int ks, int lane) {
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int krow = ks * 16 + (gi >> 1) * 8 + 4 * h + j;
-    char* p = tile + krow * 256 + ((lc ^ ((krow & 3) << 2)) << 4) + (half << 3);
+    char* p = tile + krow * pitch + ((lc ^ ((krow & 3) << 2)) << 4) + (half << 3);
     const v4s_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)(__attribute__((address_space(3))) char*)p);
     w[2 * h] = (uint32_t)(uint16_t)v[0] | ((uint32_t)(uint16_t)v[1] << 16);
     w[2 * h + 1] = (uint32_t)(uint16_t)v[2] | ((uint32_t)(uint16_t)v[3] << 16);
@@ -608,24 +620,50 @@ MOE_DEV uint4 frag_mc(char* tile, int rbase, int ks, int lane) {
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-template <int AMODE, int BMODE, int GROUPING, int EPI, int BSPL, int S>
-__global__ __launch_bounds__(256) void grouped_gemm_dma_kernel(GemmParams P) {
+// Tile order: super-columns of kSuperCols n-tiles; inside one, all m-tiles,
+// n fastest.  Together with the XCD remap, the workgroups that run together on
+// one XCD share a few weight panels and a few row panels in its L2.
+constexpr int kSuperCols = 8;
+MOE_DEV void supercol_tile(int64_t lin, int mt_total, int ntn, int& mt, int& nt) {
+  const int full = ntn / kSuperCols, rem = ntn % kSuperCols;
+  const int64_t span = (int64_t)mt_total * kSuperCols;
+  const int64_t sc = lin / span;
+  if (sc < full) {
+    const int64_t w = lin - sc * span;
+    mt = (int)(w / kSuperCols);
+    nt = (int)(sc * kSuperCols + w % kSuperCols);
+  } else {
+    const int64_t w = lin - (int64_t)full * span;
+    mt = (int)(w / rem);
+    nt = full * kSuperCols + (int)(w % rem);
+  }
+}
+
+// BMT x 128 tiles, NW = BMT / 32 waves (a (BMT/64) x 2 grid of 64 x 64 wave
+// tiles), S LDS stages.
+template <int AMODE, int BMODE, int GROUPING, int EPI, int BSPL, int BMT, int S>
+__global__ __launch_bounds__(BMT * 2) void grouped_gemm_dma_kernel(GemmParams P) {
   typedef bf16_t T;
   constexpr int BK = 64;
-  constexpr int TILE = 16384;  // bytes of one operand slab
+  constexpr int NW = BMT / 32;
+  constexpr int ATILE = BMT * 128;   // bytes of the A slab
+  constexpr int BTILE = 16384;       // bytes of the B slab (128 x 64 bf16)
+  constexpr int A_PER_WAVE = ATILE / 1024 / NW;  // DMA instructions per wave
+  constexpr int B_PER_WAVE = BTILE / 1024 / NW;
+  static_assert(A_PER_WAVE * NW * 1024 == ATILE && B_PER_WAVE * NW * 1024 == BTILE, "split");
+  static_assert(S == 2 || S == 3, "two or three stages");
+  static_assert(S * (ATILE + BTILE) >= NW * 16384, "the epilogue needs 16 KB per wave");
   // one LDS array per stage and operand: distinct objects let the compiler
   // see that the DMA into one stage does not alias the reads of another, so
   // it inserts no blanket wait for the loads in flight
-  __shared__ __attribute__((aligned(1024))) char sA0[TILE];
-  __shared__ __attribute__((aligned(1024))) char sB0[TILE];
-  __shared__ __attribute__((aligned(1024))) char sA1[TILE];
-  __shared__ __attribute__((aligned(1024))) char sB1[TILE];
-  __shared__ __attribute__((aligned(1024))) char sA2[S == 3 ? TILE : 16];
-  __shared__ __attribute__((aligned(1024))) char sB2[S == 3 ? TILE : 16];
-  static_assert(S == 2 || S == 3, "two or three stages");
+  __shared__ __attribute__((aligned(1024))) char sA0[ATILE];
+  __shared__ __attribute__((aligned(1024))) char sB0[BTILE];
+  __shared__ __attribute__((aligned(1024))) char sA1[ATILE];
+  __shared__ __attribute__((aligned(1024))) char sB1[BTILE];
+  __shared__ __attribute__((aligned(1024))) char sA2[S == 3 ? ATILE : 16];
+  __shared__ __attribute__((aligned(1024))) char sB2[S == 3 ? BTILE : 16];
   const int64_t lin = remap_xcd(blockIdx.x, P.nblocks);
-  // wave index as a scalar: the LDS destinations of the DMA loads must be
-  // wave-uniform
+  // the wave index as a scalar: DMA destinations must be wave-uniform
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int wm = wave >> 1, wn = wave & 1;
@@ -634,24 +672,25 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma_kernel(GemmParams P) {
   int64_t arow0;
   int nrows_g = 0;
   if constexpr (GROUPING == GROUP_M) {
-    const int mt = (int)(lin / P.ntn), nt = (int)(lin % P.ntn);
-    int mtl;
-    if (!find_group(P.offsets, P.G, mt, g, mtl)) return;
+    int mt, nt, mtl;
+    supercol_tile(lin, P.mt_total, P.ntn, mt, nt);
+    if (!find_group(P.offsets, P.G, mt, g, mtl, BMT)) return;
     g = __builtin_amdgcn_readfirstlane(g);
     mtl = __builtin_amdgcn_readfirstlane(mtl);
     nrows_g = P.offsets[g + 1] - P.offsets[g];
-    m0 = mtl * kBM;
+    m0 = mtl * BMT;
     n0 = nt * kBN;
-    rows_valid = min(kBM, nrows_g - m0);
+    rows_valid = min(BMT, nrows_g - m0);
     kdim = P.Kdim;
     arow0 = P.offsets[g];
   } else {
-    const int per = P.ntm * P.ntn;
+    const int64_t per = (int64_t)P.ntm * P.ntn;
     g = (int)(lin / per);
-    const int rem = (int)(lin % per);
-    m0 = (rem / P.ntn) * kBM;
-    n0 = (rem % P.ntn) * kBN;
-    rows_valid = kBM;
+    int mt, nt;
+    supercol_tile(lin - (int64_t)g * per, P.ntm, P.ntn, mt, nt);
+    m0 = mt * BMT;
+    n0 = nt * kBN;
+    rows_valid = BMT;
     kdim = P.offsets[g + 1] - P.offsets[g];
     arow0 = P.offsets[g];
   }
@@ -662,45 +701,43 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma_kernel(GemmParams P) {
                                  : reinterpret_cast<const T*>(P.A_sh);
   const int64_t a_rows = (GROUPING == GROUP_M) ? nrows_g : kdim;
   const __amdgpu_buffer_rsrc_t a_rs = make_rsrc(a_base, a_rows * P.lda * 2);
-  // per-lane byte offsets of this wave's 4 A instructions at k0 = 0
-  uint32_t a_off[4];
+  uint32_t a_off[A_PER_WAVE];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int t = wave * 4 + u;
-    int r, lc;
+  for (int u = 0; u < A_PER_WAVE; ++u) {
+    const int P_ = 64 * (wave * A_PER_WAVE + u) + lane;  // 16-byte chunk of the slab
     if constexpr (AMODE == KC) {
-      kc_slot(t, lane, r, lc);
+      const int r = P_ >> 3, lc = (P_ & 7) ^ swz(r);
       a_off[u] = (uint32_t)(((int64_t)(m0 + r) * P.lda + 8 * lc) * 2);
     } else {
-      mc_slot(t, lane, r, lc);
-      a_off[u] = (uint32_t)(((int64_t)r * P.lda + m0 + 8 * lc) * 2);
+      constexpr int CPR = BMT / 8;  // chunks per k-row
+      const int kr = P_ / CPR, lc = (P_ % CPR) ^ ((kr & 3) << 2);
+      a_off[u] = (uint32_t)(((int64_t)kr * P.lda + m0 + 8 * lc) * 2);
     }
   }
-  // ---- B source
-  // GROUP_M: weights, full tiles, per-lane global addresses
-  // GROUP_K: activations (k = rows of the group), buffer over the group rows
-  const T* b_ptr[4];
-  uint32_t b_off[4];
+  // ---- B source.  GROUP_M: weights, full tiles, per-lane global addresses.
+  // GROUP_K: activations (k = rows of the group), buffer over the group rows.
+  const T* b_ptr[B_PER_WAVE];
+  uint32_t b_off[B_PER_WAVE];
   __amdgpu_buffer_rsrc_t b_rs;
   const T* Bw0 = reinterpret_cast<const T*>(P.B0) + (int64_t)g * P.strideB;
   const T* Bw1 = (BSPL != BS_NONE) ? reinterpret_cast<const T*>(P.B1) + (int64_t)g * P.strideB
                                    : nullptr;
   if constexpr (GROUPING == GROUP_M) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int t = wave * 4 + u;
-      int r, lc;
+    for (int u = 0; u < B_PER_WAVE; ++u) {
+      const int P_ = 64 * (wave * B_PER_WAVE + u) + lane;
       if constexpr (BMODE == KC) {
-        kc_slot(t, lane, r, lc);
-        b_ptr[u] = Bw0 + (int64_t)(n0 + r) * P.ldb + 8 * lc;   // k0 added per slab
-      } else if constexpr (BSPL == BS_N) {
-        mc_slot(t, lane, r, lc);
-        const int col0 = n0 / 2;
-        b_ptr[u] = (lc < 8) ? Bw0 + (int64_t)r * P.ldb + col0 + 8 * lc
-                            : Bw1 + (int64_t)r * P.ldb + col0 + 8 * (lc - 8);
+        const int r = P_ >> 3, lc = (P_ & 7) ^ swz(r);
+        b_ptr[u] = Bw0 + (int64_t)(n0 + r) * P.ldb + 8 * lc;  // + k0 per slab
       } else {
-        mc_slot(t, lane, r, lc);
-        b_ptr[u] = Bw0 + (int64_t)r * P.ldb + n0 + 8 * lc;
+        const int kr = P_ >> 4, lc = (P_ & 15) ^ ((kr & 3) << 2);
+        if constexpr (BSPL == BS_N) {
+          const int col0 = n0 / 2;
+          b_ptr[u] = (lc < 8) ? Bw0 + (int64_t)kr * P.ldb + col0 + 8 * lc
+                              : Bw1 + (int64_t)kr * P.ldb + col0 + 8 * (lc - 8);
+        } else {
+          b_ptr[u] = Bw0 + (int64_t)kr * P.ldb + n0 + 8 * lc;
+        }
       }
     }
     b_rs = make_rsrc(Bw0, 16);
@@ -709,27 +746,23 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma_kernel(GemmParams P) {
                                    : reinterpret_cast<const T*>(P.B1);
     b_rs = make_rsrc(b_base, (int64_t)kdim * P.ldb * 2);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int t = wave * 4 + u;
-      int r, lc;
-      mc_slot(t, lane, r, lc);
-      b_off[u] = (uint32_t)(((int64_t)r * P.ldb + n0 + 8 * lc) * 2);
+    for (int u = 0; u < B_PER_WAVE; ++u) {
+      const int P_ = 64 * (wave * B_PER_WAVE + u) + lane;
+      const int kr = P_ >> 4, lc = (P_ & 15) ^ ((kr & 3) << 2);
+      b_off[u] = (uint32_t)(((int64_t)kr * P.ldb + n0 + 8 * lc) * 2);
     }
   }
 
-  // issue the 8 DMA instructions of this wave for slab kt into (la, lb)
+  // issue this wave's DMA instructions for slab kt into (la, lb)
   auto issue = [&](int kt, char* la, char* lb) {
     const int k0 = kt * BK;
+    const uint32_t kadd = (AMODE == KC) ? (uint32_t)(k0 * 2) : (uint32_t)((int64_t)k0 * P.lda * 2);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int t = wave * 4 + u;
-      const uint32_t kadd = (AMODE == KC) ? (uint32_t)(k0 * 2) : (uint32_t)((int64_t)k0 * P.lda * 2);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rs, to_lds(la + t * 1024), 16, a_off[u] + kadd, 0,
-                                               0, 0);
-    }
+    for (int u = 0; u < A_PER_WAVE; ++u)
+      dma16_buffer(a_rs, to_lds(la + (wave * A_PER_WAVE + u) * 1024), a_off[u] + kadd);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int t = wave * 4 + u;
+    for (int u = 0; u < B_PER_WAVE; ++u) {
+      char* dst = lb + (wave * B_PER_WAVE + u) * 1024;
       if constexpr (GROUPING == GROUP_M) {
         const T* src;
         if constexpr (BMODE == KC) {
@@ -742,11 +775,9 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma_kernel(GemmParams P) {
         } else {
           src = b_ptr[u] + (int64_t)k0 * P.ldb;
         }
-        __builtin_amdgcn_global_load_lds(src, to_lds(lb + t * 1024), 16, 0, 0);
+        dma16_global(src, to_lds(dst));
       } else {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rs, to_lds(lb + t * 1024), 16,
-                                                 b_off[u] + (uint32_t)((int64_t)k0 * P.ldb * 2),
-                                                 0, 0, 0);
+        dma16_buffer(b_rs, to_lds(dst), b_off[u] + (uint32_t)((int64_t)k0 * P.ldb * 2));
       }
     }
   };
@@ -770,17 +801,17 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma_kernel(GemmParams P) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // one pipeline step: slab kt is in (la, lb); slab kt + S - 1 goes to (na, nb)
   auto mma = [&](char* la, char* lb) {
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
       uint4 fa[2], fb[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        fa[i] = (AMODE == KC) ? frag_kc(la, ra[i], ks, lane) : frag_mc(la, ra[i], ks, lane);
+        fa[i] = (AMODE == KC) ? frag_kc(la, ra[i], ks, lane)
+                              : frag_mc(la, ra[i], ks, lane, BMT * 2);
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        fb[j] = (BMODE == KC) ? frag_kc(lb, rb[j], ks, lane) : frag_mc(lb, rb[j], ks, lane);
+        fb[j] = (BMODE == KC) ? frag_kc(lb, rb[j], ks, lane) : frag_mc(lb, rb[j], ks, lane, 256);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -791,9 +822,11 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma_kernel(GemmParams P) {
     }
   };
   const int nk = (kdim + BK - 1) / BK;
+  constexpr int PER_SLAB = A_PER_WAVE + B_PER_WAVE;  // DMA instructions per slab
+  // one pipeline step: slab kt is in (la, lb); slab kt + S - 1 goes to (na, nb)
   auto step = [&](int kt, char* la, char* lb, char* na, char* nb) {
     // slab kt has landed once at most the next slab's loads are outstanding
-    if (S == 3 && kt + 1 < nk) wait_vmcnt<8>();
+    if (S == 3 && kt + 1 < nk) wait_vmcnt<PER_SLAB>();
     else wait_vmcnt<0>();
     __syncthreads();
     if (kt + S - 1 < nk) issue(kt + S - 1, na, nb);
@@ -819,8 +852,15 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma_kernel(GemmParams P) {
     if (kt + 1 < nk) step(kt + 1, sA1, sB1, sA0, sB0);
   }
   __syncthreads();
-  gemm_epilogue<T, GROUPING, EPI>(P, acc, sA0, sB0, sA1, sB1, m0, n0, rows_valid, cols_valid,
-                                  arow0, g);
+  // 16 KB of LDS per wave for the epilogue, carved from the stage arrays
+  char* region;
+  if constexpr (BMT == 128) {
+    region = wave == 0 ? sA0 : wave == 1 ? sB0 : wave == 2 ? sA1 : sB1;
+  } else {
+    region = wave < 2 ? sA0 + wave * 16384 : wave == 2 ? sB0 : wave < 5 ? sA1 + (wave - 3) * 16384
+           : wave == 5 ? sB1 : sA2 + (wave - 6) * 16384;
+  }
+  gemm_epilogue<T, GROUPING, EPI>(P, acc, region, m0, n0, rows_valid, cols_valid, arow0, g);
 }
 
 // ---------------------------------------------------------------------------
@@ -828,42 +868,60 @@ __global__ __launch_bounds__(256) void grouped_gemm_dma_kernel(GemmParams P) {
 // ---------------------------------------------------------------------------
 static int groups_of(const moe_config& c) { return (c.expert_hi - c.expert_lo) + c.n_shared; }
 
-// upper bound of m-tiles over all groups: sum ceil(n_g/BM) <= rows/BM + G
-static int64_t mtiles_bound(const moe_config& c) {
-  const int64_t routed = (int64_t)c.T * c.K;
-  const int EL = c.expert_hi - c.expert_lo;
-  int64_t b = (EL > 0) ? cdiv(routed, kBM) + EL : 0;
-  if (c.n_shared) b += cdiv(c.T, kBM) * c.n_shared;
-  return b;
+// tile-space sizes for tiles of bm rows
+static void tile_space(GemmParams& P, int grouping, int bm) {
+  if (grouping == GROUP_M) {
+    // sum over groups of ceil(n_g / bm) <= ceil(rows / bm) + groups
+    int64_t b = (P.routed_rows_max > 0) ? cdiv(P.routed_rows_max, bm) + P.n_routed : 0;
+    if (P.shared_rows > 0) b += cdiv(P.shared_rows, bm);
+    P.mt_total = (int)b;
+    P.nblocks = b * P.ntn;
+  } else {
+    P.ntm = (int)cdiv(P.Mfix, bm);
+    P.nblocks = (int64_t)P.G * P.ntm * P.ntn;
+  }
 }
 
-static int dma_stages() {
-  static int s = [] {
-    const char* e = getenv("MOE_GEMM_STAGES");
-    const int v = e ? atoi(e) : 2;
-    return (v == 3) ? 3 : (v == 0 ? 0 : 2);
+// GEMM configuration of the LDS-DMA kernel: 0 = register-staged kernel,
+// 1 = 128-row tiles / 2 stages, 2 = 256-row tiles / 3 stages.
+// MOE_GEMM_CFG overrides the choice (measurement only).
+static int cfg_override() {
+  static int v = [] {
+    const char* e = getenv("MOE_GEMM_CFG");
+    return e ? atoi(e) : -1;
   }();
-  return s;
+  return v;
 }
 
-// bf16 with whole 128-column (and, for the weight gradients, 128-row) tiles
-// runs on the LDS-DMA kernel; fp32 and ragged shapes on the register-staged one
+template <int AM, int BM_, int GR, int EPI, int BS, int BMT, int S>
+static int launch_dma(const char* name, GemmParams P, hipStream_t st) {
+  tile_space(P, GR, BMT);
+  if (P.nblocks <= 0) return MOE_OK;
+  MOE_LAUNCH(name, (grouped_gemm_dma_kernel<AM, BM_, GR, EPI, BS, BMT, S>),
+             dim3((unsigned)P.nblocks), dim3(BMT * 2), 0, st, P);
+  return MOE_OK;
+}
+
+// bf16 with whole 128-column (and, for the weight gradients, whole-tile-row)
+// tiles runs on the LDS-DMA kernel -- 256-row tiles when that still gives at
+// least two workgroups per CU, else 128-row tiles; fp32 and ragged shapes
+// run on the register-staged kernel.
 template <typename T, int AM, int BM_, int GR, int EPI, int BS>
 static int run_gemm(const char* name, GemmParams& P, hipStream_t st) {
-  if (P.nblocks <= 0) return MOE_OK;
-  const bool full = (P.N % kBN == 0) && (GR == GROUP_M ? P.Kdim % 64 == 0 : P.Mfix % kBM == 0);
   if constexpr (sizeof(T) == 2) {
-    if (full && dma_stages() == 3) {
-      MOE_LAUNCH(name, (grouped_gemm_dma_kernel<AM, BM_, GR, EPI, BS, 3>),
-                 dim3((unsigned)P.nblocks), dim3(kThreads), 0, st, P);
-      return MOE_OK;
+    const bool full128 = (P.N % kBN == 0) && (GR == GROUP_M ? P.Kdim % 64 == 0 : P.Mfix % 128 == 0);
+    const bool full256 = full128 && (GR == GROUP_M || P.Mfix % 256 == 0);
+    int cfg = cfg_override();
+    if (cfg < 0) {
+      GemmParams Q = P;
+      tile_space(Q, GR, 256);
+      cfg = (full256 && Q.nblocks >= 512) ? 2 : 1;
     }
-    if (full && dma_stages() == 2) {
-      MOE_LAUNCH(name, (grouped_gemm_dma_kernel<AM, BM_, GR, EPI, BS, 2>),
-                 dim3((unsigned)P.nblocks), dim3(kThreads), 0, st, P);
-      return MOE_OK;
-    }
+    if (cfg == 2 && full256) return launch_dma<AM, BM_, GR, EPI, BS, 256, 3>(name, P, st);
+    if (cfg >= 1 && full128) return launch_dma<AM, BM_, GR, EPI, BS, 128, 2>(name, P, st);
   }
+  tile_space(P, GR, kBM);
+  if (P.nblocks <= 0) return MOE_OK;
   MOE_LAUNCH(name, (grouped_gemm_kernel<T, AM, BM_, GR, EPI, BS>), dim3((unsigned)P.nblocks),
              dim3(kThreads), 0, st, P);
   return MOE_OK;
@@ -873,6 +931,9 @@ static GemmParams base_params(const moe_config& c, const int32_t* offsets) {
   GemmParams P = {};
   P.G = groups_of(c);
   P.EL_A = P.EL_B = c.expert_hi - c.expert_lo;
+  P.n_routed = c.expert_hi - c.expert_lo;
+  P.routed_rows_max = (P.n_routed > 0) ? (int64_t)c.T * c.K : 0;
+  P.shared_rows = (int64_t)c.n_shared * c.T;
   P.offsets = offsets;
   P.F = c.F;
   P.csplit = 1 << 30;
@@ -886,7 +947,6 @@ int gemm_swiglu_fwd(const moe_config& c, const void* x, const void* x_perm,
   P.N = 2 * c.F;
   P.Kdim = c.D;
   P.ntn = (int)cdiv(P.N, kBN);
-  P.nblocks = mtiles_bound(c) * P.ntn;
   P.A = x_perm; P.A_sh = x; P.lda = c.D;
   P.B0 = wg; P.B1 = wu; P.ldb = c.F; P.strideB = (int64_t)c.D * c.F;
   P.C1 = h; P.act_out = act;
@@ -900,7 +960,6 @@ int gemm_down_fwd(const moe_config& c, const int32_t* offsets, const void* h, co
   P.N = c.D;
   P.Kdim = c.F;
   P.ntn = (int)cdiv(P.N, kBN);
-  P.nblocks = mtiles_bound(c) * P.ntn;
   // shared rows of h live in the same row buffer: every group reads its rows
   P.EL_A = P.G;
   P.A = h; P.A_sh = h; P.lda = c.F;
@@ -916,7 +975,6 @@ int gemm_down_dgrad(const moe_config& c, const int32_t* offsets, const void* d_o
   P.N = c.F;
   P.Kdim = c.D;
   P.ntn = (int)cdiv(P.N, kBN);
-  P.nblocks = mtiles_bound(c) * P.ntn;
   P.A = d_o; P.A_sh = dy; P.lda = c.D;
   // B(k = d, n = f) = W_down[f][d]: row n, K contiguous
   P.B0 = wd; P.ldb = c.D; P.strideB = (int64_t)c.F * c.D;
@@ -931,7 +989,6 @@ int gemm_up_dgrad(const moe_config& c, const int32_t* offsets, const void* dact,
   P.N = c.D;
   P.Kdim = 2 * c.F;
   P.ntn = (int)cdiv(P.N, kBN);
-  P.nblocks = mtiles_bound(c) * P.ntn;
   P.EL_A = P.G;  // dact holds the shared rows too
   P.A = dact; P.A_sh = dact; P.lda = 2 * c.F;
   // B(k = f, n = d) = W_gate[d][f] for f < F, W_up[d][f - F] above
@@ -946,9 +1003,7 @@ int gemm_down_wgrad(const moe_config& c, const int32_t* offsets, const void* h, 
   GemmParams P = base_params(c, offsets);
   P.Mfix = c.F;
   P.N = c.D;
-  P.ntm = (int)cdiv(P.Mfix, kBM);
   P.ntn = (int)cdiv(P.N, kBN);
-  P.nblocks = (int64_t)P.G * P.ntm * P.ntn;
   // A(m = f, k = row) = h[row][f]: every group (shared too) reads its h rows;
   // B(k = row, n = d) = d_o[row][d] for routed groups, dy[token][d] for shared
   P.EL_A = P.G;
@@ -964,9 +1019,7 @@ int gemm_up_wgrad(const moe_config& c, const int32_t* offsets, const void* x, co
   GemmParams P = base_params(c, offsets);
   P.Mfix = c.D;
   P.N = 2 * c.F;
-  P.ntm = (int)cdiv(P.Mfix, kBM);
   P.ntn = (int)cdiv(P.N, kBN);
-  P.nblocks = (int64_t)P.G * P.ntm * P.ntn;
   P.A = x_perm; P.A_sh = x; P.lda = c.D;
   // B(k = row, n) = dact[row][n], n in [0, 2F): every group reads dact rows
   P.EL_B = P.G;
