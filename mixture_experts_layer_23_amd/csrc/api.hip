@@ -79,12 +79,11 @@ Workspace workspace_layout(const moe_config& c) {
   L.ntiles = (int)std::max<int64_t>(1, cdiv(TK, kSlotTile));
   L.aux_blocks = (int)std::max<int64_t>(1, cdiv(c.T, aux_tokens_per_block(c.E)));
   if (c.E <= 16) {
-    // token chunks of the few-expert router weight gradient: about 256
-    // workgroups, chunks of at most 256 tokens
-    const int64_t dblk = cdiv(c.D, 256);
-    int64_t nchunk = std::max<int64_t>(1, cdiv(256, dblk));
-    nchunk = std::min<int64_t>(nchunk, std::max<int64_t>(1, cdiv(c.T, 8)));
-    nchunk = std::max<int64_t>(nchunk, cdiv(c.T, 256));
+    // token chunks of the few-expert router weight gradient: about 320
+    // workgroups, chunks of at least 16 tokens
+    const int64_t dblk = cdiv(c.D, 64 * router_wgrad_width(c));
+    int64_t nchunk = std::max<int64_t>(1, cdiv(320, dblk));
+    nchunk = std::min<int64_t>(nchunk, std::max<int64_t>(1, cdiv(c.T, 16)));
     // every chunk must be non-empty: re-derive the count from the chunk length
     const int64_t len = cdiv(std::max<int64_t>(c.T, 1), nchunk);
     L.dwr_splits = (int)std::max<int64_t>(1, cdiv(std::max<int64_t>(c.T, 1), len));
@@ -105,6 +104,13 @@ Workspace workspace_layout(const moe_config& c) {
   L.ds = o;          o += al((size_t)c.T * c.E * 4);
   L.dxr = o;         o += (c.E > 16) ? al((size_t)c.T * c.D * 4) : 0;
   L.dwr_part = o;    o += al((size_t)L.dwr_splits * (((size_t)c.E * c.D + c.E + 3) & ~(size_t)3) * 4);
+  // router-bias partials (large E): chunks of at least 128 tokens, at most 64
+  {
+    const int64_t T1 = std::max<int64_t>(c.T, 1);
+    const int64_t len = std::max<int64_t>(128, cdiv(T1, 64));
+    L.rb_splits = (int)cdiv(T1, len);
+  }
+  L.rb_part = o;     o += al((size_t)L.rb_splits * (((size_t)c.E + 3) & ~(size_t)3) * 4);
   L.total = o;
   return L;
 }

@@ -92,18 +92,28 @@ __global__ __launch_bounds__(256) void aux_partial_kernel(const float* __restric
   }
 }
 
+// column sums of the partials (E mean-probability sums and the z-loss sum):
+// wave w takes columns w, w+16, ..., its lanes take blocks lane, lane+64, ...,
+// butterfly-added; then sum_e f_e P_e in a fixed tree.  No atomics.
 __global__ __launch_bounds__(1024) void aux_final_kernel(const float* __restrict__ part,
                                                          int nblk, const int32_t* __restrict__ counts,
                                                          int T_, int E, int K, float alpha,
                                                          float zlam, float* __restrict__ losses) {
+  __shared__ float col[1025];
   __shared__ float red[1024];
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  for (int c = wave; c <= E; c += 16) {
+    float s = 0.f;
+    for (int b = lane; b < nblk; b += 64) s += part[(size_t)b * (E + 1) + c];
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m, 64);
+    if (lane == 0) col[c] = s;
+  }
+  __syncthreads();
   float v = 0.f;
   for (int e = tid; e < E; e += 1024) {
-    float P = 0.f;
-    for (int b = 0; b < nblk; ++b) P += part[(size_t)b * (E + 1) + e];
     const float f = (float)counts[e] / ((float)T_ * (float)K);
-    v += f * (P / (float)T_);
+    v += f * (col[e] / (float)T_);
   }
   red[tid] = v;
   __syncthreads();
@@ -112,8 +122,7 @@ __global__ __launch_bounds__(1024) void aux_final_kernel(const float* __restrict
     __syncthreads();
   }
   if (tid == 0) {
-    float z2 = 0.f;
-    for (int b = 0; b < nblk; ++b) z2 += part[(size_t)b * (E + 1) + E];
+    const float z2 = col[E];
     losses[0] = alpha * (float)E * red[0];
     losses[1] = zlam * z2 / (float)T_;
     losses[2] = z2 / (float)T_;

@@ -139,75 +139,141 @@ static int launch_gating_bwd(const moe_config& c, const float* lg, const int32_t
 }
 
 // ---------------------------------------------------------------------------
-// router weight gradient, few experts (E <= 16): each thread owns one model
-// dim and sums ds[t,e] * x[t,d] over a chunk of tokens
-// (the chunk's ds rows staged in LDS); chunk partials are reduced in a fixed
-// order afterwards.  The d-block 0 threads also sum the router-bias partial.
-// The chunk length is chosen on the host so that about 256 workgroups run.
+// router weight gradient, few experts (E <= 16):
+//   part[chunk][e][d] = sum_{t in chunk} ds[t,e] x[t,d],  part[chunk][E+e] = sum ds[t,e]
+// A workgroup owns 64*W model dims (W consecutive per lane, one 8- or 16-byte
+// load per token) and one token chunk; its four waves take every fourth token
+// and are added in wave order at the end.  ds rows are wave-uniform scalar
+// loads.  Workgroups with blockIdx.x == 0 also form the router-bias partial.
+// The chunk partials are reduced in a fixed order afterwards.
 // ---------------------------------------------------------------------------
-constexpr int kRouterChunkMax = 256;
+template <typename T, int W> struct RowLoad;
+template <> struct RowLoad<float, 4> {
+  static MOE_DEV void f32(const float* p, float* o) {
+    const float4 v = *reinterpret_cast<const float4*>(p);
+    o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+  }
+};
+template <> struct RowLoad<bf16_t, 4> {
+  static MOE_DEV void f32(const bf16_t* p, float* o) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    o[0] = __uint_as_float(v.x << 16); o[1] = __uint_as_float(v.x & 0xFFFF0000u);
+    o[2] = __uint_as_float(v.y << 16); o[3] = __uint_as_float(v.y & 0xFFFF0000u);
+  }
+};
+template <> struct RowLoad<bf16_t, 8> {
+  static MOE_DEV void f32(const bf16_t* p, float* o) {
+    Vec16<bf16_t> v;
+    v.load(p);
+    v.to_f32(o);
+  }
+};
 
-template <typename T, int EM>
+template <typename T, int EM, int W>
 __global__ __launch_bounds__(256) void router_wgrad_skinny_kernel(
     const float* __restrict__ ds, const T* __restrict__ x, int T_, int D, int E, int chunk_len,
     float* __restrict__ part) {
-  __shared__ float sds[kRouterChunkMax * EM];
+  __shared__ float red[3][64 * W];
+  __shared__ float redb[4][EM];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int chunk = blockIdx.y;
   const int t0 = chunk * chunk_len;
-  const int nt = min(chunk_len, T_ - t0);
-  for (int i = threadIdx.x; i < nt * E; i += blockDim.x) sds[i] = ds[(size_t)t0 * E + i];
-  __syncthreads();
-  const int d = blockIdx.x * blockDim.x + threadIdx.x;
-  if (d >= D) return;
-  float acc[EM], accb[EM];
+  const int t1 = min(T_, t0 + chunk_len);
+  const int d = blockIdx.x * 64 * W + lane * W;
+  const bool dok = d < D;
+  float acc[EM][W], accb[EM];
 #pragma unroll
-  for (int e = 0; e < EM; ++e) { acc[e] = 0.f; accb[e] = 0.f; }
-  const T* xp = x + (size_t)t0 * D + d;
-  for (int t = 0; t < nt; ++t) {
-    const float xv = Elem<T>::to_f32(xp[(size_t)t * D]);
+  for (int e = 0; e < EM; ++e) {
+    accb[e] = 0.f;
+#pragma unroll
+    for (int i = 0; i < W; ++i) acc[e][i] = 0.f;
+  }
+#pragma unroll 4
+  for (int t = t0 + wave; t < t1; t += 4) {
+    float xv[W];
+    if (dok) RowLoad<T, W>::f32(x + (size_t)t * D + d, xv);
+    else
+#pragma unroll
+      for (int i = 0; i < W; ++i) xv[i] = 0.f;
+    const float* dsr = ds + (size_t)t * E;
 #pragma unroll
     for (int e = 0; e < EM; ++e) {
       if (e < E) {
-        const float s = sds[t * E + e];
+        const float s = dsr[e];
         accb[e] += s;
-        acc[e] = fmaf(s, xv, acc[e]);
+#pragma unroll
+        for (int i = 0; i < W; ++i) acc[e][i] = fmaf(s, xv[i], acc[e][i]);
       }
     }
   }
   // partial row stride rounded up to 4 floats (shared with the workspace layout)
   float* p = part + (size_t)chunk * (((size_t)E * D + E + 3) & ~(size_t)3);
 #pragma unroll
-  for (int e = 0; e < EM; ++e)
-    if (e < E) p[(size_t)e * D + d] = acc[e];
-  if (d == 0)
+  for (int e = 0; e < EM; ++e) {
+    if (e >= E) break;
+    if (wave > 0)
 #pragma unroll
-    for (int e = 0; e < EM; ++e)
-      if (e < E) p[(size_t)E * D + e] = accb[e];
+      for (int i = 0; i < W; ++i) red[wave - 1][lane * W + i] = acc[e][i];
+    __syncthreads();
+    if (wave == 0 && dok) {
+      float o[W];
+#pragma unroll
+      for (int i = 0; i < W; ++i)
+        o[i] = ((acc[e][i] + red[0][lane * W + i]) + red[1][lane * W + i]) + red[2][lane * W + i];
+#pragma unroll
+      for (int i = 0; i < W; i += 4)
+        *reinterpret_cast<float4*>(p + (size_t)e * D + d + i) =
+            make_float4(o[i], o[i + 1], o[i + 2], o[i + 3]);
+    }
+    __syncthreads();
+  }
+  if (blockIdx.x == 0) {
+    if (lane == 0)
+#pragma unroll
+      for (int e = 0; e < EM; ++e) redb[wave][e] = accb[e];
+    __syncthreads();
+    if (threadIdx.x < E)
+      p[(size_t)E * D + threadIdx.x] = ((redb[0][threadIdx.x] + redb[1][threadIdx.x]) +
+                                        redb[2][threadIdx.x]) + redb[3][threadIdx.x];
+  }
 }
 
 // fixed-order sum of the split partials: out[i] = sum_s part[s * stride + i].
-// 16 columns x 16 split lanes per workgroup; lane ty sums splits ty, ty+16, ...
-// and the 16 lane sums are added in lane order, so the result does not depend
-// on scheduling.
+// 64 columns (16 float4 lanes) x 16 split lanes per workgroup; lane ty sums
+// splits ty, ty+16, ... and the 16 lane sums are added in lane order, so the
+// result does not depend on scheduling.  stride and n_first are multiples of 4
+// and part holds stride floats per split (columns n..stride-1 are padding).
 __global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restrict__ part,
                                                             int nsplit, int64_t n,
                                                             int64_t stride, float* __restrict__ out,
                                                             float* __restrict__ out2,
                                                             int64_t n_first) {
-  __shared__ float red[16][17];
+  __shared__ float4 red[16][17];
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-  const int64_t i = (int64_t)blockIdx.x * 16 + tx;
-  float s = 0.f;
+  const int64_t i = ((int64_t)blockIdx.x * 16 + tx) * 4;
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
   if (i < n)
-    for (int k = ty; k < nsplit; k += 16) s += part[(size_t)k * stride + i];
+#pragma unroll 4
+    for (int k = ty; k < nsplit; k += 16) {
+      const float4 v = *reinterpret_cast<const float4*>(part + (size_t)k * stride + i);
+      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    }
   red[ty][tx] = s;
   __syncthreads();
   if (ty == 0 && i < n) {
-    float t = 0.f;
+    float t[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k = 0; k < 16; ++k) t += red[k][tx];
-    if (i < n_first) out[i] = t;
-    else if (out2) out2[i - n_first] = t;
+    for (int k = 0; k < 16; ++k) {
+      const float4 v = red[k][tx];
+      t[0] += v.x; t[1] += v.y; t[2] += v.z; t[3] += v.w;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t c = i + j;
+      if (c >= n) break;
+      if (c < n_first) out[c] = t[j];
+      else if (out2) out2[c - n_first] = t[j];
+    }
   }
 }
 
@@ -298,14 +364,24 @@ __global__ __launch_bounds__(256) void simt_gemm_kernel(const TA* __restrict__ A
   }
 }
 
-// d r_b[e] = sum_t ds[t,e] (fixed order), one thread per expert
-__global__ void rbias_grad_kernel(const float* __restrict__ ds, int T_, int E,
-                                  float* __restrict__ drb) {
-  const int e = blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= E) return;
+// d r_b partials: part[chunk][e] = sum_{t in chunk} ds[t,e].  64 experts x 4
+// token lanes per workgroup (lane ty takes every fourth token of the chunk),
+// lanes added in order; the chunk partials are reduced in a fixed order after.
+__global__ __launch_bounds__(256) void rbias_partial_kernel(const float* __restrict__ ds, int T_,
+                                                            int E, int chunk_len, int64_t stride,
+                                                            float* __restrict__ part) {
+  __shared__ float red[4][64];
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const int e = blockIdx.x * 64 + tx;
+  const int t0 = blockIdx.y * chunk_len, t1 = min(T_, t0 + chunk_len);
   float s = 0.f;
-  for (int t = 0; t < T_; ++t) s += ds[(size_t)t * E + e];
-  drb[e] = s;
+  if (e < E)
+#pragma unroll 8
+    for (int t = t0 + ty; t < t1; t += 4) s += ds[(size_t)t * E + e];
+  red[ty][tx] = s;
+  __syncthreads();
+  if (ty == 0 && e < E)
+    part[(size_t)blockIdx.y * stride + e] = ((red[0][tx] + red[1][tx]) + red[2][tx]) + red[3][tx];
 }
 
 template <typename T>
@@ -317,17 +393,25 @@ static int router_bwd_t(const moe_config& c, const void* x, const float* wr, con
   if (E <= 16) {
     const int nchunk = L.dwr_splits;
     const int chunk_len = (int)cdiv(T_, nchunk);
-    dim3 grid((unsigned)cdiv(D, 256), (unsigned)nchunk);
-#define RW(EMV)                                                                               \
-  MOE_LAUNCH("router_wgrad", (router_wgrad_skinny_kernel<T, EMV>), grid, dim3(256), 0, st, ds, \
-             (const T*)x, T_, D, E, chunk_len, part)
-    if (E <= 4) RW(4);
-    else if (E <= 8) RW(8);
-    else RW(16);
+    const int W = router_wgrad_width(c);
+    dim3 grid((unsigned)cdiv(D, 64 * W), (unsigned)nchunk);
+#define RW(EMV, WV)                                                                        \
+  MOE_LAUNCH("router_wgrad", (router_wgrad_skinny_kernel<T, EMV, WV>), grid, dim3(256), 0, st, \
+             ds, (const T*)x, T_, D, E, chunk_len, part)
+#define RWE(WV)                \
+  if (E <= 4) RW(4, WV);       \
+  else if (E <= 8) RW(8, WV);  \
+  else RW(16, WV);
+    if constexpr (sizeof(T) == 2) {
+      if (W == 8) { RWE(8) } else { RWE(4) }
+    } else {
+      RWE(4)
+    }
+#undef RWE
 #undef RW
     const int64_t n = (int64_t)E * D + E;
     const int64_t stride = (n + 3) & ~(int64_t)3;
-    MOE_LAUNCH("router_wgrad_reduce", reduce_splits_kernel, dim3((unsigned)cdiv(n, 16)),
+    MOE_LAUNCH("router_wgrad_reduce", reduce_splits_kernel, dim3((unsigned)cdiv(n, 64)),
                dim3(256), 0, st, part, nchunk, n, stride, dwr, drb, (int64_t)E * D);
   } else {
     // dxr[T,D] = ds[T,E] W_r[E,D]
@@ -342,11 +426,19 @@ static int router_bwd_t(const moe_config& c, const void* x, const float* wr, con
                (int64_t)E, (const T*)x, (int64_t)D, E, D, T_, kper, part, (int64_t)D,
                (int64_t)E * D);
     const int64_t n = (int64_t)E * D;
-    MOE_LAUNCH("router_wgrad_reduce", reduce_splits_kernel, dim3((unsigned)cdiv(n, 16)),
+    MOE_LAUNCH("router_wgrad_reduce", reduce_splits_kernel, dim3((unsigned)cdiv(n, 64)),
                dim3(256), 0, st, part, splits, n, n, dwr, (float*)nullptr, n);
-    if (drb)
-      MOE_LAUNCH("router_bias_grad", rbias_grad_kernel, dim3((unsigned)cdiv(E, 256)), dim3(256),
-                 0, st, ds, T_, E, drb);
+    if (drb) {
+      float* rpart = reinterpret_cast<float*>(ws + L.rb_part);
+      const int64_t rstride = ((int64_t)E + 3) & ~(int64_t)3;
+      const int clen = (int)cdiv(T_, L.rb_splits);
+      MOE_LAUNCH("router_bias_grad", rbias_partial_kernel,
+                 dim3((unsigned)cdiv(E, 64), (unsigned)L.rb_splits), dim3(256), 0, st, ds, T_, E,
+                 clen, rstride, rpart);
+      MOE_LAUNCH("router_bias_reduce", reduce_splits_kernel, dim3((unsigned)cdiv(E, 64)),
+                 dim3(256), 0, st, rpart, L.rb_splits, (int64_t)E, rstride, drb, (float*)nullptr,
+                 (int64_t)E);
+    }
   }
   return MOE_OK;
 }

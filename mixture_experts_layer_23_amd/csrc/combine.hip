@@ -9,48 +9,49 @@
 // slot this device does not serve (sentinel) -- and, by the same rule, for a
 // dropped slot.
 //
-// All three kernels are HBM-bound row streams: 16-byte vector loads, fp32
-// accumulation in a fixed k order (no atomics, deterministic).
+// All three kernels are HBM-bound row streams, one wave per token: 16-byte
+// vector loads, fp32 accumulation in a fixed k order (no atomics,
+// deterministic).
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 
-// y[t] = sum_k [row>=0] g[t,k] * o[row] + o[shared row of t]
+// y[t] = sum_k [row>=0] g[t,k] * o[row] + o[shared row of t]; one wave per
+// token, lane k holds slot k's row and weight, lanes stride over the row's
+// 16-byte vectors
 template <typename T>
 __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ o,
                                                       const int32_t* __restrict__ slot_row,
                                                       const float* __restrict__ topk_w,
                                                       const int32_t* __restrict__ offsets,
                                                       int EL, int n_shared, int T_, int K, int D,
-                                                      int nv, T* __restrict__ y) {
+                                                      T* __restrict__ y) {
   constexpr int VEC = Elem<T>::VEC;
-  const int64_t total = (int64_t)T_ * nv;
-  const int64_t b0 = (int64_t)blockIdx.x * 1024 + threadIdx.x;
-  const int shared0 = n_shared ? offsets[EL] : 0;
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int64_t it = b0 + u * 256;
-    if (it >= total) break;
-    const int t = (int)(it / nv);
-    const int c = (int)(it - (int64_t)t * nv);
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= T_) return;
+  const int my_row = lane < K ? slot_row[(size_t)t * K + lane] : -1;
+  const float my_g = lane < K ? topk_w[(size_t)t * K + lane] : 0.f;
+  const int64_t srow = n_shared ? (int64_t)offsets[EL] + t : -1;
+  for (int d0 = lane * VEC; d0 < D; d0 += 64 * VEC) {
     float acc[VEC];
 #pragma unroll
     for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
     for (int k = 0; k < K; ++k) {
-      const int row = slot_row[(size_t)t * K + k];
+      const int row = __shfl(my_row, k, 64);
       if (row < 0) continue;
-      const float g = topk_w[(size_t)t * K + k];
+      const float g = __shfl(my_g, k, 64);
       Vec16<T> v;
-      v.load(o + (size_t)row * D + (size_t)c * VEC);
+      v.load(o + (size_t)row * D + d0);
       float f[VEC];
       v.to_f32(f);
 #pragma unroll
       for (int i = 0; i < VEC; ++i) acc[i] = fmaf(g, f[i], acc[i]);
     }
-    if (n_shared) {
+    if (srow >= 0) {
       Vec16<T> v;
-      v.load(o + (size_t)(shared0 + t) * D + (size_t)c * VEC);
+      v.load(o + (size_t)srow * D + d0);
       float f[VEC];
       v.to_f32(f);
 #pragma unroll
@@ -58,7 +59,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ o,
     }
     Vec16<T> out;
     out.from_f32(acc);
-    out.store(y + (size_t)t * D + (size_t)c * VEC);
+    out.store(y + (size_t)t * D + d0);
   }
 }
 
@@ -108,28 +109,30 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const T* __restrict__ 
 
 // dx[t] = sum_k [row>=0] dx_perm[row] + dx_perm[shared row of t]
 //         + router part: sum_e ds[t,e] W_r[e,:] (inline for E <= EM) or dxr[t]
+// one wave per token, lanes stride over 16-byte vectors of the row
 template <typename T, int EM>
 __global__ __launch_bounds__(256) void unpermute_kernel(
     const T* __restrict__ dxp, const int32_t* __restrict__ slot_row,
     const int32_t* __restrict__ offsets, int EL, int n_shared, const float* __restrict__ ds,
     const float* __restrict__ wr, int E, const float* __restrict__ dxr, int T_, int K, int D,
-    int nv, T* __restrict__ dx) {
+    T* __restrict__ dx) {
   constexpr int VEC = Elem<T>::VEC;
-  const int64_t total = (int64_t)T_ * nv;
-  const int64_t b0 = (int64_t)blockIdx.x * 1024 + threadIdx.x;
-  const int shared0 = n_shared ? offsets[EL] : 0;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= T_) return;
+  const int my_row = lane < K ? slot_row[(size_t)t * K + lane] : -1;
+  const int64_t srow = n_shared ? (int64_t)offsets[EL] + t : -1;
+  float s_e[EM > 0 ? EM : 1];
+  if constexpr (EM > 0) {
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int64_t it = b0 + u * 256;
-    if (it >= total) break;
-    const int t = (int)(it / nv);
-    const int c = (int)(it - (int64_t)t * nv);
-    const int d0 = c * VEC;
+    for (int e = 0; e < EM; ++e) s_e[e] = (e < E) ? ds[(size_t)t * E + e] : 0.f;
+  }
+  for (int d0 = lane * VEC; d0 < D; d0 += 64 * VEC) {
     float acc[VEC];
 #pragma unroll
     for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
     for (int k = 0; k < K; ++k) {
-      const int row = slot_row[(size_t)t * K + k];
+      const int row = __shfl(my_row, k, 64);
       if (row < 0) continue;
       Vec16<T> v;
       v.load(dxp + (size_t)row * D + d0);
@@ -138,9 +141,9 @@ __global__ __launch_bounds__(256) void unpermute_kernel(
 #pragma unroll
       for (int i = 0; i < VEC; ++i) acc[i] += f[i];
     }
-    if (n_shared) {
+    if (srow >= 0) {
       Vec16<T> v;
-      v.load(dxp + (size_t)(shared0 + t) * D + d0);
+      v.load(dxp + (size_t)srow * D + d0);
       float f[VEC];
       v.to_f32(f);
 #pragma unroll
@@ -150,10 +153,9 @@ __global__ __launch_bounds__(256) void unpermute_kernel(
 #pragma unroll
       for (int e = 0; e < EM; ++e) {
         if (e < E) {
-          const float s = ds[(size_t)t * E + e];
           const float* w = wr + (size_t)e * D + d0;
 #pragma unroll
-          for (int i = 0; i < VEC; ++i) acc[i] = fmaf(s, w[i], acc[i]);
+          for (int i = 0; i < VEC; ++i) acc[i] = fmaf(s_e[e], w[i], acc[i]);
         }
       }
     } else {
@@ -170,19 +172,15 @@ __global__ __launch_bounds__(256) void unpermute_kernel(
 int launch_combine(const moe_config& c, const void* o_perm, const int32_t* offsets,
                    const int32_t* slot_row, const float* topk_w, void* y, hipStream_t st) {
   const int EL = c.expert_hi - c.expert_lo;
-  if (c.dtype == MOE_BF16) {
-    const int nv = c.D / 8;
-    const int grid = (int)cdiv((int64_t)c.T * nv, 1024);
+  const int grid = (int)cdiv(c.T, 4);
+  if (c.dtype == MOE_BF16)
     MOE_LAUNCH("combine", combine_kernel<bf16_t>, dim3(grid), dim3(256), 0, st,
                (const bf16_t*)o_perm, slot_row, topk_w, offsets, EL, c.n_shared, c.T, c.K, c.D,
-               nv, (bf16_t*)y);
-  } else {
-    const int nv = c.D / 4;
-    const int grid = (int)cdiv((int64_t)c.T * nv, 1024);
+               (bf16_t*)y);
+  else
     MOE_LAUNCH("combine", combine_kernel<float>, dim3(grid), dim3(256), 0, st,
                (const float*)o_perm, slot_row, topk_w, offsets, EL, c.n_shared, c.T, c.K, c.D,
-               nv, (float*)y);
-  }
+               (float*)y);
   return MOE_OK;
 }
 
@@ -206,13 +204,12 @@ static int unpermute_t(const moe_config& c, const void* dxp, const int32_t* slot
                        const int32_t* offsets, const float* ds, const float* wr,
                        const float* dxr, void* dx, hipStream_t st) {
   const int EL = c.expert_hi - c.expert_lo;
-  const int nv = c.D / Elem<T>::VEC;
-  const int grid = (int)cdiv((int64_t)c.T * nv, 1024);
+  const int grid = (int)cdiv(c.T, 4);
   const int E = c.E;
 #define UNPERM(EMV)                                                                          \
   MOE_LAUNCH("unpermute_dx", (unpermute_kernel<T, EMV>), dim3(grid), dim3(256), 0, st,        \
              (const T*)dxp, slot_row, offsets, EL, c.n_shared, ds, wr, E, dxr, c.T, c.K, c.D, \
-             nv, (T*)dx)
+             (T*)dx)
   if (dxr) UNPERM(0);
   else if (E <= 4) UNPERM(4);
   else if (E <= 8) UNPERM(8);

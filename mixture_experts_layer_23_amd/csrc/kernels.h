@@ -16,8 +16,9 @@ struct Workspace {
   size_t dg, ds;                   // float [T][K], [T][E]
   size_t dxr;                      // float [T][D] (router dgrad, large E)
   size_t dwr_part;                 // float [splits][E][D] (+ [splits][E] bias)
+  size_t rb_part;                  // float [rb_splits][E rounded to 4] (large E)
   size_t total;
-  int ntiles, aux_blocks, dwr_splits;
+  int ntiles, aux_blocks, dwr_splits, rb_splits;
 };
 Workspace workspace_layout(const moe_config& c);
 
@@ -25,6 +26,11 @@ constexpr int kSlotTile = 256;  // slots per histogram / rank tile
 // tokens per aux-loss workgroup: up to 64, with the [TB][E] probability tile
 // plus four [TB] vectors kept within 64 KB of LDS
 inline int aux_tokens_per_block(int E) { return std::max(1, std::min(64, (16384 - 256) / E)); }
+// elements per lane of the few-expert router weight gradient: 8 bf16 (16-byte
+// loads) when whole 512-wide d-blocks fit, else 4
+inline int router_wgrad_width(const moe_config& c) {
+  return (c.dtype == MOE_BF16 && c.D % 512 == 0) ? 8 : 4;
+}
 
 int launch_route(const moe_config& c, const void* x, const float* wr, const float* rb,
                  const float* selb, float* logits, int32_t* idx, float* w, float* lse,

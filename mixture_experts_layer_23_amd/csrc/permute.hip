@@ -31,71 +31,96 @@ __global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ i
     tile_counts[(size_t)blockIdx.x * E + e] = hist[e];
 }
 
-// K2: exclusive scan over tiles per expert, global counts, capacity, group
-// offsets and the dropped count.  One workgroup of 1024 threads.
-__global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ tile_counts,
-                                                    int ntiles, int E, int lo, int hi,
-                                                    int n_shared, int T_, int capacity,
-                                                    int32_t* __restrict__ tile_base,
-                                                    int32_t* __restrict__ counts_all,
-                                                    int32_t* __restrict__ offsets,
-                                                    int32_t* __restrict__ n_dropped) {
-  __shared__ int32_t sc[1024];
-  __shared__ int32_t sd[1024];
-  const int tid = threadIdx.x;
-  for (int e = tid; e < E; e += 1024) {
-    int run = 0;
-    for (int t = 0; t < ntiles; ++t) {
-      const int v = tile_counts[(size_t)t * E + e];
-      tile_base[(size_t)t * E + e] = run;
-      run += v;
+// K2: exclusive scan over the tiles of one expert (one workgroup per expert):
+// tile_base[t][e] = sum_{t' < t} tile_counts[t'][e], counts_all[e] = total.
+__global__ __launch_bounds__(256) void scan_tiles_kernel(const int32_t* __restrict__ tile_counts,
+                                                         int ntiles, int E,
+                                                         int32_t* __restrict__ tile_base,
+                                                         int32_t* __restrict__ counts_all) {
+  __shared__ int32_t wsum[4];
+  const int e = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int carry = 0;
+  for (int t0 = 0; t0 < ntiles; t0 += 256) {
+    const int t = t0 + tid;
+    const int v = t < ntiles ? tile_counts[(size_t)t * E + e] : 0;
+    int incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += u;
     }
-    counts_all[e] = run;
-    sc[e] = run;  // E <= 1024
-  }
-  __syncthreads();
-  const int EL = hi - lo;
-  int kept = 0, drop = 0;
-  if (tid < EL) {
-    const int n = sc[lo + tid];
-    kept = (capacity >= 0 && n > capacity) ? capacity : n;
-    drop = n - kept;
-  }
-  __syncthreads();
-  sc[tid] = kept;
-  sd[tid] = drop;
-  __syncthreads();
-  // inclusive Hillis-Steele scan of kept, tree sum of drop
-  for (int o = 1; o < 1024; o <<= 1) {
-    const int a = (tid >= o) ? sc[tid - o] : 0;
-    const int b = (tid + o < 1024 && (tid % (2 * o)) == 0) ? sd[tid + o] : 0;
+    if (lane == 63) wsum[wave] = incl;
     __syncthreads();
-    sc[tid] += a;
-    sd[tid] += b;
+    int before = carry;
+    for (int w = 0; w < wave; ++w) before += wsum[w];
+    if (t < ntiles) tile_base[(size_t)t * E + e] = before + incl - v;
+    carry += wsum[0] + wsum[1] + wsum[2] + wsum[3];
     __syncthreads();
   }
-  if (tid < EL) offsets[tid + 1] = sc[tid];
-  if (tid == 0) {
-    offsets[0] = 0;
-    const int tot = EL > 0 ? sc[EL - 1] : 0;
-    for (int s = 0; s < n_shared; ++s) offsets[EL + 1 + s] = tot + (s + 1) * T_;
-    *n_dropped = sd[0];
-  }
+  if (tid == 0) counts_all[e] = carry;
 }
 
 // K3: stable rank inside each tile (one wave per tile, 64 slots per round,
-// running per-expert counters in LDS), then the slot and row maps.
+// running per-expert counters in LDS), then the slot and row maps.  Every
+// workgroup first derives the group offsets from the expert counts (capacity
+// applied, exclusive scan over the local experts); workgroup 0 also publishes
+// them, with the shared-expert blocks after the routed rows, and the number
+// of dropped slots.
 __global__ __launch_bounds__(64) void rank_kernel(const int32_t* __restrict__ idx, int64_t TK,
                                                   int K, int E, int lo, int hi, int capacity,
-                                                  int nbits, const int32_t* __restrict__ tile_base,
-                                                  const int32_t* __restrict__ offsets,
+                                                  int nbits, int n_shared, int T_,
+                                                  const int32_t* __restrict__ tile_base,
+                                                  const int32_t* __restrict__ counts_all,
+                                                  int32_t* __restrict__ offsets,
+                                                  int32_t* __restrict__ n_dropped,
                                                   int32_t* __restrict__ slot_row,
                                                   int32_t* __restrict__ row_token,
                                                   int32_t* __restrict__ row_slot) {
-  extern __shared__ int32_t cnt[];
+  extern __shared__ int32_t lds[];
+  int32_t* cnt = lds;       // [E] running per-expert counts of this tile
+  int32_t* off = lds + E;   // [EL + 1] group offsets
   const int lane = threadIdx.x;
+  const int EL = hi - lo;
   for (int e = lane; e < E; e += 64) cnt[e] = 0;
-  __syncthreads();
+  {
+    // lane j owns local experts [j*per, (j+1)*per)
+    const int per = (EL + 63) / 64;
+    int kept = 0, drop = 0;
+    for (int i = 0; i < per; ++i) {
+      const int e = lane * per + i;
+      if (e < EL) {
+        const int n = counts_all[lo + e];
+        const int k = (capacity >= 0 && n > capacity) ? capacity : n;
+        kept += k;
+        drop += n - k;
+      }
+    }
+    int incl = kept;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += u;
+    }
+    int run = incl - kept;
+    for (int i = 0; i < per; ++i) {
+      const int e = lane * per + i;
+      if (e < EL) {
+        off[e] = run;
+        const int n = counts_all[lo + e];
+        run += (capacity >= 0 && n > capacity) ? capacity : n;
+      }
+    }
+    if (lane == 63) off[EL] = incl;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) drop += __shfl_xor(drop, o, 64);
+    __syncthreads();
+    if (blockIdx.x == 0) {
+      for (int e = lane; e <= EL; e += 64) offsets[e] = off[e];
+      for (int s = lane; s < n_shared; s += 64) offsets[EL + 1 + s] = off[EL] + (s + 1) * T_;
+      if (lane == 0) *n_dropped = drop;
+    }
+  }
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int r = 0; r < kSlotTile / 64; ++r) {
     const int64_t s = (int64_t)blockIdx.x * kSlotTile + r * 64 + lane;
@@ -119,7 +144,7 @@ __global__ __launch_bounds__(64) void rank_kernel(const int32_t* __restrict__ id
     } else if (capacity >= 0 && pos >= capacity) {
       slot_row[s] = -1;
     } else {
-      const int row = offsets[e - lo] + pos;
+      const int row = off[e - lo] + pos;
       slot_row[s] = row;
       row_token[row] = (int32_t)(s / K);
       row_slot[row] = (int32_t)s;
@@ -138,33 +163,24 @@ __global__ void shared_rows_kernel(const int32_t* __restrict__ offsets, int EL, 
   row_slot[r] = -1;
 }
 
-// K4: x_perm[r] = x[row_token[r]] for the routed rows; 16-byte vectors,
-// four in flight per thread; surplus threads (rows beyond offsets[EL]) exit.
+// K4: x_perm[r] = x[row_token[r]] for the routed rows; one wave per row,
+// lanes stride over 16-byte vectors; rows beyond offsets[EL] exit.
 template <typename T>
 __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ x,
                                                      const int32_t* __restrict__ row_token,
                                                      const int32_t* __restrict__ offsets, int EL,
-                                                     int nv, int D, T* __restrict__ x_perm) {
-  const int64_t nrows = offsets[EL];
-  const int64_t total = nrows * nv;
-  const int64_t b0 = (int64_t)blockIdx.x * 1024 + threadIdx.x;
-  Vec16<T> v[4];
-  int64_t dst[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int64_t it = b0 + u * 256;
-    dst[u] = -1;
-    if (it < total) {
-      const int64_t r = it / nv;
-      const int c = (int)(it - r * nv);
-      const int src = row_token[r];
-      v[u].load(x + (size_t)src * D + (size_t)c * Elem<T>::VEC);
-      dst[u] = r * D + (int64_t)c * Elem<T>::VEC;
-    }
+                                                     int D, T* __restrict__ x_perm) {
+  constexpr int VEC = Elem<T>::VEC;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= offsets[EL]) return;
+  const T* src = x + (size_t)row_token[r] * D;
+  T* dst = x_perm + (size_t)r * D;
+  for (int d0 = lane * VEC; d0 < D; d0 += 64 * VEC) {
+    Vec16<T> v;
+    v.load(src + d0);
+    v.store(dst + d0);
   }
-#pragma unroll
-  for (int u = 0; u < 4; ++u)
-    if (dst[u] >= 0) v[u].store(x_perm + dst[u]);
 }
 
 int launch_permute(const moe_config& c, int capacity, const int32_t* idx, const void* x,
@@ -179,29 +195,25 @@ int launch_permute(const moe_config& c, int capacity, const int32_t* idx, const 
   while ((1 << nbits) < E) ++nbits;
   MOE_LAUNCH("permute_hist", hist_kernel, dim3(L.ntiles), dim3(256), E * sizeof(int32_t), st, idx,
              TK, E, tile_counts);
-  MOE_LAUNCH("permute_scan", scan_kernel, dim3(1), dim3(1024), 0, st, tile_counts, L.ntiles, E,
-             c.expert_lo, c.expert_hi, c.n_shared, c.T, capacity, tile_base, counts_all, offsets,
-             n_dropped);
-  MOE_LAUNCH("permute_rank", rank_kernel, dim3(L.ntiles), dim3(64), E * sizeof(int32_t), st, idx,
-             TK, c.K, E, c.expert_lo, c.expert_hi, capacity, nbits, tile_base, offsets, slot_row,
-             row_token, row_slot);
+  MOE_LAUNCH("permute_scan", scan_tiles_kernel, dim3(E), dim3(256), 0, st, tile_counts,
+             L.ntiles, E, tile_base, counts_all);
+  MOE_LAUNCH("permute_rank", rank_kernel, dim3(L.ntiles), dim3(64),
+             (size_t)(E + EL + 1) * sizeof(int32_t), st, idx, TK, c.K, E, c.expert_lo,
+             c.expert_hi, capacity, nbits, c.n_shared, c.T, tile_base, counts_all, offsets,
+             n_dropped, slot_row, row_token, row_slot);
   if (c.n_shared > 0) {
     const int64_t n = (int64_t)c.n_shared * c.T;
     MOE_LAUNCH("permute_shared_rows", shared_rows_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256),
                0, st, offsets, EL, c.T, c.n_shared, row_token, row_slot);
   }
   if (EL > 0) {
-    if (c.dtype == MOE_BF16) {
-      const int nv = c.D / 8;
-      const int grid = (int)cdiv(TK * nv, 1024);
+    const int grid = (int)cdiv(TK, 4);
+    if (c.dtype == MOE_BF16)
       MOE_LAUNCH("permute_gather", gather_kernel<bf16_t>, dim3(grid), dim3(256), 0, st,
-                 (const bf16_t*)x, row_token, offsets, EL, nv, c.D, (bf16_t*)x_perm);
-    } else {
-      const int nv = c.D / 4;
-      const int grid = (int)cdiv(TK * nv, 1024);
+                 (const bf16_t*)x, row_token, offsets, EL, c.D, (bf16_t*)x_perm);
+    else
       MOE_LAUNCH("permute_gather", gather_kernel<float>, dim3(grid), dim3(256), 0, st,
-                 (const float*)x, row_token, offsets, EL, nv, c.D, (float*)x_perm);
-    }
+                 (const float*)x, row_token, offsets, EL, c.D, (float*)x_perm);
   }
   return MOE_OK;
 }

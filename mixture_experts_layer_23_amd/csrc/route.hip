@@ -88,58 +88,119 @@ __global__ __launch_bounds__(256) void router_skinny_kernel(const T* __restrict_
   }
 }
 
-// Tiled router (E > 16): 64 tokens x 64 experts per workgroup, k-slabs of 16
-// staged in LDS as double, 4x4 register micro-tile per thread.
+// Tiled router (E > 16) on the fp64 matrix cores: 32 tokens x 64 experts per
+// workgroup, four waves of 16 tokens x 32 experts (two 16x16 blocks of
+// v_mfma_f64_16x16x4f64).  k-slabs of 32 are staged in LDS as binary32 (exact
+// for both operands; rows padded by 4 floats) and widened to double when the
+// fragments are read; the next slab is fetched into registers while the
+// current one is multiplied.
+//   MFMA operands: lane l gives A[m = l%16][k = l/16] and B[k = l/16][n = l%16];
+//   accumulator element r of lane l is C[m = l/16 + 4r][n = l%16] (the f64
+//   form interleaves rows, unlike the f32 16x16 layout).
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
+constexpr int kRtT = 32, kRtE = 64, kRtK = 32, kRtP = kRtK + 4;
+
+template <typename T> struct RtLoad;
+template <> struct RtLoad<bf16_t> {
+  // x slab: 32 rows x 32 k = 128 chunks of 8 bf16
+  static MOE_DEV void load(const bf16_t* x, int T_, int D, int t0, int k0, int tid, float* v) {
+    if (tid < 128) {
+      const int r = tid >> 2, kc = (tid & 3) * 8;
+      const int t = min(t0 + r, T_ - 1);
+      Vec16<bf16_t> q;
+      q.load(x + (size_t)t * D + k0 + kc);
+      q.to_f32(v);
+      if (t0 + r >= T_)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = 0.f;
+    }
+  }
+  static MOE_DEV void store(float (*sx)[kRtP], int tid, const float* v) {
+    if (tid < 128) {
+      const int r = tid >> 2, kc = (tid & 3) * 8;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sx[r][kc + i] = v[i];
+    }
+  }
+};
+template <> struct RtLoad<float> {
+  // x slab: 32 rows x 32 k = 256 chunks of 4 floats
+  static MOE_DEV void load(const float* x, int T_, int D, int t0, int k0, int tid, float* v) {
+    const int r = tid >> 3, kc = (tid & 7) * 4;
+    const int t = min(t0 + r, T_ - 1);
+    const float4 q = *reinterpret_cast<const float4*>(x + (size_t)t * D + k0 + kc);
+    const bool ok = t0 + r < T_;
+    v[0] = ok ? q.x : 0.f; v[1] = ok ? q.y : 0.f; v[2] = ok ? q.z : 0.f; v[3] = ok ? q.w : 0.f;
+  }
+  static MOE_DEV void store(float (*sx)[kRtP], int tid, const float* v) {
+    const int r = tid >> 3, kc = (tid & 7) * 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sx[r][kc + i] = v[i];
+  }
+};
+
 template <typename T>
 __global__ __launch_bounds__(256) void router_tiled_kernel(const T* __restrict__ x,
                                                            const float* __restrict__ wr,
                                                            const float* __restrict__ rb,
                                                            float* __restrict__ logits, int T_,
                                                            int D, int E) {
-  __shared__ double sx[16][65];
-  __shared__ double sw[16][65];
-  const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-  const int lr = threadIdx.x >> 2, lk = (threadIdx.x & 3) * 4;  // loader: row, 4 k's
-  double acc[4][4];
+  __shared__ float sx[kRtT][kRtP];
+  __shared__ float sw[kRtE][kRtP];
+  const int t0 = blockIdx.x * kRtT, e0 = blockIdx.y * kRtE;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wt = (wave & 1) * 16, we = (wave >> 1) * 32;
+  // W slab: 64 rows x 32 k = 512 chunks of 4 floats, two per thread
+  float xv[8], wv[2][4];
+  auto load = [&](int k0) {
+    RtLoad<T>::load(x, T_, D, t0, k0, tid, xv);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int u = 0; u < 2; ++u) {
+      const int ch = tid + 256 * u, r = ch >> 3, kc = (ch & 7) * 4;
+      const int e = min(e0 + r, E - 1);
+      const float4 q = *reinterpret_cast<const float4*>(wr + (size_t)e * D + k0 + kc);
+      const bool ok = e0 + r < E;
+      wv[u][0] = ok ? q.x : 0.f; wv[u][1] = ok ? q.y : 0.f;
+      wv[u][2] = ok ? q.z : 0.f; wv[u][3] = ok ? q.w : 0.f;
+    }
+  };
+  f64x4_t acc[2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
-  for (int k0 = 0; k0 < D; k0 += 16) {
-    double xv[4], wv[4];
-    const int t = t0 + lr, e = e0 + lr;
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      xv[i] = (t < T_) ? (double)Elem<T>::to_f32(x[(size_t)t * D + k0 + lk + i]) : 0.0;
-      wv[i] = (e < E) ? (double)wr[(size_t)e * D + k0 + lk + i] : 0.0;
+    for (int r = 0; r < 4; ++r) acc[j][r] = 0.0;
+  load(0);
+  for (int k0 = 0; k0 < D; k0 += kRtK) {
+    __syncthreads();
+    RtLoad<T>::store(sx, tid, xv);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int ch = tid + 256 * u, r = ch >> 3, kc = (ch & 7) * 4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sw[r][kc + i] = wv[u][i];
     }
     __syncthreads();
+    if (k0 + kRtK < D) load(k0 + kRtK);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sx[lk + i][lr] = xv[i];
-      sw[lk + i][lr] = wv[i];
-    }
-    __syncthreads();
+    for (int ks = 0; ks < kRtK; ks += 4) {
+      const int kk = ks + (lane >> 4), i16 = lane & 15;
+      const double a = (double)sx[wt + i16][kk];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      double a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) { a[i] = sx[k][ty + 16 * i]; b[i] = sw[k][tx + 16 * i]; }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
+      for (int j = 0; j < 2; ++j) {
+        const double b = (double)sw[we + 16 * j + i16][kk];
+        acc[j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, acc[j], 0, 0, 0);
+      }
     }
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = t0 + ty + 16 * i;
-    if (t >= T_) continue;
+  for (int j = 0; j < 2; ++j) {
+    const int e = e0 + we + 16 * j + (lane & 15);
+    if (e >= E) continue;
+    const double bias = rb ? (double)rb[e] : 0.0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = e0 + tx + 16 * j;
-      if (e < E) logits[(size_t)t * E + e] = (float)(acc[i][j] + (rb ? (double)rb[e] : 0.0));
+    for (int r = 0; r < 4; ++r) {
+      const int t = t0 + wt + (lane >> 4) + 4 * r;
+      if (t < T_) logits[(size_t)t * E + e] = (float)(acc[j][r] + bias);
     }
   }
 }
@@ -309,7 +370,7 @@ int launch_route(const moe_config& c, const void* x, const float* wr, const floa
         else MOE_LAUNCH("router_logits", (router_skinny_kernel<float, 16>), dim3(grid), dim3(256), shm, st, (const float*)x, wr, rb, logits, T_, D, E);
       }
     } else {
-      dim3 grid((unsigned)cdiv(T_, 64), (unsigned)cdiv(E, 64));
+      dim3 grid((unsigned)cdiv(T_, kRtT), (unsigned)cdiv(E, kRtE));
       if (c.dtype == MOE_BF16)
         MOE_LAUNCH("router_logits", (router_tiled_kernel<bf16_t>), grid, dim3(256), 0, st, (const bf16_t*)x, wr, rb, logits, T_, D, E);
       else
