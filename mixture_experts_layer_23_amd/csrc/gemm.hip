@@ -28,6 +28,7 @@
 // store.  Workgroup ids are remapped so that consecutive tiles (same rows,
 // same expert weights) land on the same XCD and share its L2.
 #include <cstdlib>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -801,23 +802,29 @@ __global__ __launch_bounds__(BMT * 2) void grouped_gemm_dma_kernel(GemmParams P)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+  // fragments of k-step ks + 1 are read while the MFMAs of k-step ks run
   auto mma = [&](char* la, char* lb) {
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      uint4 fa[2], fb[2];
+    uint4 fa[2][2], fb[2][2];
+    auto frags = [&](int ks, uint4* a, uint4* b) {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        fa[i] = (AMODE == KC) ? frag_kc(la, ra[i], ks, lane)
-                              : frag_mc(la, ra[i], ks, lane, BMT * 2);
+        a[i] = (AMODE == KC) ? frag_kc(la, ra[i], ks, lane) : frag_mc(la, ra[i], ks, lane, BMT * 2);
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        fb[j] = (BMODE == KC) ? frag_kc(lb, rb[j], ks, lane) : frag_mc(lb, rb[j], ks, lane, 256);
+        b[j] = (BMODE == KC) ? frag_kc(lb, rb[j], ks, lane) : frag_mc(lb, rb[j], ks, lane, 256);
+    };
+    frags(0, fa[0], fb[0]);
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const int cur = ks & 1;
+      if (ks + 1 < BK / 16) frags(ks + 1, fa[cur ^ 1], fb[cur ^ 1]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8_t, fa[i]), __builtin_bit_cast(bf16x8_t, fb[j]),
+              __builtin_bit_cast(bf16x8_t, fa[cur][i]), __builtin_bit_cast(bf16x8_t, fb[cur][j]),
               acc[i][j], 0, 0, 0);
     }
   };
@@ -830,6 +837,9 @@ __global__ __launch_bounds__(BMT * 2) void grouped_gemm_dma_kernel(GemmParams P)
     else wait_vmcnt<0>();
     __syncthreads();
     if (kt + S - 1 < nk) issue(kt + S - 1, na, nb);
+    // keep the DMA at the head of this slab's MFMAs (the compiler would
+    // otherwise sink it towards the next wait)
+    __builtin_amdgcn_sched_barrier(0);
     mma(la, lb);
   };
   if (nk > 0) issue(0, sA0, sB0);
@@ -864,6 +874,411 @@ __global__ __launch_bounds__(BMT * 2) void grouped_gemm_dma_kernel(GemmParams P)
 }
 
 // ---------------------------------------------------------------------------
+// Large tiles: 256 x BN outputs (BN = 256 or 128) per workgroup of NW = 4 or
+// 8 waves.  Wave grid and wave tile:
+//   BN 256, 4 waves: 2 x 2 of 128 x 128     BN 256, 8 waves: 2 x 4 of 128 x 64
+//   BN 128, 4 waves: 2 x 2 of 128 x 64      BN 128, 8 waves: 4 x 2 of 64 x 64
+// Wave tiles of 128 rows let each 16-byte fragment read from LDS feed several
+// MFMAs; eight waves give each SIMD a second wave to issue from while the
+// other waits on LDS or on the DMA queue.  K-slabs of 64 arrive by LDS-DMA,
+// double-buffered; the MFMA operands are swapped (B first) so that lane l
+// holds output row l % 32 of each block in 4-column runs.  The epilogue
+// stages each 32-row block of a wave through LDS and writes whole 16-byte
+// row segments.
+// ---------------------------------------------------------------------------
+MOE_DEV uint2 pack_bf16x4(const float* v) {
+  return make_uint2((uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
+                    (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16));
+}
+
+template <int BN, int NW>
+struct BigShape {
+  static constexpr int WMW = (NW == 8 && BN == 128) ? 4 : 2;  // waves along M
+  static constexpr int WNW = NW / WMW;                          // waves along N
+  static constexpr int WTM = 256 / WMW, WTN = BN / WNW;        // wave tile
+  static constexpr int NI = WTM / 32, NJ = WTN / 32;           // 32 x 32 blocks
+};
+
+template <int AMODE, int BMODE, int GROUPING, int EPI, int BSPL, int BN, int NW>
+__global__ __launch_bounds__(NW * 64) void grouped_gemm_big_kernel(GemmParams P) {
+  typedef bf16_t T;
+  typedef BigShape<BN, NW> S;
+  constexpr int BM = 256, BK = 64;
+  constexpr int NI = S::NI, NJ = S::NJ, WTM = S::WTM, WTN = S::WTN;
+  constexpr int ATILE = BM * 128;    // bytes of the A slab
+  constexpr int BTILE = BN * 128;    // bytes of the B slab
+  constexpr int A_PER_WAVE = ATILE / 1024 / NW;
+  constexpr int B_PER_WAVE = BTILE / 1024 / NW;
+  constexpr int CPRB = BN / 8;       // 16-byte chunks per k-row of an MC B slab
+  static_assert(A_PER_WAVE * NW * 1024 == ATILE && B_PER_WAVE * NW * 1024 == BTILE, "split");
+  // epilogue staging: 32 rows x WTN fp32 per wave, half the waves in each A slab
+  static_assert((NW / 2) * 32 * WTN * 4 <= ATILE, "epilogue staging");
+  __shared__ __attribute__((aligned(1024))) char sA0[ATILE];
+  __shared__ __attribute__((aligned(1024))) char sB0[BTILE];
+  __shared__ __attribute__((aligned(1024))) char sA1[ATILE];
+  __shared__ __attribute__((aligned(1024))) char sB1[BTILE];
+  const int64_t lin = remap_xcd(blockIdx.x, P.nblocks);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int wm = wave / S::WNW, wn = wave % S::WNW;
+
+  int g, m0, n0, rows_valid, kdim;
+  int64_t arow0;
+  int nrows_g = 0;
+  if constexpr (GROUPING == GROUP_M) {
+    int mt, nt, mtl;
+    supercol_tile(lin, P.mt_total, P.ntn, mt, nt);
+    if (!find_group(P.offsets, P.G, mt, g, mtl, BM)) return;
+    g = __builtin_amdgcn_readfirstlane(g);
+    mtl = __builtin_amdgcn_readfirstlane(mtl);
+    nrows_g = P.offsets[g + 1] - P.offsets[g];
+    m0 = mtl * BM;
+    n0 = nt * BN;
+    rows_valid = min(BM, nrows_g - m0);
+    kdim = P.Kdim;
+    arow0 = P.offsets[g];
+  } else {
+    const int64_t per = (int64_t)P.ntm * P.ntn;
+    g = (int)(lin / per);
+    int mt, nt;
+    supercol_tile(lin - (int64_t)g * per, P.ntm, P.ntn, mt, nt);
+    m0 = mt * BM;
+    n0 = nt * BN;
+    rows_valid = BM;
+    kdim = P.offsets[g + 1] - P.offsets[g];
+    arow0 = P.offsets[g];
+  }
+
+  // ---- A source: buffer over this group's rows (rows past the end read 0)
+  const T* a_base = (g < P.EL_A) ? reinterpret_cast<const T*>(P.A) + arow0 * P.lda
+                                 : reinterpret_cast<const T*>(P.A_sh);
+  const int64_t a_rows = (GROUPING == GROUP_M) ? nrows_g : kdim;
+  const __amdgpu_buffer_rsrc_t a_rs = make_rsrc(a_base, a_rows * P.lda * 2);
+  uint32_t a_off[A_PER_WAVE];
+#pragma unroll
+  for (int u = 0; u < A_PER_WAVE; ++u) {
+    const int P_ = 64 * (wave * A_PER_WAVE + u) + lane;
+    if constexpr (AMODE == KC) {
+      const int r = P_ >> 3, lc = (P_ & 7) ^ swz(r);
+      a_off[u] = (uint32_t)(((int64_t)(m0 + r) * P.lda + 8 * lc) * 2);
+    } else {
+      const int kr = P_ / 32, lc = (P_ % 32) ^ ((kr & 3) << 2);
+      a_off[u] = (uint32_t)(((int64_t)kr * P.lda + m0 + 8 * lc) * 2);
+    }
+  }
+  // ---- B source (GROUP_M: weights, per-lane global addresses; GROUP_K:
+  // activation rows of the group through a buffer)
+  const T* b_ptr[B_PER_WAVE];
+  uint32_t b_off[B_PER_WAVE];
+  __amdgpu_buffer_rsrc_t b_rs;
+  const T* Bw0 = reinterpret_cast<const T*>(P.B0) + (int64_t)g * P.strideB;
+  const T* Bw1 = (BSPL != BS_NONE) ? reinterpret_cast<const T*>(P.B1) + (int64_t)g * P.strideB
+                                   : nullptr;
+  if constexpr (GROUPING == GROUP_M) {
+#pragma unroll
+    for (int u = 0; u < B_PER_WAVE; ++u) {
+      const int P_ = 64 * (wave * B_PER_WAVE + u) + lane;
+      if constexpr (BMODE == KC) {
+        const int r = P_ >> 3, lc = (P_ & 7) ^ swz(r);
+        b_ptr[u] = Bw0 + (int64_t)(n0 + r) * P.ldb + 8 * lc;
+      } else {
+        const int kr = P_ / CPRB, lc = (P_ % CPRB) ^ ((kr & 3) << 2);
+        if constexpr (BSPL == BS_N) {
+          const int col0 = n0 / 2;
+          b_ptr[u] = (lc < CPRB / 2) ? Bw0 + (int64_t)kr * P.ldb + col0 + 8 * lc
+                                     : Bw1 + (int64_t)kr * P.ldb + col0 + 8 * (lc - CPRB / 2);
+        } else {
+          b_ptr[u] = Bw0 + (int64_t)kr * P.ldb + n0 + 8 * lc;
+        }
+      }
+    }
+    b_rs = make_rsrc(Bw0, 16);
+  } else {
+    const T* b_base = (g < P.EL_B) ? reinterpret_cast<const T*>(P.B0) + arow0 * P.ldb
+                                   : reinterpret_cast<const T*>(P.B1);
+    b_rs = make_rsrc(b_base, (int64_t)kdim * P.ldb * 2);
+#pragma unroll
+    for (int u = 0; u < B_PER_WAVE; ++u) {
+      const int P_ = 64 * (wave * B_PER_WAVE + u) + lane;
+      const int kr = P_ / CPRB, lc = (P_ % CPRB) ^ ((kr & 3) << 2);
+      b_off[u] = (uint32_t)(((int64_t)kr * P.ldb + n0 + 8 * lc) * 2);
+    }
+  }
+
+  // DMA of slab kt.  Slabs at or past nk (the even padding and the two the
+  // pipeline runs ahead at the end) load zeros for A -- an offset past the
+  // buffer range reads 0 without touching memory (GROUP_K: B too, its rows
+  // run out the same way) -- and, for GROUP_M, re-read the last weight slab:
+  // any finite B times a zero A adds nothing.
+  const int nk = (kdim + BK - 1) / BK;
+  auto issue = [&](int kt, char* la, char* lb) __attribute__((always_inline)) {
+    const bool pad = kt >= nk;
+    const int k0 = (GROUPING == GROUP_M && pad) ? (nk - 1) * BK : kt * BK;
+    const uint32_t kadd = (AMODE == KC) ? (uint32_t)(k0 * 2) : (uint32_t)((int64_t)k0 * P.lda * 2);
+#pragma unroll
+    for (int u = 0; u < A_PER_WAVE; ++u)
+      dma16_buffer(a_rs, to_lds(la + (wave * A_PER_WAVE + u) * 1024),
+                   (GROUPING == GROUP_M && pad) ? 0x80000000u : a_off[u] + kadd);
+#pragma unroll
+    for (int u = 0; u < B_PER_WAVE; ++u) {
+      char* dst = lb + (wave * B_PER_WAVE + u) * 1024;
+      if constexpr (GROUPING == GROUP_M) {
+        const T* src;
+        if constexpr (BMODE == KC) {
+          if constexpr (BSPL == BS_K) {
+            src = (k0 < P.bsplit) ? b_ptr[u] + k0 : (b_ptr[u] - Bw0) + Bw1 + (k0 - P.bsplit);
+          } else {
+            src = b_ptr[u] + k0;
+          }
+        } else {
+          src = b_ptr[u] + (int64_t)k0 * P.ldb;
+        }
+        dma16_global(src, to_lds(dst));
+      } else {
+        dma16_buffer(b_rs, to_lds(dst), b_off[u] + (uint32_t)((int64_t)k0 * P.ldb * 2));
+      }
+    }
+  };
+
+  // B-slab columns of this wave's blocks.  SwiGLU forward: the slab holds
+  // [gate | up] halves; block j < NJ/2 is gate, j + NJ/2 the up block of the
+  // same f's.
+  int rb[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    if constexpr (EPI == EPI_SWIGLU_FWD)
+      rb[j] = (j < NJ / 2) ? wn * (WTN / 2) + j * 32 : BN / 2 + wn * (WTN / 2) + (j - NJ / 2) * 32;
+    else
+      rb[j] = wn * WTN + j * 32;
+  }
+
+  f32x16_t acc[NI][NJ];
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // Software pipeline.  Fragments of k-step ks + 1 are read into the other
+  // register slot while the MFMAs of k-step ks run.  The slab hand-over sits
+  // inside the last k-step: wait for the next slab's DMA, barrier (every wave
+  // has its last fragments of this slab in registers by then), start the DMA
+  // two slabs ahead into the buffer just released, read the first fragments
+  // of the next slab -- all while the MFMAs already issued keep the matrix
+  // cores busy.  Scheduling barriers keep the compiler from moving the
+  // reads and the DMA behind the MFMAs.
+  uint4 fa[2][NI], fb[2][NJ];
+  auto frags = [&](const char* la, const char* lb, int ks, int slot) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      fa[slot][i] = (AMODE == KC) ? frag_kc(la, wm * WTM + i * 32, ks, lane)
+                                  : frag_mc(const_cast<char*>(la), wm * WTM + i * 32, ks, lane, BM * 2);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      fb[slot][j] = (BMODE == KC) ? frag_kc(lb, rb[j], ks, lane)
+                                  : frag_mc(const_cast<char*>(lb), rb[j], ks, lane, BN * 2);
+  };
+  auto mfmas = [&](int slot) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8_t, fb[slot][j]), __builtin_bit_cast(bf16x8_t, fa[slot][i]),
+            acc[i][j], 0, 0, 0);
+  };
+  constexpr int PER_SLAB = A_PER_WAVE + B_PER_WAVE;  // DMA instructions per slab
+  // Slab kt is in (la, lb) with its k-step 0 fragments in register slot 0;
+  // slab kt + 1 is landing in (na, nb).  The body is branch-free: the slab
+  // count is padded to even and the DMA runs on past the end (see issue).
+  auto step = [&](int kt, char* la, char* lb, char* na, char* nb) __attribute__((always_inline)) {
+    frags(la, lb, 1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(0);
+    frags(la, lb, 2, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(1);
+    frags(la, lb, 3, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(0);
+    wait_vmcnt<0>();
+    __syncthreads();
+    issue(kt + 2, la, lb);
+    frags(na, nb, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(1);
+  };
+  const int nkp = nk + (nk & 1);
+  if (nkp > 0) {
+    issue(0, sA0, sB0);
+    issue(1, sA1, sB1);
+    wait_vmcnt<PER_SLAB>();
+    __syncthreads();
+    frags(sA0, sB0, 0, 0);
+  }
+  for (int kt = 0; kt < nkp; kt += 2) {
+    step(kt, sA0, sB0, sA1, sB1);
+    step(kt + 1, sA1, sB1, sA0, sB0);
+  }
+  // the run-ahead DMA must land, and every wave be done with the slabs,
+  // before the stage buffers are reused for the epilogue
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  // ---- epilogue.  Element r of block (i, j) is row l % 32 of block i and
+  // column (r / 4) * 8 + (l / 32) * 4 + r % 4 of block j.  Each 32-row block
+  // of the wave is staged in the wave's own LDS region (16-byte chunks
+  // XOR-swizzled by row) and written back as row segments.
+  char* reg = (wave < NW / 2 ? sA0 : sA1) + (wave % (NW / 2)) * (32 * WTN * 4);
+  const int lrow = lane & 31, lcol = (lane >> 5) * 4;
+  // bf16 staging of a [32][W] array at base: 4 values at (lrow, col); the
+  // chunk swizzle stays inside the row (W / 8 chunks, at most 8 permuted)
+  auto put4 = [&](char* base, int W, int col, const float* v) __attribute__((always_inline)) {
+    const int ch = col >> 3, half = (col >> 2) & 1, msk = min(W / 8, 8) - 1;
+    *reinterpret_cast<uint2*>(base + lrow * W * 2 + ((ch ^ (lrow & msk)) << 4) + (half << 3)) =
+        pack_bf16x4(v);
+  };
+  auto get16 = [&](const char* base, int W, int row, int ch) __attribute__((always_inline)) {
+    const int msk = min(W / 8, 8) - 1;
+    return *reinterpret_cast<const uint4*>(base + row * W * 2 + ((ch ^ (row & msk)) << 4));
+  };
+  // SwiGLU backward: activation rows of 32-row block ib, 8 columns per lane
+  constexpr int ACT_IT = (EPI == EPI_SWIGLU_BWD) ? 32 / (64 / (WTN / 8)) : 1;
+  uint4 av[2][ACT_IT], bv[2][ACT_IT];
+  auto load_act = [&](int ib, uint4* a, uint4* b) __attribute__((always_inline)) {
+    constexpr int CPR = WTN / 8, RPI = 64 / CPR;
+    const int f = n0 + wn * WTN + (lane % CPR) * 8;
+#pragma unroll
+    for (int it = 0; it < ACT_IT; ++it) {
+      const int row_t = wm * WTM + ib * 32 + it * RPI + lane / CPR;
+      if (row_t < rows_valid) {
+        const T* act = reinterpret_cast<const T*>(P.act) + (arow0 + m0 + row_t) * 2 * P.F;
+        a[it] = *reinterpret_cast<const uint4*>(act + f);
+        b[it] = *reinterpret_cast<const uint4*>(act + P.F + f);
+      }
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int row_t0 = wm * WTM + i * 32;  // tile-relative first row of the block
+    if (row_t0 >= rows_valid) break;       // uniform
+    const int64_t grow0 = arow0 + m0 + row_t0;
+    if constexpr (EPI == EPI_SWIGLU_FWD) {
+      constexpr int W = WTN / 2;            // f columns of the wave
+      char* sa = reg;
+      char* sb = reg + 32 * W * 2;
+      char* sh = reg + 64 * W * 2;
+#pragma unroll
+      for (int j = 0; j < NJ / 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float a[4], b[4], h[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            a[e] = acc[i][j][4 * q + e];
+            b[e] = acc[i][j + NJ / 2][4 * q + e];
+            h[e] = silu_f(a[e]) * b[e];
+          }
+          const int col = j * 32 + q * 8 + lcol;
+          put4(sa, W, col, a);
+          put4(sb, W, col, b);
+          put4(sh, W, col, h);
+        }
+      constexpr int CPR = W / 8, RPI = 64 / CPR;
+      const int ch = lane % CPR;
+      const int f = n0 / 2 + wn * W + ch * 8;
+#pragma unroll
+      for (int it = 0; it < 32 / RPI; ++it) {
+        const int row = it * RPI + lane / CPR;
+        if (row_t0 + row >= rows_valid) continue;
+        const int64_t grow = grow0 + row;
+        T* aout = reinterpret_cast<T*>(P.act_out) + grow * 2 * P.F;
+        *reinterpret_cast<uint4*>(aout + f) = get16(sa, W, row, ch);
+        *reinterpret_cast<uint4*>(aout + P.F + f) = get16(sb, W, row, ch);
+        *reinterpret_cast<uint4*>(reinterpret_cast<T*>(P.C1) + grow * P.F + f) = get16(sh, W, row, ch);
+      }
+    } else if constexpr (EPI == EPI_SWIGLU_BWD) {
+      // dh stays fp32: 16-byte chunks of 4 floats, swizzled by row.  The
+      // activations of block i + 1 are loaded while block i is processed
+      // (those of block 0 before the loop), so their latency overlaps.
+      constexpr int CPR = WTN / 8, RPI = 64 / CPR;   // lanes per row: 8 columns each
+      const int ch = lane % CPR;
+      const int f = n0 + wn * WTN + ch * 8;
+      if (i == 0) load_act(0, av[0], bv[0]);
+      if (i + 1 < NI) load_act(i + 1, av[(i + 1) & 1], bv[(i + 1) & 1]);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c4 = (j * 32 + q * 8 + lcol) >> 2;
+          *reinterpret_cast<float4*>(reg + lrow * WTN * 4 + ((c4 ^ (lrow & 15)) << 4)) =
+              make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                          acc[i][j][4 * q + 3]);
+        }
+#pragma unroll
+      for (int it = 0; it < 32 / RPI; ++it) {
+        const int row = it * RPI + lane / CPR;
+        if (row_t0 + row >= rows_valid) continue;
+        float v[8], a[8], b[8], da[8], db[8];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int c4 = 2 * ch + hh;
+          const float4 d = *reinterpret_cast<const float4*>(reg + row * WTN * 4 + ((c4 ^ (row & 15)) << 4));
+          v[4 * hh] = d.x; v[4 * hh + 1] = d.y; v[4 * hh + 2] = d.z; v[4 * hh + 3] = d.w;
+        }
+        Vec16<T> va, vb;
+        va.v = av[i & 1][it];
+        vb.v = bv[i & 1][it];
+        va.to_f32(a);
+        vb.to_f32(b);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float sg = 1.0f / (1.0f + expf(-a[e]));
+          da[e] = v[e] * b[e] * sg * (1.0f + a[e] * (1.0f - sg));
+          db[e] = v[e] * a[e] * sg;
+        }
+        T* dact = reinterpret_cast<T*>(P.C0) + (grow0 + row) * 2 * P.F;
+        Vec16<T> oa, ob;
+        oa.from_f32(da);
+        ob.from_f32(db);
+        oa.store(dact + f);
+        ob.store(dact + P.F + f);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
+          put4(reg, WTN, j * 32 + q * 8 + lcol, v);
+        }
+      constexpr int CPR = WTN / 8, RPI = 64 / CPR;
+      const int ch = lane % CPR;
+      const int col = n0 + wn * WTN + ch * 8;  // output column of the chunk
+#pragma unroll
+      for (int it = 0; it < 32 / RPI; ++it) {
+        const int row = it * RPI + lane / CPR;
+        if (row_t0 + row >= rows_valid) continue;
+        const uint4 v = get16(reg, WTN, row, ch);
+        if constexpr (GROUPING == GROUP_M) {
+          *reinterpret_cast<uint4*>(reinterpret_cast<T*>(P.C0) + (grow0 + row) * P.ldc + col) = v;
+        } else {
+          const int64_t mrow = m0 + row_t0 + row;
+          T* C = (col < P.csplit)
+                     ? reinterpret_cast<T*>(P.C0) + (int64_t)g * P.strideC + mrow * P.ldc + col
+                     : reinterpret_cast<T*>(P.C1) + (int64_t)g * P.strideC + mrow * P.ldc +
+                           (col - P.csplit);
+          *reinterpret_cast<uint4*>(C) = v;
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 static int groups_of(const moe_config& c) { return (c.expert_hi - c.expert_lo) + c.n_shared; }
@@ -882,8 +1297,9 @@ static void tile_space(GemmParams& P, int grouping, int bm) {
   }
 }
 
-// GEMM configuration of the LDS-DMA kernel: 0 = register-staged kernel,
-// 1 = 128-row tiles / 2 stages, 2 = 256-row tiles / 3 stages.
+// GEMM configuration of the LDS-DMA kernels: 0 = register-staged kernel,
+// 1 = 128-row tiles / 2 stages, 2 = 256-row tiles / 3 stages, 3 / 4 = 256 x
+// 256 / 256 x 128 large tiles on 4 waves, 5 / 6 = the same on 8 waves.
 // MOE_GEMM_CFG overrides the choice (measurement only).
 static int cfg_override() {
   static int v = [] {
@@ -906,17 +1322,44 @@ static int launch_dma(const char* name, GemmParams P, hipStream_t st) {
 // tiles runs on the LDS-DMA kernel -- 256-row tiles when that still gives at
 // least two workgroups per CU, else 128-row tiles; fp32 and ragged shapes
 // run on the register-staged kernel.
+template <int AM, int BM_, int GR, int EPI, int BS, int BN, int NW>
+static int launch_big(const char* name, GemmParams P, hipStream_t st) {
+  P.ntn = P.N / BN;
+  tile_space(P, GR, 256);
+  if (P.nblocks <= 0) return MOE_OK;
+  MOE_LAUNCH(name, (grouped_gemm_big_kernel<AM, BM_, GR, EPI, BS, BN, NW>),
+             dim3((unsigned)P.nblocks), dim3(NW * 64), 0, st, P);
+  return MOE_OK;
+}
+
 template <typename T, int AM, int BM_, int GR, int EPI, int BS>
 static int run_gemm(const char* name, GemmParams& P, hipStream_t st) {
   if constexpr (sizeof(T) == 2) {
     const bool full128 = (P.N % kBN == 0) && (GR == GROUP_M ? P.Kdim % 64 == 0 : P.Mfix % 128 == 0);
     const bool full256 = full128 && (GR == GROUP_M || P.Mfix % 256 == 0);
+    const bool wide = full256 && P.N % 256 == 0;
     int cfg = cfg_override();
     if (cfg < 0) {
+      // 256 x 256 tiles on 8 waves when they give enough tiles (a weight
+      // gradient, with its long reduction over the group rows, needs fewer);
+      // else 256 x 128 or 128 x 128 tiles on the 8- / 4-wave DMA kernel.
       GemmParams Q = P;
-      tile_space(Q, GR, 256);
-      cfg = (full256 && Q.nblocks >= 512) ? 2 : 1;
+      if (wide) {
+        Q.ntn = P.N / 256;
+        tile_space(Q, GR, 256);
+      }
+      if (wide && Q.nblocks >= (GR == GROUP_K ? 192 : 384)) {
+        cfg = 5;
+      } else {
+        Q = P;
+        tile_space(Q, GR, 256);
+        cfg = (full256 && Q.nblocks >= 512) ? 2 : 1;
+      }
     }
+    if (cfg == 3 && wide) return launch_big<AM, BM_, GR, EPI, BS, 256, 4>(name, P, st);
+    if (cfg == 4 && full256) return launch_big<AM, BM_, GR, EPI, BS, 128, 4>(name, P, st);
+    if (cfg == 5 && wide) return launch_big<AM, BM_, GR, EPI, BS, 256, 8>(name, P, st);
+    if (cfg == 6 && full256) return launch_big<AM, BM_, GR, EPI, BS, 128, 8>(name, P, st);
     if (cfg == 2 && full256) return launch_dma<AM, BM_, GR, EPI, BS, 256, 3>(name, P, st);
     if (cfg >= 1 && full128) return launch_dma<AM, BM_, GR, EPI, BS, 128, 2>(name, P, st);
   }
