@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--k", type=int, default=None, help="override top-K")
     ap.add_argument("--gating", choices=["A", "B"], default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step replayed as one HIP graph (reported as ms_per_step_graph)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=None)
     ap.add_argument("--json-out", default=None)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -161,15 +163,26 @@ def main():
         layer.forward(x)
         layer.backward(dy)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms = elapsed * 1000.0 / max(args.steps, 1)
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1000.0 / max(args.steps, 1)
+
+    # the reported rate: kernel-by-kernel launches on the caller's stream
+    # (the library overlaps independent backward parts on its side streams);
+    # with --graph also the same step replayed as one HIP graph
+    ms = timed(step)
+    ms_graph = None
+    if args.graph:
+        from mixture_experts_layer_23_amd.layer import StepGraph
+        sg = StepGraph(layer, x, dy)
+        ms_graph = timed(sg.replay)
+        del sg
 
     # second pass: per-kernel durations from HIP events recorded by the
     # library on the stream each kernel runs on
@@ -252,7 +265,9 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if wl.dtype == S.BF16 else "f32",
         "data": "synthetic (seeded, on-device Philox normals)",
-        "config": {"workload": wl_name(wl), "tokens": wl.T, "local_rows": n_rows_local,
+        "ms_per_step_graph": ms_graph,
+        "config": {"workload": wl_name(wl), "launch": "eager",
+                   "tokens": wl.T, "local_rows": n_rows_local,
                    "shared_rows": wl.n_shared * wl.T, "dropped": n_dropped,
                    "expert_load": counts.tolist() if wl.E <= 16 else None},
         "grouped_gemm": {"tflops": gemm_flops / (gemm_ms * 1e-3) / 1e12 if gemm_ms else None,

@@ -459,16 +459,26 @@ int launch_backward(const moe_config& c, const void* x, const float* wr, const f
   int rc;
   if ((rc = launch_combine_bwd(c, o_perm, dy, slot_row, topk_w, dg, d_o, st))) return rc;
   if ((rc = launch_gating_bwd(c, logits, idx, topk_w, dg, dlx, ds, d_logits_out, st))) return rc;
-  if ((rc = gemm_down_dgrad(c, offsets, d_o, dy, wd, act, dact, st))) return rc;
-  if ((rc = gemm_down_wgrad(c, offsets, h, d_o, dy, dwd, st))) return rc;
-  if ((rc = gemm_up_dgrad(c, offsets, dact, wg, wu, dxp, st))) return rc;
-  if ((rc = gemm_up_wgrad(c, offsets, x, x_perm, dact, dwg, dwu, st))) return rc;
+  // Independent parts overlap on two side streams:
+  //   main:   down dgrad -> up dgrad -> (router) -> un-permute
+  //   side 0: down wgrad -> (after down dgrad) up wgrad
+  //   side 1: router weight / bias gradient (and dgrad for many experts)
+  hipStream_t s0 = side_stream(0), s1 = side_stream(1);
+  if (!s0 || !s1) { set_error("side streams", hipErrorInvalidResourceHandle); return MOE_ELAUNCH; }
+  if ((rc = fork_stream(st, s0)) || (rc = fork_stream(st, s1))) return rc;
   if (c.dtype == MOE_BF16) {
-    if ((rc = router_bwd_t<bf16_t>(c, x, wr, ds, dxr, dwr, drb, ws, L, st))) return rc;
+    if ((rc = router_bwd_t<bf16_t>(c, x, wr, ds, dxr, dwr, drb, ws, L, s1))) return rc;
   } else {
-    if ((rc = router_bwd_t<float>(c, x, wr, ds, dxr, dwr, drb, ws, L, st))) return rc;
+    if ((rc = router_bwd_t<float>(c, x, wr, ds, dxr, dwr, drb, ws, L, s1))) return rc;
   }
-  return launch_unpermute(c, dxp, slot_row, offsets, ds, wr, dxr, dx, st);
+  if ((rc = gemm_down_wgrad(c, offsets, h, d_o, dy, dwd, s0))) return rc;
+  if ((rc = gemm_down_dgrad(c, offsets, d_o, dy, wd, act, dact, st))) return rc;
+  if ((rc = fork_stream(st, s0))) return rc;  // dact is ready
+  if ((rc = gemm_up_wgrad(c, offsets, x, x_perm, dact, dwg, dwu, s0))) return rc;
+  if ((rc = gemm_up_dgrad(c, offsets, dact, wg, wu, dxp, st))) return rc;
+  if ((rc = fork_stream(s1, st))) return rc;  // join: router part of dx
+  if ((rc = launch_unpermute(c, dxp, slot_row, offsets, ds, wr, dxr, dx, st))) return rc;
+  return fork_stream(s0, st);                 // join: weight gradients
 }
 
 }  // namespace moe

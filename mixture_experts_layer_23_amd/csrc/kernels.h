@@ -60,6 +60,12 @@ int launch_backward(const moe_config& c, const void* x, const float* wr, const f
                     void* dwg, void* dwu, void* dwd, float* d_logits_out, char* ws,
                     const Workspace& L, hipStream_t st);
 
+// side streams (streams.hip): per-device side stream i (0 or 1), or null if
+// they could not be created; fork_stream makes `to` wait for the work issued
+// to `from` so far (join: the same, the other way)
+hipStream_t side_stream(int i);
+int fork_stream(hipStream_t from, hipStream_t to);
+
 // grouped GEMM launchers (gemm.hip)
 int gemm_swiglu_fwd(const moe_config& c, const void* x, const void* x_perm,
                     const int32_t* offsets, const void* wg, const void* wu, void* act, void* h,

@@ -344,21 +344,23 @@ int launch_route(const moe_config& c, const void* x, const float* wr, const floa
       int grid = (int)std::min<int64_t>(cdiv(waves_needed, 4), 2048);
       const size_t shm = (size_t)E * D * 4;
       if (shm > 64 * 1024) {
-        // W_r tiles above 64 KB need the kernel's dynamic-LDS limit raised
-        hipError_t e1 = hipFuncSetAttribute((const void*)router_skinny_kernel<bf16_t, 8>,
-                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-        hipError_t e2 = hipFuncSetAttribute((const void*)router_skinny_kernel<float, 8>,
-                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-        hipError_t e3 = hipFuncSetAttribute((const void*)router_skinny_kernel<bf16_t, 16>,
-                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-        hipError_t e4 = hipFuncSetAttribute((const void*)router_skinny_kernel<float, 16>,
-                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-        hipError_t e5 = hipFuncSetAttribute((const void*)router_skinny_kernel<bf16_t, 4>,
-                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-        hipError_t e6 = hipFuncSetAttribute((const void*)router_skinny_kernel<float, 4>,
-                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-        for (hipError_t e : {e1, e2, e3, e4, e5, e6})
-          if (e != hipSuccess) { set_error("router_logits (LDS limit)", e); return MOE_ELAUNCH; }
+        // W_r tiles above 64 KB need the kernels' dynamic-LDS limit raised:
+        // once per process (outside any stream capture that comes later)
+        static hipError_t lim = [] {
+          const void* fns[] = {(const void*)router_skinny_kernel<bf16_t, 4>,
+                               (const void*)router_skinny_kernel<bf16_t, 8>,
+                               (const void*)router_skinny_kernel<bf16_t, 16>,
+                               (const void*)router_skinny_kernel<float, 4>,
+                               (const void*)router_skinny_kernel<float, 8>,
+                               (const void*)router_skinny_kernel<float, 16>};
+          for (const void* f : fns) {
+            hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               128 * 1024);
+            if (e != hipSuccess) return e;
+          }
+          return hipSuccess;
+        }();
+        if (lim != hipSuccess) { set_error("router_logits (LDS limit)", lim); return MOE_ELAUNCH; }
       }
       if (c.dtype == MOE_BF16) {
         if (E <= 4) MOE_LAUNCH("router_logits", (router_skinny_kernel<bf16_t, 4>), dim3(grid), dim3(256), shm, st, (const bf16_t*)x, wr, rb, logits, T_, D, E);

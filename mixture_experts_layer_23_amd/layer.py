@@ -122,3 +122,30 @@ class MoELayer:
                        self.dlogits_aux if use else None, self.dx, self.dw_r, self.d_rbias,
                        self.dw_gate, self.dw_up, self.dw_down, self.d_logits, self.ws)
         return self.dx
+
+
+class StepGraph:
+    """One forward + backward of a ``MoELayer`` on fixed input buffers, captured
+    once in a HIP graph and replayed: the same kernels, launched as one graph
+    instead of one by one.  The library's side streams join the capture through
+    their fork / join events.  ``x`` and ``dy`` are read in place at every
+    replay, so refill them (``copy_``) to step on new data."""
+
+    def __init__(self, layer: MoELayer, x, dy, with_aux: bool | None = None):
+        self.layer, self.x, self.dy, self.with_aux = layer, x, dy, with_aux
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            self._step()  # first launches (one-time set-up) outside the capture
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self._step()
+
+    def _step(self):
+        self.layer.forward(self.x)
+        self.layer.backward(self.dy, self.with_aux)
+
+    def replay(self):
+        self.graph.replay()
