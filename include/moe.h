@@ -232,6 +232,14 @@ const char* moe_error_string(int code);
  */
 int moe_timing_enable(int32_t on);
 int moe_timing_report(char* buf, size_t len);
+/*
+ * Restrict timing to launches of one kernel name (as reported by
+ * moe_timing_report); NULL or "" times every launch again.  Timing one
+ * kernel adds two event records per launch of it and nothing to the others,
+ * so it can stay on inside a timed run.  Events come from a pool that is
+ * reused after each report.
+ */
+int moe_timing_select(const char* kernel_name);
 
 #ifdef __cplusplus
 }

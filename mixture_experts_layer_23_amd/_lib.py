@@ -21,7 +21,8 @@ MOE_ROUTE_LOGITS_GIVEN = 1
 
 EXPORTS = ["moe_capacity", "moe_rows_max", "moe_workspace_size", "moe_route", "moe_permute",
            "moe_expert_ffn", "moe_combine", "aux_balance_loss", "moe_backward",
-           "moe_error_string", "moe_timing_enable", "moe_timing_report"]
+           "moe_error_string", "moe_timing_enable", "moe_timing_report",
+           "moe_timing_select"]
 
 
 class MoeConfig(C.Structure):
@@ -63,6 +64,7 @@ def lib():
             "moe_error_string": [C.c_int],
             "moe_timing_enable": [I],
             "moe_timing_report": [C.c_char_p, S],
+            "moe_timing_select": [C.c_char_p],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -172,6 +174,10 @@ def moe_backward(cfg, x, w_r, logits, topk_idx, topk_w, offsets, slot_row, x_per
 
 def timing_enable(on: bool) -> None:
     _check("moe_timing_enable", lib().moe_timing_enable(1 if on else 0))
+
+
+def timing_select(name: str | None) -> None:
+    _check("moe_timing_select", lib().moe_timing_select(name.encode() if name else None))
 
 
 def timing_report() -> dict:

@@ -19,25 +19,45 @@ void set_error(const char* where, hipError_t e) {
 }
 
 // --- timing ----------------------------------------------------------------
+// Events come from a pool that grows on demand and is reused after each
+// report, so that timing a run creates no events inside it after the first.
 struct TimedLaunch {
   std::string name;
   hipEvent_t a, b;
 };
 static bool g_timing = false;
+static std::string g_only;               // time only launches of this name ("" = all)
 static std::vector<TimedLaunch> g_records;
+static std::vector<hipEvent_t> g_pool;
+static size_t g_pool_next = 0;
+static bool g_last_timed = false;
 
 bool timing_on() { return g_timing; }
 
+static bool pool_event(hipEvent_t* e) {
+  if (g_pool_next == g_pool.size()) {
+    hipEvent_t n;
+    if (hipEventCreate(&n) != hipSuccess) return false;
+    g_pool.push_back(n);
+  }
+  *e = g_pool[g_pool_next++];
+  return true;
+}
+
 void timing_before(const char* name, hipStream_t s) {
+  g_last_timed = false;
+  if (!g_only.empty() && g_only != name) return;
   TimedLaunch r;
   r.name = name;
-  if (hipEventCreate(&r.a) != hipSuccess || hipEventCreate(&r.b) != hipSuccess) return;
+  if (!pool_event(&r.a) || !pool_event(&r.b)) return;
   (void)hipEventRecord(r.a, s);
   g_records.push_back(r);
+  g_last_timed = true;
 }
 
 void timing_after(hipStream_t s) {
-  if (!g_records.empty()) (void)hipEventRecord(g_records.back().b, s);
+  if (g_last_timed && !g_records.empty()) (void)hipEventRecord(g_records.back().b, s);
+  g_last_timed = false;
 }
 
 // --- configuration ----------------------------------------------------------
@@ -257,6 +277,11 @@ int moe_timing_enable(int32_t on) {
   return MOE_OK;
 }
 
+int moe_timing_select(const char* kernel_name) {
+  g_only = kernel_name ? kernel_name : "";
+  return MOE_OK;
+}
+
 int moe_timing_report(char* buf, size_t len) {
   if (!buf || len == 0) return MOE_EINVAL;
   std::map<std::string, std::pair<int, double>> agg;
@@ -268,10 +293,9 @@ int moe_timing_report(char* buf, size_t len) {
       agg[r.name].first += 1;
       agg[r.name].second += ms;
     }
-    (void)hipEventDestroy(r.a);
-    (void)hipEventDestroy(r.b);
   }
   g_records.clear();
+  g_pool_next = 0;
   std::string out;
   for (auto& n : order) {
     char line[256];
