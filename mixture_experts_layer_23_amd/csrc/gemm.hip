@@ -1279,6 +1279,438 @@ __global__ __launch_bounds__(NW * 64) void grouped_gemm_big_kernel(GemmParams P)
 }
 
 // ---------------------------------------------------------------------------
+// Persistent large tiles: the same 256 x BN tile and 8-wave main loop as
+// grouped_gemm_big_kernel, but each workgroup walks a strided list of tiles
+// and the DMA pipeline runs straight across tile boundaries: the two slabs
+// the loop fetches ahead at the end of a tile are the first two slabs of the
+// workgroup's next tile, so they land while the epilogue of the current tile
+// runs.  The epilogue therefore stages through an LDS region of its own (4 KB
+// per wave; the SwiGLU epilogues in two 16-row passes), not the stage
+// buffers.  Tile state is uniform (scalars); per-lane DMA offsets are fixed
+// for the whole kernel.  Every tile runs at least two slabs (padding), which
+// keeps the hand-over identical for empty weight-gradient groups.
+// ---------------------------------------------------------------------------
+template <int AMODE, int BMODE, int GROUPING, int EPI, int BSPL, int BN>
+__global__ __launch_bounds__(512) void grouped_gemm_persist_kernel(GemmParams P) {
+  typedef bf16_t T;
+  constexpr int NW = 8;
+  typedef BigShape<BN, NW> S;
+  constexpr int BM = 256, BK = 64;
+  constexpr int NI = S::NI, NJ = S::NJ, WTM = S::WTM, WTN = S::WTN;
+  constexpr int ATILE = BM * 128, BTILE = BN * 128;
+  constexpr int A_PER_WAVE = ATILE / 1024 / NW, B_PER_WAVE = BTILE / 1024 / NW;
+  constexpr int CPRB = BN / 8;
+  constexpr int EREG = 4096;  // epilogue staging bytes per wave
+  static_assert(WTN == 64, "epilogue staging sized for 64-column wave tiles");
+  __shared__ __attribute__((aligned(1024))) char sA0[ATILE];
+  __shared__ __attribute__((aligned(1024))) char sB0[BTILE];
+  __shared__ __attribute__((aligned(1024))) char sA1[ATILE];
+  __shared__ __attribute__((aligned(1024))) char sB1[BTILE];
+  __shared__ __attribute__((aligned(1024))) char sE[NW * EREG];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int wm = wave / S::WNW, wn = wave % S::WNW;
+
+  // ---- number of real tiles (GROUP_M: from the group sizes)
+  int64_t n_tiles;
+  int mt_real = 0;
+  if constexpr (GROUPING == GROUP_M) {
+    const int gpl = (P.G + 63) / 64;
+    int mine = 0;
+    for (int j = 0; j < gpl; ++j) {
+      const int g = lane * gpl + j;
+      if (g < P.G) mine += (P.offsets[g + 1] - P.offsets[g] + BM - 1) / BM;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mine += __shfl_xor(mine, o, 64);
+    mt_real = __builtin_amdgcn_readfirstlane(mine);
+    n_tiles = (int64_t)mt_real * P.ntn;
+  } else {
+    n_tiles = (int64_t)P.G * P.ntm * P.ntn;
+  }
+  const int64_t nwg = gridDim.x;
+  if ((int64_t)blockIdx.x >= n_tiles) return;
+
+  // ---- per-lane DMA offsets, fixed for the kernel
+  uint32_t a_lane[A_PER_WAVE];
+#pragma unroll
+  for (int u = 0; u < A_PER_WAVE; ++u) {
+    const int P_ = 64 * (wave * A_PER_WAVE + u) + lane;
+    if constexpr (AMODE == KC) {
+      const int r = P_ >> 3, lc = (P_ & 7) ^ swz(r);
+      a_lane[u] = (uint32_t)(((int64_t)r * P.lda + 8 * lc) * 2);
+    } else {
+      const int kr = P_ / 32, lc = (P_ % 32) ^ ((kr & 3) << 2);
+      a_lane[u] = (uint32_t)(((int64_t)kr * P.lda + 8 * lc) * 2);
+    }
+  }
+  int64_t b_lane[B_PER_WAVE];  // elements (GROUP_M) or bytes (GROUP_K)
+  bool b_hi[B_PER_WAVE];       // BS_N: chunk from the second (up) matrix
+#pragma unroll
+  for (int u = 0; u < B_PER_WAVE; ++u) {
+    const int P_ = 64 * (wave * B_PER_WAVE + u) + lane;
+    b_hi[u] = false;
+    if constexpr (GROUPING == GROUP_M) {
+      if constexpr (BMODE == KC) {
+        const int r = P_ >> 3, lc = (P_ & 7) ^ swz(r);
+        b_lane[u] = (int64_t)r * P.ldb + 8 * lc;
+      } else {
+        const int kr = P_ / CPRB, lc = (P_ % CPRB) ^ ((kr & 3) << 2);
+        if constexpr (BSPL == BS_N) {
+          b_hi[u] = lc >= CPRB / 2;
+          b_lane[u] = (int64_t)kr * P.ldb + 8 * (lc % (CPRB / 2));
+        } else {
+          b_lane[u] = (int64_t)kr * P.ldb + 8 * lc;
+        }
+      }
+    } else {
+      const int kr = P_ / CPRB, lc = (P_ % CPRB) ^ ((kr & 3) << 2);
+      b_lane[u] = ((int64_t)kr * P.ldb + 8 * lc) * 2;
+    }
+  }
+
+  // ---- tile state (uniform)
+  struct Tile {
+    int g, m0, n0, rows_valid, nk;
+    int64_t arow0;
+    bool real;
+    __amdgpu_buffer_rsrc_t a_rs, b_rs;
+  };
+  auto decode = [&](int64_t j, bool real) __attribute__((always_inline)) {
+    Tile t;
+    t.real = real;
+    const int64_t lin = remap_xcd(j, n_tiles);
+    int kdim, nrows_g = 0;
+    if constexpr (GROUPING == GROUP_M) {
+      int mt, nt, mtl, g;
+      supercol_tile(lin, mt_real, P.ntn, mt, nt);
+      find_group(P.offsets, P.G, mt, g, mtl, BM);
+      t.g = __builtin_amdgcn_readfirstlane(g);
+      mtl = __builtin_amdgcn_readfirstlane(mtl);
+      nrows_g = P.offsets[t.g + 1] - P.offsets[t.g];
+      t.m0 = mtl * BM;
+      t.n0 = nt * BN;
+      t.rows_valid = min(BM, nrows_g - t.m0);
+      kdim = P.Kdim;
+    } else {
+      const int64_t per = (int64_t)P.ntm * P.ntn;
+      t.g = (int)(lin / per);
+      int mt, nt;
+      supercol_tile(lin - (int64_t)t.g * per, P.ntm, P.ntn, mt, nt);
+      t.m0 = mt * BM;
+      t.n0 = nt * BN;
+      t.rows_valid = BM;
+      kdim = P.offsets[t.g + 1] - P.offsets[t.g];
+    }
+    t.arow0 = P.offsets[t.g];
+    t.nk = max(2, (kdim + BK - 1) / BK);
+    t.nk += t.nk & 1;  // even: the next tile's slab 0 always lands in stage 0
+    const T* a_base = (t.g < P.EL_A) ? reinterpret_cast<const T*>(P.A) + t.arow0 * P.lda
+                                     : reinterpret_cast<const T*>(P.A_sh);
+    const int64_t a_rows = (GROUPING == GROUP_M) ? nrows_g : kdim;
+    t.a_rs = make_rsrc(a_base, a_rows * P.lda * 2);
+    if constexpr (GROUPING == GROUP_K) {
+      const T* b_base = (t.g < P.EL_B) ? reinterpret_cast<const T*>(P.B0) + t.arow0 * P.ldb
+                                       : reinterpret_cast<const T*>(P.B1);
+      t.b_rs = make_rsrc(b_base, (int64_t)kdim * P.ldb * 2);
+    } else {
+      t.b_rs = make_rsrc(P.B0, 16);
+    }
+    // slabs holding real data: the rest of the (padded) slab count reads 0
+    t.rows_valid = real ? t.rows_valid : 0;
+    return t;
+  };
+  // real k-slabs of a tile (for GROUP_M: Kdim / BK; GROUP_K: the group rows)
+  auto real_slabs = [&](const Tile& t) __attribute__((always_inline)) {
+    if constexpr (GROUPING == GROUP_M) return (P.Kdim + BK - 1) / BK;
+    else return (P.offsets[t.g + 1] - P.offsets[t.g] + BK - 1) / BK;
+  };
+
+  // DMA of slab s of tile t into (la, lb); slabs past the real ones read
+  // zeros for A (offset past the buffer range; GROUP_K: B too) and, for
+  // GROUP_M, re-read the tile's last weight slab (times a zero A: nothing)
+  auto issue = [&](const Tile& t, int nreal, int s, char* la, char* lb) __attribute__((always_inline)) {
+    const bool pad = !t.real || s >= nreal;
+    const int k0 = (GROUPING == GROUP_M && pad) ? max(nreal - 1, 0) * BK : s * BK;
+    const uint32_t tbase = (AMODE == KC) ? (uint32_t)((int64_t)t.m0 * P.lda * 2) : (uint32_t)(t.m0 * 2);
+    const uint32_t kadd = (AMODE == KC) ? (uint32_t)(k0 * 2) : (uint32_t)((int64_t)k0 * P.lda * 2);
+#pragma unroll
+    for (int u = 0; u < A_PER_WAVE; ++u)
+      dma16_buffer(t.a_rs, to_lds(la + (wave * A_PER_WAVE + u) * 1024),
+                   pad ? 0x80000000u : tbase + a_lane[u] + kadd);
+#pragma unroll
+    for (int u = 0; u < B_PER_WAVE; ++u) {
+      char* dst = lb + (wave * B_PER_WAVE + u) * 1024;
+      if constexpr (GROUPING == GROUP_M) {
+        const T* Bw0 = reinterpret_cast<const T*>(P.B0) + (int64_t)t.g * P.strideB;
+        const T* src;
+        if constexpr (BMODE == KC) {
+          const T* row = Bw0 + (int64_t)t.n0 * P.ldb + b_lane[u];
+          if constexpr (BSPL == BS_K) {
+            const T* Bw1 = reinterpret_cast<const T*>(P.B1) + (int64_t)t.g * P.strideB;
+            src = (k0 < P.bsplit) ? row + k0 : (row - Bw0) + Bw1 + (k0 - P.bsplit);
+          } else {
+            src = row + k0;
+          }
+        } else {
+          if constexpr (BSPL == BS_N) {
+            const T* Bw1 = reinterpret_cast<const T*>(P.B1) + (int64_t)t.g * P.strideB;
+            src = (b_hi[u] ? Bw1 : Bw0) + t.n0 / 2 + b_lane[u] + (int64_t)k0 * P.ldb;
+          } else {
+            src = Bw0 + t.n0 + b_lane[u] + (int64_t)k0 * P.ldb;
+          }
+        }
+        dma16_global(src, to_lds(dst));
+      } else {
+        dma16_buffer(t.b_rs, to_lds(dst),
+                     pad ? 0x80000000u
+                         : (uint32_t)(t.n0 * 2 + b_lane[u] + (int64_t)k0 * P.ldb * 2));
+      }
+    }
+  };
+
+  int rb[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    if constexpr (EPI == EPI_SWIGLU_FWD)
+      rb[j] = (j < NJ / 2) ? wn * (WTN / 2) + j * 32 : BN / 2 + wn * (WTN / 2) + (j - NJ / 2) * 32;
+    else
+      rb[j] = wn * WTN + j * 32;
+  }
+  f32x16_t acc[NI][NJ];
+  auto zero_acc = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  };
+  uint4 fa[2][NI], fb[2][NJ];
+  auto frags = [&](const char* la, const char* lb, int ks, int slot) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      fa[slot][i] = (AMODE == KC) ? frag_kc(la, wm * WTM + i * 32, ks, lane)
+                                  : frag_mc(const_cast<char*>(la), wm * WTM + i * 32, ks, lane, BM * 2);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      fb[slot][j] = (BMODE == KC) ? frag_kc(lb, rb[j], ks, lane)
+                                  : frag_mc(const_cast<char*>(lb), rb[j], ks, lane, BN * 2);
+  };
+  auto mfmas = [&](int slot) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8_t, fb[slot][j]), __builtin_bit_cast(bf16x8_t, fa[slot][i]),
+            acc[i][j], 0, 0, 0);
+  };
+  constexpr int PER_SLAB = A_PER_WAVE + B_PER_WAVE;
+
+  int64_t j = blockIdx.x;
+  Tile cur = decode(j, true);
+  int cur_real = real_slabs(cur);
+  Tile nxt = (j + nwg < n_tiles) ? decode(j + nwg, true) : decode(j, false);
+  int nxt_real = real_slabs(nxt);
+  issue(cur, cur_real, 0, sA0, sB0);
+  issue(cur, cur_real, 1, sA1, sB1);
+  wait_vmcnt<PER_SLAB>();
+  __syncthreads();
+  frags(sA0, sB0, 0, 0);
+  zero_acc();
+
+  // one pipeline step (see grouped_gemm_big_kernel); the DMA two slabs ahead
+  // belongs to the next tile once the current one runs out
+  auto step = [&](int kt, char* la, char* lb, char* na, char* nb) __attribute__((always_inline)) {
+    frags(la, lb, 1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(0);
+    frags(la, lb, 2, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(1);
+    frags(la, lb, 3, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(0);
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (kt + 2 < cur.nk) issue(cur, cur_real, kt + 2, la, lb);
+    else issue(nxt, nxt_real, kt + 2 - cur.nk, la, lb);
+    frags(na, nb, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(1);
+  };
+
+  const int lrow = lane & 31, lcol = (lane >> 5) * 4;
+  char* reg = sE + wave * EREG;
+  // bf16 staging of a [rows][W] array at base (chunk swizzle inside the row)
+  auto put4 = [&](char* base, int W, int row, int col, const float* v) __attribute__((always_inline)) {
+    const int ch = col >> 3, half = (col >> 2) & 1, msk = min(W / 8, 8) - 1;
+    *reinterpret_cast<uint2*>(base + row * W * 2 + ((ch ^ (row & msk)) << 4) + (half << 3)) =
+        pack_bf16x4(v);
+  };
+  auto get16 = [&](const char* base, int W, int row, int ch) __attribute__((always_inline)) {
+    const int msk = min(W / 8, 8) - 1;
+    return *reinterpret_cast<const uint4*>(base + row * W * 2 + ((ch ^ (row & msk)) << 4));
+  };
+
+  for (;;) {
+    for (int kt = 0; kt < cur.nk; kt += 2) {
+      step(kt, sA0, sB0, sA1, sB1);
+      step(kt + 1, sA1, sB1, sA0, sB0);
+    }
+    // ---- epilogue of cur (its own LDS region; the next tile's first slabs
+    // are landing meanwhile)
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int row_t0 = wm * WTM + i * 32;
+      if (row_t0 >= cur.rows_valid) break;
+      const int64_t grow0 = cur.arow0 + cur.m0 + row_t0;
+      if constexpr (EPI == EPI_SWIGLU_FWD) {
+        constexpr int W = WTN / 2;  // 32 f columns
+        char* sa = reg;
+        char* sb = reg + 16 * W * 2;
+        char* sh = reg + 32 * W * 2;
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+          if ((lrow >> 4) == pass) {
+#pragma unroll
+            for (int jj = 0; jj < NJ / 2; ++jj)
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                float a[4], b[4], h[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  a[e] = acc[i][jj][4 * q + e];
+                  b[e] = acc[i][jj + NJ / 2][4 * q + e];
+                  h[e] = silu_f(a[e]) * b[e];
+                }
+                const int col = jj * 32 + q * 8 + lcol;
+                put4(sa, W, lrow & 15, col, a);
+                put4(sb, W, lrow & 15, col, b);
+                put4(sh, W, lrow & 15, col, h);
+              }
+          }
+          // 16 rows x 4 chunks: one row per 4 lanes
+          const int row = lane >> 2, ch = lane & 3;
+          const int rt = row_t0 + pass * 16 + row;
+          if (rt < cur.rows_valid) {
+            const int64_t grow = cur.arow0 + cur.m0 + rt;
+            const int f = cur.n0 / 2 + wn * W + ch * 8;
+            T* aout = reinterpret_cast<T*>(P.act_out) + grow * 2 * P.F;
+            *reinterpret_cast<uint4*>(aout + f) = get16(sa, W, row, ch);
+            *reinterpret_cast<uint4*>(aout + P.F + f) = get16(sb, W, row, ch);
+            *reinterpret_cast<uint4*>(reinterpret_cast<T*>(P.C1) + grow * P.F + f) =
+                get16(sh, W, row, ch);
+          }
+        }
+      } else if constexpr (EPI == EPI_SWIGLU_BWD) {
+        // dh in fp32, 16 rows per pass: 8 lanes per row (8 columns each)
+        const int ch = lane & 7, rsub = lane >> 3;  // rows rsub and rsub + 8 of the pass
+        const int f = cur.n0 + wn * WTN + ch * 8;
+        uint4 av[2][2], bv[2][2];
+        auto load_pass = [&](int pass, uint4* a, uint4* b) __attribute__((always_inline)) {
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const int rt = row_t0 + pass * 16 + h2 * 8 + rsub;
+            if (rt < cur.rows_valid) {
+              const T* act = reinterpret_cast<const T*>(P.act) + (cur.arow0 + cur.m0 + rt) * 2 * P.F;
+              a[h2] = *reinterpret_cast<const uint4*>(act + f);
+              b[h2] = *reinterpret_cast<const uint4*>(act + P.F + f);
+            }
+          }
+        };
+        load_pass(0, av[0], bv[0]);
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+          if (pass == 0) load_pass(1, av[1], bv[1]);
+          if ((lrow >> 4) == pass) {
+#pragma unroll
+            for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const int c4 = (jj * 32 + q * 8 + lcol) >> 2;
+                const int r16 = lrow & 15;
+                *reinterpret_cast<float4*>(reg + r16 * WTN * 4 + ((c4 ^ r16) << 4)) =
+                    make_float4(acc[i][jj][4 * q], acc[i][jj][4 * q + 1], acc[i][jj][4 * q + 2],
+                                acc[i][jj][4 * q + 3]);
+              }
+          }
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const int r16 = h2 * 8 + rsub;
+            const int rt = row_t0 + pass * 16 + r16;
+            if (rt >= cur.rows_valid) continue;
+            float v[8], a[8], b[8], da[8], db[8];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+              const int c4 = 2 * ch + hh;
+              const float4 d = *reinterpret_cast<const float4*>(reg + r16 * WTN * 4 + ((c4 ^ r16) << 4));
+              v[4 * hh] = d.x; v[4 * hh + 1] = d.y; v[4 * hh + 2] = d.z; v[4 * hh + 3] = d.w;
+            }
+            Vec16<T> va, vb;
+            va.v = av[pass][h2];
+            vb.v = bv[pass][h2];
+            va.to_f32(a);
+            vb.to_f32(b);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float sg = 1.0f / (1.0f + expf(-a[e]));
+              da[e] = v[e] * b[e] * sg * (1.0f + a[e] * (1.0f - sg));
+              db[e] = v[e] * a[e] * sg;
+            }
+            T* dact = reinterpret_cast<T*>(P.C0) + (cur.arow0 + cur.m0 + rt) * 2 * P.F;
+            Vec16<T> oa, ob;
+            oa.from_f32(da);
+            ob.from_f32(db);
+            oa.store(dact + f);
+            ob.store(dact + P.F + f);
+          }
+        }
+      } else {
+        // 32 rows x 64 columns of bf16 in one pass
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = acc[i][jj][4 * q + e];
+            put4(reg, WTN, lrow, jj * 32 + q * 8 + lcol, v);
+          }
+        const int ch = lane & 7;
+        const int col = cur.n0 + wn * WTN + ch * 8;
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          const int row = it * 8 + (lane >> 3);
+          if (row_t0 + row >= cur.rows_valid) continue;
+          const uint4 v = get16(reg, WTN, row, ch);
+          if constexpr (GROUPING == GROUP_M) {
+            *reinterpret_cast<uint4*>(reinterpret_cast<T*>(P.C0) + (grow0 + row) * P.ldc + col) = v;
+          } else {
+            const int64_t mrow = cur.m0 + row_t0 + row;
+            T* Cp = (col < P.csplit)
+                        ? reinterpret_cast<T*>(P.C0) + (int64_t)cur.g * P.strideC + mrow * P.ldc + col
+                        : reinterpret_cast<T*>(P.C1) + (int64_t)cur.g * P.strideC + mrow * P.ldc +
+                              (col - P.csplit);
+            *reinterpret_cast<uint4*>(Cp) = v;
+          }
+        }
+      }
+    }
+    zero_acc();
+    if (!nxt.real) break;
+    j += nwg;
+    cur = nxt;
+    cur_real = nxt_real;
+    nxt = (j + nwg < n_tiles) ? decode(j + nwg, true) : decode(j, false);
+    nxt_real = real_slabs(nxt);
+  }
+  // the run-ahead DMA (padding) must land before the LDS is released
+  wait_vmcnt<0>();
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 static int groups_of(const moe_config& c) { return (c.expert_hi - c.expert_lo) + c.n_shared; }
@@ -1299,7 +1731,8 @@ static void tile_space(GemmParams& P, int grouping, int bm) {
 
 // GEMM configuration of the LDS-DMA kernels: 0 = register-staged kernel,
 // 1 = 128-row tiles / 2 stages, 2 = 256-row tiles / 3 stages, 3 / 4 = 256 x
-// 256 / 256 x 128 large tiles on 4 waves, 5 / 6 = the same on 8 waves.
+// 256 / 256 x 128 large tiles on 4 waves, 5 / 6 = the same on 8 waves,
+// 7 / 8 = persistent 256 x 256 / 256 x 128 on 8 waves.
 // MOE_GEMM_CFG overrides the choice (measurement only).
 static int cfg_override() {
   static int v = [] {
@@ -1332,6 +1765,18 @@ static int launch_big(const char* name, GemmParams P, hipStream_t st) {
   return MOE_OK;
 }
 
+// one persistent workgroup per CU (at most one tile each when there are fewer)
+template <int AM, int BM_, int GR, int EPI, int BS, int BN>
+static int launch_persist(const char* name, GemmParams P, hipStream_t st) {
+  P.ntn = P.N / BN;
+  tile_space(P, GR, 256);
+  if (P.nblocks <= 0) return MOE_OK;
+  const int64_t grid = std::min<int64_t>(P.nblocks, 256);
+  MOE_LAUNCH(name, (grouped_gemm_persist_kernel<AM, BM_, GR, EPI, BS, BN>), dim3((unsigned)grid),
+             dim3(512), 0, st, P);
+  return MOE_OK;
+}
+
 template <typename T, int AM, int BM_, int GR, int EPI, int BS>
 static int run_gemm(const char* name, GemmParams& P, hipStream_t st) {
   if constexpr (sizeof(T) == 2) {
@@ -1349,7 +1794,10 @@ static int run_gemm(const char* name, GemmParams& P, hipStream_t st) {
         tile_space(Q, GR, 256);
       }
       if (wide && Q.nblocks >= (GR == GROUP_K ? 192 : 384)) {
-        cfg = 5;
+        // the plain-store row GEMM (down projection forward) runs persistent:
+        // measured 10-30 % faster there; the fused epilogues and the weight
+        // gradients are not (register pressure, store waits at tile change)
+        cfg = (GR == GROUP_M && EPI == EPI_STORE && BS == BS_NONE) ? 7 : 5;
       } else {
         Q = P;
         tile_space(Q, GR, 256);
@@ -1359,6 +1807,8 @@ static int run_gemm(const char* name, GemmParams& P, hipStream_t st) {
     if (cfg == 3 && wide) return launch_big<AM, BM_, GR, EPI, BS, 256, 4>(name, P, st);
     if (cfg == 4 && full256) return launch_big<AM, BM_, GR, EPI, BS, 128, 4>(name, P, st);
     if (cfg == 5 && wide) return launch_big<AM, BM_, GR, EPI, BS, 256, 8>(name, P, st);
+    if (cfg == 7 && wide) return launch_persist<AM, BM_, GR, EPI, BS, 256>(name, P, st);
+    if (cfg == 8 && full256) return launch_persist<AM, BM_, GR, EPI, BS, 128>(name, P, st);
     if (cfg == 6 && full256) return launch_big<AM, BM_, GR, EPI, BS, 128, 8>(name, P, st);
     if (cfg == 2 && full256) return launch_dma<AM, BM_, GR, EPI, BS, 256, 3>(name, P, st);
     if (cfg >= 1 && full128) return launch_dma<AM, BM_, GR, EPI, BS, 128, 2>(name, P, st);
