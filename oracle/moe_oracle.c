@@ -502,6 +502,98 @@ void orc_aux(const orc_cfg* c, const double* logits, const int* counts_all, doub
 }
 
 /* ------------------------------------------------------------------------ */
+/* Load-driven selection-bias update ([P5] course notes 8.6; [P4] section on  */
+/* the auxiliary-loss-free route): experts select on s_e + b_e; after a step  */
+/* an overloaded expert lowers its b_e, an underloaded one raises it, by a    */
+/* fixed step gamma.  Reading: overloaded means more slots than the mean load */
+/* T*K/E (over all E, before capacity), underloaded fewer; an expert exactly  */
+/* at the mean keeps b_e.  The comparison is exact in integers              */
+/* (counts_e * E vs T * K); the update is one binary32 add or subtract.       */
+/* ------------------------------------------------------------------------ */
+void orc_bias_update(const orc_cfg* c, const int* counts_all, float gamma, float* selb) {
+  const long long mean_num = (long long)c->T * c->K;
+  for (int e = 0; e < c->E; ++e) {
+    const long long load = (long long)counts_all[e] * c->E;
+    if (load > mean_num) selb[e] = selb[e] - gamma;
+    else if (load < mean_num) selb[e] = selb[e] + gamma;
+  }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Sequence-wise balance loss ([P5] 8.6: a small complementary loss that is  */
+/* kept beside the bias rule; 8.5: the balance loss L = alpha E sum_e f_e P_e */
+/* with f the hard assignment fraction, held constant in the gradient, and P  */
+/* the mean soft probability).  Reading: the same loss on each sequence of S  */
+/* consecutive tokens, averaged over the T / S sequences:                     */
+/*   f_{b,e} = n_{b,e} / (S K),   n = slots of sequence b that chose e       */
+/*   P_{b,e} = (1/S) sum_{t in b} p_{t,e}                                     */
+/*   L_seq   = alpha E (S / T) sum_b sum_e f_{b,e} P_{b,e}                    */
+/* with p the scoring function's normalised probabilities: softmax(s) for     */
+/* softmax scoring; sigma(s_e) / sum_j sigma(s_j) for sigmoid scoring.       */
+/* Gradient (f constant), u_{b,e} = alpha E (S / T) f_{b,e} / S:              */
+/*   d/ds_{t,i} = w_{t,i} (u_{b,i} - sum_e p_{t,e} u_{b,e}),                   */
+/*   w = p_i (softmax) or sigma_i (1 - sigma_i) / sum_j sigma_j (sigmoid).    */
+/* With S = T it is the batch loss above (f over all T).                     */
+/* dlogits (optional) receives the gradient ([T][E]).                        */
+/* ------------------------------------------------------------------------ */
+static void seq_probs(const orc_cfg* c, const double* s, double* p, double* w) {
+  const int E = c->E;
+  if (c->score == 0) {
+    double m = -INFINITY, z = 0.0;
+    for (int e = 0; e < E; ++e) if (s[e] > m) m = s[e];
+    for (int e = 0; e < E; ++e) z += exp(s[e] - m);
+    for (int e = 0; e < E; ++e) { p[e] = exp(s[e] - m) / z; w[e] = p[e]; }
+  } else {
+    double z = 0.0;
+    for (int e = 0; e < E; ++e) z += sigm(s[e]);
+    for (int e = 0; e < E; ++e) {
+      const double sg = sigm(s[e]);
+      p[e] = sg / z;
+      w[e] = sg * (1.0 - sg) / z;
+    }
+  }
+}
+
+int orc_seq_aux(const orc_cfg* c, const double* logits, const int* idx, int S, double alpha,
+                double* loss, double* dlogits) {
+  const int T = c->T, E = c->E, K = c->K;
+  if (S <= 0 || T % S) return -1;
+  const int B = T / S;
+  double* p = (double*)malloc(sizeof(double) * E);
+  double* w = (double*)malloc(sizeof(double) * E);
+  double* P = (double*)malloc(sizeof(double) * E);
+  double* u = (double*)malloc(sizeof(double) * E);
+  int* n = (int*)malloc(sizeof(int) * E);
+  double L = 0.0;
+  for (int b = 0; b < B; ++b) {
+    for (int e = 0; e < E; ++e) { P[e] = 0.0; n[e] = 0; }
+    for (int t = b * S; t < (b + 1) * S; ++t) {
+      seq_probs(c, logits + (size_t)t * E, p, w);
+      for (int e = 0; e < E; ++e) P[e] += p[e];
+      for (int k = 0; k < K; ++k) n[idx[(size_t)t * K + k]] += 1;
+    }
+    double Lb = 0.0;
+    for (int e = 0; e < E; ++e) {
+      const double f = (double)n[e] / ((double)S * K);
+      Lb += f * (P[e] / S);
+      u[e] = alpha * E * ((double)S / T) * f / S;
+    }
+    L += Lb;
+    if (dlogits) {
+      for (int t = b * S; t < (b + 1) * S; ++t) {
+        seq_probs(c, logits + (size_t)t * E, p, w);
+        double pu = 0.0;
+        for (int e = 0; e < E; ++e) pu += p[e] * u[e];
+        for (int e = 0; e < E; ++e) dlogits[(size_t)t * E + e] = w[e] * (u[e] - pu);
+      }
+    }
+  }
+  *loss = alpha * E * ((double)S / T) * L;
+  free(p); free(w); free(P); free(u); free(n);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* O9-O12: backward                                                          */
 /* ------------------------------------------------------------------------ */
 /*

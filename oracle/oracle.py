@@ -100,6 +100,9 @@ def lib():
         L.orc_expert_rows.argtypes = [P, P, C.c_int, P, P, P, C.c_int, P, P, C.c_int, P, P, P, P]
         L.orc_aux.argtypes = [P, P, P, C.c_double, C.c_double, P, P]
         L.orc_gate_grad.argtypes = [P, P, P, P, P, P]
+        L.orc_bias_update.argtypes = [P, P, C.c_float, P]
+        L.orc_seq_aux.argtypes = [P, P, P, C.c_int, C.c_double, P, P]
+        L.orc_seq_aux.restype = C.c_int
         L.orc_backward.argtypes = [P, P, C.c_int, P, P, P, P, C.c_int, P, P, P, P, P, C.c_int,
                                    P, P, P, C.c_int, P, P, P, P, P, P, P]
         _lib = L
@@ -226,6 +229,31 @@ def aux(cfg: Cfg, lg, counts_all, alpha: float, zlam: float, want_grad: bool = T
     c = cfg.c()
     lib().orc_aux(C.byref(c), _p(lg), _p(cnt), float(alpha), float(zlam), _p(losses), _p(dl))
     return losses, dl
+
+
+def bias_update(cfg: Cfg, counts_all, gamma: float, selb) -> np.ndarray:
+    """Load-driven selection-bias step: returns the updated fp32 b (the input
+    is not modified)."""
+    cnt = np.ascontiguousarray(counts_all, dtype=np.int32)
+    b = np.array(selb, dtype=np.float32, copy=True)
+    c = cfg.c()
+    lib().orc_bias_update(C.byref(c), _p(cnt), float(gamma), _p(b))
+    return b
+
+
+def seq_aux(cfg: Cfg, lg, idx, seq_len: int, alpha: float, want_grad: bool = True):
+    """Sequence-wise balance loss over sequences of seq_len tokens and its
+    logit gradient [T,E] (f held constant)."""
+    lg = np.ascontiguousarray(lg, dtype=np.float64)
+    ix = np.ascontiguousarray(idx, dtype=np.int32)
+    loss = np.zeros(1, np.float64)
+    dl = np.empty((cfg.T, cfg.E), np.float64) if want_grad else None
+    c = cfg.c()
+    rc = lib().orc_seq_aux(C.byref(c), _p(lg), _p(ix), int(seq_len), float(alpha), _p(loss),
+                           _p(dl))
+    if rc != 0:
+        raise ValueError(f"seq_len {seq_len} must divide T = {cfg.T}")
+    return float(loss[0]), dl
 
 
 def gate_grad(cfg: Cfg, lg, idx, w, dg) -> np.ndarray:

@@ -578,3 +578,83 @@ def test_thread_count_does_not_change_results(orc):
         orc.set_threads(n0)
     for key in ("y", "dx", "dwr", "dwg", "dwd"):
         np.testing.assert_array_equal(a[key], b[key])
+
+
+# ---------------------------------------------------------------------------
+# sequence-wise balance loss and the load-driven bias update (next rows)
+# ---------------------------------------------------------------------------
+def test_seq_aux_worked_examples(orc):
+    g = gold("seq_aux_example.json")["softmax"]
+    p0 = np.array(g["p0"])
+    lg = np.log(np.stack([p0, 1 - p0], 1))
+    cfg = orc.Cfg(T=4, D=1, E=2, K=1, F=8)
+    idx = np.array(g["choice"], np.int32)[:, None]
+    L2, dl2 = orc.seq_aux(cfg, lg, idx, 2, g["alpha"])
+    assert abs(L2 - g["S2"]["L"]) < 1e-12
+    np.testing.assert_allclose(dl2[0], g["S2"]["dlogits_seq1"], atol=1e-15)
+    np.testing.assert_allclose(dl2[1], g["S2"]["dlogits_seq1"], atol=1e-15)
+    np.testing.assert_allclose(dl2[2:], 0.0, atol=1e-15)
+    L4, _ = orc.seq_aux(cfg, lg, idx, 4, g["alpha"])
+    assert abs(L4 - g["S4"]["L"]) < 1e-12
+    with pytest.raises(ValueError):
+        orc.seq_aux(cfg, lg, idx, 3, g["alpha"])
+
+
+def test_seq_aux_sigmoid_worked_example(orc):
+    g = gold("seq_aux_example.json")["sigmoid"]
+    lg = np.array([[np.log(4.0), -np.log(4.0)], [np.log(1.5), -np.log(1.5)]])
+    cfg = orc.Cfg(T=2, D=1, E=2, K=1, F=8, score=1)
+    idx = np.array(g["choice"], np.int32)[:, None]
+    L, dl = orc.seq_aux(cfg, lg, idx, g["S"], g["alpha"])
+    assert abs(L - g["L"]) < 1e-12
+    np.testing.assert_allclose(dl[0], g["dlogits_t0"], rtol=1e-12)
+
+
+def test_seq_aux_full_sequence_is_batch_loss(orc):
+    """S = T reduces to the batch balance loss (pinned by the worked example of
+    section 8.5) on random routings, softmax scoring."""
+    rng = np.random.default_rng(3)
+    for E, K, T in [(4, 2, 32), (8, 1, 24), (6, 3, 12)]:
+        cfg = orc.Cfg(T=T, D=1, E=E, K=K, F=8)
+        lg = rng.normal(size=(T, E))
+        idx, _, _, _ = orc.route(cfg, lg.astype(np.float32).astype(np.float64))
+        counts = np.bincount(idx.ravel(), minlength=E)
+        losses, dla = orc.aux(cfg, lg, counts, 0.02, 0.0)
+        L, dls = orc.seq_aux(cfg, lg, idx, T, 0.02)
+        assert abs(L - losses[0]) < 1e-14
+        np.testing.assert_allclose(dls, dla, atol=1e-16)
+
+
+@pytest.mark.parametrize("score", [0, 1])
+def test_seq_aux_gradient_finite_differences(orc, score):
+    """Central differences of the loss with the selection (and so f) held fixed."""
+    rng = np.random.default_rng(11 + score)
+    T, E, K, S = 12, 5, 2, 4
+    cfg = orc.Cfg(T=T, D=1, E=E, K=K, F=8, score=score)
+    lg = rng.normal(size=(T, E))
+    idx = np.stack([rng.choice(E, K, replace=False) for _ in range(T)]).astype(np.int32)
+    _, dl = orc.seq_aux(cfg, lg, idx, S, 0.05)
+    h = 1e-6
+    fd = np.zeros_like(lg)
+    for t in range(T):
+        for e in range(E):
+            a = lg.copy(); a[t, e] += h
+            b = lg.copy(); b[t, e] -= h
+            fd[t, e] = (orc.seq_aux(cfg, a, idx, S, 0.05, False)[0]
+                        - orc.seq_aux(cfg, b, idx, S, 0.05, False)[0]) / (2 * h)
+    np.testing.assert_allclose(dl, fd, atol=1e-9 * np.abs(fd).max() + 1e-13, rtol=1e-6)
+
+
+def test_bias_update_rule(orc):
+    g = gold("seq_aux_example.json")["bias_update"]
+    cfg = orc.Cfg(T=g["T"], D=1, E=g["E"], K=g["K"], F=8)
+    b = orc.bias_update(cfg, g["counts"], g["gamma"], g["b_in"])
+    b_in = np.array(g["b_in"], np.float32)
+    gam = np.float32(g["gamma"])
+    want = [b_in[e] + gam * np.float32(s) if s else b_in[e] for e, s in enumerate(g["expect_sign"])]
+    np.testing.assert_array_equal(b, np.array(want, np.float32))
+    # overloaded / underloaded is decided exactly in integers: a load one
+    # above or below the mean moves the bias, the mean itself does not
+    cfg2 = orc.Cfg(T=1000, D=1, E=3, K=1, F=8)
+    b2 = orc.bias_update(cfg2, [334, 333, 333], 0.5, [0.0, 0.0, 0.0])
+    np.testing.assert_array_equal(b2, np.array([-0.5, 0.5, 0.5], np.float32))
