@@ -43,6 +43,11 @@ def parse():
     ap.add_argument("--k", type=int, default=None, help="override top-K")
     ap.add_argument("--gating", choices=["A", "B"], default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seq-len", type=int, default=0,
+                    help="add the sequence-wise balance loss over sequences of this length")
+    ap.add_argument("--seq-alpha", type=float, default=1e-3)
+    ap.add_argument("--bias-gamma", type=float, default=0.0,
+                    help="add the load-driven selection-bias step (sigmoid routing)")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step replayed as one HIP graph (reported as ms_per_step_graph)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=None)
@@ -154,7 +159,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     inp = S.device_inputs(wl, device="cuda")
-    spec = LayerSpec.from_workload(wl)
+    spec = LayerSpec.from_workload(wl, seq_len=args.seq_len,
+                                   seq_alpha=args.seq_alpha if args.seq_len else 0.0,
+                                   bias_gamma=args.bias_gamma)
     layer = MoELayer(spec, inp["wr"], inp["wg"], inp["wu"], inp["wd"], inp["rb"], inp["selb"])
     x, dy = inp["x"], inp["dy"]
     torch.cuda.synchronize()
@@ -232,6 +239,9 @@ def main():
         "router_logits": wl.T * Dsz + wl.E * wl.D * 4 + wl.T * wl.E * 4,
         "router_wgrad": wl.T * Dsz + wl.T * wl.E * 4,
         "aux_partial": wl.T * wl.E * 4 * (2 if wl.alpha or wl.zlam else 1),
+        # logits read twice (probabilities, then the gradient), routing read,
+        # gradient written (read as well when accumulating)
+        "seq_aux": wl.T * wl.E * 4 * (4 if layer.use_aux else 3) + wl.T * wl.K * 4,
     }
     for name, b in stage_bytes.items():
         if name in kernels:
@@ -281,7 +291,8 @@ def main():
         "config": {"workload": wl_name(wl), "launch": "eager",
                    "tokens": wl.T, "local_rows": n_rows_local,
                    "shared_rows": wl.n_shared * wl.T, "dropped": n_dropped,
-                   "expert_load": counts.tolist() if wl.E <= 16 else None},
+                   "expert_load": counts.tolist() if wl.E <= 16 else None,
+                   "seq_len": args.seq_len or None, "bias_gamma": args.bias_gamma or None},
         "grouped_gemm": {"tflops": gemm_flops / (gemm_ms * 1e-3) / 1e12 if gemm_ms else None,
                          "frac_of_peak": (gemm_flops / (gemm_ms * 1e-3) / 1e12 / peak_t)
                          if gemm_ms else None,

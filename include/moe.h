@@ -219,6 +219,46 @@ int moe_backward(const moe_config* cfg, const void* x, const float* w_r, const f
                  float* d_rbias, void* dw_gate, void* dw_up, void* dw_down, float* d_logits_out,
                  void* ws, size_t ws_bytes, moe_stream_t stream);
 
+/*
+ * Load-driven selection-bias step ("Course notes 08 MoE", section 8.6: the
+ * experts select on s_e + b_e; an overloaded expert lowers b_e, an
+ * underloaded one raises it, by a fixed step; the gate weights keep using the
+ * raw scores).  For every expert e:
+ *   counts_all[e] * E > T * K  ->  sel_bias[e] -= gamma
+ *   counts_all[e] * E < T * K  ->  sel_bias[e] += gamma    (binary32 add)
+ *   otherwise unchanged.
+ * counts_all: int32 [E] as written by moe_permute (all E, before capacity);
+ * sel_bias: fp32 [E], updated in place, caller-owned device memory.  Meant
+ * to run once per training step after the routing has consumed sel_bias.
+ * Errors: MOE_EINVAL (bad config, non-finite gamma, null), MOE_EALIGN.
+ */
+int moe_bias_update(const moe_config* cfg, const int32_t* counts_all, float gamma,
+                    float* sel_bias, moe_stream_t stream);
+
+/*
+ * Sequence-wise balance loss (course notes section 8.5's balance loss
+ * applied to each sequence of seq_len consecutive tokens and averaged over
+ * the T / seq_len sequences; section 8.6 keeps such a term beside the bias
+ * rule):
+ *   f_{b,e} = (slots of sequence b that chose e) / (seq_len * K)
+ *   P_{b,e} = mean over the tokens t of b of p_{t,e}
+ *   loss    = alpha * E * (seq_len / T) * sum_b sum_e f_{b,e} P_{b,e}
+ * with p = softmax(s) for softmax scoring and sigma(s_e) / sum_j sigma(s_j)
+ * for sigmoid scoring; the gradient holds f constant:
+ *   d_logits[t,i] = w_{t,i} (u_{b,i} - sum_e p_{t,e} u_{b,e}),
+ *   u_{b,e} = alpha * E / T * f_{b,e},  w = p (softmax) or
+ *   sigma_i (1 - sigma_i) / sum_j sigma_j (sigmoid).
+ * logits: fp32 [T][E]; topk_idx: int32 [T][K] (moe_route); loss: fp32 [1]
+ * out; d_logits: fp32 [T][E] out (NULL: loss only), overwritten, or added to
+ * when accumulate != 0 (to combine with aux_balance_loss's gradient before
+ * moe_backward); ws: the layer workspace.  seq_len must divide T.
+ * Errors: MOE_EINVAL (bad config, seq_len, non-finite alpha, null),
+ * MOE_EALIGN, MOE_EWORKSPACE.
+ */
+int aux_seq_loss(const moe_config* cfg, const float* logits, const int32_t* topk_idx,
+                 int32_t seq_len, float alpha, float* loss, float* d_logits, int32_t accumulate,
+                 void* ws, size_t ws_bytes, moe_stream_t stream);
+
 /* Text for an error code (thread-local detail for MOE_ELAUNCH). */
 const char* moe_error_string(int code);
 

@@ -22,7 +22,7 @@ MOE_ROUTE_LOGITS_GIVEN = 1
 EXPORTS = ["moe_capacity", "moe_rows_max", "moe_workspace_size", "moe_route", "moe_permute",
            "moe_expert_ffn", "moe_combine", "aux_balance_loss", "moe_backward",
            "moe_error_string", "moe_timing_enable", "moe_timing_report",
-           "moe_timing_select"]
+           "moe_timing_select", "moe_bias_update", "aux_seq_loss"]
 
 
 class MoeConfig(C.Structure):
@@ -65,6 +65,8 @@ def lib():
             "moe_timing_enable": [I],
             "moe_timing_report": [C.c_char_p, S],
             "moe_timing_select": [C.c_char_p],
+            "moe_bias_update": [cfg, P, C.c_float, P, P],
+            "aux_seq_loss": [cfg, P, P, I, C.c_float, P, P, I, P, S, P],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -174,6 +176,20 @@ def moe_backward(cfg, x, w_r, logits, topk_idx, topk_w, offsets, slot_row, x_per
 
 def timing_enable(on: bool) -> None:
     _check("moe_timing_enable", lib().moe_timing_enable(1 if on else 0))
+
+
+def moe_bias_update(cfg, counts_all, gamma, sel_bias, stream=None):
+    _check("moe_bias_update",
+           lib().moe_bias_update(C.byref(cfg), ptr(counts_all), float(gamma), ptr(sel_bias),
+                                 stream_handle(stream)))
+
+
+def aux_seq_loss(cfg, logits, topk_idx, seq_len, alpha, loss, d_logits, accumulate, ws,
+                 stream=None):
+    _check("aux_seq_loss",
+           lib().aux_seq_loss(C.byref(cfg), ptr(logits), ptr(topk_idx), int(seq_len),
+                              float(alpha), ptr(loss), ptr(d_logits), 1 if accumulate else 0,
+                              ptr(ws), ws.numel() * ws.element_size(), stream_handle(stream)))
 
 
 def timing_select(name: str | None) -> None:

@@ -131,6 +131,9 @@ Workspace workspace_layout(const moe_config& c) {
     L.rb_splits = (int)cdiv(T1, len);
   }
   L.rb_part = o;     o += al((size_t)L.rb_splits * (((size_t)c.E + 3) & ~(size_t)3) * 4);
+  L.seq_part = o;    o += al((size_t)std::max(c.T, 1) * 4);
+  L.seq_blk_n = o;   o += al((size_t)std::max(c.T, 1) * c.E * 4);
+  L.seq_blk_p = o;   o += al((size_t)std::max(c.T, 1) * c.E * 4);
   L.total = o;
   return L;
 }
@@ -235,6 +238,30 @@ int aux_balance_loss(const moe_config* cfg, const float* logits, const int32_t* 
   if (cfg->T == 0) return MOE_OK;
   return launch_aux(*cfg, logits, counts_all, alpha, z_lambda, losses, d_logits, (char*)ws, L,
                     (hipStream_t)stream);
+}
+
+int moe_bias_update(const moe_config* cfg, const int32_t* counts_all, float gamma,
+                    float* sel_bias, moe_stream_t stream) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (!std::isfinite(gamma)) return MOE_EINVAL;
+  REQ(counts_all); REQ(sel_bias);
+  return launch_bias_update(*cfg, counts_all, gamma, sel_bias, (hipStream_t)stream);
+}
+
+int aux_seq_loss(const moe_config* cfg, const float* logits, const int32_t* topk_idx,
+                 int32_t seq_len, float alpha, float* loss, float* d_logits, int32_t accumulate,
+                 void* ws, size_t ws_bytes, moe_stream_t stream) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (!std::isfinite(alpha) || seq_len <= 0) return MOE_EINVAL;
+  if (cfg->T % seq_len) return MOE_EINVAL;
+  REQ(logits); REQ(topk_idx); REQ(loss); OPT(d_logits); REQ(ws);
+  const Workspace L = workspace_layout(*cfg);
+  if (ws_bytes < L.total) return MOE_EWORKSPACE;
+  if (cfg->T == 0) return MOE_OK;
+  return launch_seq_aux(*cfg, logits, topk_idx, seq_len, alpha, loss, d_logits, accumulate != 0,
+                        (char*)ws, L, (hipStream_t)stream);
 }
 
 int moe_backward(const moe_config* cfg, const void* x, const float* w_r, const float* logits,

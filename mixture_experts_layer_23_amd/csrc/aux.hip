@@ -13,6 +13,8 @@
 // logit gradient p (u - sum p u) + lambda (2/T) lse p; then per expert the
 // workgroup's sum of p_e in token order.  A final single-workgroup kernel
 // sums the partials in workgroup order.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -139,6 +141,226 @@ int launch_aux(const moe_config& c, const float* logits, const int32_t* counts_a
              counts_all, c.T, c.E, c.K, TB, alpha, zlam, part, d_logits);
   MOE_LAUNCH("aux_final", aux_final_kernel, dim3(1), dim3(1024), 0, st, part, L.aux_blocks,
              counts_all, c.T, c.E, c.K, alpha, zlam, losses);
+  return MOE_OK;
+}
+
+}  // namespace moe
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// Load-driven selection-bias step ([P5] course notes 8.6): experts select on
+// s_e + b_e; an expert with more slots than the mean load T*K/E lowers b_e by
+// gamma, one with fewer raises it, one exactly at the mean keeps it.  The
+// comparison is exact in integers (counts_e * E vs T * K).
+// ---------------------------------------------------------------------------
+__global__ void bias_update_kernel(const int32_t* __restrict__ counts, int E, int64_t tk,
+                                   float gamma, float* __restrict__ b) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= E) return;
+  const int64_t load = (int64_t)counts[e] * E;
+  if (load > tk) b[e] = b[e] - gamma;
+  else if (load < tk) b[e] = b[e] + gamma;
+}
+
+int launch_bias_update(const moe_config& c, const int32_t* counts, float gamma, float* b,
+                       hipStream_t st) {
+  MOE_LAUNCH("bias_update", bias_update_kernel, dim3((unsigned)cdiv(c.E, 256)), dim3(256), 0,
+             st, counts, c.E, (int64_t)c.T * c.K, gamma, b);
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Sequence-wise balance loss ([P5] 8.5 balance loss applied per sequence of S
+// consecutive tokens, averaged over the T/S sequences; 8.6 keeps such a term
+// beside the bias rule):
+//   f_{b,e} = n_{b,e} / (S K),  P_{b,e} = mean_{t in b} p_{t,e}
+//   L = alpha E (S/T) sum_b sum_e f_{b,e} P_{b,e}
+//   dL/ds_{t,i} = w_{t,i} (u_{b,i} - sum_e p_{t,e} u_{b,e}),
+//   u_{b,e} = alpha E (S/T) f_{b,e} / S
+// p = softmax(s) (w = p) or sigma(s_e) / sum_j sigma(s_j)
+// (w = sigma_i (1 - sigma_i) / sum_j sigma_j).
+// Three passes over blocks of tokens and sequences (below); no global
+// atomics, every sum in a fixed order, so the result does not depend on
+// scheduling.
+// ---------------------------------------------------------------------------
+struct TokProb {
+  float m, z;  // softmax: max and normaliser; sigmoid: z = sum_j sigma_j
+};
+
+__device__ __forceinline__ TokProb tok_norm(const float* s, int E, int lane, int score) {
+  TokProb r;
+  if (score == MOE_SCORE_SOFTMAX) {
+    float m = -INFINITY;
+    for (int e = lane; e < E; e += 64) m = fmaxf(m, s[e]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    float z = 0.f;
+    for (int e = lane; e < E; e += 64) z += expf(s[e] - m);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) z += __shfl_xor(z, o, 64);
+    r.m = m;
+    r.z = z;
+  } else {
+    float z = 0.f;
+    for (int e = lane; e < E; e += 64) z += 1.0f / (1.0f + expf(-s[e]));
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) z += __shfl_xor(z, o, 64);
+    r.m = 0.f;
+    r.z = z;
+  }
+  return r;
+}
+
+__device__ __forceinline__ void tok_prob(float s, const TokProb& n, int score, float& p, float& w) {
+  if (score == MOE_SCORE_SOFTMAX) {
+    p = expf(s - n.m) / n.z;
+    w = p;
+  } else {
+    const float sg = 1.0f / (1.0f + expf(-s));
+    p = sg / n.z;
+    w = sg * (1.0f - sg) / n.z;
+  }
+}
+
+// Pass 1, one workgroup per block of TB tokens (TB divides S, so a block
+// never straddles two sequences): the block's expert histogram (integer LDS
+// atomics, order-free) and its probability sums (each of the four waves takes
+// every fourth token of the block, lanes own experts, the four wave rows are
+// added in wave order) -> pN[blk][E], pP[blk][E].
+__global__ __launch_bounds__(256) void seq_aux_blocks_kernel(const float* __restrict__ logits,
+                                                             const int32_t* __restrict__ idx,
+                                                             int E, int K, int TB, int score,
+                                                             int32_t* __restrict__ pN,
+                                                             float* __restrict__ pP) {
+  extern __shared__ float sh[];
+  int32_t* cnt = reinterpret_cast<int32_t*>(sh);  // [E]
+  float* Pw = sh + E;                             // [4][E]
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int64_t t0 = (int64_t)blockIdx.x * TB;
+  for (int e = tid; e < E; e += 256) cnt[e] = 0;
+  for (int i = tid; i < 4 * E; i += 256) Pw[i] = 0.f;
+  __syncthreads();
+  for (int i = tid; i < TB * K; i += 256) atomicAdd(&cnt[idx[t0 * K + i]], 1);
+  for (int t = wave; t < TB; t += 4) {
+    const float* s = logits + (size_t)(t0 + t) * E;
+    const TokProb n = tok_norm(s, E, lane, score);
+    for (int e = lane; e < E; e += 64) {
+      float p, w;
+      tok_prob(s[e], n, score, p, w);
+      Pw[wave * E + e] += p;
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += 256) {
+    pN[(size_t)blockIdx.x * E + e] = cnt[e];
+    pP[(size_t)blockIdx.x * E + e] = ((Pw[e] + Pw[E + e]) + Pw[2 * E + e]) + Pw[3 * E + e];
+  }
+}
+
+// Pass 2, one workgroup per sequence: sums its S/TB blocks in block order,
+// writes u_{b,e} = alpha E / T * n_{b,e} / (S K) over the sequence's first
+// block row of pP, and the sequence's sum_e f_e P_e.
+__global__ __launch_bounds__(256) void seq_aux_seqs_kernel(const int32_t* __restrict__ pN,
+                                                           float* __restrict__ pP, int T_, int E,
+                                                           int K, int S, int TB, float alpha,
+                                                           float* __restrict__ part) {
+  __shared__ float red[4];
+  const int b = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int nb = S / TB;
+  const size_t r0 = (size_t)b * nb;
+  const float inv_sk = 1.0f / ((float)S * (float)K);
+  float acc = 0.f;
+  for (int e = tid; e < E; e += 256) {
+    int n = 0;
+    float P = 0.f;
+    for (int j = 0; j < nb; ++j) {
+      n += pN[(r0 + j) * E + e];
+      P += pP[(r0 + j) * E + e];
+    }
+    const float f = (float)n * inv_sk;
+    acc += f * (P / (float)S);
+    pP[r0 * E + e] = alpha * (float)E / (float)T_ * f;  // u (after every read of row r0)
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
+  if (lane == 0) red[wave] = acc;
+  __syncthreads();
+  if (tid == 0) part[b] = ((red[0] + red[1]) + red[2]) + red[3];
+}
+
+// Pass 3, one workgroup per block of TB tokens, one wave per token: the
+// logit gradient w (u_b - sum_e p u_b), written or added.
+__global__ __launch_bounds__(256) void seq_aux_grad_kernel(const float* __restrict__ logits,
+                                                           const float* __restrict__ pP, int E,
+                                                           int S, int TB, int score,
+                                                           float* __restrict__ dlog,
+                                                           int accumulate) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int64_t t0 = (int64_t)blockIdx.x * TB;
+  const int64_t seq = t0 / S;
+  const float* u = pP + (size_t)(seq * (S / TB)) * E;
+  for (int t = wave; t < TB; t += 4) {
+    const float* s = logits + (size_t)(t0 + t) * E;
+    const TokProb n = tok_norm(s, E, lane, score);
+    float pu = 0.f;
+    for (int e = lane; e < E; e += 64) {
+      float p, w;
+      tok_prob(s[e], n, score, p, w);
+      pu += p * u[e];
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) pu += __shfl_xor(pu, o, 64);
+    float* d = dlog + (size_t)(t0 + t) * E;
+    for (int e = lane; e < E; e += 64) {
+      float p, w;
+      tok_prob(s[e], n, score, p, w);
+      const float g = w * (u[e] - pu);
+      d[e] = accumulate ? d[e] + g : g;
+    }
+  }
+}
+
+// loss = alpha E (S/T) sum_b part[b]; 1024 threads, thread i sums b = i,
+// i + 1024, ... then a fixed tree
+__global__ __launch_bounds__(1024) void seq_aux_final_kernel(const float* __restrict__ part,
+                                                             int nseq, float coef,
+                                                             float* __restrict__ loss) {
+  __shared__ float red[1024];
+  const int tid = threadIdx.x;
+  float v = 0.f;
+  for (int b = tid; b < nseq; b += 1024) v += part[b];
+  red[tid] = v;
+  __syncthreads();
+  for (int o = 512; o >= 1; o >>= 1) {
+    if (tid < o) red[tid] += red[tid + o];
+    __syncthreads();
+  }
+  if (tid == 0) *loss = coef * red[0];
+}
+
+int launch_seq_aux(const moe_config& c, const float* logits, const int32_t* idx, int S,
+                   float alpha, float* loss, float* dlog, bool accumulate, char* ws,
+                   const Workspace& L, hipStream_t st) {
+  // token blocks of TB | S tokens: the largest divisor of S up to 16
+  int TB = 1;
+  for (int d = std::min(S, 16); d >= 1; --d)
+    if (S % d == 0) { TB = d; break; }
+  const int nblk = c.T / TB, nseq = c.T / S;
+  int32_t* pN = reinterpret_cast<int32_t*>(ws + L.seq_blk_n);
+  float* pP = reinterpret_cast<float*>(ws + L.seq_blk_p);
+  float* part = reinterpret_cast<float*>(ws + L.seq_part);
+  const size_t shm = (size_t)5 * c.E * 4;
+  MOE_LAUNCH("seq_aux", seq_aux_blocks_kernel, dim3(nblk), dim3(256), shm, st, logits, idx, c.E,
+             c.K, TB, c.score_fn, pN, pP);
+  MOE_LAUNCH("seq_aux_seqs", seq_aux_seqs_kernel, dim3(nseq), dim3(256), 0, st, pN, pP, c.T, c.E,
+             c.K, S, TB, alpha, part);
+  if (dlog)
+    MOE_LAUNCH("seq_aux_grad", seq_aux_grad_kernel, dim3(nblk), dim3(256), 0, st, logits, pP,
+               c.E, S, TB, c.score_fn, dlog, accumulate ? 1 : 0);
+  const float coef = alpha * (float)c.E * ((float)S / (float)c.T);
+  MOE_LAUNCH("seq_aux_final", seq_aux_final_kernel, dim3(1), dim3(1024), 0, st, part, nseq, coef,
+             loss);
   return MOE_OK;
 }
 

@@ -17,6 +17,8 @@ struct Workspace {
   size_t dxr;                      // float [T][D] (router dgrad, large E)
   size_t dwr_part;                 // float [splits][E][D] (+ [splits][E] bias)
   size_t rb_part;                  // float [rb_splits][E rounded to 4] (large E)
+  size_t seq_part;                 // float [T] per-sequence balance-loss partials
+  size_t seq_blk_n, seq_blk_p;     // int32 / float [T][E] per-token-block partials
   size_t total;
   int ntiles, aux_blocks, dwr_splits, rb_splits;
 };
@@ -51,6 +53,12 @@ int launch_combine(const moe_config& c, const void* o_perm, const int32_t* offse
 int launch_aux(const moe_config& c, const float* logits, const int32_t* counts_all, float alpha,
                float zlam, float* losses, float* d_logits, char* ws, const Workspace& L,
                hipStream_t st);
+
+int launch_bias_update(const moe_config& c, const int32_t* counts, float gamma, float* b,
+                       hipStream_t st);
+int launch_seq_aux(const moe_config& c, const float* logits, const int32_t* idx, int S,
+                   float alpha, float* loss, float* dlog, bool accumulate, char* ws,
+                   const Workspace& L, hipStream_t st);
 
 int launch_backward(const moe_config& c, const void* x, const float* wr, const float* logits,
                     const int32_t* idx, const float* topk_w, const int32_t* offsets,

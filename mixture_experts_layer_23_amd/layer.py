@@ -30,6 +30,9 @@ class LayerSpec:
     cap: float = 0.0
     alpha: float = 0.0
     zlam: float = 0.0
+    seq_len: int = 0          # sequence-wise balance loss over sequences of this length (0: off)
+    seq_alpha: float = 0.0
+    bias_gamma: float = 0.0   # load-driven selection-bias step after each routing (0: off)
 
     def config(self) -> L.MoeConfig:
         return L.make_config(self.T, self.D, self.E, self.K, self.F, self.lo,
@@ -81,6 +84,7 @@ class MoELayer:
         self.o_perm = z(rows, s.D, dt=tdt)
         self.y = z(T1, s.D, dt=tdt)
         self.losses = z(4, dt=f32)
+        self.seq_loss = z(4, dt=f32)
         self.dlogits_aux = z(T1, s.E, dt=f32)
         self.ws = torch.empty(max(L.workspace_size(self.cfg), 256), dtype=torch.uint8,
                               device=self.dev)
@@ -97,6 +101,14 @@ class MoELayer:
     def use_aux(self) -> bool:
         return self.spec.score == L.MOE_SCORE_SOFTMAX and (self.spec.alpha != 0 or self.spec.zlam != 0)
 
+    @property
+    def use_seq(self) -> bool:
+        return self.spec.seq_len > 0 and self.spec.seq_alpha != 0
+
+    @property
+    def has_dlogits(self) -> bool:
+        return self.use_aux or self.use_seq
+
     def route(self, x, logits_given: bool = False):
         L.moe_route(self.cfg, x, self.w_r, self.r_bias, self.sel_bias, self.logits, self.topk_idx,
                     self.topk_w, self.lse, L.MOE_ROUTE_LOGITS_GIVEN if logits_given else 0)
@@ -112,10 +124,16 @@ class MoELayer:
         if self.use_aux:
             L.aux_balance_loss(self.cfg, self.logits, self.counts, self.spec.alpha,
                                self.spec.zlam, self.losses, self.dlogits_aux, self.ws)
+        if self.use_seq:
+            L.aux_seq_loss(self.cfg, self.logits, self.topk_idx, self.spec.seq_len,
+                           self.spec.seq_alpha, self.seq_loss, self.dlogits_aux,
+                           self.use_aux, self.ws)
+        if self.spec.bias_gamma != 0 and self.sel_bias is not None:
+            L.moe_bias_update(self.cfg, self.counts, self.spec.bias_gamma, self.sel_bias)
         return self.y
 
     def backward(self, dy, with_aux: bool | None = None):
-        use = self.use_aux if with_aux is None else with_aux
+        use = self.has_dlogits if with_aux is None else with_aux
         L.moe_backward(self.cfg, self.x, self.w_r, self.logits, self.topk_idx, self.topk_w,
                        self.offsets, self.slot_row, self.x_perm, self.act, self.h, self.o_perm,
                        self.w_gate, self.w_up, self.w_down, dy,
