@@ -616,6 +616,8 @@ int orc_seq_aux(const orc_cfg* c, const double* logits, const int* idx, int S, d
  * With K = 1 and B, g = 1 exactly so ds = 1 * (dg - dg) = 0 exactly
  * ([P2] section 2, [P5] 8.3).  The selection bias b_e gets no gradient.
  * Router backward: dx_t += ds_t W_r;  dW_r += ds_t^T x_t;  d r_b += ds_t.
+ * With router-logit jitter s~ = s * u ([P3] ST-MoE), ds (taken w.r.t. s~)
+ * is multiplied by u first; ds is then returned w.r.t. the raw logits.
  *
  * bug_mode (negative control for [P1]): a sentinel slot is computed by local
  * expert 0 and only its forward weight is zero; the backward takes
@@ -670,6 +672,7 @@ void orc_gate_grad(const orc_cfg* c, const double* logits, const int* idx, const
 typedef struct {
   ffn_w W; const double* lg; const double* wr; const int* idx; const double* gw;
   const int* slot_row; const int* tok; int ntok; const double* dy; const double* dlx;
+  const float* jit;   /* router-logit jitter u [T][E] (NULL: none) */
   double* dx; double* ds;
   /* per-(token,slot) intermediates for the weight-gradient pass */
   double* r_da; double* r_db; double* r_h; double* r_do;   /* [ntok*K(+S)][F or D] */
@@ -749,6 +752,9 @@ static void bw_tok(void* p, long i) {
   gate_bwd(c, a->lg + (size_t)t * E, a->idx + (size_t)t * K, a->gw + (size_t)t * K, dg, ds);
   if (a->dlx)
     for (int e = 0; e < E; ++e) ds[e] += a->dlx[(size_t)t * E + e];
+  /* jittered logits s~ = s * u ([P3] ST-MoE): back to the raw logits */
+  if (a->jit)
+    for (int e = 0; e < E; ++e) ds[e] *= (double)a->jit[(size_t)t * E + e];
   for (int d = 0; d < D; ++d) {
     double acc = 0.0;
     for (int e = 0; e < E; ++e) acc += ds[e] * a->wr[(size_t)e * D + d];
@@ -831,7 +837,7 @@ void orc_backward(const orc_cfg* c, const void* x, int xdt, const double* wr, co
                   const void* wu, const void* wd, int wdt, const double* logits, const int* idx,
                   const double* gw, const int* slot_row, const int* tok, int ntok, const double* dy,
                   const double* dlx, const int* fsel, int nf, double* dx, double* ds, double* dwr,
-                  double* drb, double* dwg, double* dwu, double* dwd) {
+                  double* drb, double* dwg, double* dwu, double* dwd, const float* jit) {
   const int D = c->D, F = c->F, K = c->K, S = c->n_shared;
   const int G = (c->hi - c->lo) + S;
   const size_t nrow = (size_t)ntok * (K + S);
@@ -839,7 +845,7 @@ void orc_backward(const orc_cfg* c, const void* x, int xdt, const double* wr, co
   memset(&b, 0, sizeof b);
   b.W.c = c; b.W.x = x; b.W.xdt = xdt; b.W.wg = wg; b.W.wu = wu; b.W.wd = wd; b.W.wdt = wdt;
   b.lg = logits; b.wr = wr; b.idx = idx; b.gw = gw; b.slot_row = slot_row; b.tok = tok;
-  b.ntok = ntok; b.dy = dy; b.dlx = dlx; b.dx = dx; b.ds = ds;
+  b.ntok = ntok; b.dy = dy; b.dlx = dlx; b.dx = dx; b.ds = ds; b.jit = jit;
   b.r_da = (double*)malloc(sizeof(double) * nrow * F);
   b.r_db = (double*)malloc(sizeof(double) * nrow * F);
   b.r_h = (double*)malloc(sizeof(double) * nrow * F);

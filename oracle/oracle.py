@@ -104,7 +104,7 @@ def lib():
         L.orc_seq_aux.argtypes = [P, P, P, C.c_int, C.c_double, P, P]
         L.orc_seq_aux.restype = C.c_int
         L.orc_backward.argtypes = [P, P, C.c_int, P, P, P, P, C.c_int, P, P, P, P, P, C.c_int,
-                                   P, P, P, C.c_int, P, P, P, P, P, P, P]
+                                   P, P, P, C.c_int, P, P, P, P, P, P, P, P]
         _lib = L
     return _lib
 
@@ -241,6 +241,43 @@ def bias_update(cfg: Cfg, counts_all, gamma: float, selb) -> np.ndarray:
     return b
 
 
+def route_noisy(cfg: Cfg, lg, jit=None, eps=None, nlg=None, selb=None, exact: bool = False):
+    """Noisy top-K selection and router-logit jitter.
+
+    [P3] ST-MoE: the router logits are multiplied by random factors u in
+    [0.99, 1.01]:  s~ = s * u  (one binary32 multiply; in double when exact).
+    [P3] KeepTopK / [P5] 8.6: the selection key adds input-dependent noise,
+    H_e = s~_e + eps_e * softplus(n_e),  n = x W_noise,  eps ~ N(0, 1) per
+    token and expert; evaluated in double and rounded once to binary32 (like
+    the logits), then the usual top-K rounds (lowest index on ties).  [P3]
+    states that the weights still come from the selected experts' noise-free
+    logits (the noise only selects): weights, lse and probabilities are taken
+    on s~ with the selected indices.  Noise is for softmax scoring only.
+    Returns (idx, w, lse, probs, s~)."""
+    s = np.asarray(lg, dtype=np.float64)
+    if jit is not None:
+        u = np.asarray(jit, dtype=np.float64)
+        st = s * u if exact else (s.astype(np.float32) * u.astype(np.float32)).astype(np.float64)
+    else:
+        st = s
+    if eps is None:
+        idx, w, lse, probs = route(cfg, st, selb)
+        return idx, w, lse, probs, st
+    assert cfg.score == SOFTMAX, "noisy top-K is defined for softmax scoring"
+    key = st + np.asarray(eps, np.float64) * np.logaddexp(0.0, np.asarray(nlg, np.float64))
+    if not exact:
+        key = key.astype(np.float32).astype(np.float64)
+    idx = route(cfg, key)[0]
+    m = st.max(1, keepdims=True)
+    ex = np.exp(st - m)
+    z = ex.sum(1, keepdims=True)
+    probs = ex / z
+    lse = (m + np.log(z))[:, 0]
+    sel = np.take_along_axis(ex, idx.astype(np.int64), 1)
+    w = sel / z if cfg.gating == 0 else sel / sel.sum(1, keepdims=True)
+    return idx, w, lse, probs, st
+
+
 def seq_aux(cfg: Cfg, lg, idx, seq_len: int, alpha: float, want_grad: bool = True):
     """Sequence-wise balance loss over sequences of seq_len tokens and its
     logit gradient [T,E] (f held constant)."""
@@ -269,7 +306,7 @@ def gate_grad(cfg: Cfg, lg, idx, w, dg) -> np.ndarray:
 
 
 def backward(cfg: Cfg, x, wr, wg, wu, wd, lg, idx, w, slot_row, dy, tok=None, dlx=None,
-             fsel=None, want_wgrad=True, want_rgrad=True):
+             fsel=None, want_wgrad=True, want_rgrad=True, jit=None):
     """O9-O12.  dy rows belong to the listed tokens (all when tok is None);
     every other token has dy = 0.  Returns dx and ds for the listed tokens,
     dW_r, d r_b and the expert weight gradients on the F-columns fsel."""
@@ -284,6 +321,7 @@ def backward(cfg: Cfg, x, wr, wg, wu, wd, lg, idx, w, slot_row, dy, tok=None, dl
     dy = np.ascontiguousarray(dy, dtype=np.float64)
     assert dy.shape == (len(tk), cfg.D)
     dlx = None if dlx is None else np.ascontiguousarray(dlx, dtype=np.float64)
+    jt = None if jit is None else np.ascontiguousarray(jit, dtype=np.float32)
     fs = None if fsel is None else np.ascontiguousarray(fsel, dtype=np.int32)
     nf = cfg.F if fs is None else len(fs)
     G = cfg.groups
@@ -297,7 +335,7 @@ def backward(cfg: Cfg, x, wr, wg, wu, wd, lg, idx, w, slot_row, dy, tok=None, dl
     lib().orc_backward(C.byref(c), _p(x), _DT[x.dtype], _p(wr), _p(wg), _p(wu), _p(wd),
                        _DT[wg.dtype], _p(lg), _p(idx), _p(w), _p(slot_row), _p(tk), len(tk),
                        _p(dy), _p(dlx), _p(fs), nf, _p(dx), _p(ds), _p(dwr), _p(drb),
-                       _p(dwg), _p(dwu), _p(dwd))
+                       _p(dwg), _p(dwu), _p(dwd), _p(jt))
     return dict(dx=dx, ds=ds, dwr=dwr, drb=drb, dwg=dwg, dwu=dwu, dwd=dwd)
 
 

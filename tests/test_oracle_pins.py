@@ -658,3 +658,103 @@ def test_bias_update_rule(orc):
     cfg2 = orc.Cfg(T=1000, D=1, E=3, K=1, F=8)
     b2 = orc.bias_update(cfg2, [334, 333, 333], 0.5, [0.0, 0.0, 0.0])
     np.testing.assert_array_equal(b2, np.array([-0.5, 0.5, 0.5], np.float32))
+
+
+# ---------------------------------------------------------------------------
+# noisy top-K selection and router-logit jitter (next row 2)
+# ---------------------------------------------------------------------------
+def test_noisy_topk_worked_example(orc):
+    g = gold("noisy_topk_example.json")["noise"]
+    s = np.array([g["s"]])
+    eps, n = np.array([g["eps"]]), np.array([g["n"]])
+    for K, gating in [(1, 0), (1, 1), (2, 1)]:
+        cfg = orc.Cfg(T=1, D=1, E=4, K=K, F=8, gating=gating)
+        idx, w, _, _, _ = orc.route_noisy(cfg, s, eps=eps, nlg=n)
+        np.testing.assert_array_equal(idx[0], g[f"K{K}"]["idx"])
+        if K == 1 and gating == 0:
+            want = np.exp(1.9) / (np.exp(2.0) + np.exp(1.9) + 2.0)
+            assert abs(w[0, 0] - want) < 1e-15
+        elif K == 1:
+            assert w[0, 0] == 1.0
+        else:
+            np.testing.assert_allclose(w[0], np.array([np.exp(1.9), np.exp(2.0)]) /
+                                       (np.exp(1.9) + np.exp(2.0)), rtol=1e-15)
+    cfg = orc.Cfg(T=1, D=1, E=4, K=1, F=8)
+    assert orc.route(cfg, s)[0][0, 0] == g["without_noise_K1_idx"][0]
+
+
+def test_jitter_worked_example(orc):
+    g = gold("noisy_topk_example.json")["jitter"]
+    s, u = np.array([g["s"]]), np.array([g["u"]])
+    cfg = orc.Cfg(T=1, D=1, E=2, K=1, F=8, gating=0)
+    idx, w, _, _, st = orc.route_noisy(cfg, s, jit=u, exact=True)
+    assert idx[0, 0] == g["K1"]["idx"][0]
+    np.testing.assert_allclose(st[0], g["s_jittered"], rtol=1e-15)
+    assert abs(w[0, 0] - np.exp(1.01) / (np.exp(1.01) + np.exp(1.005))) < 1e-15
+    assert orc.route(cfg, s)[0][0, 0] == g["without_jitter_K1_idx"][0]
+
+
+def test_noise_and_jitter_reduce_to_plain_routing(orc):
+    """eps = 0 and u = 1 give exactly the plain routing (special case)."""
+    rng = np.random.default_rng(21)
+    T, E, K = 40, 16, 4
+    for gating in (0, 1):
+        cfg = orc.Cfg(T=T, D=1, E=E, K=K, F=8, gating=gating)
+        lg = rng.normal(size=(T, E)).astype(np.float32).astype(np.float64)
+        a = orc.route(cfg, lg)
+        b = orc.route_noisy(cfg, lg, jit=np.ones((T, E)), eps=np.zeros((T, E)),
+                            nlg=rng.normal(size=(T, E)))
+        np.testing.assert_array_equal(a[0], b[0])
+        np.testing.assert_allclose(b[1], a[1], rtol=1e-14)
+        np.testing.assert_allclose(b[2], a[2], rtol=1e-14)
+
+
+def test_noise_only_selects(orc):
+    """With noise the weights are the noise-free gate weights of the chosen
+    set: gating B on s~ restricted to idx, summing to 1."""
+    rng = np.random.default_rng(22)
+    T, E, K = 50, 8, 3
+    cfg = orc.Cfg(T=T, D=1, E=E, K=K, F=8, gating=1)
+    lg = rng.normal(size=(T, E)).astype(np.float32).astype(np.float64)
+    eps, n = rng.normal(size=(T, E)), rng.normal(size=(T, E))
+    idx, w, _, probs, _ = orc.route_noisy(cfg, lg, eps=eps, nlg=n)
+    sel = np.take_along_axis(probs, idx.astype(np.int64), 1)
+    np.testing.assert_allclose(w, sel / sel.sum(1, keepdims=True), rtol=1e-13)
+    plain = orc.route(cfg, lg)[0]
+    assert np.any(np.sort(idx, 1) != np.sort(plain, 1))  # the noise changed some choices
+
+
+@pytest.mark.parametrize("gating", [0, 1])
+def test_jitter_noise_torch_autograd_tiny(orc, gating):
+    """Router gradients with jitter (and the noisy selection held fixed)
+    against torch autograd of s~ = (x W_r^T) * u on tiny fp64 inputs."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(23)
+    T, D, E, K, F = 10, 6, 6, 3, 5
+    x, wr, wg, wu, wd, dy = tiny_inputs(rng, T, D, E, F, E)
+    cfg = orc.Cfg(T=T, D=D, E=E, K=K, F=F, gating=gating)
+    u = rng.uniform(0.99, 1.01, size=(T, E)).astype(np.float32).astype(np.float64)
+    eps = rng.normal(size=(T, E))
+    lg = orc.logits(cfg, x, wr, exact=True)
+    nlg = rng.normal(size=(T, E))
+    idx, w, _, _, st = orc.route_noisy(cfg, lg, jit=u, eps=eps, nlg=nlg, exact=True)
+    d = orc.dispatch(cfg, idx)
+    y = orc.forward(cfg, x, wg, wu, wd, idx, w, d["slot_row"])
+    bw = orc.backward(cfg, x, wr, wg, wu, wd, st, idx, w, d["slot_row"], dy,
+                      jit=u.astype(np.float32))
+    tx, twr = torch.tensor(x, requires_grad=True), torch.tensor(wr, requires_grad=True)
+    s = (tx @ twr.T) * torch.tensor(u.astype(np.float32).astype(np.float64))
+    tidx = torch.from_numpy(idx.astype(np.int64))
+    p = torch.softmax(s, -1)
+    sel = torch.gather(p, 1, tidx)
+    gw = sel if gating == 0 else sel / sel.sum(1, keepdim=True)
+    ty = torch.zeros(T, D, dtype=torch.float64)
+    for t in range(T):
+        for k in range(K):
+            e = int(tidx[t, k])
+            a, b = tx[t] @ torch.tensor(wg[e]), tx[t] @ torch.tensor(wu[e])
+            ty[t] = ty[t] + gw[t, k] * ((torch.nn.functional.silu(a) * b) @ torch.tensor(wd[e]))
+    (ty * torch.from_numpy(dy)).sum().backward()
+    np.testing.assert_allclose(y, ty.detach().numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(bw["dwr"], twr.grad.numpy(), rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(bw["dx"], tx.grad.numpy(), rtol=1e-9, atol=1e-12)
