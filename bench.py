@@ -48,6 +48,10 @@ def parse():
     ap.add_argument("--seq-alpha", type=float, default=1e-3)
     ap.add_argument("--bias-gamma", type=float, default=0.0,
                     help="add the load-driven selection-bias step (sigmoid routing)")
+    ap.add_argument("--jitter", action="store_true",
+                    help="multiply the router logits by per-step U[0.99, 1.01] draws")
+    ap.add_argument("--noise", action="store_true",
+                    help="noisy top-K selection (noise router + per-step N(0,1) draws)")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step replayed as one HIP graph (reported as ms_per_step_graph)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=None)
@@ -162,12 +166,16 @@ def main():
     spec = LayerSpec.from_workload(wl, seq_len=args.seq_len,
                                    seq_alpha=args.seq_alpha if args.seq_len else 0.0,
                                    bias_gamma=args.bias_gamma)
-    layer = MoELayer(spec, inp["wr"], inp["wg"], inp["wu"], inp["wd"], inp["rb"], inp["selb"])
+    u = eps = wn = None
+    if args.jitter or args.noise:
+        u, eps, wn = S.routing_noise(wl, device="cuda")
+    layer = MoELayer(spec, inp["wr"], inp["wg"], inp["wu"], inp["wd"], inp["rb"], inp["selb"],
+                     w_noise=wn if args.noise else None)
     x, dy = inp["x"], inp["dy"]
     torch.cuda.synchronize()
 
     def step():
-        layer.forward(x)
+        layer.forward(x, jitter=u if args.jitter else None, noise_eps=eps if args.noise else None)
         layer.backward(dy)
 
     def timed(fn, live=None):
@@ -292,7 +300,8 @@ def main():
                    "tokens": wl.T, "local_rows": n_rows_local,
                    "shared_rows": wl.n_shared * wl.T, "dropped": n_dropped,
                    "expert_load": counts.tolist() if wl.E <= 16 else None,
-                   "seq_len": args.seq_len or None, "bias_gamma": args.bias_gamma or None},
+                   "seq_len": args.seq_len or None, "bias_gamma": args.bias_gamma or None,
+                   "jitter": args.jitter or None, "noise": args.noise or None},
         "grouped_gemm": {"tflops": gemm_flops / (gemm_ms * 1e-3) / 1e12 if gemm_ms else None,
                          "frac_of_peak": (gemm_flops / (gemm_ms * 1e-3) / 1e12 / peak_t)
                          if gemm_ms else None,

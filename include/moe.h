@@ -220,6 +220,44 @@ int moe_backward(const moe_config* cfg, const void* x, const float* w_r, const f
                  void* ws, size_t ws_bytes, moe_stream_t stream);
 
 /*
+ * Routing with router-logit jitter and noisy top-K selection ("MoE" tutorial
+ * chapter, sections ST-MoE and KeepTopK; course notes section 8.6).
+ *   jitter: fp32 [T][E] factors u (the tutorial draws them from
+ *     [0.99, 1.01]) or NULL; s~ = s * u (one binary32 multiply) is written to
+ *     `logits` and replaces the logits everywhere downstream (selection,
+ *     weights, lse, losses, backward).  With MOE_ROUTE_LOGITS_GIVEN the
+ *     given logits are jittered in place.
+ *   w_noise: fp32 [E][D] or NULL.  With it, n = x W_noise^T (binary32 from a
+ *     double sum) is written to noise_logits [T][E] and the selection key is
+ *     fl32(s~ + eps * softplus(n)), evaluated in double, with eps =
+ *     noise_eps [T][E] (standard-normal draws, one per token and expert);
+ *     the gate weights and lse stay on s~: the noise only selects.  Noise
+ *     requires softmax scoring (MOE_EINVAL otherwise).
+ * The random draws are inputs: the library draws nothing.  Every other
+ * argument is as in moe_route, which is this call with no jitter or noise.
+ */
+int moe_route_ex(const moe_config* cfg, const void* x, const float* w_r, const float* r_bias,
+                 const float* sel_bias, const float* jitter, const float* w_noise,
+                 const float* noise_eps, float* noise_logits, float* logits, int32_t* topk_idx,
+                 float* topk_w, float* lse, int32_t flags, moe_stream_t stream);
+
+/*
+ * moe_backward with router-logit jitter: `logits` are the jittered s~ that
+ * moe_route_ex wrote and `jitter` the same u ([T][E] fp32, or NULL: this is
+ * moe_backward).  The gating gradient w.r.t. s~ (plus d_logits_extra, which
+ * is taken w.r.t. s~ as well) is multiplied by u, so dx, dw_r, d_rbias and
+ * d_logits_out are gradients w.r.t. the raw logits s = x W_r^T + r_b.  The
+ * noise logits get no gradient: the noise only selects.
+ */
+int moe_backward_ex(const moe_config* cfg, const void* x, const float* w_r, const float* logits,
+                    const int32_t* topk_idx, const float* topk_w, const int32_t* offsets,
+                    const int32_t* slot_row, const void* x_perm, const void* act, const void* h,
+                    const void* o_perm, const void* w_gate, const void* w_up, const void* w_down,
+                    const void* dy, const float* d_logits_extra, const float* jitter, void* dx,
+                    float* dw_r, float* d_rbias, void* dw_gate, void* dw_up, void* dw_down,
+                    float* d_logits_out, void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/*
  * Load-driven selection-bias step ("Course notes 08 MoE", section 8.6: the
  * experts select on s_e + b_e; an overloaded expert lowers b_e, an
  * underloaded one raises it, by a fixed step; the gate weights keep using the

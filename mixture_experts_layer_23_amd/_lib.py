@@ -22,7 +22,8 @@ MOE_ROUTE_LOGITS_GIVEN = 1
 EXPORTS = ["moe_capacity", "moe_rows_max", "moe_workspace_size", "moe_route", "moe_permute",
            "moe_expert_ffn", "moe_combine", "aux_balance_loss", "moe_backward",
            "moe_error_string", "moe_timing_enable", "moe_timing_report",
-           "moe_timing_select", "moe_bias_update", "aux_seq_loss"]
+           "moe_timing_select", "moe_bias_update", "aux_seq_loss", "moe_route_ex",
+           "moe_backward_ex"]
 
 
 class MoeConfig(C.Structure):
@@ -66,6 +67,8 @@ def lib():
             "moe_timing_report": [C.c_char_p, S],
             "moe_timing_select": [C.c_char_p],
             "moe_bias_update": [cfg, P, C.c_float, P, P],
+            "moe_route_ex": [cfg, P, P, P, P, P, P, P, P, P, P, P, P, I, P],
+            "moe_backward_ex": [cfg] + [P] * 25 + [S, P],
             "aux_seq_loss": [cfg, P, P, I, C.c_float, P, P, I, P, S, P],
         }
         for name, args in sig.items():
@@ -176,6 +179,26 @@ def moe_backward(cfg, x, w_r, logits, topk_idx, topk_w, offsets, slot_row, x_per
 
 def timing_enable(on: bool) -> None:
     _check("moe_timing_enable", lib().moe_timing_enable(1 if on else 0))
+
+
+def moe_route_ex(cfg, x, w_r, r_bias, sel_bias, jitter, w_noise, noise_eps, noise_logits, logits,
+                 topk_idx, topk_w, lse, flags=0, stream=None):
+    _check("moe_route_ex",
+           lib().moe_route_ex(C.byref(cfg), ptr(x), ptr(w_r), ptr(r_bias), ptr(sel_bias),
+                              ptr(jitter), ptr(w_noise), ptr(noise_eps), ptr(noise_logits),
+                              ptr(logits), ptr(topk_idx), ptr(topk_w), ptr(lse), int(flags),
+                              stream_handle(stream)))
+
+
+def moe_backward_ex(cfg, x, w_r, logits, topk_idx, topk_w, offsets, slot_row, x_perm, act, h,
+                    o_perm, w_gate, w_up, w_down, dy, d_logits_extra, jitter, dx, dw_r, d_rbias,
+                    dw_gate, dw_up, dw_down, d_logits_out, ws, stream=None):
+    args = [x, w_r, logits, topk_idx, topk_w, offsets, slot_row, x_perm, act, h, o_perm, w_gate,
+            w_up, w_down, dy, d_logits_extra, jitter, dx, dw_r, d_rbias, dw_gate, dw_up, dw_down,
+            d_logits_out, ws]
+    _check("moe_backward_ex",
+           lib().moe_backward_ex(C.byref(cfg), *[ptr(a) for a in args],
+                                 ws.numel() * ws.element_size(), stream_handle(stream)))
 
 
 def moe_bias_update(cfg, counts_all, gamma, sel_bias, stream=None):

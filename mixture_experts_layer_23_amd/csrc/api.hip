@@ -173,19 +173,33 @@ int moe_workspace_size(const moe_config* cfg, size_t* bytes) {
   return MOE_OK;
 }
 
-int moe_route(const moe_config* cfg, const void* x, const float* w_r, const float* r_bias,
-              const float* sel_bias, float* logits, int32_t* topk_idx, float* topk_w, float* lse,
-              int32_t flags, moe_stream_t stream) {
+int moe_route_ex(const moe_config* cfg, const void* x, const float* w_r, const float* r_bias,
+                 const float* sel_bias, const float* jitter, const float* w_noise,
+                 const float* noise_eps, float* noise_logits, float* logits, int32_t* topk_idx,
+                 float* topk_w, float* lse, int32_t flags, moe_stream_t stream) {
   int rc = check_cfg(cfg);
   if (rc) return rc;
   if (flags & ~MOE_ROUTE_LOGITS_GIVEN) return MOE_EINVAL;
   const bool given = (flags & MOE_ROUTE_LOGITS_GIVEN) != 0;
   if (!given) { REQ(x); REQ(w_r); OPT(r_bias); }
-  OPT(sel_bias);
+  OPT(sel_bias); OPT(jitter);
+  if (w_noise) {
+    // noisy top-K is defined on softmax scores; it needs x, eps and the
+    // noise-logit output
+    if (cfg->score_fn != MOE_SCORE_SOFTMAX) return MOE_EINVAL;
+    REQ(x); REQ(w_noise); REQ(noise_eps); REQ(noise_logits);
+  }
   REQ(logits); REQ(topk_idx); REQ(topk_w); OPT(lse);
   if (cfg->T == 0) return MOE_OK;
-  return launch_route(*cfg, x, w_r, r_bias, sel_bias, logits, topk_idx, topk_w, lse, given,
-                      (hipStream_t)stream);
+  return launch_route(*cfg, x, w_r, r_bias, sel_bias, jitter, w_noise, noise_eps, noise_logits,
+                      logits, topk_idx, topk_w, lse, given, (hipStream_t)stream);
+}
+
+int moe_route(const moe_config* cfg, const void* x, const float* w_r, const float* r_bias,
+              const float* sel_bias, float* logits, int32_t* topk_idx, float* topk_w, float* lse,
+              int32_t flags, moe_stream_t stream) {
+  return moe_route_ex(cfg, x, w_r, r_bias, sel_bias, nullptr, nullptr, nullptr, nullptr, logits,
+                      topk_idx, topk_w, lse, flags, stream);
 }
 
 int moe_permute(const moe_config* cfg, const int32_t* topk_idx, const void* x,
@@ -264,18 +278,18 @@ int aux_seq_loss(const moe_config* cfg, const float* logits, const int32_t* topk
                         (char*)ws, L, (hipStream_t)stream);
 }
 
-int moe_backward(const moe_config* cfg, const void* x, const float* w_r, const float* logits,
-                 const int32_t* topk_idx, const float* topk_w, const int32_t* offsets,
-                 const int32_t* slot_row, const void* x_perm, const void* act, const void* h,
-                 const void* o_perm, const void* w_gate, const void* w_up, const void* w_down,
-                 const void* dy, const float* d_logits_extra, void* dx, float* dw_r,
-                 float* d_rbias, void* dw_gate, void* dw_up, void* dw_down, float* d_logits_out,
-                 void* ws, size_t ws_bytes, moe_stream_t stream) {
+int moe_backward_ex(const moe_config* cfg, const void* x, const float* w_r, const float* logits,
+                    const int32_t* topk_idx, const float* topk_w, const int32_t* offsets,
+                    const int32_t* slot_row, const void* x_perm, const void* act, const void* h,
+                    const void* o_perm, const void* w_gate, const void* w_up, const void* w_down,
+                    const void* dy, const float* d_logits_extra, const float* jitter, void* dx,
+                    float* dw_r, float* d_rbias, void* dw_gate, void* dw_up, void* dw_down,
+                    float* d_logits_out, void* ws, size_t ws_bytes, moe_stream_t stream) {
   int rc = check_cfg(cfg);
   if (rc) return rc;
   REQ(x); REQ(w_r); REQ(logits); REQ(topk_idx); REQ(topk_w); REQ(offsets); REQ(slot_row);
   REQ(x_perm); REQ(act); REQ(h); REQ(o_perm); REQ(dy);
-  OPT(d_logits_extra); REQ(dx); REQ(dw_r); OPT(d_rbias); OPT(d_logits_out); REQ(ws);
+  OPT(d_logits_extra); OPT(jitter); REQ(dx); REQ(dw_r); OPT(d_rbias); OPT(d_logits_out); REQ(ws);
   if (groups(*cfg) > 0) {
     REQ(w_gate); REQ(w_up); REQ(w_down); REQ(dw_gate); REQ(dw_up); REQ(dw_down);
   }
@@ -283,8 +297,21 @@ int moe_backward(const moe_config* cfg, const void* x, const float* w_r, const f
   if (ws_bytes < L.total) return MOE_EWORKSPACE;
   if (cfg->T == 0) return MOE_OK;
   return launch_backward(*cfg, x, w_r, logits, topk_idx, topk_w, offsets, slot_row, x_perm, act,
-                         h, o_perm, w_gate, w_up, w_down, dy, d_logits_extra, dx, dw_r, d_rbias,
-                         dw_gate, dw_up, dw_down, d_logits_out, (char*)ws, L, (hipStream_t)stream);
+                         h, o_perm, w_gate, w_up, w_down, dy, d_logits_extra, jitter, dx, dw_r,
+                         d_rbias, dw_gate, dw_up, dw_down, d_logits_out, (char*)ws, L,
+                         (hipStream_t)stream);
+}
+
+int moe_backward(const moe_config* cfg, const void* x, const float* w_r, const float* logits,
+                 const int32_t* topk_idx, const float* topk_w, const int32_t* offsets,
+                 const int32_t* slot_row, const void* x_perm, const void* act, const void* h,
+                 const void* o_perm, const void* w_gate, const void* w_up, const void* w_down,
+                 const void* dy, const float* d_logits_extra, void* dx, float* dw_r,
+                 float* d_rbias, void* dw_gate, void* dw_up, void* dw_down, float* d_logits_out,
+                 void* ws, size_t ws_bytes, moe_stream_t stream) {
+  return moe_backward_ex(cfg, x, w_r, logits, topk_idx, topk_w, offsets, slot_row, x_perm, act, h,
+                         o_perm, w_gate, w_up, w_down, dy, d_logits_extra, nullptr, dx, dw_r,
+                         d_rbias, dw_gate, dw_up, dw_down, d_logits_out, ws, ws_bytes, stream);
 }
 
 const char* moe_error_string(int code) {

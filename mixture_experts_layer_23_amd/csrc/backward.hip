@@ -32,8 +32,8 @@ template <int L, int EPL>
 __global__ __launch_bounds__(256) void gating_bwd_kernel(
     const float* __restrict__ logits, const int32_t* __restrict__ idx,
     const float* __restrict__ gw, const float* __restrict__ dg, const float* __restrict__ dlx,
-    int T_, int E, int K, int score, int gating, float* __restrict__ ds,
-    float* __restrict__ ds_copy) {
+    const float* __restrict__ jit, int T_, int E, int K, int score, int gating,
+    float* __restrict__ ds, float* __restrict__ ds_copy) {
   const int gid = blockIdx.x * blockDim.x + threadIdx.x;
   const int t = gid / L, sub = gid % L;
   if (t >= T_) return;
@@ -104,6 +104,8 @@ __global__ __launch_bounds__(256) void gating_bwd_kernel(
     if (e >= E) continue;
     float v = out[j];
     if (dlx) v += dlx[(size_t)t * E + e];
+    // jittered logits s~ = s u: the gradient w.r.t. the raw logits
+    if (jit) v *= jit[(size_t)t * E + e];
     ds[(size_t)t * E + e] = v;
     if (ds_copy) ds_copy[(size_t)t * E + e] = v;
   }
@@ -111,19 +113,19 @@ __global__ __launch_bounds__(256) void gating_bwd_kernel(
 
 template <int L, int EPL>
 static int launch_gating_bwd_t(const moe_config& c, const float* lg, const int32_t* idx,
-                               const float* gw, const float* dg, const float* dlx, float* ds,
-                               float* ds_copy, hipStream_t st) {
+                               const float* gw, const float* dg, const float* dlx,
+                               const float* jit, float* ds, float* ds_copy, hipStream_t st) {
   const int grid = (int)cdiv((int64_t)c.T * L, 256);
   MOE_LAUNCH("gating_bwd", (gating_bwd_kernel<L, EPL>), dim3(grid), dim3(256), 0, st, lg, idx,
-             gw, dg, dlx, c.T, c.E, c.K, c.score_fn, c.gating, ds, ds_copy);
+             gw, dg, dlx, jit, c.T, c.E, c.K, c.score_fn, c.gating, ds, ds_copy);
   return MOE_OK;
 }
 
 static int launch_gating_bwd(const moe_config& c, const float* lg, const int32_t* idx,
-                             const float* gw, const float* dg, const float* dlx, float* ds,
-                             float* ds_copy, hipStream_t st) {
+                             const float* gw, const float* dg, const float* dlx, const float* jit,
+                             float* ds, float* ds_copy, hipStream_t st) {
   const int E = c.E;
-#define GB(Lv, Ev) return launch_gating_bwd_t<Lv, Ev>(c, lg, idx, gw, dg, dlx, ds, ds_copy, st)
+#define GB(Lv, Ev) return launch_gating_bwd_t<Lv, Ev>(c, lg, idx, gw, dg, dlx, jit, ds, ds_copy, st)
   if (E <= 1) GB(1, 1);
   if (E <= 2) GB(2, 1);
   if (E <= 4) GB(4, 1);
@@ -447,8 +449,8 @@ int launch_backward(const moe_config& c, const void* x, const float* wr, const f
                     const int32_t* idx, const float* topk_w, const int32_t* offsets,
                     const int32_t* slot_row, const void* x_perm, const void* act, const void* h,
                     const void* o_perm, const void* wg, const void* wu, const void* wd,
-                    const void* dy, const float* dlx, void* dx, float* dwr, float* drb,
-                    void* dwg, void* dwu, void* dwd, float* d_logits_out, char* ws,
+                    const void* dy, const float* dlx, const float* jit, void* dx, float* dwr,
+                    float* drb, void* dwg, void* dwu, void* dwd, float* d_logits_out, char* ws,
                     const Workspace& L, hipStream_t st) {
   void* d_o = ws + L.d_o;
   void* dact = ws + L.dact;
@@ -458,7 +460,8 @@ int launch_backward(const moe_config& c, const void* x, const float* wr, const f
   float* dxr = (c.E > 16) ? reinterpret_cast<float*>(ws + L.dxr) : nullptr;
   int rc;
   if ((rc = launch_combine_bwd(c, o_perm, dy, slot_row, topk_w, dg, d_o, st))) return rc;
-  if ((rc = launch_gating_bwd(c, logits, idx, topk_w, dg, dlx, ds, d_logits_out, st))) return rc;
+  if ((rc = launch_gating_bwd(c, logits, idx, topk_w, dg, dlx, jit, ds, d_logits_out, st)))
+    return rc;
   // Independent parts overlap on two side streams:
   //   main:   down dgrad -> up dgrad -> (router) -> un-permute
   //   side 0: down wgrad -> (after down dgrad) up wgrad

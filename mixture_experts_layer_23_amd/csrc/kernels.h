@@ -35,8 +35,9 @@ inline int router_wgrad_width(const moe_config& c) {
 }
 
 int launch_route(const moe_config& c, const void* x, const float* wr, const float* rb,
-                 const float* selb, float* logits, int32_t* idx, float* w, float* lse,
-                 bool logits_given, hipStream_t st);
+                 const float* selb, const float* jit, const float* wn, const float* eps,
+                 float* nlg, float* logits, int32_t* idx, float* w, float* lse, bool logits_given,
+                 hipStream_t st);
 
 int launch_permute(const moe_config& c, int capacity, const int32_t* idx, const void* x,
                    int32_t* counts_all, int32_t* offsets, int32_t* slot_row, int32_t* row_token,
@@ -64,8 +65,8 @@ int launch_backward(const moe_config& c, const void* x, const float* wr, const f
                     const int32_t* idx, const float* topk_w, const int32_t* offsets,
                     const int32_t* slot_row, const void* x_perm, const void* act, const void* h,
                     const void* o_perm, const void* wg, const void* wu, const void* wd,
-                    const void* dy, const float* dlx, void* dx, float* dwr, float* drb,
-                    void* dwg, void* dwu, void* dwd, float* d_logits_out, char* ws,
+                    const void* dy, const float* dlx, const float* jit, void* dx, float* dwr,
+                    float* drb, void* dwg, void* dwu, void* dwd, float* d_logits_out, char* ws,
                     const Workspace& L, hipStream_t st);
 
 // side streams (streams.hip): per-device side stream i (0 or 1), or null if

@@ -249,16 +249,26 @@ MOE_DEV bool better(float ka, int ia, float kb, int ib) {
   return (ka > kb) || (ka == kb && ia < ib);
 }
 
+// softplus in double, the overflow-free form log(1 + e^n) = max(n, 0) +
+// log1p(e^-|n|)
+MOE_DEV double softplus64(double n) { return fmax(n, 0.0) + log1p(exp(-fabs(n))); }
+
+// Router-logit jitter and noisy selection ([P3] ST-MoE, KeepTopK; [P5] 8.6):
+// with jit, s~ = s * u (one binary32 multiply) replaces the logits everywhere
+// (written back to `logits`); with eps, the selection key is
+// fl32(s~ + eps * softplus(n)) evaluated in double (n = the noise logits),
+// while the weights and lse stay on s~ (the noise only selects).
 template <int L, int EPL>
 __global__ __launch_bounds__(256) void route_select_kernel(
-    const float* __restrict__ logits, const float* __restrict__ selb, int T_, int E, int K,
+    float* __restrict__ logits, const float* __restrict__ selb, const float* __restrict__ jit,
+    const float* __restrict__ eps, const float* __restrict__ nlg, int T_, int E, int K,
     int score, int gating, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
     float* __restrict__ lse_out) {
   const int gid = blockIdx.x * blockDim.x + threadIdx.x;
   const int t = gid / L, sub = gid % L;
   const bool active = t < T_;  // whole L-groups are (in)active together
   if (!active) return;
-  const float* s = logits + (size_t)t * E;
+  float* s = logits + (size_t)t * E;
   float sv[EPL], key[EPL];
   bool used[EPL];
   float m = -INFINITY;
@@ -267,8 +277,18 @@ __global__ __launch_bounds__(256) void route_select_kernel(
     const int e = sub + L * j;
     const bool ok = e < E;
     sv[j] = ok ? s[e] : -INFINITY;
-    if (score == 0) key[j] = sv[j];
-    else key[j] = ok ? (sig32(sv[j]) + (selb ? selb[e] : 0.0f)) : -INFINITY;
+    if (jit && ok) {
+      sv[j] = sv[j] * jit[(size_t)t * E + e];
+      s[e] = sv[j];
+    }
+    if (score == 0) {
+      key[j] = sv[j];
+      if (eps && ok)
+        key[j] = (float)((double)sv[j] + (double)eps[(size_t)t * E + e] *
+                                             softplus64((double)nlg[(size_t)t * E + e]));
+    } else {
+      key[j] = ok ? (sig32(sv[j]) + (selb ? selb[e] : 0.0f)) : -INFINITY;
+    }
     used[j] = !ok;
     m = fmaxf(m, sv[j]);
   }
@@ -303,7 +323,13 @@ __global__ __launch_bounds__(256) void route_select_kernel(
 #pragma unroll
     for (int j = 0; j < EPL; ++j)
       if (sub + L * j == bi) used[j] = true;
-    const float sc = s[bi];
+    // the chosen expert's (jittered) logit, from the lane that holds it
+    float sc = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j)
+      if (sub + L * j == bi) sc = sv[j];
+#pragma unroll
+    for (int o = L / 2; o >= 1; o >>= 1) sc = fmaxf(sc, __shfl_xor(sc, o, 64));
     float g;
     if (score == 0) g = expf(sc - m);                 // unnormalised softmax term
     else g = 1.0f / (1.0f + expf(-sc));               // raw sigmoid score
@@ -324,21 +350,28 @@ __global__ __launch_bounds__(256) void route_select_kernel(
   }
 }
 
+struct SelectExtras {
+  const float* jit;
+  const float* eps;
+  const float* nlg;
+};
+
 template <int L, int EPL>
-static int launch_select(const float* lg, const float* selb, int T_, int E, int K, int score,
-                         int gating, int32_t* idx, float* w, float* lse, hipStream_t st) {
+static int launch_select(float* lg, const float* selb, const SelectExtras& x, int T_, int E, int K,
+                         int score, int gating, int32_t* idx, float* w, float* lse,
+                         hipStream_t st) {
   const int64_t threads = (int64_t)T_ * L;
   const int grid = (int)cdiv(threads, 256);
   MOE_LAUNCH("route_select", (route_select_kernel<L, EPL>), dim3(grid), dim3(256), 0, st, lg, selb,
-             T_, E, K, score, gating, idx, w, lse);
+             x.jit, x.eps, x.nlg, T_, E, K, score, gating, idx, w, lse);
   return MOE_OK;
 }
 
-int launch_route(const moe_config& c, const void* x, const float* wr, const float* rb,
-                 const float* selb, float* logits, int32_t* idx, float* w, float* lse,
-                 bool logits_given, hipStream_t st) {
+// router logits out[T][E] = fl32(x W^T + b), fp64 accumulation
+static int router_logits(const moe_config& c, const void* x, const float* wr, const float* rb,
+                         float* logits, hipStream_t st) {
   const int T_ = c.T, D = c.D, E = c.E;
-  if (!logits_given) {
+  {
     if (E <= 16 && (size_t)E * D * 4 <= 128 * 1024) {
       const int waves_needed = (int)cdiv(T_, 2);
       int grid = (int)std::min<int64_t>(cdiv(waves_needed, 4), 2048);
@@ -379,19 +412,33 @@ int launch_route(const moe_config& c, const void* x, const float* wr, const floa
         MOE_LAUNCH("router_logits", (router_tiled_kernel<float>), grid, dim3(256), 0, st, (const float*)x, wr, rb, logits, T_, D, E);
     }
   }
+  return MOE_OK;
+}
+
+int launch_route(const moe_config& c, const void* x, const float* wr, const float* rb,
+                 const float* selb, const float* jit, const float* wn, const float* eps,
+                 float* nlg, float* logits, int32_t* idx, float* w, float* lse, bool logits_given,
+                 hipStream_t st) {
+  const int T_ = c.T, E = c.E;
+  int rc;
+  if (!logits_given && (rc = router_logits(c, x, wr, rb, logits, st))) return rc;
+  if (wn && (rc = router_logits(c, x, wn, nullptr, nlg, st))) return rc;
   const int K = c.K, sc = c.score_fn, ga = c.gating;
   const float* sb = (sc == MOE_SCORE_SIGMOID) ? selb : nullptr;
-  if (E <= 1) return launch_select<1, 1>(logits, sb, T_, E, K, sc, ga, idx, w, lse, st);
-  if (E <= 2) return launch_select<2, 1>(logits, sb, T_, E, K, sc, ga, idx, w, lse, st);
-  if (E <= 4) return launch_select<4, 1>(logits, sb, T_, E, K, sc, ga, idx, w, lse, st);
-  if (E <= 8) return launch_select<8, 1>(logits, sb, T_, E, K, sc, ga, idx, w, lse, st);
-  if (E <= 16) return launch_select<16, 1>(logits, sb, T_, E, K, sc, ga, idx, w, lse, st);
-  if (E <= 32) return launch_select<32, 1>(logits, sb, T_, E, K, sc, ga, idx, w, lse, st);
-  if (E <= 64) return launch_select<64, 1>(logits, sb, T_, E, K, sc, ga, idx, w, lse, st);
-  if (E <= 128) return launch_select<64, 2>(logits, sb, T_, E, K, sc, ga, idx, w, lse, st);
-  if (E <= 256) return launch_select<64, 4>(logits, sb, T_, E, K, sc, ga, idx, w, lse, st);
-  if (E <= 512) return launch_select<64, 8>(logits, sb, T_, E, K, sc, ga, idx, w, lse, st);
-  return launch_select<64, 16>(logits, sb, T_, E, K, sc, ga, idx, w, lse, st);
+  const SelectExtras xs = {jit, wn ? eps : nullptr, wn ? nlg : nullptr};
+#define SEL(Lv, Ev) return launch_select<Lv, Ev>(logits, sb, xs, T_, E, K, sc, ga, idx, w, lse, st)
+  if (E <= 1) SEL(1, 1);
+  if (E <= 2) SEL(2, 1);
+  if (E <= 4) SEL(4, 1);
+  if (E <= 8) SEL(8, 1);
+  if (E <= 16) SEL(16, 1);
+  if (E <= 32) SEL(32, 1);
+  if (E <= 64) SEL(64, 1);
+  if (E <= 128) SEL(64, 2);
+  if (E <= 256) SEL(64, 4);
+  if (E <= 512) SEL(64, 8);
+  SEL(64, 16);
+#undef SEL
 }
 
 }  // namespace moe

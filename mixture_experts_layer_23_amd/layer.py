@@ -54,7 +54,7 @@ class LayerSpec:
 
 class MoELayer:
     def __init__(self, spec: LayerSpec, w_r, w_gate, w_up, w_down, r_bias=None, sel_bias=None,
-                 device="cuda"):
+                 device="cuda", w_noise=None):
         self.spec = spec
         self.cfg = spec.config()
         self.dev = torch.device(device)
@@ -63,6 +63,8 @@ class MoELayer:
         self.tdt = tdt
         self.w_r, self.w_gate, self.w_up, self.w_down = w_r, w_gate, w_up, w_down
         self.r_bias, self.sel_bias = r_bias, sel_bias
+        self.w_noise = w_noise  # noisy top-K: [E][D] fp32 noise router, or None
+        self.jitter = None      # router-logit jitter of the last forward ([T][E] fp32)
         rows = max(L.rows_max(self.cfg), 1)
         T1 = max(s.T, 1)
         G = s.groups
@@ -95,6 +97,7 @@ class MoELayer:
         self.dw_up = torch.empty_like(w_up)
         self.dw_down = torch.empty_like(w_down)
         self.d_logits = z(T1, s.E, dt=f32)
+        self.noise_logits = z(T1, s.E, dt=f32) if w_noise is not None else None
         self.x = None
 
     @property
@@ -109,13 +112,23 @@ class MoELayer:
     def has_dlogits(self) -> bool:
         return self.use_aux or self.use_seq
 
-    def route(self, x, logits_given: bool = False):
-        L.moe_route(self.cfg, x, self.w_r, self.r_bias, self.sel_bias, self.logits, self.topk_idx,
-                    self.topk_w, self.lse, L.MOE_ROUTE_LOGITS_GIVEN if logits_given else 0)
+    def route(self, x, logits_given: bool = False, jitter=None, noise_eps=None):
+        flags = L.MOE_ROUTE_LOGITS_GIVEN if logits_given else 0
+        self.jitter = jitter
+        if jitter is None and self.w_noise is None:
+            L.moe_route(self.cfg, x, self.w_r, self.r_bias, self.sel_bias, self.logits,
+                        self.topk_idx, self.topk_w, self.lse, flags)
+        else:
+            L.moe_route_ex(self.cfg, x, self.w_r, self.r_bias, self.sel_bias, jitter,
+                           self.w_noise, noise_eps if self.w_noise is not None else None,
+                           self.noise_logits, self.logits, self.topk_idx, self.topk_w, self.lse,
+                           flags)
 
-    def forward(self, x, logits_given: bool = False):
+    def forward(self, x, logits_given: bool = False, jitter=None, noise_eps=None):
+        """jitter / noise_eps: the step's random draws ([T][E] fp32) for the
+        router-logit jitter and the noisy top-K selection (None: off)."""
         self.x = x
-        self.route(x, logits_given)
+        self.route(x, logits_given, jitter, noise_eps)
         L.moe_permute(self.cfg, self.topk_idx, x, self.counts, self.offsets, self.slot_row,
                       self.row_token, self.row_slot, self.n_dropped, self.x_perm, self.ws)
         L.moe_expert_ffn(self.cfg, x, self.x_perm, self.offsets, self.w_gate, self.w_up,
@@ -134,11 +147,12 @@ class MoELayer:
 
     def backward(self, dy, with_aux: bool | None = None):
         use = self.has_dlogits if with_aux is None else with_aux
-        L.moe_backward(self.cfg, self.x, self.w_r, self.logits, self.topk_idx, self.topk_w,
-                       self.offsets, self.slot_row, self.x_perm, self.act, self.h, self.o_perm,
-                       self.w_gate, self.w_up, self.w_down, dy,
-                       self.dlogits_aux if use else None, self.dx, self.dw_r, self.d_rbias,
-                       self.dw_gate, self.dw_up, self.dw_down, self.d_logits, self.ws)
+        L.moe_backward_ex(self.cfg, self.x, self.w_r, self.logits, self.topk_idx, self.topk_w,
+                          self.offsets, self.slot_row, self.x_perm, self.act, self.h,
+                          self.o_perm, self.w_gate, self.w_up, self.w_down, dy,
+                          self.dlogits_aux if use else None, self.jitter, self.dx, self.dw_r,
+                          self.d_rbias, self.dw_gate, self.dw_up, self.dw_down, self.d_logits,
+                          self.ws)
         return self.dx
 
 

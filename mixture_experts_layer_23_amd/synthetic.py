@@ -197,3 +197,29 @@ def random_logits(T: int, E: int, seed: int, scale: float = 1.0, ties: bool = Fa
     if ties:
         lg = np.round(lg * 2) / 2
     return lg.astype(np.float32)
+
+
+def routing_noise(wl: Workload, seed: int | None = None, device=None):
+    """The random draws of the router-noise variants, as inputs:
+    jitter u ~ U[0.99, 1.01] [T][E] (ST-MoE logit jitter), eps ~ N(0, 1) [T][E]
+    (noisy top-K, one draw per token and expert) and a noise router
+    W_noise ~ N(0, 0.02) [E][D] (same scale as W_r), all fp32.  numpy arrays
+    (device None) or torch tensors on `device` (seeded Philox)."""
+    seed = (wl.seed if seed is None else seed) + 7919
+    if device is None:
+        ch = np.random.SeedSequence(seed).spawn(3)
+        u = np.random.Generator(np.random.PCG64(ch[0])).uniform(0.99, 1.01, (wl.T, wl.E))
+        eps = np.random.Generator(np.random.PCG64(ch[1])).standard_normal((wl.T, wl.E))
+        wn = np.random.Generator(np.random.PCG64(ch[2])).standard_normal((wl.E, wl.D)) * 0.02
+        return u.astype(np.float32), eps.astype(np.float32), wn.astype(np.float32)
+    import torch
+    seeds = [int(s) for s in np.random.SeedSequence(seed).generate_state(3, dtype=np.uint32)]
+    gens = []
+    for s in seeds:
+        g = torch.Generator(device=device)
+        g.manual_seed(s)
+        gens.append(g)
+    u = torch.rand(wl.T, wl.E, generator=gens[0], device=device) * 0.02 + 0.99
+    eps = torch.randn(wl.T, wl.E, generator=gens[1], device=device)
+    wn = torch.randn(wl.E, wl.D, generator=gens[2], device=device) * 0.02
+    return u, eps, wn

@@ -145,3 +145,122 @@ def test_bias_update_in_layer():
     want = O().bias_update(ocfg(wl), to_host(layer.counts), 1e-3, b0)
     np.testing.assert_array_equal(to_host(layer.sel_bias), want)
     assert np.any(want != b0)
+
+
+# ---------------------------------------------------------------------------
+# router-logit jitter and noisy top-K (next row 2)
+# ---------------------------------------------------------------------------
+NOISE_CASES = {
+    "minimind_small_B": S.WORKLOADS["minimind"].with_(T=512, D=256, F=512),
+    "minimind_small_A": S.WORKLOADS["minimind"].with_(T=512, D=256, F=512, gating=S.GATE_A),
+    "olmoe_small": S.WORKLOADS["olmoe_share"].with_(T=300, D=128, E=16, K=4, F=128, hi=8),
+    "olmoe_e64": S.WORKLOADS["olmoe_share"].with_(T=256, D=128, E=64, K=8, F=128),
+    "deepseek_small_jitter": S.WORKLOADS["deepseek_v3"].with_(T=256, D=128, E=64, F=128),
+}
+
+
+def _noise_route_check(wl, layer, x, u, eps, wn, use_noise):
+    """Plain routing gives s; the extended routing on the same x must give
+    s~ = fl32(s u) bit for bit, n = x W_noise^T bit for bit (vs the oracle's
+    logits), the oracle's indices bit for bit and its weights at fp32."""
+    o = O()
+    oc = ocfg(wl)
+    L.moe_route(layer.cfg, x, layer.w_r, layer.r_bias, layer.sel_bias, layer.logits,
+                layer.topk_idx, layer.topk_w, layer.lse, 0)
+    torch.cuda.synchronize()
+    s = to_host(layer.logits).copy()
+    tdev = lambda a: to_dev(a, torch) if a is not None else None
+    nl = torch.empty(wl.T, wl.E, dtype=torch.float32, device="cuda")
+    L.moe_route_ex(layer.cfg, x, layer.w_r, layer.r_bias, layer.sel_bias, tdev(u),
+                   tdev(wn) if use_noise else None, tdev(eps) if use_noise else None,
+                   nl if use_noise else None, layer.logits, layer.topk_idx, layer.topk_w,
+                   layer.lse, 0)
+    torch.cuda.synchronize()
+    st = to_host(layer.logits)
+    if u is not None:
+        np.testing.assert_array_equal(st, s * u)  # one binary32 multiply
+    nlg = None
+    if use_noise:
+        hin_x = to_host(x)
+        nlg = o.logits(oc, hin_x, wn)
+        np.testing.assert_array_equal(to_host(nl), nlg)
+    selb = to_host(layer.sel_bias) if layer.sel_bias is not None else None
+    idx, w, lse, _, _ = o.route_noisy(oc, s.astype(np.float64), jit=u,
+                                      eps=eps if use_noise else None,
+                                      nlg=nlg.astype(np.float64) if use_noise else None,
+                                      selb=selb)
+    got = to_host(layer.topk_idx)
+    nbad = int(np.sum(np.any(got != idx, 1)))
+    assert nbad == 0, f"{nbad} tokens routed differently"
+    assert_close("topk_w", to_host(layer.topk_w), w, 1e-5)
+    assert_close("lse", to_host(layer.lse), lse, 1e-5)
+    plain = o.route(oc, s.astype(np.float64), selb)[0]
+    return int(np.sum(np.any(np.sort(idx, 1) != np.sort(plain, 1), 1)))
+
+
+@pytest.mark.parametrize("case", list(NOISE_CASES))
+def test_jitter_noise_routing_parity(case):
+    wl = NOISE_CASES[case]
+    hin = S.host_inputs(wl, 0)
+    u, eps, wn = S.routing_noise(wl)
+    layer = build_layer(wl, hin, torch)
+    x = to_dev(hin.x, torch)
+    changed = _noise_route_check(wl, layer, x, u, None, None, False)
+    note(f"{case}: jitter changed the expert set of {changed} of {wl.T} tokens")
+    if wl.score == 0:
+        changed = _noise_route_check(wl, layer, x, None, eps, wn, True)
+        note(f"{case}: noise changed the expert set of {changed} of {wl.T} tokens")
+        _noise_route_check(wl, layer, x, u, eps, wn, True)
+
+
+@pytest.mark.parametrize("case", ["minimind_small_B", "olmoe_small", "deepseek_small_jitter"])
+def test_jitter_noise_layer_backward(case):
+    """Forward + backward with jitter (and noise for softmax scoring) through
+    the layer against the oracle: y, dx, dW_r, d r_b and the expert weight
+    gradients, on the GPU's routing."""
+    wl = NOISE_CASES[case]
+    hin = S.host_inputs(wl, 0)
+    u, eps, wn = S.routing_noise(wl)
+    use_noise = wl.score == 0
+    from mixture_experts_layer_23_amd.layer import LayerSpec, MoELayer
+    td = lambda a: to_dev(a, torch) if a is not None else None
+    layer = MoELayer(LayerSpec.from_workload(wl), td(hin.wr), td(hin.wg), td(hin.wu),
+                     td(hin.wd), td(hin.rb), td(hin.selb), w_noise=td(wn) if use_noise else None)
+    x, dy = td(hin.x), td(hin.dy)
+    layer.forward(x, jitter=td(u), noise_eps=td(eps) if use_noise else None)
+    layer.backward(dy)
+    torch.cuda.synchronize()
+    o = O()
+    oc = ocfg(wl)
+    st = to_host(layer.logits).astype(np.float64)  # s~ as the layer used it
+    idx = to_host(layer.topk_idx)
+    w = to_host(layer.topk_w).astype(np.float64)
+    d = o.dispatch(oc, idx)
+    from gpu_common import as_f64
+    tol = 2e-2 if wl.dtype == S.BF16 else 1e-5
+    y = o.forward(oc, hin.x, hin.wg, hin.wu, hin.wd, idx, w, d["slot_row"])
+    assert_close("y", as_f64(to_host(layer.y)), y, tol)
+    dl = None
+    if layer.use_aux:
+        _, dl = o.aux(oc, st, d["counts_all"], wl.alpha, wl.zlam)
+    bw = o.backward(oc, hin.x, hin.wr, hin.wg, hin.wu, hin.wd, st, idx, w, d["slot_row"],
+                    as_f64(hin.dy), dlx=dl, jit=u)
+    assert_close("dx", as_f64(to_host(layer.dx)), bw["dx"], tol)
+    assert_close("dW_r", to_host(layer.dw_r), bw["dwr"], tol)
+    assert_close("d_logits (raw)", to_host(layer.d_logits), bw["ds"], tol)
+    assert_close("dW_down", as_f64(to_host(layer.dw_down)), bw["dwd"], tol)
+
+
+@pytest.mark.parametrize("name", ["minimind", "olmoe_share"])
+def test_jitter_noise_routing_fullsize(name):
+    """Full-size routing with jitter and noise: every token's expert set and
+    order equal the oracle's (given the GPU's plain logits)."""
+    from mixture_experts_layer_23_amd.layer import LayerSpec, MoELayer
+    wl = S.WORKLOADS[name]
+    inp = S.device_inputs(wl, device="cuda")
+    u, eps, wn = S.routing_noise(wl, device="cuda")
+    layer = MoELayer(LayerSpec.from_workload(wl), inp["wr"], inp["wg"], inp["wu"], inp["wd"],
+                     inp["rb"], inp["selb"])
+    note(f"full-size noisy routing {name}: T={wl.T} E={wl.E} K={wl.K}")
+    changed = _noise_route_check(wl, layer, inp["x"], to_host(u), to_host(eps), to_host(wn), True)
+    note(f"  noise + jitter changed the expert set of {changed} of {wl.T} tokens")
