@@ -502,6 +502,81 @@ void orc_aux(const orc_cfg* c, const double* logits, const int* counts_all, doub
 }
 
 /* ------------------------------------------------------------------------ */
+/* Expert-choice routing ([P5] course notes 8.4: every expert takes a fixed  */
+/* number of tokens from the batch; a token may be taken by several experts  */
+/* or by none).  Reading: affinities p_{t,e} = softmax(s_t)_e; each local    */
+/* expert e takes the C tokens with the largest p_{t,e}, C = ceil(c T K / E) */
+/* (K: the average number of experts per token, c the capacity factor, 1 if  */
+/* not given), at most T; equal keys go to the lower token.  The key is the  */
+/* log-probability s_{t,e} - lse_t evaluated in double and rounded once to   */
+/* binary32 (strictly increasing in p within a column).  The gate weight of  */
+/* a taken pair is p_{t,e} (double).  Rows: expert-major, token order within */
+/* an expert, then the shared expert.                                       */
+/*   slot_row[t*E+e] = row, -1 (not taken), -2 (expert not local)            */
+/*   w[t*E+e] = p_{t,e} for every pair (the gating backward needs them all)  */
+/* ------------------------------------------------------------------------ */
+long orc_ec_capacity(const orc_cfg* c) {
+  const double cf = (c->cap > 0.0) ? c->cap : 1.0;
+  long C = (long)ceil(cf * (double)c->T * (double)c->K / (double)c->E);
+  return C < c->T ? C : c->T;
+}
+
+typedef struct { float key; int t; } ec_item;
+static int ec_cmp(const void* a, const void* b) {
+  const ec_item* x = (const ec_item*)a;
+  const ec_item* y = (const ec_item*)b;
+  if (x->key > y->key) return -1;
+  if (x->key < y->key) return 1;
+  return (x->t < y->t) ? -1 : (x->t > y->t);
+}
+
+int orc_route_ec(const orc_cfg* c, const double* logits, int* slot_row, double* w, int* row_token,
+                 int* offsets, double* lse_out) {
+  const int T = c->T, E = c->E, EL = c->hi - c->lo, S = c->n_shared;
+  if (c->score != 0) return -1;
+  const long C = orc_ec_capacity(c);
+  double* lse = (double*)malloc(sizeof(double) * (T > 0 ? T : 1));
+  for (int t = 0; t < T; ++t) {
+    const double* s = logits + (size_t)t * E;
+    double m = -INFINITY, z = 0.0;
+    for (int e = 0; e < E; ++e) if (s[e] > m) m = s[e];
+    for (int e = 0; e < E; ++e) z += exp(s[e] - m);
+    lse[t] = m + log(z);
+    if (lse_out) lse_out[t] = lse[t];
+    for (int e = 0; e < E; ++e) {
+      w[(size_t)t * E + e] = exp(s[e] - lse[t]);
+      slot_row[(size_t)t * E + e] = (e >= c->lo && e < c->hi) ? -1 : -2;
+    }
+  }
+  ec_item* items = (ec_item*)malloc(sizeof(ec_item) * (T > 0 ? T : 1));
+  int* taken = (int*)malloc(sizeof(int) * (T > 0 ? T : 1));
+  for (int g = 0; g < EL; ++g) {
+    const int e = c->lo + g;
+    for (int t = 0; t < T; ++t) {
+      items[t].key = (float)(logits[(size_t)t * E + e] - lse[t]);
+      items[t].t = t;
+    }
+    qsort(items, (size_t)T, sizeof(ec_item), ec_cmp);
+    for (int t = 0; t < T; ++t) taken[t] = 0;
+    for (long i = 0; i < C; ++i) taken[items[i].t] = 1;
+    long r = (long)g * C;
+    for (int t = 0; t < T; ++t)
+      if (taken[t]) {
+        slot_row[(size_t)t * E + e] = (int)r;
+        row_token[r] = t;
+        ++r;
+      }
+  }
+  for (int g = 0; g <= EL; ++g) offsets[g] = (int)((long)g * C);
+  for (int s = 0; s < S; ++s) {
+    offsets[EL + 1 + s] = (int)((long)EL * C + (long)(s + 1) * T);
+    for (int t = 0; t < T; ++t) row_token[(long)EL * C + (long)s * T + t] = t;
+  }
+  free(items); free(taken); free(lse);
+  return (int)C;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Load-driven selection-bias update ([P5] course notes 8.6; [P4] section on  */
 /* the auxiliary-loss-free route): experts select on s_e + b_e; after a step  */
 /* an overloaded expert lowers its b_e, an underloaded one raises it, by a    */

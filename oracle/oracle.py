@@ -101,6 +101,10 @@ def lib():
         L.orc_aux.argtypes = [P, P, P, C.c_double, C.c_double, P, P]
         L.orc_gate_grad.argtypes = [P, P, P, P, P, P]
         L.orc_bias_update.argtypes = [P, P, C.c_float, P]
+        L.orc_ec_capacity.argtypes = [P]
+        L.orc_ec_capacity.restype = C.c_long
+        L.orc_route_ec.argtypes = [P, P, P, P, P, P, P]
+        L.orc_route_ec.restype = C.c_int
         L.orc_seq_aux.argtypes = [P, P, P, C.c_int, C.c_double, P, P]
         L.orc_seq_aux.restype = C.c_int
         L.orc_backward.argtypes = [P, P, C.c_int, P, P, P, P, C.c_int, P, P, P, P, P, C.c_int,
@@ -239,6 +243,40 @@ def bias_update(cfg: Cfg, counts_all, gamma: float, selb) -> np.ndarray:
     c = cfg.c()
     lib().orc_bias_update(C.byref(c), _p(cnt), float(gamma), _p(b))
     return b
+
+
+def ec_capacity(cfg: Cfg) -> int:
+    """Expert-choice capacity: min(ceil(c T K / E), T), c = 1 when not given."""
+    c = cfg.c()
+    return int(lib().orc_ec_capacity(C.byref(c)))
+
+
+def route_ec(cfg: Cfg, lg):
+    """Expert-choice routing (softmax affinities; every local expert takes its
+    C best tokens, equal keys to the lower token).  Returns a dict with
+    slot_row [T,E] (row, -1 not taken, -2 not local), w [T,E] (p for every
+    pair), row_token, offsets, lse, C, and the token-choice-shaped views
+    idx [T,E] (identity) and cfg_w, the config with K = E and gating A under
+    which forward() / backward() compute this layer."""
+    lg = np.ascontiguousarray(lg, dtype=np.float64)
+    c = cfg.c()
+    T, E = cfg.T, cfg.E
+    slot = np.empty((T, E), np.int32)
+    w = np.empty((T, E), np.float64)
+    Cap = ec_capacity(cfg)
+    nrows = (cfg.n_local * Cap) + cfg.n_shared * T
+    row_token = np.empty(max(nrows, 1), np.int32)
+    offsets = np.empty(cfg.groups + 1, np.int32)
+    lse = np.empty(T, np.float64)
+    rc = lib().orc_route_ec(C.byref(c), _p(lg), _p(slot), _p(w), _p(row_token), _p(offsets),
+                            _p(lse))
+    if rc < 0:
+        raise ValueError("expert choice needs softmax scoring")
+    cw = Cfg(T=T, D=cfg.D, E=E, K=E, F=cfg.F, lo=cfg.lo, hi=cfg.hi, n_shared=cfg.n_shared,
+             score=SOFTMAX, gating=0, cap=0.0)
+    idx = np.tile(np.arange(E, dtype=np.int32), (T, 1))
+    return dict(slot_row=slot, w=w, row_token=row_token[:nrows], offsets=offsets, lse=lse, C=rc,
+                idx=idx, cfg_w=cw)
 
 
 def route_noisy(cfg: Cfg, lg, jit=None, eps=None, nlg=None, selb=None, exact: bool = False):

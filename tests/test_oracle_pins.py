@@ -758,3 +758,95 @@ def test_jitter_noise_torch_autograd_tiny(orc, gating):
     np.testing.assert_allclose(y, ty.detach().numpy(), rtol=1e-10, atol=1e-12)
     np.testing.assert_allclose(bw["dwr"], twr.grad.numpy(), rtol=1e-9, atol=1e-12)
     np.testing.assert_allclose(bw["dx"], tx.grad.numpy(), rtol=1e-9, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# expert-choice routing (next row 3)
+# ---------------------------------------------------------------------------
+def test_expert_choice_worked_example(orc):
+    g = gold("expert_choice_example.json")
+    cfg = orc.Cfg(T=g["T"], D=1, E=g["E"], K=g["K"], F=8, cap=g["c"])
+    lg = np.log(np.array(g["p"]))
+    r = orc.route_ec(cfg, lg)
+    assert r["C"] == g["C"]
+    np.testing.assert_array_equal(r["slot_row"], g["slot_row"])
+    np.testing.assert_array_equal((r["slot_row"] >= 0).sum(1), g["times_taken"])
+    np.testing.assert_allclose(r["w"], g["p"], rtol=1e-12)
+
+
+def test_expert_choice_brute_force(orc):
+    """Each local expert's taken set against Python sorted() on (-key, t)."""
+    rng = np.random.default_rng(31)
+    for T, E, K, cap, lo, hi in [(40, 6, 2, 1.0, 0, 6), (33, 5, 1, 1.3, 1, 4), (16, 4, 3, 0.0, 0, 4),
+                                 (12, 8, 8, 2.0, 0, 8)]:
+        cfg = orc.Cfg(T=T, D=1, E=E, K=K, F=8, lo=lo, hi=hi, cap=cap)
+        lg = rng.normal(size=(T, E)).astype(np.float32).astype(np.float64)
+        lg[3] = lg[5]  # exact ties between tokens
+        r = orc.route_ec(cfg, lg)
+        C = min(int(np.ceil((cap if cap > 0 else 1.0) * T * K / E)), T)
+        assert r["C"] == C
+        m = lg.max(1, keepdims=True)
+        lse = (m + np.log(np.exp(lg - m).sum(1, keepdims=True)))[:, 0]
+        key = (lg - lse[:, None]).astype(np.float32)
+        row = 0
+        for e in range(E):
+            col = r["slot_row"][:, e]
+            if not (lo <= e < hi):
+                assert np.all(col == -2)
+                continue
+            want = sorted(range(T), key=lambda t: (-float(key[t, e]), t))[:C]
+            got = np.nonzero(col >= 0)[0]
+            np.testing.assert_array_equal(got, sorted(want))
+            np.testing.assert_array_equal(col[got], np.arange(row, row + C))  # token order
+            row += C
+        np.testing.assert_array_equal(r["offsets"][: hi - lo + 1], np.arange(hi - lo + 1) * C)
+
+
+def test_expert_choice_full_capacity_is_dense_soft_mixture(orc):
+    """C = T: every expert takes every token, so the layer is the dense soft
+    mixture y = sum_e softmax(s)_e FFN_e(x) -- the token-choice layer with
+    K = E and truncated gating A."""
+    rng = np.random.default_rng(32)
+    T, D, E, F = 12, 6, 4, 5
+    x, wr, wg, wu, wd, dy = tiny_inputs(rng, T, D, E, F, E)
+    cfg = orc.Cfg(T=T, D=D, E=E, K=E, F=F, cap=1.0)  # C = T
+    lg = orc.logits(cfg, x, wr, exact=True)
+    r = orc.route_ec(cfg, lg)
+    assert r["C"] == T
+    cw = r["cfg_w"]
+    y_ec = orc.forward(cw, x, wg, wu, wd, r["idx"], r["w"], r["slot_row"])
+    dense = orc.Cfg(T=T, D=D, E=E, K=E, F=F, gating=0)
+    idx, w, _, _ = orc.route(dense, lg)
+    d = orc.dispatch(dense, idx)
+    y_tc = orc.forward(dense, x, wg, wu, wd, idx, w, d["slot_row"])
+    np.testing.assert_allclose(y_ec, y_tc, rtol=1e-12, atol=1e-14)
+
+
+def test_expert_choice_torch_autograd_tiny(orc):
+    """Expert-choice forward and backward (selection held fixed) against torch
+    autograd on tiny fp64 inputs, with local experts [1, 4) of 5."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(33)
+    T, D, E, F = 14, 6, 5, 4
+    x, wr, wg, wu, wd, dy = tiny_inputs(rng, T, D, E, F, 3)
+    cfg = orc.Cfg(T=T, D=D, E=E, K=2, F=F, lo=1, hi=4)
+    lg = orc.logits(cfg, x, wr, exact=True)
+    r = orc.route_ec(cfg, lg)
+    cw = r["cfg_w"]
+    y = orc.forward(cw, x, wg, wu, wd, r["idx"], r["w"], r["slot_row"])
+    bw = orc.backward(cw, x, wr, wg, wu, wd, lg, r["idx"], r["w"], r["slot_row"], dy)
+    tx, twr = torch.tensor(x, requires_grad=True), torch.tensor(wr, requires_grad=True)
+    twg, twu, twd = (torch.tensor(a, requires_grad=True) for a in (wg, wu, wd))
+    p = torch.softmax(tx @ twr.T, -1)
+    ty = torch.zeros(T, D, dtype=torch.float64)
+    for t in range(T):
+        for e in range(E):
+            if r["slot_row"][t, e] < 0:
+                continue
+            g = e - 1
+            a, b = tx[t] @ twg[g], tx[t] @ twu[g]
+            ty[t] = ty[t] + p[t, e] * ((torch.nn.functional.silu(a) * b) @ twd[g])
+    (ty * torch.from_numpy(dy)).sum().backward()
+    np.testing.assert_allclose(y, ty.detach().numpy(), rtol=1e-10, atol=1e-12)
+    for mine, ref in [("dx", tx), ("dwr", twr), ("dwg", twg), ("dwu", twu), ("dwd", twd)]:
+        np.testing.assert_allclose(bw[mine], ref.grad.numpy(), rtol=1e-9, atol=1e-12)
