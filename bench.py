@@ -52,6 +52,9 @@ def parse():
                     help="multiply the router logits by per-step U[0.99, 1.01] draws")
     ap.add_argument("--noise", action="store_true",
                     help="noisy top-K selection (noise router + per-step N(0,1) draws)")
+    ap.add_argument("--routing", choices=["token", "expert"], default="token",
+                    help="token choice (top-K per token) or expert choice (top-C tokens per "
+                         "expert, softmax gating A)")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step replayed as one HIP graph (reported as ms_per_step_graph)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=None)
@@ -68,6 +71,8 @@ def workload(args):
         wl = wl.with_(K=args.k)
     if args.gating is not None:
         wl = wl.with_(gating=S.GATE_A if args.gating == "A" else S.GATE_B)
+    if args.routing == "expert":
+        wl = wl.with_(gating=S.GATE_A)  # a pair is weighted by its softmax probability
     return wl
 
 
@@ -104,11 +109,11 @@ def measured_traffic(kernel, wl):
     return None
 
 
-def cpu_baseline(wl, host, n_tok):
+def cpu_baseline(wl, host, n_tok, expert_choice=False):
     """The oracle as it stands, on a bounded sample of the same workload:
-    routing of all T tokens (logits, top-K, dispatch), then forward and the
-    full backward (dx, dW_r and every expert-weight gradient contribution) of
-    the first n_tok tokens.  Reported in tokens/s."""
+    routing of all T tokens (logits, top-K or expert choice, dispatch), then
+    forward and the full backward (dx, dW_r and every expert-weight gradient
+    contribution) of the first n_tok tokens.  Reported in tokens/s."""
     import numpy as np
     from oracle import oracle as O
 
@@ -118,15 +123,21 @@ def cpu_baseline(wl, host, n_tok):
     tok = np.arange(n_tok, dtype=np.int32)
     t0 = time.perf_counter()
     lg = O.logits(oc, x, wr, rb)
-    idx, w, lse, _ = O.route(oc, lg, selb)
-    d = O.dispatch(oc, idx)
-    O.forward(oc, x, wg, wu, wd, idx, w, d["slot_row"], tok=tok)
+    if expert_choice:
+        r = O.route_ec(oc, lg)
+        cw, idx, w, slot_row = r["cfg_w"], r["idx"], r["w"], r["slot_row"]
+        counts = [r["C"]] * wl.E
+    else:
+        idx, w, lse, _ = O.route(oc, lg, selb)
+        d = O.dispatch(oc, idx)
+        cw, slot_row, counts = oc, d["slot_row"], d["counts_all"]
+    O.forward(cw, x, wg, wu, wd, idx, w, slot_row, tok=tok)
     dl = None
     if wl.score == 0 and (wl.alpha or wl.zlam):
-        _, dl = O.aux(oc, lg, d["counts_all"], wl.alpha, wl.zlam)
+        _, dl = O.aux(oc, lg, counts, wl.alpha, wl.zlam)
     dyt = dy[tok].astype(np.float64) if dy.dtype != np.uint16 else \
         ((dy[tok].astype(np.uint32) << 16).view(np.float32).astype(np.float64))
-    O.backward(oc, x, wr, wg, wu, wd, lg, idx, w, d["slot_row"], dyt, tok=tok, dlx=dl)
+    O.backward(cw, x, wr, wg, wu, wd, lg, idx, w, slot_row, dyt, tok=tok, dlx=dl)
     dt = time.perf_counter() - t0
     return dict(value=n_tok / dt, unit="tokens/s", cores=O.threads(), kind="oracle",
                 sample=(f"routing of all {wl.T} tokens + forward and backward (dx, dW_r, all "
@@ -165,12 +176,15 @@ def main():
     inp = S.device_inputs(wl, device="cuda")
     spec = LayerSpec.from_workload(wl, seq_len=args.seq_len,
                                    seq_alpha=args.seq_alpha if args.seq_len else 0.0,
-                                   bias_gamma=args.bias_gamma)
+                                   bias_gamma=args.bias_gamma,
+                                   routing=(L.MOE_EXPERT_CHOICE if args.routing == "expert"
+                                            else L.MOE_TOKEN_CHOICE))
+    ec = spec.expert_choice
     u = eps = wn = None
     if args.jitter or args.noise:
         u, eps, wn = S.routing_noise(wl, device="cuda")
-    layer = MoELayer(spec, inp["wr"], inp["wg"], inp["wu"], inp["wd"], inp["rb"], inp["selb"],
-                     w_noise=wn if args.noise else None)
+    layer = MoELayer(spec, inp["wr"], inp["wg"], inp["wu"], inp["wd"], inp["rb"],
+                     None if ec else inp["selb"], w_noise=wn if args.noise else None)
     x, dy = inp["x"], inp["dy"]
     torch.cuda.synchronize()
 
@@ -223,7 +237,8 @@ def main():
     counts = layer.counts.cpu().numpy()
     n_rows_local = int(offsets[wl.n_local]) if wl.n_local > 0 else 0
     rows = n_rows_local + wl.n_shared * wl.T
-    n_dropped = int(layer.n_dropped.cpu().numpy()[0])
+    n_dropped = None if ec else int(layer.n_dropped.cpu().numpy()[0])
+    W = spec.width  # slots per token: K, or E under expert choice
     esz = 2 if wl.dtype == S.BF16 else 4
     kernels = {}
     gemm_flops = gemm_ms = 0.0
@@ -240,9 +255,15 @@ def main():
     Dsz = wl.D * esz
     stage_bytes = {
         "permute_gather": n_rows_local * Dsz * 2,
-        "combine": rows * Dsz + wl.T * Dsz + wl.T * wl.K * 8,
-        "combine_bwd": n_rows_local * Dsz * 2 + wl.T * Dsz + wl.T * wl.K * 8,
-        "unpermute_dx": rows * Dsz + wl.T * Dsz + wl.T * wl.K * 4,
+        "combine": rows * Dsz + wl.T * Dsz + wl.T * W * 8,
+        "combine_bwd": n_rows_local * Dsz * 2 + wl.T * Dsz + wl.T * W * 8,
+        "unpermute_dx": rows * Dsz + wl.T * Dsz + wl.T * W * 4,
+        # logits read; p, keys of the local experts, sentinel columns written
+        "ec_token": wl.T * wl.E * 4 * 2 + wl.T * wl.n_local * 4
+                    + wl.T * (wl.E - wl.n_local) * 4,
+        # keys read by three digit passes and the compaction; the local
+        # columns of the slot table and two row maps written
+        "ec_select": wl.T * wl.n_local * 4 * 4 + wl.T * wl.n_local * 4 + n_rows_local * 8,
         "route_select": wl.T * wl.E * 4 + wl.T * wl.K * 8 + wl.T * 4,
         "router_logits": wl.T * Dsz + wl.E * wl.D * 4 + wl.T * wl.E * 4,
         "router_wgrad": wl.T * Dsz + wl.T * wl.E * 4,
@@ -280,7 +301,7 @@ def main():
                 *[t.cpu().view(torch.int16).numpy().view(np.uint16) if wl.dtype == S.BF16
                   else t.cpu().numpy() for t in (inp["wg"], inp["wu"], inp["wd"], inp["dy"])])
         n_tok = args.cpu_sample_tokens or min(wl.T, 4096)
-        cpu = cpu_baseline(wl, host, n_tok)
+        cpu = cpu_baseline(wl, host, n_tok, expert_choice=ec)
 
     out = {
         "metric": "MoE layer fwd+bwd tokens/s",
@@ -301,7 +322,9 @@ def main():
                    "shared_rows": wl.n_shared * wl.T, "dropped": n_dropped,
                    "expert_load": counts.tolist() if wl.E <= 16 else None,
                    "seq_len": args.seq_len or None, "bias_gamma": args.bias_gamma or None,
-                   "jitter": args.jitter or None, "noise": args.noise or None},
+                   "jitter": args.jitter or None, "noise": args.noise or None,
+                   "routing": "expert choice" if ec else "token choice",
+                   "expert_capacity": L.capacity(layer.cfg) if ec else None},
         "grouped_gemm": {"tflops": gemm_flops / (gemm_ms * 1e-3) / 1e12 if gemm_ms else None,
                          "frac_of_peak": (gemm_flops / (gemm_ms * 1e-3) / 1e12 / peak_t)
                          if gemm_ms else None,

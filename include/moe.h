@@ -35,11 +35,20 @@
  *    kept in full precision).  dtype MOE_F32: all of those are fp32.
  *  - "rows": routed rows are expert-major (local expert lo..hi-1), in token
  *    order within an expert; the shared expert's rows follow, one per token.
- *    rows_max = T*K + n_shared*T bounds every row buffer.
+ *    rows_max (moe_rows_max) bounds every row buffer.
+ *  - Routing (cfg->routing).  MOE_TOKEN_CHOICE: slot tables (topk_idx,
+ *    topk_w, slot_row) are [T][K], slot t*K+k.  MOE_EXPERT_CHOICE (course
+ *    notes 8.4): moe_route_expert_choice replaces moe_route and moe_permute;
+ *    slot tables are [T][E], slot t*E+e is the pair (token t, expert e),
+ *    topk_w holds p = softmax(s) for every pair and topk_idx is not used (an
+ *    implicit identity); K is the average number of experts per token, which
+ *    sets the per-expert capacity C; moe_expert_ffn, moe_combine,
+ *    aux_balance_loss and moe_backward take the same [T][E] tables.
  *  - Pointers must be 16-byte aligned device pointers (MOE_EALIGN).
  *  - Requirements: T >= 0; D and F positive multiples of 64; 1 <= K <= E;
- *    K <= 64; E <= 1024; 0 <= expert_lo <= expert_hi <= E; n_shared in {0,1}
- *    (MOE_EINVAL).  T == 0 is a successful no-op.
+ *    K <= 64 for token choice; E <= 1024; 0 <= expert_lo <= expert_hi <= E;
+ *    n_shared in {0,1}; expert choice needs softmax scoring and
+ *    MOE_GATE_TRUNCATED (MOE_EINVAL).  T == 0 is a successful no-op.
  *  - Inputs are assumed finite; no entry point checks for NaN or Inf.
  *  - Return value: MOE_OK or a negative MOE_E* code; moe_error_string() gives
  *    text (for MOE_ELAUNCH it includes the HIP error of the failed launch).
@@ -68,6 +77,8 @@ enum { MOE_GATE_TRUNCATED = 0, /* gating A: g = p over all E, not renormalised *
        MOE_GATE_RENORM = 1 };  /* gating B: renormalised over the top-K        */
 enum { MOE_F32 = 0, MOE_BF16 = 1 };
 enum { MOE_ROUTE_LOGITS_GIVEN = 1 }; /* moe_route flag: logits is an input   */
+enum { MOE_TOKEN_CHOICE = 0,   /* every token picks its top-K experts            */
+       MOE_EXPERT_CHOICE = 1 }; /* every expert picks its top-C tokens          */
 
 /* Plain configuration record, read during the call and never retained. */
 typedef struct moe_config {
@@ -78,6 +89,7 @@ typedef struct moe_config {
   int32_t gating;                /* MOE_GATE_* */
   int32_t dtype;                 /* MOE_F32 or MOE_BF16 */
   double capacity_factor;        /* <= 0: no capacity (dropless); C = ceil(c*T*K/E) in double */
+  int32_t routing;               /* MOE_TOKEN_CHOICE or MOE_EXPERT_CHOICE */
 } moe_config;
 
 /* A hipStream_t (NULL: the null stream). */
@@ -85,10 +97,13 @@ typedef void* moe_stream_t;
 
 /* Capacity per expert, C = ceil(c*T*K/E) with the global E, evaluated in
  * double ([P5] 8.5; [P3] Switch Transformers capacity factor).  Writes -1
- * when capacity_factor <= 0.  Host-only. */
+ * when capacity_factor <= 0.  Expert choice: the number of tokens every
+ * expert takes, min(ceil(c*T*K/E), T) with c = 1 when capacity_factor <= 0.
+ * Host-only. */
 int moe_capacity(const moe_config* cfg, int32_t* capacity);
 
-/* rows_max = T*K + n_shared*T.  Host-only. */
+/* rows_max = T*K + n_shared*T (token choice) or (expert_hi - expert_lo)*C +
+ * n_shared*T (expert choice, C from moe_capacity).  Host-only. */
 int moe_rows_max(const moe_config* cfg, int64_t* rows);
 
 /* Bytes of device workspace needed by moe_permute, aux_balance_loss and
@@ -115,6 +130,7 @@ int moe_workspace_size(const moe_config* cfg, size_t* bytes);
  * order.  Selection key: softmax -> the logit; sigmoid -> sig32(s) + b, a
  * fixed binary32 sequence (range reduction by ln2 split in two parts, degree-7
  * Taylor polynomial with fma, scaling by 2^n, IEEE division).
+ * Token choice only (MOE_EINVAL under expert choice).
  */
 int moe_route(const moe_config* cfg, const void* x, const float* w_r, const float* r_bias,
               const float* sel_bias, float* logits, int32_t* topk_idx, float* topk_w, float* lse,
@@ -140,6 +156,7 @@ int moe_route(const moe_config* cfg, const void* x, const float* w_r, const floa
  *   ws, ws_bytes             workspace of moe_workspace_size() bytes
  * Deterministic: the rank inside an expert comes from counts and scans, not
  * from atomic slot grabbing.
+ * Token choice only (MOE_EINVAL under expert choice).
  */
 int moe_permute(const moe_config* cfg, const int32_t* topk_idx, const void* x,
                 int32_t* counts_all, int32_t* offsets, int32_t* slot_row, int32_t* row_token,
@@ -171,7 +188,8 @@ int moe_expert_ffn(const moe_config* cfg, const void* x, const void* x_perm, con
  *   y[t] = sum_k [slot_row >= 0] topk_w[t,k] * o_perm[slot_row[t,k]]
  *          + o_perm[offsets[G-1] + t] (shared)          fp32 accumulation
  * Sentinel and dropped slots contribute nothing; a token with all slots
- * dropped gets y = 0 (the residual path is outside the layer).
+ * dropped gets y = 0 (the residual path is outside the layer).  Expert
+ * choice: k runs over the E pairs of the [T][E] tables.
  */
 int moe_combine(const moe_config* cfg, const void* o_perm, const int32_t* offsets,
                 const int32_t* slot_row, const float* topk_w, void* y, moe_stream_t stream);
@@ -181,7 +199,9 @@ int moe_combine(const moe_config* cfg, const void* o_perm, const int32_t* offset
  * for softmax scoring only (MOE_EINVAL for sigmoid).
  * [P5] 8.5 (L = alpha*E*sum_e f_e P_e with f held constant), [P4] load
  * balance section; [P3] ST-MoE and [P5] 8.6 (z-loss on log-sum-exp).
- *   f_e = counts_all[e]/(T*K), P_e = mean_t softmax(s_t)_e
+ *   f_e = counts_all[e]/(T*K), P_e = mean_t softmax(s_t)_e  (under expert
+ *   choice f_e = C/(T*K) for every e, so the balance term is constant and
+ *   its gradient zero up to rounding; the z-loss is unchanged)
  *   losses[0] = alpha*E*sum_e f_e P_e;  losses[1] = z_lambda*mean_t lse_t^2;
  *   losses[2] = mean_t lse_t^2 (raw)                         [3] fp32, device
  *   d_logits [T][E] fp32 (NULL: not written) = d(losses[0]+losses[1])/ds
@@ -198,6 +218,9 @@ int aux_balance_loss(const moe_config* cfg, const float* logits, const int32_t* 
  * gate weights (top-K indices are piecewise constant).
  *   saved forward tensors: x, w_r, logits, topk_idx, topk_w, offsets,
  *   slot_row, x_perm, act, h, o_perm; weights w_gate, w_up, w_down.
+ *   Expert choice: topk_idx may be NULL (the [T][E] tables are indexed by
+ *   expert); the gating gradient is that of softmax A over all E pairs,
+ *   ds_i = p_i (dg_i - sum_j p_j dg_j), dg = 0 for pairs not taken.
  *   dy [T][D]               in
  *   d_logits_extra [T][E]   in, NULL = none (e.g. from aux_balance_loss)
  *   dx [T][D]               out  through the experts and the router
@@ -268,6 +291,7 @@ int moe_backward_ex(const moe_config* cfg, const void* x, const float* w_r, cons
  * counts_all: int32 [E] as written by moe_permute (all E, before capacity);
  * sel_bias: fp32 [E], updated in place, caller-owned device memory.  Meant
  * to run once per training step after the routing has consumed sel_bias.
+ * Token choice only (expert choice has no selection bias).
  * Errors: MOE_EINVAL (bad config, non-finite gamma, null), MOE_EALIGN.
  */
 int moe_bias_update(const moe_config* cfg, const int32_t* counts_all, float gamma,
@@ -290,12 +314,47 @@ int moe_bias_update(const moe_config* cfg, const int32_t* counts_all, float gamm
  * out; d_logits: fp32 [T][E] out (NULL: loss only), overwritten, or added to
  * when accumulate != 0 (to combine with aux_balance_loss's gradient before
  * moe_backward); ws: the layer workspace.  seq_len must divide T.
+ * Token choice only (every expert's load is fixed under expert choice).
  * Errors: MOE_EINVAL (bad config, seq_len, non-finite alpha, null),
  * MOE_EALIGN, MOE_EWORKSPACE.
  */
 int aux_seq_loss(const moe_config* cfg, const float* logits, const int32_t* topk_idx,
                  int32_t seq_len, float alpha, float* loss, float* d_logits, int32_t accumulate,
                  void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/*
+ * Expert-choice routing ("Course notes 08 MoE", section 8.4: each expert
+ * takes a fixed number of tokens from the batch, so a token can be served by
+ * several experts or by none; every expert's load is exactly C).  Replaces
+ * moe_route + moe_permute when cfg->routing == MOE_EXPERT_CHOICE.
+ *   x [T][D] dtype, w_r [E][D] fp32, r_bias [E] fp32 or NULL   in
+ *   logits   [T][E] fp32  out (in with MOE_ROUTE_LOGITS_GIVEN: then x is
+ *                              still read by the gather, w_r and r_bias not)
+ *   gate_w   [T][E] fp32  out  p_{t,e} = softmax(s_t)_e for every pair
+ *   lse      [T] fp32     out  log-sum-exp of the logits (may be NULL)
+ *   counts_all [E] int32  out  C for every expert (each takes exactly C)
+ *   offsets  [G+1] int32  out  g*C for the local experts, then the shared block
+ *   slot_row [T][E] int32 out  row of pair (t,e); -1 not taken; -2 expert
+ *                              outside [expert_lo, expert_hi)
+ *   row_token, row_slot [rows_max] int32  out  token t and pair t*E+e of
+ *                              each routed row (row_slot -1 for shared rows)
+ *   x_perm   [rows_max][D] dtype  out  x rows of the routed rows
+ *   ws, ws_bytes             workspace of moe_workspace_size() bytes
+ * Selection: every local expert e takes the C tokens with the largest key
+ * fl32(s_{t,e} - lse_t), s and lse evaluated in double and rounded once, equal
+ * keys going to the lower token; its rows are e's block of C rows in token
+ * order.  C = min(ceil(c*T*K/E), T), c = capacity_factor or 1 when <= 0.
+ * The layer output is y_t = sum over the experts that took t of
+ * p_{t,e} FFN_e(x_t) (plus the shared expert): moe_combine with these tables.
+ * Deterministic; bit-identical selection for identical logits.
+ * Errors: MOE_EINVAL (config not expert choice, NULL, flags), MOE_EALIGN,
+ * MOE_EWORKSPACE, MOE_ELAUNCH.
+ */
+int moe_route_expert_choice(const moe_config* cfg, const void* x, const float* w_r,
+                            const float* r_bias, float* logits, float* gate_w, float* lse,
+                            int32_t* counts_all, int32_t* offsets, int32_t* slot_row,
+                            int32_t* row_token, int32_t* row_slot, void* x_perm, int32_t flags,
+                            void* ws, size_t ws_bytes, moe_stream_t stream);
 
 /* Text for an error code (thread-local detail for MOE_ELAUNCH). */
 const char* moe_error_string(int code);

@@ -18,19 +18,21 @@ MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 MOE_GATE_TRUNCATED, MOE_GATE_RENORM = 0, 1
 MOE_F32, MOE_BF16 = 0, 1
 MOE_ROUTE_LOGITS_GIVEN = 1
+MOE_TOKEN_CHOICE, MOE_EXPERT_CHOICE = 0, 1
 
 EXPORTS = ["moe_capacity", "moe_rows_max", "moe_workspace_size", "moe_route", "moe_permute",
            "moe_expert_ffn", "moe_combine", "aux_balance_loss", "moe_backward",
            "moe_error_string", "moe_timing_enable", "moe_timing_report",
            "moe_timing_select", "moe_bias_update", "aux_seq_loss", "moe_route_ex",
-           "moe_backward_ex"]
+           "moe_backward_ex", "moe_route_expert_choice"]
 
 
 class MoeConfig(C.Structure):
     _fields_ = [("T", C.c_int32), ("D", C.c_int32), ("E", C.c_int32), ("K", C.c_int32),
                 ("F", C.c_int32), ("expert_lo", C.c_int32), ("expert_hi", C.c_int32),
                 ("n_shared", C.c_int32), ("score_fn", C.c_int32), ("gating", C.c_int32),
-                ("dtype", C.c_int32), ("capacity_factor", C.c_double)]
+                ("dtype", C.c_int32), ("capacity_factor", C.c_double),
+                ("routing", C.c_int32)]
 
 
 class MoeError(RuntimeError):
@@ -70,6 +72,7 @@ def lib():
             "moe_route_ex": [cfg, P, P, P, P, P, P, P, P, P, P, P, P, I, P],
             "moe_backward_ex": [cfg] + [P] * 25 + [S, P],
             "aux_seq_loss": [cfg, P, P, I, C.c_float, P, P, I, P, S, P],
+            "moe_route_expert_choice": [cfg] + [P] * 12 + [I, P, S, P],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -105,9 +108,9 @@ def stream_handle(stream=None) -> int | None:
 
 
 def make_config(T, D, E, K, F, expert_lo=0, expert_hi=None, n_shared=0, score_fn=0, gating=1,
-                dtype=MOE_BF16, capacity_factor=0.0) -> MoeConfig:
+                dtype=MOE_BF16, capacity_factor=0.0, routing=MOE_TOKEN_CHOICE) -> MoeConfig:
     return MoeConfig(T, D, E, K, F, expert_lo, E if expert_hi is None else expert_hi, n_shared,
-                     score_fn, gating, dtype, float(capacity_factor))
+                     score_fn, gating, dtype, float(capacity_factor), int(routing))
 
 
 # ---- host-only queries ------------------------------------------------------
@@ -199,6 +202,16 @@ def moe_backward_ex(cfg, x, w_r, logits, topk_idx, topk_w, offsets, slot_row, x_
     _check("moe_backward_ex",
            lib().moe_backward_ex(C.byref(cfg), *[ptr(a) for a in args],
                                  ws.numel() * ws.element_size(), stream_handle(stream)))
+
+
+def moe_route_expert_choice(cfg, x, w_r, r_bias, logits, gate_w, lse, counts_all, offsets,
+                            slot_row, row_token, row_slot, x_perm, ws, flags=0, stream=None):
+    args = [x, w_r, r_bias, logits, gate_w, lse, counts_all, offsets, slot_row, row_token,
+            row_slot, x_perm]
+    _check("moe_route_expert_choice",
+           lib().moe_route_expert_choice(C.byref(cfg), *[ptr(a) for a in args], int(flags),
+                                         ptr(ws), ws.numel() * ws.element_size(),
+                                         stream_handle(stream)))
 
 
 def moe_bias_update(cfg, counts_all, gamma, sel_bias, stream=None):

@@ -67,21 +67,29 @@ static int check_cfg(const moe_config* c) {
   if (!c) return MOE_EINVAL;
   if (c->T < 0 || c->D <= 0 || c->F <= 0 || c->E < 1 || c->E > 1024) return MOE_EINVAL;
   if (c->D % 64 || c->F % 64) return MOE_EINVAL;
-  if (c->K < 1 || c->K > c->E || c->K > 64) return MOE_EINVAL;
+  if (c->routing != MOE_TOKEN_CHOICE && c->routing != MOE_EXPERT_CHOICE) return MOE_EINVAL;
+  if (c->K < 1 || c->K > c->E) return MOE_EINVAL;
+  if (c->routing == MOE_TOKEN_CHOICE && c->K > 64) return MOE_EINVAL;
   if (c->expert_lo < 0 || c->expert_lo > c->expert_hi || c->expert_hi > c->E) return MOE_EINVAL;
   if (c->n_shared < 0 || c->n_shared > 1) return MOE_EINVAL;
   if (c->score_fn != MOE_SCORE_SOFTMAX && c->score_fn != MOE_SCORE_SIGMOID) return MOE_EINVAL;
   if (c->gating != MOE_GATE_TRUNCATED && c->gating != MOE_GATE_RENORM) return MOE_EINVAL;
   if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return MOE_EDTYPE;
   if (!std::isfinite(c->capacity_factor)) return MOE_EINVAL;
-  // row indices and element offsets of row buffers fit the kernels' int32 /
-  // int64 arithmetic
-  const int64_t rows = (int64_t)c->T * c->K + (int64_t)c->n_shared * c->T;
+  // expert choice weighs a pair by its softmax probability (gating A)
+  if (c->routing == MOE_EXPERT_CHOICE &&
+      (c->score_fn != MOE_SCORE_SOFTMAX || c->gating != MOE_GATE_TRUNCATED))
+    return MOE_EINVAL;
+  // row indices, slot indices and element offsets of row buffers fit the
+  // kernels' int32 / int64 arithmetic
+  const int64_t rows = routed_rows_max(*c) + (int64_t)c->n_shared * c->T;
   if (rows > INT32_MAX / 2) return MOE_EINVAL;
+  if ((int64_t)c->T * slot_width(*c) > INT32_MAX / 2) return MOE_EINVAL;
   return MOE_OK;
 }
 
 static int capacity_of(const moe_config& c) {
+  if (c.routing == MOE_EXPERT_CHOICE) return (int)ec_capacity(c);
   if (!(c.capacity_factor > 0.0)) return -1;
   const double v = std::ceil((c.capacity_factor * (double)c.T * (double)c.K) / (double)c.E);
   return v > (double)INT32_MAX ? INT32_MAX : (int)v;
@@ -93,10 +101,12 @@ static int groups(const moe_config& c) { return (c.expert_hi - c.expert_lo) + c.
 
 Workspace workspace_layout(const moe_config& c) {
   Workspace L = {};
+  const bool ec = c.routing == MOE_EXPERT_CHOICE;
   const int64_t TK = (int64_t)c.T * c.K;
-  const int64_t rows = TK + (int64_t)c.n_shared * c.T;
+  const int64_t TW = (int64_t)c.T * slot_width(c);
+  const int64_t rows = routed_rows_max(c) + (int64_t)c.n_shared * c.T;
   const size_t esz = c.dtype == MOE_BF16 ? 2 : 4;
-  L.ntiles = (int)std::max<int64_t>(1, cdiv(TK, kSlotTile));
+  L.ntiles = ec ? 1 : (int)std::max<int64_t>(1, cdiv(TK, kSlotTile));
   L.aux_blocks = (int)std::max<int64_t>(1, cdiv(c.T, aux_tokens_per_block(c.E)));
   if (c.E <= 16) {
     // token chunks of the few-expert router weight gradient: about 320
@@ -120,7 +130,7 @@ Workspace workspace_layout(const moe_config& c) {
   L.d_o = o;         o += al((size_t)rows * c.D * esz);
   L.dact = o;        o += al((size_t)rows * 2 * c.F * esz);
   L.dx_perm = o;     o += al((size_t)rows * c.D * esz);
-  L.dg = o;          o += al((size_t)TK * 4);
+  L.dg = o;          o += al((size_t)TW * 4);
   L.ds = o;          o += al((size_t)c.T * c.E * 4);
   L.dxr = o;         o += (c.E > 16) ? al((size_t)c.T * c.D * 4) : 0;
   L.dwr_part = o;    o += al((size_t)L.dwr_splits * (((size_t)c.E * c.D + c.E + 3) & ~(size_t)3) * 4);
@@ -134,6 +144,7 @@ Workspace workspace_layout(const moe_config& c) {
   L.seq_part = o;    o += al((size_t)std::max(c.T, 1) * 4);
   L.seq_blk_n = o;   o += al((size_t)std::max(c.T, 1) * c.E * 4);
   L.seq_blk_p = o;   o += al((size_t)std::max(c.T, 1) * c.E * 4);
+  L.ec_keys = o;     o += ec ? al((size_t)(c.expert_hi - c.expert_lo) * std::max(c.T, 1) * 4) : 0;
   L.total = o;
   return L;
 }
@@ -161,7 +172,7 @@ int moe_rows_max(const moe_config* cfg, int64_t* rows) {
   int rc = check_cfg(cfg);
   if (rc) return rc;
   if (!rows) return MOE_EINVAL;
-  *rows = (int64_t)cfg->T * cfg->K + (int64_t)cfg->n_shared * cfg->T;
+  *rows = routed_rows_max(*cfg) + (int64_t)cfg->n_shared * cfg->T;
   return MOE_OK;
 }
 
@@ -179,6 +190,7 @@ int moe_route_ex(const moe_config* cfg, const void* x, const float* w_r, const f
                  float* topk_w, float* lse, int32_t flags, moe_stream_t stream) {
   int rc = check_cfg(cfg);
   if (rc) return rc;
+  if (cfg->routing != MOE_TOKEN_CHOICE) return MOE_EINVAL;
   if (flags & ~MOE_ROUTE_LOGITS_GIVEN) return MOE_EINVAL;
   const bool given = (flags & MOE_ROUTE_LOGITS_GIVEN) != 0;
   if (!given) { REQ(x); REQ(w_r); OPT(r_bias); }
@@ -202,12 +214,34 @@ int moe_route(const moe_config* cfg, const void* x, const float* w_r, const floa
                       topk_idx, topk_w, lse, flags, stream);
 }
 
+int moe_route_expert_choice(const moe_config* cfg, const void* x, const float* w_r,
+                            const float* r_bias, float* logits, float* gate_w, float* lse,
+                            int32_t* counts_all, int32_t* offsets, int32_t* slot_row,
+                            int32_t* row_token, int32_t* row_slot, void* x_perm, int32_t flags,
+                            void* ws, size_t ws_bytes, moe_stream_t stream) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (cfg->routing != MOE_EXPERT_CHOICE) return MOE_EINVAL;
+  if (flags & ~MOE_ROUTE_LOGITS_GIVEN) return MOE_EINVAL;
+  const bool given = (flags & MOE_ROUTE_LOGITS_GIVEN) != 0;
+  REQ(x);
+  if (!given) { REQ(w_r); OPT(r_bias); }
+  REQ(logits); REQ(gate_w); OPT(lse); REQ(counts_all); REQ(offsets); REQ(slot_row);
+  REQ(row_token); REQ(row_slot); REQ(x_perm); REQ(ws);
+  const Workspace L = workspace_layout(*cfg);
+  if (ws_bytes < L.total) return MOE_EWORKSPACE;
+  if (cfg->T == 0) return MOE_OK;
+  return launch_route_ec(*cfg, x, w_r, r_bias, logits, gate_w, lse, counts_all, offsets, slot_row,
+                         row_token, row_slot, x_perm, given, (char*)ws, L, (hipStream_t)stream);
+}
+
 int moe_permute(const moe_config* cfg, const int32_t* topk_idx, const void* x,
                 int32_t* counts_all, int32_t* offsets, int32_t* slot_row, int32_t* row_token,
                 int32_t* row_slot, int32_t* n_dropped, void* x_perm, void* ws, size_t ws_bytes,
                 moe_stream_t stream) {
   int rc = check_cfg(cfg);
   if (rc) return rc;
+  if (cfg->routing != MOE_TOKEN_CHOICE) return MOE_EINVAL;
   REQ(topk_idx); REQ(x); REQ(counts_all); REQ(offsets); REQ(slot_row); REQ(row_token);
   REQ(row_slot); REQ(n_dropped); REQ(x_perm); REQ(ws);
   const Workspace L = workspace_layout(*cfg);
@@ -258,6 +292,7 @@ int moe_bias_update(const moe_config* cfg, const int32_t* counts_all, float gamm
                     float* sel_bias, moe_stream_t stream) {
   int rc = check_cfg(cfg);
   if (rc) return rc;
+  if (cfg->routing != MOE_TOKEN_CHOICE) return MOE_EINVAL;
   if (!std::isfinite(gamma)) return MOE_EINVAL;
   REQ(counts_all); REQ(sel_bias);
   return launch_bias_update(*cfg, counts_all, gamma, sel_bias, (hipStream_t)stream);
@@ -268,6 +303,7 @@ int aux_seq_loss(const moe_config* cfg, const float* logits, const int32_t* topk
                  void* ws, size_t ws_bytes, moe_stream_t stream) {
   int rc = check_cfg(cfg);
   if (rc) return rc;
+  if (cfg->routing != MOE_TOKEN_CHOICE) return MOE_EINVAL;
   if (!std::isfinite(alpha) || seq_len <= 0) return MOE_EINVAL;
   if (cfg->T % seq_len) return MOE_EINVAL;
   REQ(logits); REQ(topk_idx); REQ(loss); OPT(d_logits); REQ(ws);
@@ -287,8 +323,11 @@ int moe_backward_ex(const moe_config* cfg, const void* x, const float* w_r, cons
                     float* d_logits_out, void* ws, size_t ws_bytes, moe_stream_t stream) {
   int rc = check_cfg(cfg);
   if (rc) return rc;
-  REQ(x); REQ(w_r); REQ(logits); REQ(topk_idx); REQ(topk_w); REQ(offsets); REQ(slot_row);
+  REQ(x); REQ(w_r); REQ(logits); REQ(topk_w); REQ(offsets); REQ(slot_row);
   REQ(x_perm); REQ(act); REQ(h); REQ(o_perm); REQ(dy);
+  // expert choice indexes its [T][E] tables by expert: no top-K list
+  if (cfg->routing == MOE_EXPERT_CHOICE) topk_idx = nullptr;
+  else REQ(topk_idx);
   OPT(d_logits_extra); OPT(jitter); REQ(dx); REQ(dw_r); OPT(d_rbias); OPT(d_logits_out); REQ(ws);
   if (groups(*cfg) > 0) {
     REQ(w_gate); REQ(w_up); REQ(w_down); REQ(dw_gate); REQ(dw_up); REQ(dw_down);

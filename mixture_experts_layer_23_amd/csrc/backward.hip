@@ -38,66 +38,85 @@ __global__ __launch_bounds__(256) void gating_bwd_kernel(
   const int t = gid / L, sub = gid % L;
   if (t >= T_) return;
   const float* s = logits + (size_t)t * E;
-  const int32_t* it = idx + (size_t)t * K;
   const float* g = gw + (size_t)t * K;
   const float* d = dg + (size_t)t * K;
-  float G = 0.f;
-  for (int k = 0; k < K; ++k) G = fmaf(g[k], d[k], G);
   float out[EPL];
 #pragma unroll
   for (int j = 0; j < EPL; ++j) out[j] = 0.f;
-  if (score == 0 && gating == 0) {
-    float sv[EPL], m = -INFINITY;
+  if (!idx) {
+    // expert choice: one slot per expert (K = E), g = p for every pair, so
+    // ds_e = p_e (dg_e - G) with G = sum_e p_e dg_e (lane partials, then a
+    // fixed shuffle tree)
+    float G = 0.f;
 #pragma unroll
     for (int j = 0; j < EPL; ++j) {
       const int e = sub + L * j;
-      sv[j] = (e < E) ? s[e] : -INFINITY;
-      m = fmaxf(m, sv[j]);
+      if (e < E) G = fmaf(g[e], d[e], G);
     }
 #pragma unroll
-    for (int o = L / 2; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-    float z = 0.f;
+    for (int o = L / 2; o >= 1; o >>= 1) G += __shfl_xor(G, o, 64);
 #pragma unroll
-    for (int j = 0; j < EPL; ++j)
-      if (sub + L * j < E) z += expf(sv[j] - m);
+    for (int j = 0; j < EPL; ++j) {
+      const int e = sub + L * j;
+      if (e < E) out[j] = g[e] * (d[e] - G);
+    }
+  } else {
+    const int32_t* it = idx + (size_t)t * K;
+    float G = 0.f;
+    for (int k = 0; k < K; ++k) G = fmaf(g[k], d[k], G);
+    if (score == 0 && gating == 0) {
+      float sv[EPL], m = -INFINITY;
 #pragma unroll
-    for (int o = L / 2; o >= 1; o >>= 1) z += __shfl_xor(z, o, 64);
-    float dp[EPL];
+      for (int j = 0; j < EPL; ++j) {
+        const int e = sub + L * j;
+        sv[j] = (e < E) ? s[e] : -INFINITY;
+        m = fmaxf(m, sv[j]);
+      }
 #pragma unroll
-    for (int j = 0; j < EPL; ++j) dp[j] = 0.f;
-    for (int k = 0; k < K; ++k) {
-      const int e = it[k];
-      if ((e % L) == sub) {
+      for (int o = L / 2; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+      float z = 0.f;
+#pragma unroll
+      for (int j = 0; j < EPL; ++j)
+        if (sub + L * j < E) z += expf(sv[j] - m);
+#pragma unroll
+      for (int o = L / 2; o >= 1; o >>= 1) z += __shfl_xor(z, o, 64);
+      float dp[EPL];
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) dp[j] = 0.f;
+      for (int k = 0; k < K; ++k) {
+        const int e = it[k];
+        if ((e % L) == sub) {
+          const int jj = e / L;
+#pragma unroll
+          for (int j = 0; j < EPL; ++j)
+            if (j == jj) dp[j] += d[k];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < EPL; ++j)
+        if (sub + L * j < E) out[j] = (expf(sv[j] - m) / z) * (dp[j] - G);
+    } else {
+      float S = 0.f;
+      if (score == 1 && gating == 1)
+        for (int k = 0; k < K; ++k) S += 1.0f / (1.0f + expf(-s[it[k]]));
+      for (int k = 0; k < K; ++k) {
+        const int e = it[k];
+        if ((e % L) != sub) continue;
+        float v;
+        if (score == 0) {
+          v = g[k] * (d[k] - G);
+        } else {
+          const float sg = 1.0f / (1.0f + expf(-s[e]));
+          const float dsig = sg * (1.0f - sg);
+          v = (gating == 0) ? d[k] * dsig : ((d[k] - G) / S) * dsig;
+        }
         const int jj = e / L;
 #pragma unroll
         for (int j = 0; j < EPL; ++j)
-          if (j == jj) dp[j] += d[k];
+          if (j == jj) out[j] = v;
       }
     }
-#pragma unroll
-    for (int j = 0; j < EPL; ++j)
-      if (sub + L * j < E) out[j] = (expf(sv[j] - m) / z) * (dp[j] - G);
-  } else {
-    float S = 0.f;
-    if (score == 1 && gating == 1)
-      for (int k = 0; k < K; ++k) S += 1.0f / (1.0f + expf(-s[it[k]]));
-    for (int k = 0; k < K; ++k) {
-      const int e = it[k];
-      if ((e % L) != sub) continue;
-      float v;
-      if (score == 0) {
-        v = g[k] * (d[k] - G);
-      } else {
-        const float sg = 1.0f / (1.0f + expf(-s[e]));
-        const float dsig = sg * (1.0f - sg);
-        v = (gating == 0) ? d[k] * dsig : ((d[k] - G) / S) * dsig;
-      }
-      const int jj = e / L;
-#pragma unroll
-      for (int j = 0; j < EPL; ++j)
-        if (j == jj) out[j] = v;
-    }
-  }
+  }  // token choice
 #pragma unroll
   for (int j = 0; j < EPL; ++j) {
     const int e = sub + L * j;
@@ -117,7 +136,7 @@ static int launch_gating_bwd_t(const moe_config& c, const float* lg, const int32
                                const float* jit, float* ds, float* ds_copy, hipStream_t st) {
   const int grid = (int)cdiv((int64_t)c.T * L, 256);
   MOE_LAUNCH("gating_bwd", (gating_bwd_kernel<L, EPL>), dim3(grid), dim3(256), 0, st, lg, idx,
-             gw, dg, dlx, jit, c.T, c.E, c.K, c.score_fn, c.gating, ds, ds_copy);
+             gw, dg, dlx, jit, c.T, c.E, slot_width(c), c.score_fn, c.gating, ds, ds_copy);
   return MOE_OK;
 }
 

@@ -18,8 +18,10 @@
 namespace moe {
 
 // y[t] = sum_k [row>=0] g[t,k] * o[row] + o[shared row of t]; one wave per
-// token, lane k holds slot k's row and weight, lanes stride over the row's
-// 16-byte vectors
+// token, lanes stride over the row's 16-byte vectors.  The slots are taken in
+// chunks of 64 (lane k holds slot k0+k's row and weight); a ballot of the
+// taken slots skips the dropped, sentinel and (expert choice) untaken ones,
+// and the kept slots are added in increasing k.
 template <typename T>
 __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ o,
                                                       const int32_t* __restrict__ slot_row,
@@ -31,24 +33,37 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ o,
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (t >= T_) return;
-  const int my_row = lane < K ? slot_row[(size_t)t * K + lane] : -1;
-  const float my_g = lane < K ? topk_w[(size_t)t * K + lane] : 0.f;
   const int64_t srow = n_shared ? (int64_t)offsets[EL] + t : -1;
-  for (int d0 = lane * VEC; d0 < D; d0 += 64 * VEC) {
+  // the first chunk (all slots when K <= 64) stays in registers over the
+  // row.  The d loop runs on the whole wave (lanes past D only skip their
+  // loads and stores) so that every ballot and shuffle sees all 64 slots.
+  const int row0 = lane < K ? slot_row[(size_t)t * K + lane] : -1;
+  const float g0 = lane < K ? topk_w[(size_t)t * K + lane] : 0.f;
+  const uint64_t m0 = __ballot(row0 >= 0);
+  for (int db = 0; db < D; db += 64 * VEC) {
+    const int d0 = db + lane * VEC;
+    const bool dok = d0 < D;
     float acc[VEC];
 #pragma unroll
     for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
-    for (int k = 0; k < K; ++k) {
-      const int row = __shfl(my_row, k, 64);
-      if (row < 0) continue;
-      const float g = __shfl(my_g, k, 64);
-      Vec16<T> v;
-      v.load(o + (size_t)row * D + d0);
-      float f[VEC];
-      v.to_f32(f);
+    for (int k0 = 0; k0 < K; k0 += 64) {
+      const int kk = k0 + lane;
+      const int my_row = k0 == 0 ? row0 : (kk < K ? slot_row[(size_t)t * K + kk] : -1);
+      const float my_g = k0 == 0 ? g0 : (kk < K ? topk_w[(size_t)t * K + kk] : 0.f);
+      for (uint64_t m = k0 == 0 ? m0 : __ballot(my_row >= 0); m; m &= m - 1) {
+        const int k = __builtin_ctzll(m);
+        const int row = __shfl(my_row, k, 64);
+        const float g = __shfl(my_g, k, 64);
+        if (!dok) continue;
+        Vec16<T> v;
+        v.load(o + (size_t)row * D + d0);
+        float f[VEC];
+        v.to_f32(f);
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) acc[i] = fmaf(g, f[i], acc[i]);
+        for (int i = 0; i < VEC; ++i) acc[i] = fmaf(g, f[i], acc[i]);
+      }
     }
+    if (!dok) continue;
     if (srow >= 0) {
       Vec16<T> v;
       v.load(o + (size_t)srow * D + d0);
@@ -63,8 +78,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ o,
   }
 }
 
-// one wave per token: dg[t,k] = dy_t . o[row] (0 for sentinel / dropped),
-// d_o[row] = g[t,k] * dy_t
+// one wave per token: dg[t,k] = dy_t . o[row] (0 for sentinel / dropped /
+// untaken slots), d_o[row] = g[t,k] * dy_t; slots in chunks of 64 as in the
+// combine
 template <typename T>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(const T* __restrict__ o,
                                                           const T* __restrict__ dy,
@@ -77,39 +93,43 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const T* __restrict__ 
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (t >= T_) return;
-  for (int k = 0; k < K; ++k) {
-    const int row = slot_row[(size_t)t * K + k];
-    if (row < 0) {  // uniform across the wave
-      if (lane == 0) dg[(size_t)t * K + k] = 0.f;
-      continue;
-    }
-    const float g = topk_w[(size_t)t * K + k];
-    float dot = 0.f;
-    for (int d0 = lane * VEC; d0 < D; d0 += 64 * VEC) {
-      Vec16<T> vy, vo;
-      vy.load(dy + (size_t)t * D + d0);
-      vo.load(o + (size_t)row * D + d0);
-      float fy[VEC], fo[VEC], fd[VEC];
-      vy.to_f32(fy);
-      vo.to_f32(fo);
+  for (int k0 = 0; k0 < K; k0 += 64) {
+    const int kk = k0 + lane;
+    const int my_row = kk < K ? slot_row[(size_t)t * K + kk] : -1;
+    const float my_g = kk < K ? topk_w[(size_t)t * K + kk] : 0.f;
+    if (kk < K && my_row < 0) dg[(size_t)t * K + kk] = 0.f;
+    for (uint64_t m = __ballot(my_row >= 0); m; m &= m - 1) {
+      const int k = __builtin_ctzll(m);
+      const int row = __shfl(my_row, k, 64);
+      const float g = __shfl(my_g, k, 64);
+      float dot = 0.f;
+      for (int d0 = lane * VEC; d0 < D; d0 += 64 * VEC) {
+        Vec16<T> vy, vo;
+        vy.load(dy + (size_t)t * D + d0);
+        vo.load(o + (size_t)row * D + d0);
+        float fy[VEC], fo[VEC], fd[VEC];
+        vy.to_f32(fy);
+        vo.to_f32(fo);
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) {
-        dot = fmaf(fy[i], fo[i], dot);
-        fd[i] = g * fy[i];
+        for (int i = 0; i < VEC; ++i) {
+          dot = fmaf(fy[i], fo[i], dot);
+          fd[i] = g * fy[i];
+        }
+        Vec16<T> vd;
+        vd.from_f32(fd);
+        vd.store(d_o + (size_t)row * D + d0);
       }
-      Vec16<T> vd;
-      vd.from_f32(fd);
-      vd.store(d_o + (size_t)row * D + d0);
-    }
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) dot += __shfl_xor(dot, m, 64);
-    if (lane == 0) dg[(size_t)t * K + k] = dot;
+      for (int mm = 32; mm >= 1; mm >>= 1) dot += __shfl_xor(dot, mm, 64);
+      if (lane == 0) dg[(size_t)t * K + k0 + k] = dot;
+    }
   }
 }
 
 // dx[t] = sum_k [row>=0] dx_perm[row] + dx_perm[shared row of t]
 //         + router part: sum_e ds[t,e] W_r[e,:] (inline for E <= EM) or dxr[t]
-// one wave per token, lanes stride over 16-byte vectors of the row
+// one wave per token, lanes stride over 16-byte vectors of the row; slots in
+// chunks of 64 as in the combine
 template <typename T, int EM>
 __global__ __launch_bounds__(256) void unpermute_kernel(
     const T* __restrict__ dxp, const int32_t* __restrict__ slot_row,
@@ -120,27 +140,35 @@ __global__ __launch_bounds__(256) void unpermute_kernel(
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (t >= T_) return;
-  const int my_row = lane < K ? slot_row[(size_t)t * K + lane] : -1;
   const int64_t srow = n_shared ? (int64_t)offsets[EL] + t : -1;
+  const int row0 = lane < K ? slot_row[(size_t)t * K + lane] : -1;
+  const uint64_t m0 = __ballot(row0 >= 0);
   float s_e[EM > 0 ? EM : 1];
   if constexpr (EM > 0) {
 #pragma unroll
     for (int e = 0; e < EM; ++e) s_e[e] = (e < E) ? ds[(size_t)t * E + e] : 0.f;
   }
-  for (int d0 = lane * VEC; d0 < D; d0 += 64 * VEC) {
+  for (int db = 0; db < D; db += 64 * VEC) {
+    const int d0 = db + lane * VEC;
+    const bool dok = d0 < D;
     float acc[VEC];
 #pragma unroll
     for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
-    for (int k = 0; k < K; ++k) {
-      const int row = __shfl(my_row, k, 64);
-      if (row < 0) continue;
-      Vec16<T> v;
-      v.load(dxp + (size_t)row * D + d0);
-      float f[VEC];
-      v.to_f32(f);
+    for (int k0 = 0; k0 < K; k0 += 64) {
+      const int kk = k0 + lane;
+      const int my_row = k0 == 0 ? row0 : (kk < K ? slot_row[(size_t)t * K + kk] : -1);
+      for (uint64_t m = k0 == 0 ? m0 : __ballot(my_row >= 0); m; m &= m - 1) {
+        const int row = __shfl(my_row, __builtin_ctzll(m), 64);
+        if (!dok) continue;
+        Vec16<T> v;
+        v.load(dxp + (size_t)row * D + d0);
+        float f[VEC];
+        v.to_f32(f);
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) acc[i] += f[i];
+        for (int i = 0; i < VEC; ++i) acc[i] += f[i];
+      }
     }
+    if (!dok) continue;
     if (srow >= 0) {
       Vec16<T> v;
       v.load(dxp + (size_t)srow * D + d0);
@@ -175,11 +203,11 @@ int launch_combine(const moe_config& c, const void* o_perm, const int32_t* offse
   const int grid = (int)cdiv(c.T, 4);
   if (c.dtype == MOE_BF16)
     MOE_LAUNCH("combine", combine_kernel<bf16_t>, dim3(grid), dim3(256), 0, st,
-               (const bf16_t*)o_perm, slot_row, topk_w, offsets, EL, c.n_shared, c.T, c.K, c.D,
+               (const bf16_t*)o_perm, slot_row, topk_w, offsets, EL, c.n_shared, c.T, slot_width(c), c.D,
                (bf16_t*)y);
   else
     MOE_LAUNCH("combine", combine_kernel<float>, dim3(grid), dim3(256), 0, st,
-               (const float*)o_perm, slot_row, topk_w, offsets, EL, c.n_shared, c.T, c.K, c.D,
+               (const float*)o_perm, slot_row, topk_w, offsets, EL, c.n_shared, c.T, slot_width(c), c.D,
                (float*)y);
   return MOE_OK;
 }
@@ -190,11 +218,11 @@ int launch_combine_bwd(const moe_config& c, const void* o_perm, const void* dy,
   const int grid = (int)cdiv(c.T, 4);
   if (c.dtype == MOE_BF16)
     MOE_LAUNCH("combine_bwd", combine_bwd_kernel<bf16_t>, dim3(grid), dim3(256), 0, st,
-               (const bf16_t*)o_perm, (const bf16_t*)dy, slot_row, topk_w, c.T, c.K, c.D, dg,
+               (const bf16_t*)o_perm, (const bf16_t*)dy, slot_row, topk_w, c.T, slot_width(c), c.D, dg,
                (bf16_t*)d_o);
   else
     MOE_LAUNCH("combine_bwd", combine_bwd_kernel<float>, dim3(grid), dim3(256), 0, st,
-               (const float*)o_perm, (const float*)dy, slot_row, topk_w, c.T, c.K, c.D, dg,
+               (const float*)o_perm, (const float*)dy, slot_row, topk_w, c.T, slot_width(c), c.D, dg,
                (float*)d_o);
   return MOE_OK;
 }
@@ -208,7 +236,7 @@ static int unpermute_t(const moe_config& c, const void* dxp, const int32_t* slot
   const int E = c.E;
 #define UNPERM(EMV)                                                                          \
   MOE_LAUNCH("unpermute_dx", (unpermute_kernel<T, EMV>), dim3(grid), dim3(256), 0, st,        \
-             (const T*)dxp, slot_row, offsets, EL, c.n_shared, ds, wr, E, dxr, c.T, c.K, c.D, \
+             (const T*)dxp, slot_row, offsets, EL, c.n_shared, ds, wr, E, dxr, c.T, slot_width(c), c.D, \
              (T*)dx)
   if (dxr) UNPERM(0);
   else if (E <= 4) UNPERM(4);

@@ -55,7 +55,7 @@ struct GemmParams {
   int ntn, ntm;       // tiles along N (and M for GROUP_K)
   int mt_total;       // m-tiles in the tile space (GROUP_M: an upper bound)
   int64_t nblocks;
-  int64_t routed_rows_max;  // T*K when the local experts exist, else 0
+  int64_t routed_rows_max;  // routed-row bound when local experts exist, else 0
   int64_t shared_rows;      // n_shared*T
   int n_routed;             // local routed groups
   // A operand: routed pointer (rows at offsets[g]) and shared pointer (row 0)
@@ -1825,7 +1825,7 @@ static GemmParams base_params(const moe_config& c, const int32_t* offsets) {
   P.G = groups_of(c);
   P.EL_A = P.EL_B = c.expert_hi - c.expert_lo;
   P.n_routed = c.expert_hi - c.expert_lo;
-  P.routed_rows_max = (P.n_routed > 0) ? (int64_t)c.T * c.K : 0;
+  P.routed_rows_max = (P.n_routed > 0) ? routed_rows_max(c) : 0;
   P.shared_rows = (int64_t)c.n_shared * c.T;
   P.offsets = offsets;
   P.F = c.F;

@@ -2,6 +2,7 @@
 #pragma once
 
 #include <algorithm>
+#include <cmath>
 #include <cstddef>
 
 #include "common.h"
@@ -13,16 +14,35 @@ struct Workspace {
   size_t tile_counts, tile_base;   // int32 [ntiles][E]
   size_t aux_part;                 // float [aux_blocks][E + 1]
   size_t d_o, dact, dx_perm;       // dtype rows buffers
-  size_t dg, ds;                   // float [T][K], [T][E]
+  size_t dg, ds;                   // float [T][W], [T][E]
   size_t dxr;                      // float [T][D] (router dgrad, large E)
   size_t dwr_part;                 // float [splits][E][D] (+ [splits][E] bias)
   size_t rb_part;                  // float [rb_splits][E rounded to 4] (large E)
   size_t seq_part;                 // float [T] per-sequence balance-loss partials
   size_t seq_blk_n, seq_blk_p;     // int32 / float [T][E] per-token-block partials
+  size_t ec_keys;                  // uint32 [EL][T] expert-choice selection keys
   size_t total;
   int ntiles, aux_blocks, dwr_splits, rb_splits;
 };
 Workspace workspace_layout(const moe_config& c);
+
+// slots per token in the slot tables: K (token choice) or E (expert choice,
+// one slot per token-expert pair)
+inline int slot_width(const moe_config& c) {
+  return c.routing == MOE_EXPERT_CHOICE ? c.E : c.K;
+}
+// expert choice: tokens taken by every expert, min(ceil(c T K / E), T) in
+// double, c = 1 when no capacity factor is given
+inline int64_t ec_capacity(const moe_config& c) {
+  const double cf = c.capacity_factor > 0.0 ? c.capacity_factor : 1.0;
+  const double v = std::ceil(cf * (double)c.T * (double)c.K / (double)c.E);
+  return v < (double)c.T ? (int64_t)v : (int64_t)c.T;
+}
+// bound on the routed rows (the shared expert's T rows come on top)
+inline int64_t routed_rows_max(const moe_config& c) {
+  if (c.routing == MOE_EXPERT_CHOICE) return (int64_t)(c.expert_hi - c.expert_lo) * ec_capacity(c);
+  return (int64_t)c.T * c.K;
+}
 
 constexpr int kSlotTile = 256;  // slots per histogram / rank tile
 // tokens per aux-loss workgroup: up to 64, with the [TB][E] probability tile
@@ -38,6 +58,19 @@ int launch_route(const moe_config& c, const void* x, const float* wr, const floa
                  const float* selb, const float* jit, const float* wn, const float* eps,
                  float* nlg, float* logits, int32_t* idx, float* w, float* lse, bool logits_given,
                  hipStream_t st);
+
+int launch_route_ec(const moe_config& c, const void* x, const float* wr, const float* rb,
+                    float* logits, float* w, float* lse, int32_t* counts_all, int32_t* offsets,
+                    int32_t* slot_row, int32_t* row_token, int32_t* row_slot, void* x_perm,
+                    bool logits_given, char* ws, const Workspace& L, hipStream_t st);
+// router logits out[T][E] = fl32(x W^T + b), fp64 accumulation (route.hip)
+int router_logits(const moe_config& c, const void* x, const float* wr, const float* rb,
+                  float* logits, hipStream_t st);
+// shared-expert row maps and the x_perm gather of the routed rows (permute.hip)
+int launch_shared_rows(const moe_config& c, const int32_t* offsets, int32_t* row_token,
+                       int32_t* row_slot, hipStream_t st);
+int launch_gather(const moe_config& c, const void* x, const int32_t* row_token,
+                  const int32_t* offsets, void* x_perm, hipStream_t st);
 
 int launch_permute(const moe_config& c, int capacity, const int32_t* idx, const void* x,
                    int32_t* counts_all, int32_t* offsets, int32_t* slot_row, int32_t* row_token,

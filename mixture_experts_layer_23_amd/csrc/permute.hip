@@ -201,13 +201,28 @@ int launch_permute(const moe_config& c, int capacity, const int32_t* idx, const 
              (size_t)(E + EL + 1) * sizeof(int32_t), st, idx, TK, c.K, E, c.expert_lo,
              c.expert_hi, capacity, nbits, c.n_shared, c.T, tile_base, counts_all, offsets,
              n_dropped, slot_row, row_token, row_slot);
+  int rc;
+  if ((rc = launch_shared_rows(c, offsets, row_token, row_slot, st))) return rc;
+  return launch_gather(c, x, row_token, offsets, x_perm, st);
+}
+
+int launch_shared_rows(const moe_config& c, const int32_t* offsets, int32_t* row_token,
+                       int32_t* row_slot, hipStream_t st) {
   if (c.n_shared > 0) {
     const int64_t n = (int64_t)c.n_shared * c.T;
     MOE_LAUNCH("permute_shared_rows", shared_rows_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256),
-               0, st, offsets, EL, c.T, c.n_shared, row_token, row_slot);
+               0, st, offsets, c.expert_hi - c.expert_lo, c.T, c.n_shared, row_token, row_slot);
   }
-  if (EL > 0) {
-    const int grid = (int)cdiv(TK, 4);
+  return MOE_OK;
+}
+
+// grid from the routed-row bound; rows at or beyond offsets[EL] exit
+int launch_gather(const moe_config& c, const void* x, const int32_t* row_token,
+                  const int32_t* offsets, void* x_perm, hipStream_t st) {
+  const int EL = c.expert_hi - c.expert_lo;
+  const int64_t rows = routed_rows_max(c);
+  if (EL > 0 && rows > 0) {
+    const int grid = (int)cdiv(rows, 4);
     if (c.dtype == MOE_BF16)
       MOE_LAUNCH("permute_gather", gather_kernel<bf16_t>, dim3(grid), dim3(256), 0, st,
                  (const bf16_t*)x, row_token, offsets, EL, c.D, (bf16_t*)x_perm);

@@ -368,8 +368,8 @@ static int launch_select(float* lg, const float* selb, const SelectExtras& x, in
 }
 
 // router logits out[T][E] = fl32(x W^T + b), fp64 accumulation
-static int router_logits(const moe_config& c, const void* x, const float* wr, const float* rb,
-                         float* logits, hipStream_t st) {
+int router_logits(const moe_config& c, const void* x, const float* wr, const float* rb,
+                  float* logits, hipStream_t st) {
   const int T_ = c.T, D = c.D, E = c.E;
   {
     if (E <= 16 && (size_t)E * D * 4 <= 128 * 1024) {

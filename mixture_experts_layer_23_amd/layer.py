@@ -2,7 +2,8 @@
 only), every computation is a call into ``libmoe_mi355x.so``.
 
 Forward:  moe_route -> moe_permute -> moe_expert_ffn -> moe_combine
-          (+ aux_balance_loss when a balance or z-loss coefficient is set)
+          (+ aux_balance_loss when a balance or z-loss coefficient is set);
+          expert choice: moe_route_expert_choice -> moe_expert_ffn -> moe_combine
 Backward: moe_backward (with the aux-loss logit gradient as d_logits_extra)
 """
 from __future__ import annotations
@@ -33,11 +34,21 @@ class LayerSpec:
     seq_len: int = 0          # sequence-wise balance loss over sequences of this length (0: off)
     seq_alpha: float = 0.0
     bias_gamma: float = 0.0   # load-driven selection-bias step after each routing (0: off)
+    routing: int = L.MOE_TOKEN_CHOICE  # MOE_EXPERT_CHOICE: experts pick tokens (gating A)
 
     def config(self) -> L.MoeConfig:
         return L.make_config(self.T, self.D, self.E, self.K, self.F, self.lo,
                              self.E if self.hi < 0 else self.hi, self.n_shared, self.score,
-                             self.gating, self.dtype, self.cap)
+                             self.gating, self.dtype, self.cap, self.routing)
+
+    @property
+    def expert_choice(self) -> bool:
+        return self.routing == L.MOE_EXPERT_CHOICE
+
+    @property
+    def width(self) -> int:
+        """Slots per token in the slot tables: K, or E under expert choice."""
+        return self.E if self.expert_choice else self.K
 
     @property
     def groups(self) -> int:
@@ -70,13 +81,14 @@ class MoELayer:
         G = s.groups
         f32, i32 = torch.float32, torch.int32
         z = lambda *shape, dt: torch.empty(*shape, dtype=dt, device=self.dev)
+        W = s.width
         self.logits = z(T1, s.E, dt=f32)
-        self.topk_idx = z(T1, s.K, dt=i32)
-        self.topk_w = z(T1, s.K, dt=f32)
+        self.topk_idx = z(T1, s.K, dt=i32) if not s.expert_choice else None
+        self.topk_w = z(T1, W, dt=f32)
         self.lse = z(T1, dt=f32)
         self.counts = z(s.E, dt=i32)
         self.offsets = z(G + 1, dt=i32)
-        self.slot_row = z(T1 * s.K, dt=i32)
+        self.slot_row = z(T1 * W, dt=i32)
         self.row_token = z(rows, dt=i32)
         self.row_slot = z(rows, dt=i32)
         self.n_dropped = z(4, dt=i32)
@@ -106,7 +118,8 @@ class MoELayer:
 
     @property
     def use_seq(self) -> bool:
-        return self.spec.seq_len > 0 and self.spec.seq_alpha != 0
+        return (self.spec.seq_len > 0 and self.spec.seq_alpha != 0
+                and not self.spec.expert_choice)
 
     @property
     def has_dlogits(self) -> bool:
@@ -128,9 +141,16 @@ class MoELayer:
         """jitter / noise_eps: the step's random draws ([T][E] fp32) for the
         router-logit jitter and the noisy top-K selection (None: off)."""
         self.x = x
-        self.route(x, logits_given, jitter, noise_eps)
-        L.moe_permute(self.cfg, self.topk_idx, x, self.counts, self.offsets, self.slot_row,
-                      self.row_token, self.row_slot, self.n_dropped, self.x_perm, self.ws)
+        if self.spec.expert_choice:
+            self.jitter = None
+            L.moe_route_expert_choice(self.cfg, x, self.w_r, self.r_bias, self.logits,
+                                      self.topk_w, self.lse, self.counts, self.offsets,
+                                      self.slot_row, self.row_token, self.row_slot, self.x_perm,
+                                      self.ws, L.MOE_ROUTE_LOGITS_GIVEN if logits_given else 0)
+        else:
+            self.route(x, logits_given, jitter, noise_eps)
+            L.moe_permute(self.cfg, self.topk_idx, x, self.counts, self.offsets, self.slot_row,
+                          self.row_token, self.row_slot, self.n_dropped, self.x_perm, self.ws)
         L.moe_expert_ffn(self.cfg, x, self.x_perm, self.offsets, self.w_gate, self.w_up,
                          self.w_down, self.act, self.h, self.o_perm)
         L.moe_combine(self.cfg, self.o_perm, self.offsets, self.slot_row, self.topk_w, self.y)
@@ -141,7 +161,8 @@ class MoELayer:
             L.aux_seq_loss(self.cfg, self.logits, self.topk_idx, self.spec.seq_len,
                            self.spec.seq_alpha, self.seq_loss, self.dlogits_aux,
                            self.use_aux, self.ws)
-        if self.spec.bias_gamma != 0 and self.sel_bias is not None:
+        if (self.spec.bias_gamma != 0 and self.sel_bias is not None
+                and not self.spec.expert_choice):
             L.moe_bias_update(self.cfg, self.counts, self.spec.bias_gamma, self.sel_bias)
         return self.y
 
