@@ -131,9 +131,93 @@ __global__ __launch_bounds__(1024) void aux_final_kernel(const float* __restrict
   }
 }
 
+// Few experts, few tokens: one workgroup of NT threads does both levels.
+// Thread i takes tokens i, i + NT, ... (the E <= EM logits of a token in
+// registers), keeps its own column sums, and the workgroup adds them in a
+// fixed tree.
+constexpr int kAuxSingleTokens = 16384;
+template <int EM, int NT>
+__global__ __launch_bounds__(NT) void aux_single_kernel(const float* __restrict__ logits,
+                                                          const int32_t* __restrict__ counts,
+                                                          int T_, int E, int K, float alpha,
+                                                          float zlam, float* __restrict__ losses,
+                                                          float* __restrict__ dlog) {
+  __shared__ float red[NT / 64][EM + 1];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float ucoef = alpha * (float)E / ((float)T_ * (float)K) / (float)T_;
+  float u[EM], P[EM];
+#pragma unroll
+  for (int e = 0; e < EM; ++e) {
+    u[e] = (e < E) ? ucoef * (float)counts[e] : 0.f;
+    P[e] = 0.f;
+  }
+  float z2 = 0.f;
+  for (int t = tid; t < T_; t += NT) {
+    const float* s = logits + (size_t)t * E;
+    float sv[EM], m = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < EM; ++e) {
+      sv[e] = (e < E) ? s[e] : -INFINITY;
+      m = fmaxf(m, sv[e]);
+    }
+    float z = 0.f;
+#pragma unroll
+    for (int e = 0; e < EM; ++e)
+      if (e < E) z += expf(sv[e] - m);
+    const float lse = m + logf(z);
+    z2 += lse * lse;
+    float pu = 0.f;
+#pragma unroll
+    for (int e = 0; e < EM; ++e) {
+      sv[e] = (e < E) ? expf(sv[e] - m) / z : 0.f;  // p
+      P[e] += sv[e];
+      pu += sv[e] * u[e];
+    }
+    if (dlog) {
+#pragma unroll
+      for (int e = 0; e < EM; ++e)
+        if (e < E)
+          dlog[(size_t)t * E + e] =
+              sv[e] * (u[e] - pu) + zlam * (2.0f / (float)T_) * lse * sv[e];
+    }
+  }
+#pragma unroll
+  for (int e = 0; e <= EM; ++e) {
+    float v = e < EM ? P[e] : z2;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    if (lane == 0) red[wave][e] = v;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float col[EM + 1];
+#pragma unroll
+    for (int e = 0; e <= EM; ++e) {
+      col[e] = 0.f;
+      for (int w = 0; w < NT / 64; ++w) col[e] += red[w][e];
+    }
+    float v = 0.f;
+#pragma unroll
+    for (int e = 0; e < EM; ++e)
+      if (e < E) v += ((float)counts[e] / ((float)T_ * (float)K)) * (col[e] / (float)T_);
+    losses[0] = alpha * (float)E * v;
+    losses[1] = zlam * col[EM] / (float)T_;
+    losses[2] = col[EM] / (float)T_;
+  }
+}
+
 int launch_aux(const moe_config& c, const float* logits, const int32_t* counts_all, float alpha,
                float zlam, float* losses, float* d_logits, char* ws, const Workspace& L,
                hipStream_t st) {
+  if (c.E <= 8 && c.T <= kAuxSingleTokens) {
+#define AUX1(EMV, NTV)                                                                        \
+  MOE_LAUNCH("aux_single", (aux_single_kernel<EMV, NTV>), dim3(1), dim3(NTV), 0, st, logits,  \
+             counts_all, c.T, c.E, c.K, alpha, zlam, losses, d_logits)
+    if (c.E <= 4) AUX1(4, 1024);
+    else AUX1(8, 512);
+#undef AUX1
+    return MOE_OK;
+  }
   float* part = reinterpret_cast<float*>(ws + L.aux_part);
   const int TB = aux_tokens_per_block(c.E);
   const size_t shm = ((size_t)TB * c.E + 4 * (size_t)TB) * sizeof(float);

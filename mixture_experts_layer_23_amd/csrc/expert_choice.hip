@@ -89,6 +89,10 @@ constexpr int kEcWaves = kEcThreads / 64;
 // three passes v* is the C-th largest code, `need` the number of tokens with
 // code == v* that are taken (the lowest tokens first) and every code > v* is
 // taken.  The compaction then walks the tokens in order, 1024 at a time.
+// Keys are read as ordered codes; with R > 0 they stay in registers.
+// R > 0: the expert's keys (R * 1024 >= T) are loaded once into registers;
+// R == 0: every pass reads them from memory.
+template <int R>
 __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(
     const uint32_t* __restrict__ keys, int T_, int E, int lo, int C,
     int32_t* __restrict__ slot_row, int32_t* __restrict__ row_token,
@@ -100,6 +104,19 @@ __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(
   const uint32_t* kp = keys + (size_t)g * T_;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint64_t lt = lane ? (~0ull >> (64 - lane)) : 0ull;
+  const int nr = R ? R : (T_ + kEcThreads - 1) / kEcThreads;
+  uint32_t kr[R ? R : 1];
+  if constexpr (R > 0) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int t = r * kEcThreads + tid;
+      kr[r] = t < T_ ? kp[t] : 0u;
+    }
+  }
+  auto key = [&](int r, int t) __attribute__((always_inline)) {
+    if constexpr (R > 0) return kr[r];
+    else return t < T_ ? kp[t] : 0u;
+  };
   uint32_t prefix = 0, pmask = 0;
   int need = C;
   for (int pass = 0; pass < 3; ++pass) {
@@ -112,9 +129,11 @@ __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(
       sel_above = 0;
     }
     __syncthreads();
-    for (int t0 = 0; t0 < T_; t0 += kEcThreads) {
-      const int t = t0 + tid;
-      const uint32_t u = t < T_ ? kp[t] : 0u;
+#pragma unroll
+    for (int r = 0; r < nr; ++r) {
+      const int t = r * kEcThreads + tid;
+      if (r * kEcThreads >= T_) break;  // uniform
+      const uint32_t u = key(r, t);
       const bool in = t < T_ && (u & pmask) == prefix;
       const uint32_t dg = (u >> shift) & dmask;
       const uint64_t act = __ballot(in);
@@ -161,10 +180,12 @@ __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(
   }
   const uint32_t vstar = prefix;
   int carry_eq = 0, carry_tk = 0;
-  for (int t0 = 0; t0 < T_; t0 += kEcThreads) {
-    const int t = t0 + tid;
+#pragma unroll
+  for (int r = 0; r < nr; ++r) {
+    const int t = r * kEcThreads + tid;
+    if (r * kEcThreads >= T_) break;  // uniform
     const bool valid = t < T_;
-    const uint32_t u = valid ? kp[t] : 0u;
+    const uint32_t u = valid ? key(r, t) : 0u;
     const bool eq = valid && u == vstar;
     const uint64_t beq = __ballot(eq);
     if (lane == 0) wsum[wave] = __popcll(beq);
@@ -237,9 +258,15 @@ int launch_route_ec(const moe_config& c, const void* x, const float* wr, const f
   else TOK(64, 16);
 #undef TOK
   if (rc) return rc;
-  if (EL > 0 && C > 0)
-    MOE_LAUNCH("ec_select", ec_select_kernel, dim3(EL), dim3(kEcThreads), 0, st, keys, c.T, E,
-               c.expert_lo, C, slot_row, row_token, row_slot);
+  if (EL > 0 && C > 0) {
+#define SEL(Rv)                                                                                \
+  MOE_LAUNCH("ec_select", ec_select_kernel<Rv>, dim3(EL), dim3(kEcThreads), 0, st, keys, c.T, E, \
+             c.expert_lo, C, slot_row, row_token, row_slot)
+    if (c.T <= 4 * kEcThreads) SEL(4);
+    else if (c.T <= 16 * kEcThreads) SEL(16);
+    else SEL(0);
+#undef SEL
+  }
   if ((rc = launch_shared_rows(c, offsets, row_token, row_slot, st))) return rc;
   return launch_gather(c, x, row_token, offsets, x_perm, st);
 }

@@ -152,6 +152,143 @@ __global__ __launch_bounds__(64) void rank_kernel(const int32_t* __restrict__ id
   }
 }
 
+// One-workgroup permute for small slot counts (hist + scan + rank in one
+// launch).  Wave w owns the contiguous slot chunk [w*CH, (w+1)*CH), CH a
+// multiple of 64, and walks it 64 slots at a time with its own per-expert
+// counters (wave-private LDS, updated by the lane that closes each group of
+// equal experts).  Pass 1 counts; the workgroup then forms the expert totals,
+// the capacity-limited offsets (as rank_kernel does) and every wave's base
+// per expert (the counts of the waves before it); pass 2 walks the chunk
+// again and assigns positions.  Chunks are in slot order, so the positions
+// are the stable in-expert ranks of the tiled path.
+constexpr int kSmallThreads = 1024;
+constexpr int kSmallWaves = kSmallThreads / 64;
+constexpr int64_t kSmallSlots = 32768;  // up to 32 groups of 64 slots per wave
+constexpr int kSmallExperts = 256;      // LDS: (17 E + EL + 1) int32
+
+MOE_DEV uint64_t same_expert_peers(bool valid, int e, int nbits) {
+  uint64_t peers = __ballot(valid);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t bb = __ballot(bit);
+    peers &= bit ? bb : ~bb;
+  }
+  return valid ? peers : 0ull;
+}
+
+template <int R>  // groups of 64 slots per wave, held in registers (16 * 64 * R >= TK)
+__global__ __launch_bounds__(kSmallThreads) void permute_small_kernel(
+    const int32_t* __restrict__ idx, int TK, int K, int E, int lo, int hi, int capacity,
+    int nbits, int n_shared, int T_, int32_t* __restrict__ counts_all,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ n_dropped,
+    int32_t* __restrict__ slot_row, int32_t* __restrict__ row_token,
+    int32_t* __restrict__ row_slot) {
+  extern __shared__ int32_t lds[];
+  const int EL = hi - lo;
+  int32_t* cnt = lds;                       // [E] slots per expert
+  int32_t* off = cnt + E;                   // [EL + 1] group offsets
+  int32_t* wc = off + EL + 1;               // [16][E] wave counts, then wave bases
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint64_t lt = lane ? (~0ull >> (64 - lane)) : 0ull;
+  int32_t* mine = wc + wave * E;            // this wave's counters
+  const int s_begin = wave * R * 64;
+  int ev[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int s = s_begin + r * 64 + lane;
+    ev[r] = s < TK ? idx[s] : -1;
+  }
+  for (int e = lane; e < E; e += 64) mine[e] = 0;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const bool valid = ev[r] >= 0;
+    const int e = valid ? ev[r] : 0;
+    const uint64_t peers = same_expert_peers(valid, e, nbits);
+    if (valid && (63 - __clzll(peers)) == lane) mine[e] += __popcll(peers);
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+  }
+  __syncthreads();
+  // expert totals and per-wave bases (exclusive scan over the 16 waves)
+  for (int x = tid; x < E; x += kSmallThreads) {
+    int r = 0;
+    for (int w = 0; w < kSmallWaves; ++w) {
+      const int c = wc[w * E + x];
+      wc[w * E + x] = r;
+      r += c;
+    }
+    cnt[x] = r;
+    counts_all[x] = r;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const int per = (EL + 63) / 64;
+    int kept = 0, drop = 0;
+    for (int i = 0; i < per; ++i) {
+      const int e = lane * per + i;
+      if (e < EL) {
+        const int n = cnt[lo + e];
+        const int k = (capacity >= 0 && n > capacity) ? capacity : n;
+        kept += k;
+        drop += n - k;
+      }
+    }
+    int incl = kept;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += u;
+    }
+    int r = incl - kept;
+    for (int i = 0; i < per; ++i) {
+      const int e = lane * per + i;
+      if (e < EL) {
+        off[e] = r;
+        offsets[e] = r;
+        const int n = cnt[lo + e];
+        r += (capacity >= 0 && n > capacity) ? capacity : n;
+      }
+    }
+    const int total = __shfl(incl, 63, 64);
+    if (lane == 0) {
+      off[EL] = total;
+      offsets[EL] = total;
+    }
+    for (int sh = lane; sh < n_shared; sh += 64) offsets[EL + 1 + sh] = total + (sh + 1) * T_;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) drop += __shfl_xor(drop, o, 64);
+    if (lane == 0) *n_dropped = drop;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int s = s_begin + r * 64 + lane;
+    const bool valid = ev[r] >= 0;
+    const int e = valid ? ev[r] : 0;
+    const uint64_t peers = same_expert_peers(valid, e, nbits);
+    const int pos = valid ? mine[e] + __popcll(peers & lt) : 0;
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    if (valid && (63 - __clzll(peers)) == lane) mine[e] += __popcll(peers);
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    if (valid) {
+      if (e < lo || e >= hi) {
+        slot_row[s] = -2;
+      } else if (capacity >= 0 && pos >= capacity) {
+        slot_row[s] = -1;
+      } else {
+        const int row = off[e - lo] + pos;
+        slot_row[s] = row;
+        row_token[row] = s / K;
+        row_slot[row] = s;
+      }
+    }
+  }
+}
+
 // shared-expert rows: one per token, after the routed rows
 __global__ void shared_rows_kernel(const int32_t* __restrict__ offsets, int EL, int T_,
                                    int n_shared, int32_t* __restrict__ row_token,
@@ -193,6 +330,21 @@ int launch_permute(const moe_config& c, int capacity, const int32_t* idx, const 
   int32_t* tile_base = reinterpret_cast<int32_t*>(ws + L.tile_base);
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
+  int rc;
+  if (TK <= kSmallSlots && E <= kSmallExperts) {
+    const size_t shm = (size_t)(E + EL + 1 + kSmallWaves * E) * sizeof(int32_t);
+#define SMALL(Rv)                                                                              \
+  MOE_LAUNCH("permute_small", permute_small_kernel<Rv>, dim3(1), dim3(kSmallThreads), shm, st, \
+             idx, (int)TK, c.K, E, c.expert_lo, c.expert_hi, capacity, nbits, c.n_shared, c.T,  \
+             counts_all, offsets, n_dropped, slot_row, row_token, row_slot)
+    if (TK <= 4 * kSmallThreads) SMALL(4);
+    else if (TK <= 8 * kSmallThreads) SMALL(8);
+    else if (TK <= 16 * kSmallThreads) SMALL(16);
+    else SMALL(32);
+#undef SMALL
+    if ((rc = launch_shared_rows(c, offsets, row_token, row_slot, st))) return rc;
+    return launch_gather(c, x, row_token, offsets, x_perm, st);
+  }
   MOE_LAUNCH("permute_hist", hist_kernel, dim3(L.ntiles), dim3(256), E * sizeof(int32_t), st, idx,
              TK, E, tile_counts);
   MOE_LAUNCH("permute_scan", scan_tiles_kernel, dim3(E), dim3(256), 0, st, tile_counts,
@@ -201,7 +353,6 @@ int launch_permute(const moe_config& c, int capacity, const int32_t* idx, const 
              (size_t)(E + EL + 1) * sizeof(int32_t), st, idx, TK, c.K, E, c.expert_lo,
              c.expert_hi, capacity, nbits, c.n_shared, c.T, tile_base, counts_all, offsets,
              n_dropped, slot_row, row_token, row_slot);
-  int rc;
   if ((rc = launch_shared_rows(c, offsets, row_token, row_slot, st))) return rc;
   return launch_gather(c, x, row_token, offsets, x_perm, st);
 }

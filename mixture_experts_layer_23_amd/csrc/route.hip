@@ -11,6 +11,56 @@
 namespace moe {
 
 // ---------------------------------------------------------------------------
+// sig32: the fixed binary32 sigmoid of the selection key (no contraction; the
+// only fma are the explicit ones).  exp32(z): clamp to [-87, 87];
+// n = rint(z * log2e); r = (z - n*L1) then fma(-n, L2, r) with L1 + L2 = ln 2
+// and n*L1 exact (L1 has 15 significant bits); Taylor degree 7 of e^r with
+// coefficients 1/k! in binary32, Horner with fma; times 2^n from exponent
+// bits.  sig32(z) = 1 / (1 + exp32(-z)) with IEEE division.
+// ---------------------------------------------------------------------------
+MOE_DEV float sig32(float z) {
+#pragma clang fp contract(off)
+  const float LOG2E = 1.44269502162933349609375f;
+  const float L1 = 0.693145751953125f;
+  const float L2 = 1.428606765330187045037746429443359375e-06f;
+  float u = -z;
+  u = u > 87.0f ? 87.0f : u;
+  u = u < -87.0f ? -87.0f : u;
+  const float t = u * LOG2E;
+  const float n = __builtin_rintf(t);
+  const float nl1 = n * L1;
+  float r = u - nl1;
+  r = __builtin_fmaf(-n, L2, r);
+  float p = (float)(1.0 / 5040.0);
+  p = __builtin_fmaf(p, r, (float)(1.0 / 720.0));
+  p = __builtin_fmaf(p, r, (float)(1.0 / 120.0));
+  p = __builtin_fmaf(p, r, (float)(1.0 / 24.0));
+  p = __builtin_fmaf(p, r, (float)(1.0 / 6.0));
+  p = __builtin_fmaf(p, r, 0.5f);
+  p = __builtin_fmaf(p, r, 1.0f);
+  p = __builtin_fmaf(p, r, 1.0f);
+  const float s = __uint_as_float((uint32_t)((int)n + 127) << 23);
+  const float e = p * s;
+  const float d = 1.0f + e;
+  return 1.0f / d;
+}
+
+MOE_DEV bool better(float ka, int ia, float kb, int ib) {
+  return (ka > kb) || (ka == kb && ia < ib);
+}
+
+// Selection fused into the few-expert router: when idx is set, the lane that
+// holds a token's logits also takes its top-K, gate weights and lse (the same
+// keys, tie rule and weight definitions as route_select_kernel below).
+struct FusedSelect {
+  const float* selb;
+  int32_t* idx;
+  float* w;
+  float* lse;
+  int K, score, gating;
+};
+
+// ---------------------------------------------------------------------------
 // Router logits.  Products of a bf16/fp32 activation and an fp32 weight are
 // exact in double, the sum is accumulated in double and rounded once to
 // binary32, so the result is (up to a ~1e-12 relative accumulation error) the
@@ -27,7 +77,7 @@ __global__ __launch_bounds__(256) void router_skinny_kernel(const T* __restrict_
                                                             const float* __restrict__ wr,
                                                             const float* __restrict__ rb,
                                                             float* __restrict__ logits, int T_,
-                                                            int D, int E) {
+                                                            int D, int E, FusedSelect fs) {
   extern __shared__ float4 sw4[];
   float* sw = reinterpret_cast<float*>(sw4);
   const int n4 = (E * D) >> 2;
@@ -84,6 +134,50 @@ __global__ __launch_bounds__(256) void router_skinny_kernel(const T* __restrict_
       const double b = rb ? (double)rb[lane] : 0.0;
       logits[(size_t)t0 * E + lane] = (float)(a0 + b);
       if (two) logits[(size_t)(t0 + 1) * E + lane] = (float)(a1 + b);
+    }
+    if (fs.idx && (lane == 0 || (lane == 1 && two))) {
+      // lane 0 selects for token t0, lane 1 for t0 + 1; every lane holds
+      // all E sums after the reduction
+      const int t = t0 + lane;
+      float sv[EM], key[EM];
+      bool used[EM];
+      float m = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < EM; ++e) {
+        const bool ok = e < E;
+        const double a = lane == 0 ? acc0[e] : acc1[e];
+        sv[e] = ok ? (float)(a + (rb ? (double)rb[e] : 0.0)) : -INFINITY;
+        key[e] = fs.score == 0 ? sv[e]
+                               : (ok ? sig32(sv[e]) + (fs.selb ? fs.selb[e] : 0.0f) : -INFINITY);
+        used[e] = !ok;
+        m = fmaxf(m, sv[e]);
+      }
+      float z = 0.f;
+#pragma unroll
+      for (int e = 0; e < EM; ++e)
+        if (e < E) z += expf(sv[e] - m);
+      if (fs.lse) fs.lse[t] = m + logf(z);
+      float gsum = 0.f;
+      for (int k = 0; k < fs.K; ++k) {
+        float bk = -INFINITY, sc = -INFINITY;
+        int bi = 0x7fffffff;
+#pragma unroll
+        for (int e = 0; e < EM; ++e)
+          if (!used[e] && better(key[e], e, bk, bi)) { bk = key[e]; bi = e; sc = sv[e]; }
+        bi = bi < E ? bi : 0;  // only reachable with non-finite logits (outside the contract)
+#pragma unroll
+        for (int e = 0; e < EM; ++e)
+          if (e == bi) used[e] = true;
+        const float g = fs.score == 0 ? expf(sc - m) : 1.0f / (1.0f + expf(-sc));
+        gsum += g;
+        fs.idx[(size_t)t * fs.K + k] = bi;
+        fs.w[(size_t)t * fs.K + k] = g;
+      }
+      float den = 1.f;
+      if (fs.score == 0) den = (fs.gating == 0) ? z : gsum;
+      else den = (fs.gating == 0) ? 1.f : gsum;
+      if (!(fs.score == 1 && fs.gating == 0))
+        for (int k = 0; k < fs.K; ++k) fs.w[(size_t)t * fs.K + k] = fs.w[(size_t)t * fs.K + k] / den;
     }
   }
 }
@@ -206,49 +300,10 @@ __global__ __launch_bounds__(256) void router_tiled_kernel(const T* __restrict__
 }
 
 // ---------------------------------------------------------------------------
-// sig32: the fixed binary32 sigmoid of the selection key (no contraction; the
-// only fma are the explicit ones).  exp32(z): clamp to [-87, 87];
-// n = rint(z * log2e); r = (z - n*L1) then fma(-n, L2, r) with L1 + L2 = ln 2
-// and n*L1 exact (L1 has 15 significant bits); Taylor degree 7 of e^r with
-// coefficients 1/k! in binary32, Horner with fma; times 2^n from exponent
-// bits.  sig32(z) = 1 / (1 + exp32(-z)) with IEEE division.
-// ---------------------------------------------------------------------------
-MOE_DEV float sig32(float z) {
-#pragma clang fp contract(off)
-  const float LOG2E = 1.44269502162933349609375f;
-  const float L1 = 0.693145751953125f;
-  const float L2 = 1.428606765330187045037746429443359375e-06f;
-  float u = -z;
-  u = u > 87.0f ? 87.0f : u;
-  u = u < -87.0f ? -87.0f : u;
-  const float t = u * LOG2E;
-  const float n = __builtin_rintf(t);
-  const float nl1 = n * L1;
-  float r = u - nl1;
-  r = __builtin_fmaf(-n, L2, r);
-  float p = (float)(1.0 / 5040.0);
-  p = __builtin_fmaf(p, r, (float)(1.0 / 720.0));
-  p = __builtin_fmaf(p, r, (float)(1.0 / 120.0));
-  p = __builtin_fmaf(p, r, (float)(1.0 / 24.0));
-  p = __builtin_fmaf(p, r, (float)(1.0 / 6.0));
-  p = __builtin_fmaf(p, r, 0.5f);
-  p = __builtin_fmaf(p, r, 1.0f);
-  p = __builtin_fmaf(p, r, 1.0f);
-  const float s = __uint_as_float((uint32_t)((int)n + 127) << 23);
-  const float e = p * s;
-  const float d = 1.0f + e;
-  return 1.0f / d;
-}
-
-// ---------------------------------------------------------------------------
 // Selection and gate weights: L lanes per token (L = min(64, pow2ceil(E))),
 // EPL experts per lane (expert e = sub + L*j).  K rounds of a group-wide
 // arg-max on (key, index) with equal keys going to the lower index.
 // ---------------------------------------------------------------------------
-MOE_DEV bool better(float ka, int ia, float kb, int ib) {
-  return (ka > kb) || (ka == kb && ia < ib);
-}
-
 // softplus in double, the overflow-free form log(1 + e^n) = max(n, 0) +
 // log1p(e^-|n|)
 MOE_DEV double softplus64(double n) { return fmax(n, 0.0) + log1p(exp(-fabs(n))); }
@@ -368,11 +423,16 @@ static int launch_select(float* lg, const float* selb, const SelectExtras& x, in
 }
 
 // router logits out[T][E] = fl32(x W^T + b), fp64 accumulation
-int router_logits(const moe_config& c, const void* x, const float* wr, const float* rb,
-                  float* logits, hipStream_t st) {
+// the few-expert router can take the selection as well (fsp != nullptr);
+// returns 1 (nothing launched) when it cannot, so the caller selects apart
+static int router_logits_sel(const moe_config& c, const void* x, const float* wr,
+                             const float* rb, float* logits, const FusedSelect* fsp,
+                             hipStream_t st) {
   const int T_ = c.T, D = c.D, E = c.E;
   {
     if (E <= 16 && (size_t)E * D * 4 <= 128 * 1024) {
+      const FusedSelect fs = fsp ? *fsp : FusedSelect{nullptr, nullptr, nullptr, nullptr, 0, 0, 0};
+      const char* name = fsp ? "route_fused" : "router_logits";
       const int waves_needed = (int)cdiv(T_, 2);
       int grid = (int)std::min<int64_t>(cdiv(waves_needed, 4), 2048);
       const size_t shm = (size_t)E * D * 4;
@@ -396,15 +456,16 @@ int router_logits(const moe_config& c, const void* x, const float* wr, const flo
         if (lim != hipSuccess) { set_error("router_logits (LDS limit)", lim); return MOE_ELAUNCH; }
       }
       if (c.dtype == MOE_BF16) {
-        if (E <= 4) MOE_LAUNCH("router_logits", (router_skinny_kernel<bf16_t, 4>), dim3(grid), dim3(256), shm, st, (const bf16_t*)x, wr, rb, logits, T_, D, E);
-        else if (E <= 8) MOE_LAUNCH("router_logits", (router_skinny_kernel<bf16_t, 8>), dim3(grid), dim3(256), shm, st, (const bf16_t*)x, wr, rb, logits, T_, D, E);
-        else MOE_LAUNCH("router_logits", (router_skinny_kernel<bf16_t, 16>), dim3(grid), dim3(256), shm, st, (const bf16_t*)x, wr, rb, logits, T_, D, E);
+        if (E <= 4) MOE_LAUNCH(name, (router_skinny_kernel<bf16_t, 4>), dim3(grid), dim3(256), shm, st, (const bf16_t*)x, wr, rb, logits, T_, D, E, fs);
+        else if (E <= 8) MOE_LAUNCH(name, (router_skinny_kernel<bf16_t, 8>), dim3(grid), dim3(256), shm, st, (const bf16_t*)x, wr, rb, logits, T_, D, E, fs);
+        else MOE_LAUNCH(name, (router_skinny_kernel<bf16_t, 16>), dim3(grid), dim3(256), shm, st, (const bf16_t*)x, wr, rb, logits, T_, D, E, fs);
       } else {
-        if (E <= 4) MOE_LAUNCH("router_logits", (router_skinny_kernel<float, 4>), dim3(grid), dim3(256), shm, st, (const float*)x, wr, rb, logits, T_, D, E);
-        else if (E <= 8) MOE_LAUNCH("router_logits", (router_skinny_kernel<float, 8>), dim3(grid), dim3(256), shm, st, (const float*)x, wr, rb, logits, T_, D, E);
-        else MOE_LAUNCH("router_logits", (router_skinny_kernel<float, 16>), dim3(grid), dim3(256), shm, st, (const float*)x, wr, rb, logits, T_, D, E);
+        if (E <= 4) MOE_LAUNCH(name, (router_skinny_kernel<float, 4>), dim3(grid), dim3(256), shm, st, (const float*)x, wr, rb, logits, T_, D, E, fs);
+        else if (E <= 8) MOE_LAUNCH(name, (router_skinny_kernel<float, 8>), dim3(grid), dim3(256), shm, st, (const float*)x, wr, rb, logits, T_, D, E, fs);
+        else MOE_LAUNCH(name, (router_skinny_kernel<float, 16>), dim3(grid), dim3(256), shm, st, (const float*)x, wr, rb, logits, T_, D, E, fs);
       }
     } else {
+      if (fsp) return 1;
       dim3 grid((unsigned)cdiv(T_, kRtT), (unsigned)cdiv(E, kRtE));
       if (c.dtype == MOE_BF16)
         MOE_LAUNCH("router_logits", (router_tiled_kernel<bf16_t>), grid, dim3(256), 0, st, (const bf16_t*)x, wr, rb, logits, T_, D, E);
@@ -415,16 +476,27 @@ int router_logits(const moe_config& c, const void* x, const float* wr, const flo
   return MOE_OK;
 }
 
+int router_logits(const moe_config& c, const void* x, const float* wr, const float* rb,
+                  float* logits, hipStream_t st) {
+  return router_logits_sel(c, x, wr, rb, logits, nullptr, st);
+}
+
 int launch_route(const moe_config& c, const void* x, const float* wr, const float* rb,
                  const float* selb, const float* jit, const float* wn, const float* eps,
                  float* nlg, float* logits, int32_t* idx, float* w, float* lse, bool logits_given,
                  hipStream_t st) {
   const int T_ = c.T, E = c.E;
-  int rc;
-  if (!logits_given && (rc = router_logits(c, x, wr, rb, logits, st))) return rc;
-  if (wn && (rc = router_logits(c, x, wn, nullptr, nlg, st))) return rc;
   const int K = c.K, sc = c.score_fn, ga = c.gating;
   const float* sb = (sc == MOE_SCORE_SIGMOID) ? selb : nullptr;
+  int rc;
+  if (!logits_given && !jit && !wn) {
+    // plain routing: the few-expert router selects in the same kernel
+    const FusedSelect fs = {sb, idx, w, lse, K, sc, ga};
+    rc = router_logits_sel(c, x, wr, rb, logits, &fs, st);
+    if (rc <= 0) return rc;
+  }
+  if (!logits_given && (rc = router_logits(c, x, wr, rb, logits, st))) return rc;
+  if (wn && (rc = router_logits(c, x, wn, nullptr, nlg, st))) return rc;
   const SelectExtras xs = {jit, wn ? eps : nullptr, wn ? nlg : nullptr};
 #define SEL(Lv, Ev) return launch_select<Lv, Ev>(logits, sb, xs, T_, E, K, sc, ga, idx, w, lse, st)
   if (E <= 1) SEL(1, 1);

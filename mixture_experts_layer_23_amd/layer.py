@@ -111,6 +111,13 @@ class MoELayer:
         self.d_logits = z(T1, s.E, dt=f32)
         self.noise_logits = z(T1, s.E, dt=f32) if w_noise is not None else None
         self.x = None
+        # the losses and the bias step read only logits, indices and counts:
+        # they run on a side stream (default priority) beside the expert FFN
+        # and the combine, and the caller's stream waits for them at the end
+        # of forward()
+        self._side = torch.cuda.Stream(device=self.dev)
+        self._fork = torch.cuda.Event()
+        self._join = torch.cuda.Event()
 
     @property
     def use_aux(self) -> bool:
@@ -151,19 +158,30 @@ class MoELayer:
             self.route(x, logits_given, jitter, noise_eps)
             L.moe_permute(self.cfg, self.topk_idx, x, self.counts, self.offsets, self.slot_row,
                           self.row_token, self.row_slot, self.n_dropped, self.x_perm, self.ws)
+        main = torch.cuda.current_stream(self.dev)
+        bias_step = (self.spec.bias_gamma != 0 and self.sel_bias is not None
+                     and not self.spec.expert_choice)
+        side = self.use_aux or self.use_seq or bias_step
+        if side:
+            self._fork.record(main)
+            self._side.wait_event(self._fork)
+            if self.use_aux:
+                L.aux_balance_loss(self.cfg, self.logits, self.counts, self.spec.alpha,
+                                   self.spec.zlam, self.losses, self.dlogits_aux, self.ws,
+                                   stream=self._side)
+            if self.use_seq:
+                L.aux_seq_loss(self.cfg, self.logits, self.topk_idx, self.spec.seq_len,
+                               self.spec.seq_alpha, self.seq_loss, self.dlogits_aux,
+                               self.use_aux, self.ws, stream=self._side)
+            if bias_step:
+                L.moe_bias_update(self.cfg, self.counts, self.spec.bias_gamma, self.sel_bias,
+                                  stream=self._side)
         L.moe_expert_ffn(self.cfg, x, self.x_perm, self.offsets, self.w_gate, self.w_up,
                          self.w_down, self.act, self.h, self.o_perm)
         L.moe_combine(self.cfg, self.o_perm, self.offsets, self.slot_row, self.topk_w, self.y)
-        if self.use_aux:
-            L.aux_balance_loss(self.cfg, self.logits, self.counts, self.spec.alpha,
-                               self.spec.zlam, self.losses, self.dlogits_aux, self.ws)
-        if self.use_seq:
-            L.aux_seq_loss(self.cfg, self.logits, self.topk_idx, self.spec.seq_len,
-                           self.spec.seq_alpha, self.seq_loss, self.dlogits_aux,
-                           self.use_aux, self.ws)
-        if (self.spec.bias_gamma != 0 and self.sel_bias is not None
-                and not self.spec.expert_choice):
-            L.moe_bias_update(self.cfg, self.counts, self.spec.bias_gamma, self.sel_bias)
+        if side:
+            self._join.record(self._side)
+            main.wait_event(self._join)
         return self.y
 
     def backward(self, dy, with_aux: bool | None = None):

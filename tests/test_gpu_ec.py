@@ -44,6 +44,9 @@ ROUTE_CASES = {
     "T65_E1000": (65, 1000, 16, 0.0, 100, 900, 0, "normal"),
     "T3000_E4_coarse": (3000, 4, 1, 0.5, 0, 4, 0, "coarse"),
     "T4096_E4_none_local": (4096, 4, 2, 0.0, 2, 2, 1, "normal"),
+    # keys beyond what the select kernel keeps in registers (16 * 1024)
+    "T20000_E8_ties": (20000, 8, 2, 1.0, 0, 8, 0, "ties"),
+    "T9000_E6_coarse": (9000, 6, 2, 1.0, 1, 6, 0, "coarse"),
 }
 
 

@@ -88,7 +88,12 @@ def test_sigmoid_key_bit_exact_on_a_sweep():
 PERM_CASES = [
     (257, 4, 2, 0, 4, 0.0, 0), (1000, 8, 2, 0, 8, 1.25, 0), (513, 64, 8, 0, 32, 0.0, 0),
     (300, 16, 4, 4, 12, 1.0, 1), (77, 256, 8, 0, 256, 0.0, 1), (256, 4, 2, 0, 4, 1.1, 0),
-    (1, 4, 2, 0, 4, 0.0, 0), (50, 6, 3, 6, 6, 0.0, 1), (64, 5, 5, 0, 5, 0.3, 0)]
+    (1, 4, 2, 0, 4, 0.0, 0), (50, 6, 3, 6, 6, 0.0, 1), (64, 5, 5, 0, 5, 0.3, 0),
+    # one-workgroup path with 16 and 32 rounds of slots in registers
+    (3000, 8, 4, 0, 8, 0.0, 0), (7000, 16, 4, 4, 16, 1.2, 1),
+    # beyond the one-workgroup path (32768 slots, 256 experts): the tiled
+    # histogram / scan / rank kernels
+    (4500, 64, 8, 8, 40, 1.0, 1), (40, 300, 4, 0, 300, 0.0, 1), (4097, 512, 8, 0, 512, 1.5, 0)]
 
 
 @pytest.mark.parametrize("T,E,K,lo,hi,cap,ns", PERM_CASES)
