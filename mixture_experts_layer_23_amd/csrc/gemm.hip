@@ -623,8 +623,10 @@ MOE_DEV uint4 frag_mc(char* tile, int rbase, int ks, int lane, int pitch) {
 
 // Tile order: super-columns of kSuperCols n-tiles; inside one, all m-tiles,
 // n fastest.  Together with the XCD remap, the workgroups that run together on
-// one XCD share a few weight panels and a few row panels in its L2.
-constexpr int kSuperCols = 8;
+// one XCD share one or two weight panels and stream the row panels past them
+// (measured against widths 1, 4, 8 and 16: width 2 is 3-8 % faster per step
+// on all five layer shapes).
+constexpr int kSuperCols = 2;
 MOE_DEV void supercol_tile(int64_t lin, int mt_total, int ntn, int& mt, int& nt) {
   const int full = ntn / kSuperCols, rem = ntn % kSuperCols;
   const int64_t span = (int64_t)mt_total * kSuperCols;
