@@ -28,6 +28,7 @@
 // store.  Workgroup ids are remapped so that consecutive tiles (same rows,
 // same expert weights) land on the same XCD and share its L2.
 #include <cstdlib>
+#include <string>
 #include <type_traits>
 
 #include "common.h"
@@ -1735,13 +1736,20 @@ static void tile_space(GemmParams& P, int grouping, int bm) {
 // 1 = 128-row tiles / 2 stages, 2 = 256-row tiles / 3 stages, 3 / 4 = 256 x
 // 256 / 256 x 128 large tiles on 4 waves, 5 / 6 = the same on 8 waves,
 // 7 / 8 = persistent 256 x 256 / 256 x 128 on 8 waves.
-// MOE_GEMM_CFG overrides the choice (measurement only).
-static int cfg_override() {
-  static int v = [] {
+// MOE_GEMM_CFG overrides the choice (measurement only): a number for every
+// GEMM, or "name=cfg" pairs separated by commas (e.g.
+// "gemm_down_dgrad=1,gemm_gate_up_fwd=5").
+static int cfg_override(const char* name) {
+  static const std::string spec = [] {
     const char* e = getenv("MOE_GEMM_CFG");
-    return e ? atoi(e) : -1;
+    return std::string(e ? e : "");
   }();
-  return v;
+  if (spec.empty()) return -1;
+  if (spec.find('=') == std::string::npos) return atoi(spec.c_str());
+  const std::string key = std::string(name) + "=";
+  const size_t at = spec.find(key);
+  if (at == std::string::npos || (at > 0 && spec[at - 1] != ',')) return -1;
+  return atoi(spec.c_str() + at + key.size());
 }
 
 template <int AM, int BM_, int GR, int EPI, int BS, int BMT, int S>
@@ -1785,7 +1793,16 @@ static int run_gemm(const char* name, GemmParams& P, hipStream_t st) {
     const bool full128 = (P.N % kBN == 0) && (GR == GROUP_M ? P.Kdim % 64 == 0 : P.Mfix % 128 == 0);
     const bool full256 = full128 && (GR == GROUP_M || P.Mfix % 256 == 0);
     const bool wide = full256 && P.N % 256 == 0;
-    int cfg = cfg_override();
+    int cfg = cfg_override(name);
+    if (cfg < 0 && (EPI == EPI_SWIGLU_BWD || (EPI == EPI_SWIGLU_FWD && P.Kdim <= 2048))) {
+      // The fused SwiGLU epilogues move as many bytes as the main loop
+      // (activations read and gradients written, or a, b and h written):
+      // 128 x 128 tiles run two workgroups per CU, so one's epilogue
+      // overlaps the other's main loop.  Measured faster for the backward
+      // at every shape and for the forward up to D = 2048 (longer
+      // reductions favour the 256-wide tiles).
+      cfg = 1;
+    }
     if (cfg < 0) {
       // 256 x 256 tiles on 8 waves when they give enough tiles (a weight
       // gradient, with its long reduction over the group rows, needs fewer);
