@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="minimind")
     ap.add_argument("--k", type=int, default=None, help="override top-K")
+    ap.add_argument("--tokens", type=int, default=None,
+                    help="override T (token sweeps of the routing / permute / combine kernels)")
     ap.add_argument("--gating", choices=["A", "B"], default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seq-len", type=int, default=0,
@@ -69,6 +71,8 @@ def workload(args):
     wl = S.WORKLOADS[args.workload]
     if args.k is not None:
         wl = wl.with_(K=args.k)
+    if args.tokens is not None:
+        wl = wl.with_(T=args.tokens)
     if args.gating is not None:
         wl = wl.with_(gating=S.GATE_A if args.gating == "A" else S.GATE_B)
     if args.routing == "expert":
@@ -266,6 +270,15 @@ def main():
         "ec_select": wl.T * wl.n_local * 4 * 4 + wl.T * wl.n_local * 4 + n_rows_local * 8,
         "route_select": wl.T * wl.E * 4 + wl.T * wl.K * 8 + wl.T * 4,
         "router_logits": wl.T * Dsz + wl.E * wl.D * 4 + wl.T * wl.E * 4,
+        # x and W_r read; logits, top-K indices and weights, lse written
+        "route_fused": wl.T * Dsz + wl.E * wl.D * 4 + wl.T * wl.E * 4 + wl.T * wl.K * 8
+                       + wl.T * 4,
+        # slot experts read (twice for the tiled rank); slot rows and the
+        # two row maps written
+        "permute_small": wl.T * wl.K * 8 + n_rows_local * 8,
+        "permute_hist": wl.T * wl.K * 4,
+        "permute_rank": wl.T * wl.K * 8 + n_rows_local * 8,
+        "aux_single": wl.T * wl.E * 4 * (2 if wl.alpha or wl.zlam else 1),
         "router_wgrad": wl.T * Dsz + wl.T * wl.E * 4,
         "aux_partial": wl.T * wl.E * 4 * (2 if wl.alpha or wl.zlam else 1),
         # logits read twice (probabilities, then the gradient), routing read,

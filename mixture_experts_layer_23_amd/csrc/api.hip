@@ -110,9 +110,12 @@ Workspace workspace_layout(const moe_config& c) {
   L.aux_blocks = (int)std::max<int64_t>(1, cdiv(c.T, aux_tokens_per_block(c.E)));
   if (c.E <= 16) {
     // token chunks of the few-expert router weight gradient: about 320
-    // workgroups, chunks of at least 16 tokens
+    // workgroups, and for long batches chunks of at most 64 tokens (up to
+    // 2048 chunks) so that the per-wave token loops stay short; chunks of at
+    // least 16 tokens
     const int64_t dblk = cdiv(c.D, 64 * router_wgrad_width(c));
     int64_t nchunk = std::max<int64_t>(1, cdiv(320, dblk));
+    nchunk = std::max<int64_t>(nchunk, std::min<int64_t>(cdiv(c.T, 64), 2048));
     nchunk = std::min<int64_t>(nchunk, std::max<int64_t>(1, cdiv(c.T, 16)));
     // every chunk must be non-empty: re-derive the count from the chunk length
     const int64_t len = cdiv(std::max<int64_t>(c.T, 1), nchunk);
