@@ -115,3 +115,71 @@ def test_zero_tokens_is_a_noop_without_device_access():
 def test_error_strings():
     for code in (0, -1, -2, -3, -4, -5, -99):
         assert isinstance(L.error_string(code), str) and L.error_string(code)
+
+
+# ---------------------------------------------------------------------------
+# expert-choice configurations (host side)
+# ---------------------------------------------------------------------------
+def ec_cfg(**kw):
+    base = dict(T=64, D=128, E=8, K=2, F=256, gating=L.MOE_GATE_TRUNCATED,
+                routing=L.MOE_EXPERT_CHOICE)
+    base.update(kw)
+    return L.make_config(**base)
+
+
+@pytest.mark.parametrize("T,E,K,cap,lo,hi,ns", [(257, 4, 2, 0.0, 0, 4, 0), (1000, 8, 2, 1.25, 0, 8, 1),
+                                                (33, 3, 3, 0.0, 0, 3, 0), (70, 256, 8, 0.0, 10, 200, 1),
+                                                (5, 4, 4, 3.0, 0, 4, 0), (64, 128, 100, 1.0, 0, 128, 0)])
+def test_expert_choice_capacity_and_rows(T, E, K, cap, lo, hi, ns):
+    c = ec_cfg(T=T, E=E, K=K, capacity_factor=cap, expert_lo=lo, expert_hi=hi, n_shared=ns)
+    C_ = O.ec_capacity(O.Cfg(T=T, D=8, E=E, K=K, F=8, cap=cap))
+    assert L.capacity(c) == C_ <= T
+    assert L.rows_max(c) == (hi - lo) * C_ + ns * T
+    assert L.workspace_size(c) > 0
+
+
+@pytest.mark.parametrize("bad", [dict(gating=L.MOE_GATE_RENORM), dict(score_fn=L.MOE_SCORE_SIGMOID),
+                                 dict(routing=2), dict(K=9)])
+def test_expert_choice_invalid_config_rejected(bad):
+    c = ec_cfg(**bad)
+    v = C.c_size_t()
+    assert L.lib().moe_workspace_size(C.byref(c), C.byref(v)) == L.MOE_EINVAL
+
+
+def test_token_choice_calls_reject_expert_choice_and_back():
+    ec, tc = ec_cfg(), cfg()
+    lib = L.lib()
+    ws = 1 << 30
+    assert lib.moe_route(C.byref(ec), FAKE, FAKE, None, None, FAKE, FAKE, FAKE, None, 0,
+                         None) == L.MOE_EINVAL
+    assert lib.moe_permute(C.byref(ec), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                           ws, None) == L.MOE_EINVAL
+    assert lib.moe_bias_update(C.byref(ec), FAKE, 1e-3, FAKE, None) == L.MOE_EINVAL
+    assert lib.aux_seq_loss(C.byref(ec), FAKE, FAKE, 16, 1e-3, FAKE, None, 0, FAKE, ws,
+                            None) == L.MOE_EINVAL
+    args = [FAKE] * 12
+    assert lib.moe_route_expert_choice(C.byref(tc), *args, 0, FAKE, ws, None) == L.MOE_EINVAL
+    # expert choice: NULL slot table, misaligned gate weights, bad flags, small workspace
+    a = list(args)
+    a[8] = None
+    assert lib.moe_route_expert_choice(C.byref(ec), *a, 0, FAKE, ws, None) == L.MOE_EINVAL
+    a = list(args)
+    a[4] = FAKE + 4
+    assert lib.moe_route_expert_choice(C.byref(ec), *a, 0, FAKE, ws, None) == L.MOE_EALIGN
+    assert lib.moe_route_expert_choice(C.byref(ec), *args, 4, FAKE, ws, None) == L.MOE_EINVAL
+    assert lib.moe_route_expert_choice(C.byref(ec), *args, 0, FAKE, 16, None) == L.MOE_EWORKSPACE
+    # T = 0: a successful no-op
+    e0 = ec_cfg(T=0)
+    assert lib.moe_route_expert_choice(C.byref(e0), *args, 0, FAKE, ws, None) == 0
+    # the backward takes no top-K list under expert choice
+    assert lib.moe_backward(C.byref(ec_cfg(T=0)), FAKE, FAKE, FAKE, None, *([FAKE] * 20), ws,
+                            None) == 0
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in r.stderr
