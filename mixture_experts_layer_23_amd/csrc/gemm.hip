@@ -622,24 +622,26 @@ MOE_DEV uint4 frag_mc(char* tile, int rbase, int ks, int lane, int pitch) {
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-// Tile order: super-columns of kSuperCols n-tiles; inside one, all m-tiles,
+// Tile order: super-columns of kSuperColsM / kSuperColsK n-tiles; inside one, all m-tiles,
 // n fastest.  Together with the XCD remap, the workgroups that run together on
 // one XCD share one or two weight panels and stream the row panels past them
 // (measured against widths 1, 4, 8 and 16: width 2 is 3-8 % faster per step
 // on all five layer shapes).
-constexpr int kSuperCols = 2;
+constexpr int kSuperColsM = 2;  // row GEMMs (forward, data gradients)
+constexpr int kSuperColsK = 2;  // weight gradients
+template <int SC>
 MOE_DEV void supercol_tile(int64_t lin, int mt_total, int ntn, int& mt, int& nt) {
-  const int full = ntn / kSuperCols, rem = ntn % kSuperCols;
-  const int64_t span = (int64_t)mt_total * kSuperCols;
+  const int full = ntn / SC, rem = ntn % SC;
+  const int64_t span = (int64_t)mt_total * SC;
   const int64_t sc = lin / span;
   if (sc < full) {
     const int64_t w = lin - sc * span;
-    mt = (int)(w / kSuperCols);
-    nt = (int)(sc * kSuperCols + w % kSuperCols);
+    mt = (int)(w / SC);
+    nt = (int)(sc * SC + w % SC);
   } else {
     const int64_t w = lin - (int64_t)full * span;
     mt = (int)(w / rem);
-    nt = full * kSuperCols + (int)(w % rem);
+    nt = full * SC + (int)(w % rem);
   }
 }
 
@@ -677,7 +679,7 @@ __global__ __launch_bounds__(BMT * 2) void grouped_gemm_dma_kernel(GemmParams P)
   int nrows_g = 0;
   if constexpr (GROUPING == GROUP_M) {
     int mt, nt, mtl;
-    supercol_tile(lin, P.mt_total, P.ntn, mt, nt);
+    supercol_tile<kSuperColsM>(lin, P.mt_total, P.ntn, mt, nt);
     if (!find_group(P.offsets, P.G, mt, g, mtl, BMT)) return;
     g = __builtin_amdgcn_readfirstlane(g);
     mtl = __builtin_amdgcn_readfirstlane(mtl);
@@ -691,7 +693,7 @@ __global__ __launch_bounds__(BMT * 2) void grouped_gemm_dma_kernel(GemmParams P)
     const int64_t per = (int64_t)P.ntm * P.ntn;
     g = (int)(lin / per);
     int mt, nt;
-    supercol_tile(lin - (int64_t)g * per, P.ntm, P.ntn, mt, nt);
+    supercol_tile<kSuperColsK>(lin - (int64_t)g * per, P.ntm, P.ntn, mt, nt);
     m0 = mt * BMT;
     n0 = nt * kBN;
     rows_valid = BMT;
@@ -930,7 +932,7 @@ __global__ __launch_bounds__(NW * 64) void grouped_gemm_big_kernel(GemmParams P)
   int nrows_g = 0;
   if constexpr (GROUPING == GROUP_M) {
     int mt, nt, mtl;
-    supercol_tile(lin, P.mt_total, P.ntn, mt, nt);
+    supercol_tile<kSuperColsM>(lin, P.mt_total, P.ntn, mt, nt);
     if (!find_group(P.offsets, P.G, mt, g, mtl, BM)) return;
     g = __builtin_amdgcn_readfirstlane(g);
     mtl = __builtin_amdgcn_readfirstlane(mtl);
@@ -944,7 +946,7 @@ __global__ __launch_bounds__(NW * 64) void grouped_gemm_big_kernel(GemmParams P)
     const int64_t per = (int64_t)P.ntm * P.ntn;
     g = (int)(lin / per);
     int mt, nt;
-    supercol_tile(lin - (int64_t)g * per, P.ntm, P.ntn, mt, nt);
+    supercol_tile<kSuperColsK>(lin - (int64_t)g * per, P.ntm, P.ntn, mt, nt);
     m0 = mt * BM;
     n0 = nt * BN;
     rows_valid = BM;
@@ -1386,7 +1388,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_persist_kernel(GemmParams P)
     int kdim, nrows_g = 0;
     if constexpr (GROUPING == GROUP_M) {
       int mt, nt, mtl, g;
-      supercol_tile(lin, mt_real, P.ntn, mt, nt);
+      supercol_tile<kSuperColsM>(lin, mt_real, P.ntn, mt, nt);
       find_group(P.offsets, P.G, mt, g, mtl, BM);
       t.g = __builtin_amdgcn_readfirstlane(g);
       mtl = __builtin_amdgcn_readfirstlane(mtl);
@@ -1399,7 +1401,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_persist_kernel(GemmParams P)
       const int64_t per = (int64_t)P.ntm * P.ntn;
       t.g = (int)(lin / per);
       int mt, nt;
-      supercol_tile(lin - (int64_t)t.g * per, P.ntm, P.ntn, mt, nt);
+      supercol_tile<kSuperColsK>(lin - (int64_t)t.g * per, P.ntm, P.ntn, mt, nt);
       t.m0 = mt * BM;
       t.n0 = nt * BN;
       t.rows_valid = BM;
