@@ -1796,13 +1796,13 @@ static int run_gemm(const char* name, GemmParams& P, hipStream_t st) {
     const bool full256 = full128 && (GR == GROUP_M || P.Mfix % 256 == 0);
     const bool wide = full256 && P.N % 256 == 0;
     int cfg = cfg_override(name);
-    if (cfg < 0 && (EPI == EPI_SWIGLU_BWD || (EPI == EPI_SWIGLU_FWD && P.Kdim <= 2048))) {
-      // The fused SwiGLU epilogues move as many bytes as the main loop
-      // (activations read and gradients written, or a, b and h written):
-      // 128 x 128 tiles run two workgroups per CU, so one's epilogue
-      // overlaps the other's main loop.  Measured faster for the backward
-      // at every shape and for the forward up to D = 2048 (longer
-      // reductions favour the 256-wide tiles).
+    if (cfg < 0 && (EPI == EPI_SWIGLU_BWD || (GR == GROUP_M && P.Kdim <= 2048))) {
+      // 128 x 128 tiles run two workgroups per CU, so one's epilogue and
+      // first-slab wait overlap the other's main loop.  That wins for the
+      // row GEMMs with short reductions (K <= 2048: a tile's main loop is
+      // then not much longer than its prologue and epilogue) and for the
+      // SwiGLU-backward epilogue (activations read, two gradients written)
+      // at every measured shape; long reductions favour the 256-wide tiles.
       cfg = 1;
     }
     if (cfg < 0) {
