@@ -121,7 +121,11 @@ Workspace workspace_layout(const moe_config& c) {
     const int64_t len = cdiv(std::max<int64_t>(c.T, 1), nchunk);
     L.dwr_splits = (int)std::max<int64_t>(1, cdiv(std::max<int64_t>(c.T, 1), len));
   } else {
-    const int64_t tiles = cdiv(c.E, 64) * cdiv(c.D, 64);
+    // token splits of the many-expert router weight gradient: about 1024
+    // workgroups of 128 x 128 (matrix-core path, E a multiple of 4) or
+    // 64 x 64 (SIMT path) output tiles, splits of at least 256 tokens
+    const int64_t tb = (c.E % 4 == 0) ? 128 : 64;
+    const int64_t tiles = cdiv(c.E, tb) * cdiv(c.D, tb);
     int64_t s = cdiv(1024, tiles);
     s = std::min<int64_t>(s, std::max<int64_t>(1, c.T / 256));
     L.dwr_splits = (int)std::max<int64_t>(1, s);

@@ -435,20 +435,40 @@ static int router_bwd_t(const moe_config& c, const void* x, const float* wr, con
     MOE_LAUNCH("router_wgrad_reduce", reduce_splits_kernel, dim3((unsigned)cdiv(n, 64)),
                dim3(256), 0, st, part, nchunk, n, stride, dwr, drb, (int64_t)E * D);
   } else {
-    // dxr[T,D] = ds[T,E] W_r[E,D]
-    dim3 g1((unsigned)cdiv(T_, 64), (unsigned)cdiv(D, 64), 1);
-    MOE_LAUNCH("router_dgrad", (simt_gemm_kernel<float, float, true>), g1, dim3(256), 0, st, ds,
-               (int64_t)E, wr, (int64_t)D, T_, D, E, E, dxr, (int64_t)D, (int64_t)0);
-    // dW_r[E,D] = ds^T x, split over tokens
-    const int splits = L.dwr_splits;
-    const int kper = (int)(cdiv(cdiv(T_, splits), 16) * 16);
-    dim3 g2((unsigned)cdiv(E, 64), (unsigned)cdiv(D, 64), (unsigned)splits);
-    MOE_LAUNCH("router_wgrad", (simt_gemm_kernel<float, T, false>), g2, dim3(256), 0, st, ds,
-               (int64_t)E, (const T*)x, (int64_t)D, E, D, T_, kper, part, (int64_t)D,
-               (int64_t)E * D);
-    const int64_t n = (int64_t)E * D;
-    MOE_LAUNCH("router_wgrad_reduce", reduce_splits_kernel, dim3((unsigned)cdiv(n, 64)),
-               dim3(256), 0, st, part, splits, n, n, dwr, (float*)nullptr, n);
+    const bool mfma = router_gemm_fits(E, D, T_, D, E, true) &&
+                      router_gemm_fits(E, D, E, D, T_, false);
+    if (mfma) {
+      // fp32 matrix cores: dxr[T,D] = ds[T,E] W_r[E,D]; dW_r[E,D] = ds^T x in
+      // token splits of a multiple of 32
+      int rc;
+      if ((rc = router_gemm("router_dgrad", true, false, ds, E, wr, D, T_, D, E,
+                            (int)cdiv(E, 32) * 32, 1, dxr, D, 0, st)))
+        return rc;
+      const int kper = (int)std::max<int64_t>(32, cdiv(cdiv(T_, L.dwr_splits), 32) * 32);
+      const int splits = (int)std::max<int64_t>(1, cdiv(T_, kper));
+      if ((rc = router_gemm("router_wgrad", false, sizeof(T) == 2, ds, E, x, D, E, D, T_, kper,
+                            splits, part, D, (int64_t)E * D, st)))
+        return rc;
+      const int64_t n = (int64_t)E * D;
+      MOE_LAUNCH("router_wgrad_reduce", reduce_splits_kernel, dim3((unsigned)cdiv(n, 64)),
+                 dim3(256), 0, st, part, splits, n, n, dwr, (float*)nullptr, n);
+    } else {
+      // SIMT fallback (E not a multiple of 4)
+      // dxr[T,D] = ds[T,E] W_r[E,D]
+      dim3 g1((unsigned)cdiv(T_, 64), (unsigned)cdiv(D, 64), 1);
+      MOE_LAUNCH("router_dgrad", (simt_gemm_kernel<float, float, true>), g1, dim3(256), 0, st, ds,
+                 (int64_t)E, wr, (int64_t)D, T_, D, E, E, dxr, (int64_t)D, (int64_t)0);
+      // dW_r[E,D] = ds^T x, split over tokens
+      const int splits = L.dwr_splits;
+      const int kper = (int)(cdiv(cdiv(T_, splits), 16) * 16);
+      dim3 g2((unsigned)cdiv(E, 64), (unsigned)cdiv(D, 64), (unsigned)splits);
+      MOE_LAUNCH("router_wgrad", (simt_gemm_kernel<float, T, false>), g2, dim3(256), 0, st, ds,
+                 (int64_t)E, (const T*)x, (int64_t)D, E, D, T_, kper, part, (int64_t)D,
+                 (int64_t)E * D);
+      const int64_t n = (int64_t)E * D;
+      MOE_LAUNCH("router_wgrad_reduce", reduce_splits_kernel, dim3((unsigned)cdiv(n, 64)),
+                 dim3(256), 0, st, part, splits, n, n, dwr, (float*)nullptr, n);
+    }
     if (drb) {
       float* rpart = reinterpret_cast<float*>(ws + L.rb_part);
       const int64_t rstride = ((int64_t)E + 3) & ~(int64_t)3;

@@ -1943,4 +1943,143 @@ int gemm_up_wgrad(const moe_config& c, const int32_t* offsets, const void* x, co
   return run_gemm<float, MC, MC, GROUP_K, EPI_STORE, BS_NONE>("gemm_gate_up_wgrad", P, st);
 }
 
+// ---------------------------------------------------------------------------
+// Router GEMMs for many experts, fp32 end to end on the fp32 matrix cores:
+//   C[z][m][n] = sum over k in [z*kper, min(Kd, (z+1)*kper)) of A(m,k) B(k,n)
+//   A(m,k) = AMODE == KC ? A[m*lda + k] : A[k*lda + m]   (fp32)
+//   B(k,n) = B[k*ldb + n]   (fp32, or bf16 widened exactly on its way to LDS)
+// 128 x 128 tiles, k-slabs of 32, the register-staged two-slab pipeline and
+// v_mfma_f32_32x32x2f32 fragments of grouped_gemm_kernel (products exact,
+// fp32 sums).  The accumulators go straight to C: each half-wave stores 32
+// consecutive columns of one row.  Shapes: lda, ldb, N and (MC) M multiples
+// of 4, (KC) Kd a multiple of 4, kper a multiple of 32; A, C and fp32 B
+// 16-byte aligned, bf16 B 8-byte aligned.
+// ---------------------------------------------------------------------------
+template <typename TB>
+struct RouterBLoader;
+template <>
+struct RouterBLoader<float> : TileLoader<float, MC> {};
+template <>
+struct RouterBLoader<bf16_t> {
+  TileLoader<float, MC> t;
+  uint2 raw[4];
+  // same element map as TileLoader<float, MC>: rows k = kg*4 + j of the four
+  // columns mg*4.., kg = tid / 32, mg = tid % 32
+  MOE_DEV void load(const bf16_t* p, int64_t ld, int r_valid, int k0, int k_valid) {
+    const int kg = threadIdx.x >> 5, mg = threadIdx.x & 31;
+    t.ok = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int k = k0 + kg * 4 + j, r = mg * 4;
+      const bool in = (k < k_valid) && (r < r_valid);
+      const bf16_t* q = in ? p + (int64_t)k * ld + r : p + (int64_t)k0 * ld;
+      raw[j] = *reinterpret_cast<const uint2*>(q);
+      t.ok |= (uint32_t)in << j;
+    }
+  }
+  MOE_DEV void store(char* lds) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      t.reg[j] = make_uint4(raw[j].x << 16, raw[j].x & 0xFFFF0000u, raw[j].y << 16,
+                            raw[j].y & 0xFFFF0000u);
+    t.store(lds);
+  }
+};
+
+template <int AMODE, typename TB>
+__global__ __launch_bounds__(256) void router_gemm_kernel(const float* __restrict__ A,
+                                                          int64_t lda, const TB* __restrict__ B,
+                                                          int64_t ldb, int M, int N, int Kd,
+                                                          int kper, float* __restrict__ C,
+                                                          int64_t ldc, int64_t split_stride) {
+  __shared__ __attribute__((aligned(16))) char smem[2][2][128 * 128];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int m0 = blockIdx.y * 128, n0 = blockIdx.x * 128;
+  const int kb = blockIdx.z * kper, ke = min(Kd, kb + kper);
+  const int rows_valid = min(128, M - m0), cols_valid = min(128, N - n0);
+  const float* At = (AMODE == KC) ? A + (int64_t)m0 * lda : A + m0;
+  const TB* Bt = B + n0;
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  TileLoader<float, AMODE> la0, la1;
+  RouterBLoader<TB> lb0, lb1;
+  const int nk = (ke - kb + 31) / 32;
+  auto load_k = [&](TileLoader<float, AMODE>& la, RouterBLoader<TB>& lb, int kt) {
+    const int k0 = kb + kt * 32;
+    la.load(At, lda, rows_valid, k0, ke);
+    lb.load(Bt, ldb, cols_valid, k0, ke);
+  };
+  const int ra[2] = {wm * 64, wm * 64 + 32};
+  const int rb[2] = {wn * 64, wn * 64 + 32};
+  if (nk > 0) {
+    load_k(la0, lb0, 0);
+    if (nk > 1) load_k(la1, lb1, 1);
+    la0.store(smem[0][0]);
+    lb0.store(smem[0][1]);
+    __syncthreads();
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+      if (kt + 2 < nk) load_k(la0, lb0, kt + 2);
+      mma_slab<float>(smem[0][0], smem[0][1], ra, rb, acc);
+      la1.store(smem[1][0]);
+      lb1.store(smem[1][1]);
+      __syncthreads();
+      if (kt + 3 < nk) load_k(la1, lb1, kt + 3);
+      mma_slab<float>(smem[1][0], smem[1][1], ra, rb, acc);
+      if (kt + 2 < nk) {
+        la0.store(smem[0][0]);
+        lb0.store(smem[0][1]);
+      }
+      __syncthreads();
+    }
+    if (kt < nk) mma_slab<float>(smem[0][0], smem[0][1], ra, rb, acc);
+  }
+
+  float* Cs = C + (int64_t)blockIdx.z * split_stride;
+  const int l32 = lane & 31, hi4 = (lane >> 5) * 4;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = wm * 64 + i * 32 + (r >> 2) * 8 + hi4 + (r & 3);
+      if (row >= rows_valid) continue;
+      float* crow = Cs + (int64_t)(m0 + row) * ldc + n0;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int col = wn * 64 + j * 32 + l32;
+        if (col < cols_valid) crow[col] = acc[i][j][r];
+      }
+    }
+}
+
+bool router_gemm_fits(int64_t lda, int64_t ldb, int M, int N, int Kd, bool a_kc) {
+  if (lda % 4 || ldb % 4 || N % 4) return false;
+  return a_kc ? (Kd % 4 == 0) : (M % 4 == 0);
+}
+
+int router_gemm(const char* name, bool a_kc, bool b_bf16, const float* A, int64_t lda,
+                const void* B, int64_t ldb, int M, int N, int Kd, int kper, int splits, float* C,
+                int64_t ldc, int64_t split_stride, hipStream_t st) {
+  if (M <= 0 || N <= 0) return MOE_OK;
+  dim3 grid((unsigned)cdiv(N, 128), (unsigned)cdiv(M, 128), (unsigned)splits);
+#define RG(AM, TBV)                                                                          \
+  MOE_LAUNCH(name, (router_gemm_kernel<AM, TBV>), grid, dim3(256), 0, st, A, lda,           \
+             reinterpret_cast<const TBV*>(B), ldb, M, N, Kd, kper, C, ldc, split_stride)
+  if (a_kc) {
+    if (b_bf16) RG(KC, bf16_t); else RG(KC, float);
+  } else {
+    if (b_bf16) RG(MC, bf16_t); else RG(MC, float);
+  }
+#undef RG
+  return MOE_OK;
+}
+
 }  // namespace moe

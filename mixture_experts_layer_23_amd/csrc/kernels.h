@@ -123,4 +123,13 @@ int gemm_up_dgrad(const moe_config& c, const int32_t* offsets, const void* dact,
 int gemm_up_wgrad(const moe_config& c, const int32_t* offsets, const void* x, const void* x_perm,
                   const void* dact, void* dwg, void* dwu, hipStream_t st);
 
+// fp32 router GEMM for many experts on the matrix cores (gemm.hip):
+//   C[z][m][n] = sum_{k in split z} A(m,k) B(k,n), A(m,k) = a_kc ? A[m*lda+k] :
+//   A[k*lda+m], B(k,n) = B[k*ldb+n] (fp32, or bf16 when b_bf16), splits of kper
+//   (a multiple of 32) k each.  router_gemm_fits says whether the shapes allow it.
+bool router_gemm_fits(int64_t lda, int64_t ldb, int M, int N, int Kd, bool a_kc);
+int router_gemm(const char* name, bool a_kc, bool b_bf16, const float* A, int64_t lda,
+                const void* B, int64_t ldb, int M, int N, int Kd, int kper, int splits, float* C,
+                int64_t ldc, int64_t split_stride, hipStream_t st);
+
 }  // namespace moe

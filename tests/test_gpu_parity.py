@@ -232,6 +232,31 @@ def test_layer_parity(name):
     compare_layer(wl, hin, layer, ref)
 
 
+# Router backward for more than 16 experts: the fp32 matrix-core GEMMs (E a
+# multiple of 4) with ragged token, model-dimension, expert and split edges,
+# and the SIMT fallback (E not a multiple of 4); both dtypes, router bias on.
+ROUTER_BWD = {
+    "mfma_fp32_E132_T1000_D192": S.WORKLOADS["tiny_fp32"].with_(
+        T=1000, D=192, E=132, K=4, F=64, hot_bias=0.5, alpha=1e-3),
+    "mfma_bf16_E36_T777_D320": S.WORKLOADS["minimind"].with_(
+        T=777, D=320, E=36, K=3, F=128, hot_bias=1.0),
+    "mfma_bf16_sigmoid_E260_T513": S.WORKLOADS["deepseek_v3"].with_(
+        T=513, D=128, E=260, K=6, F=64, hot_bias=0.3),
+    "simt_fp32_E18": S.WORKLOADS["tiny_fp32"].with_(T=300, D=128, E=18, K=2, F=64,
+                                                    hot_bias=0.5),
+    "simt_bf16_E30": S.WORKLOADS["minimind"].with_(T=450, D=192, E=30, K=4, F=64, hot_bias=1.0),
+}
+
+
+@pytest.mark.parametrize("name", list(ROUTER_BWD))
+def test_router_backward_many_experts(name):
+    wl = ROUTER_BWD[name]
+    note(f"router backward {name}: {wl}")
+    hin, layer = run_layer(wl)
+    ref = oracle_layer(wl, hin)
+    compare_layer(wl, hin, layer, ref, check_acts=False)
+
+
 def test_k1_renormalised_router_gradient_is_exactly_zero():
     wl = S.WORKLOADS["minimind"].with_(T=512, D=256, F=512, K=1, gating=S.GATE_B, alpha=0.0)
     hin, layer = run_layer(wl)
