@@ -197,6 +197,104 @@ __global__ __launch_bounds__(256) void unpermute_kernel(
   }
 }
 
+// The same sums for few slots per token (slot width <= KM <= 8): each wave
+// takes TPW consecutive tokens (1, or 8 / KM for long batches); per 16-byte
+// column chunk it issues the row
+// loads of every kept slot of its tokens before adding any (so they are in
+// flight together) and reads each router-weight chunk once for its TPW
+// tokens.  Terms are added in the order of unpermute_kernel (kept slots in
+// increasing k, the shared row, then the router part), so the results are
+// identical.
+template <typename T, int EM, int KM, int TPW>
+__global__ __launch_bounds__(256) void unpermute_few_kernel(
+    const T* __restrict__ dxp, const int32_t* __restrict__ slot_row,
+    const int32_t* __restrict__ offsets, int EL, int n_shared, const float* __restrict__ ds,
+    const float* __restrict__ wr, int E, const float* __restrict__ dxr, int T_, int K, int D,
+    T* __restrict__ dx) {
+  constexpr int VEC = Elem<T>::VEC;
+  const int lane = threadIdx.x & 63;
+  const int t0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * TPW;
+  if (t0 >= T_) return;
+  int rows[TPW][KM];
+  int64_t srow[TPW];
+  float s_e[TPW][EM > 0 ? EM : 1];
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) {
+    const int t = t0 + j;
+    const bool tv = t < T_;
+#pragma unroll
+    for (int k = 0; k < KM; ++k) rows[j][k] = (tv && k < K) ? slot_row[(size_t)t * K + k] : -1;
+    srow[j] = (tv && n_shared) ? (int64_t)offsets[EL] + t : -1;
+    if constexpr (EM > 0) {
+#pragma unroll
+      for (int e = 0; e < EM; ++e) s_e[j][e] = (tv && e < E) ? ds[(size_t)t * E + e] : 0.f;
+    }
+  }
+  for (int d0 = lane * VEC; d0 < D; d0 += 64 * VEC) {
+    Vec16<T> v[TPW][KM], vs[TPW];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+#pragma unroll
+      for (int k = 0; k < KM; ++k)
+        if (rows[j][k] >= 0) v[j][k].load(dxp + (size_t)rows[j][k] * D + d0);
+      if (srow[j] >= 0) vs[j].load(dxp + (size_t)srow[j] * D + d0);
+    }
+    float acc[TPW][VEC];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) acc[j][i] = 0.f;
+#pragma unroll
+      for (int k = 0; k < KM; ++k)
+        if (rows[j][k] >= 0) {
+          float f[VEC];
+          v[j][k].to_f32(f);
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) acc[j][i] += f[i];
+        }
+      if (srow[j] >= 0) {
+        float f[VEC];
+        vs[j].to_f32(f);
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) acc[j][i] += f[i];
+      }
+    }
+    if constexpr (EM > 0) {
+#pragma unroll
+      for (int e = 0; e < EM; ++e) {
+        if (e < E) {
+          float w[VEC];
+          const float4* wp = reinterpret_cast<const float4*>(wr + (size_t)e * D + d0);
+#pragma unroll
+          for (int q = 0; q < VEC / 4; ++q) {
+            const float4 u = wp[q];
+            w[4 * q] = u.x; w[4 * q + 1] = u.y; w[4 * q + 2] = u.z; w[4 * q + 3] = u.w;
+          }
+#pragma unroll
+          for (int j = 0; j < TPW; ++j)
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) acc[j][i] = fmaf(s_e[j][e], w[i], acc[j][i]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < TPW; ++j) {
+        if (t0 + j >= T_) continue;
+        const float* r = dxr + (size_t)(t0 + j) * D + d0;
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) acc[j][i] += r[i];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+      if (t0 + j >= T_) continue;
+      Vec16<T> out;
+      out.from_f32(acc[j]);
+      out.store(dx + (size_t)(t0 + j) * D + d0);
+    }
+  }
+}
+
 int launch_combine(const moe_config& c, const void* o_perm, const int32_t* offsets,
                    const int32_t* slot_row, const float* topk_w, void* y, hipStream_t st) {
   const int EL = c.expert_hi - c.expert_lo;
@@ -232,11 +330,34 @@ static int unpermute_t(const moe_config& c, const void* dxp, const int32_t* slot
                        const int32_t* offsets, const float* ds, const float* wr,
                        const float* dxr, void* dx, hipStream_t st) {
   const int EL = c.expert_hi - c.expert_lo;
+  const int E = c.E, W = slot_width(c);
+  if (W <= 8) {
+    // few slots per token: KM slots; 8 / KM tokens per wave when that still
+    // leaves at least 4096 waves, else one
+#define UNPERM_FEW1(EMV, KMV, TPWV)                                                           \
+  MOE_LAUNCH("unpermute_dx", (unpermute_few_kernel<T, EMV, KMV, TPWV>),                       \
+             dim3((unsigned)cdiv(c.T, 4 * TPWV)), dim3(256), 0, st, (const T*)dxp, slot_row,  \
+             offsets, EL, c.n_shared, ds, wr, E, dxr, c.T, W, c.D, (T*)dx)
+#define UNPERM_FEW(EMV, KMV)                                            \
+  if (KMV < 8 && c.T >= 4096 * (8 / KMV)) UNPERM_FEW1(EMV, KMV, 8 / KMV); \
+  else UNPERM_FEW1(EMV, KMV, 1);
+#define UNPERM_FEW_K(EMV)                   \
+  if (W <= 2) { UNPERM_FEW(EMV, 2) }        \
+  else if (W <= 4) { UNPERM_FEW(EMV, 4) }   \
+  else { UNPERM_FEW(EMV, 8) }
+    if (dxr) { UNPERM_FEW_K(0) }
+    else if (E <= 4) { UNPERM_FEW_K(4) }
+    else if (E <= 8) { UNPERM_FEW_K(8) }
+    else { UNPERM_FEW_K(16) }
+#undef UNPERM_FEW_K
+#undef UNPERM_FEW
+#undef UNPERM_FEW1
+    return MOE_OK;
+  }
   const int grid = (int)cdiv(c.T, 4);
-  const int E = c.E;
 #define UNPERM(EMV)                                                                          \
   MOE_LAUNCH("unpermute_dx", (unpermute_kernel<T, EMV>), dim3(grid), dim3(256), 0, st,        \
-             (const T*)dxp, slot_row, offsets, EL, c.n_shared, ds, wr, E, dxr, c.T, slot_width(c), c.D, \
+             (const T*)dxp, slot_row, offsets, EL, c.n_shared, ds, wr, E, dxr, c.T, W, c.D, \
              (T*)dx)
   if (dxr) UNPERM(0);
   else if (E <= 4) UNPERM(4);

@@ -69,21 +69,40 @@ struct FusedSelect {
 // implementation.
 // ---------------------------------------------------------------------------
 
-// Skinny router (E <= 16): W_r (E*D fp32, at most 128 KB) staged in LDS once
-// per workgroup; each wave takes two tokens at a time, lanes stride over D in
-// 16-byte vectors (coalesced), fp64 partials are reduced across the wave.
-template <typename T, int EM>
+// Skinny router (E <= 16): each wave takes two tokens at a time, lanes stride
+// over D in 16-byte vectors (coalesced), four vectors per lane in flight at
+// once; fp64 partials are reduced across the wave.  W_r (E*D fp32, at most
+// 128 KB) is read straight from the caches when small (STAGE false) or staged
+// in LDS once per workgroup.
+template <typename T, int EM, bool STAGE>
 __global__ __launch_bounds__(256) void router_skinny_kernel(const T* __restrict__ x,
                                                             const float* __restrict__ wr,
                                                             const float* __restrict__ rb,
                                                             float* __restrict__ logits, int T_,
                                                             int D, int E, FusedSelect fs) {
   extern __shared__ float4 sw4[];
-  float* sw = reinterpret_cast<float*>(sw4);
-  const int n4 = (E * D) >> 2;
-  for (int i = threadIdx.x; i < n4; i += blockDim.x) sw4[i] = reinterpret_cast<const float4*>(wr)[i];
-  __syncthreads();
-  constexpr int VEC = Elem<T>::VEC;
+  const float* wsrc = wr;
+  if constexpr (STAGE) {
+    // staging in batches of eight 16-byte loads per thread, all in flight
+    // before the first LDS store
+    const int n4 = (E * D) >> 2;
+    for (int i0 = 0; i0 < n4; i0 += 256 * 8) {
+      float4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u * 256 + (int)threadIdx.x;
+        if (i < n4) v[u] = reinterpret_cast<const float4*>(wr)[i];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u * 256 + (int)threadIdx.x;
+        if (i < n4) sw4[i] = v[u];
+      }
+    }
+    __syncthreads();
+    wsrc = reinterpret_cast<const float*>(sw4);
+  }
+  constexpr int VEC = Elem<T>::VEC, NV = 4;
   const int lane = threadIdx.x & 63;
   const int wave = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   const int nwave = gridDim.x * (blockDim.x >> 6);
@@ -92,26 +111,37 @@ __global__ __launch_bounds__(256) void router_skinny_kernel(const T* __restrict_
     double acc0[EM], acc1[EM];
 #pragma unroll
     for (int e = 0; e < EM; ++e) { acc0[e] = 0.0; acc1[e] = 0.0; }
-    for (int d0 = lane * VEC; d0 < D; d0 += 64 * VEC) {
-      float xa[VEC], xb[VEC];
-      Vec16<T> va, vb;
-      va.load(x + (size_t)t0 * D + d0);
-      va.to_f32(xa);
-      if (two) {
-        vb.load(x + (size_t)(t0 + 1) * D + d0);
-        vb.to_f32(xb);
-      } else {
+    for (int dc = 0; dc < D; dc += 64 * VEC * NV) {
+      Vec16<T> va[NV], vb[NV];
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) xb[i] = 0.f;
+      for (int v = 0; v < NV; ++v) {
+        const int d0 = dc + (v * 64 + lane) * VEC;
+        if (d0 < D) {
+          va[v].load(x + (size_t)t0 * D + d0);
+          if (two) vb[v].load(x + (size_t)(t0 + 1) * D + d0);
+        }
       }
 #pragma unroll
-      for (int e = 0; e < EM; ++e) {
-        if (e < E) {
-          const float* w = sw + e * D + d0;
+      for (int v = 0; v < NV; ++v) {
+        const int d0 = dc + (v * 64 + lane) * VEC;
+        if (d0 >= D) break;
+        float xa[VEC], xb[VEC];
+        va[v].to_f32(xa);
+        if (two) {
+          vb[v].to_f32(xb);
+        } else {
 #pragma unroll
-          for (int i = 0; i < VEC; ++i) {
-            acc0[e] = fma((double)xa[i], (double)w[i], acc0[e]);
-            acc1[e] = fma((double)xb[i], (double)w[i], acc1[e]);
+          for (int i = 0; i < VEC; ++i) xb[i] = 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < EM; ++e) {
+          if (e < E) {
+            const float* w = wsrc + e * D + d0;
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) {
+              acc0[e] = fma((double)xa[i], (double)w[i], acc0[e]);
+              acc1[e] = fma((double)xb[i], (double)w[i], acc1[e]);
+            }
           }
         }
       }
@@ -183,16 +213,20 @@ __global__ __launch_bounds__(256) void router_skinny_kernel(const T* __restrict_
 }
 
 // Tiled router (E > 16) on the fp64 matrix cores: 32 tokens x 64 experts per
-// workgroup, four waves of 16 tokens x 32 experts (two 16x16 blocks of
-// v_mfma_f64_16x16x4f64).  k-slabs of 32 are staged in LDS as binary32 (exact
-// for both operands; rows padded by 4 floats) and widened to double when the
-// fragments are read; the next slab is fetched into registers while the
-// current one is multiplied.
+// workgroup, each of KG k-groups of four waves (16 tokens x 32 experts each,
+// two 16x16 blocks of v_mfma_f64_16x16x4f64) takes every KG-th k-slab of 32;
+// the groups' fp64 sums are added in group order at the end, so short
+// batches (few tiles) still bring several waves per SIMD.  Slabs are staged
+// in LDS as binary32 (exact for both operands; rows padded by 4 floats) and
+// widened to double when the fragments are read; each group fetches its next
+// slab into registers while the current one is multiplied.
 //   MFMA operands: lane l gives A[m = l%16][k = l/16] and B[k = l/16][n = l%16];
 //   accumulator element r of lane l is C[m = l/16 + 4r][n = l%16] (the f64
 //   form interleaves rows, unlike the f32 16x16 layout).
 typedef double f64x4_t __attribute__((ext_vector_type(4)));
 constexpr int kRtT = 32, kRtE = 64, kRtK = 32, kRtP = kRtK + 4;
+// LDS bytes of one k-group's slab pair (x and W)
+constexpr int kRtGroupBytes = (kRtT + kRtE) * kRtP * 4;
 
 template <typename T> struct RtLoad;
 template <> struct RtLoad<bf16_t> {
@@ -233,16 +267,22 @@ template <> struct RtLoad<float> {
   }
 };
 
-template <typename T>
-__global__ __launch_bounds__(256) void router_tiled_kernel(const T* __restrict__ x,
-                                                           const float* __restrict__ wr,
-                                                           const float* __restrict__ rb,
-                                                           float* __restrict__ logits, int T_,
-                                                           int D, int E) {
-  __shared__ float sx[kRtT][kRtP];
-  __shared__ float sw[kRtE][kRtP];
+template <typename T, int KG>
+__global__ __launch_bounds__(256 * KG) void router_tiled_kernel(const T* __restrict__ x,
+                                                                const float* __restrict__ wr,
+                                                                const float* __restrict__ rb,
+                                                                float* __restrict__ logits,
+                                                                int T_, int D, int E) {
+  // KG slab pairs; after the k loop the same bytes hold the sums of groups
+  // 1..KG-1 (256 threads x 8 doubles each)
+  static_assert((KG - 1) * 256 * 8 * 8 <= KG * kRtGroupBytes, "reduction does not fit");
+  __shared__ __attribute__((aligned(16))) char smem[KG * kRtGroupBytes];
+  const int tid = threadIdx.x & 255, grp = threadIdx.x >> 8;
+  float(*sx)[kRtP] = reinterpret_cast<float(*)[kRtP]>(smem + grp * kRtGroupBytes);
+  float(*sw)[kRtP] = reinterpret_cast<float(*)[kRtP]>(smem + grp * kRtGroupBytes +
+                                                      kRtT * kRtP * 4);
   const int t0 = blockIdx.x * kRtT, e0 = blockIdx.y * kRtE;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = tid >> 6;
   const int wt = (wave & 1) * 16, we = (wave >> 1) * 32;
   // W slab: 64 rows x 32 k = 512 chunks of 4 floats, two per thread
   float xv[8], wv[2][4];
@@ -263,27 +303,57 @@ __global__ __launch_bounds__(256) void router_tiled_kernel(const T* __restrict__
   for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[j][r] = 0.0;
-  load(0);
-  for (int k0 = 0; k0 < D; k0 += kRtK) {
+  // group g takes slabs g, g + KG, ...; every group runs the same number of
+  // rounds so that the block-wide barriers match
+  const int nslab = D / kRtK, rounds = (nslab + KG - 1) / KG;
+  if (grp < nslab) load(grp * kRtK);
+  for (int rd = 0; rd < rounds; ++rd) {
+    const int k0 = (rd * KG + grp) * kRtK;
+    const bool have = k0 < D;
     __syncthreads();
-    RtLoad<T>::store(sx, tid, xv);
+    if (have) {
+      RtLoad<T>::store(sx, tid, xv);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int ch = tid + 256 * u, r = ch >> 3, kc = (ch & 7) * 4;
+      for (int u = 0; u < 2; ++u) {
+        const int ch = tid + 256 * u, r = ch >> 3, kc = (ch & 7) * 4;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sw[r][kc + i] = wv[u][i];
+        for (int i = 0; i < 4; ++i) sw[r][kc + i] = wv[u][i];
+      }
     }
     __syncthreads();
-    if (k0 + kRtK < D) load(k0 + kRtK);
+    if (k0 + KG * kRtK < D) load(k0 + KG * kRtK);
+    if (have) {
 #pragma unroll
-    for (int ks = 0; ks < kRtK; ks += 4) {
-      const int kk = ks + (lane >> 4), i16 = lane & 15;
-      const double a = (double)sx[wt + i16][kk];
+      for (int ks = 0; ks < kRtK; ks += 4) {
+        const int kk = ks + (lane >> 4), i16 = lane & 15;
+        const double a = (double)sx[wt + i16][kk];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const double b = (double)sw[we + 16 * j + i16][kk];
-        acc[j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, acc[j], 0, 0, 0);
+        for (int j = 0; j < 2; ++j) {
+          const double b = (double)sw[we + 16 * j + i16][kk];
+          acc[j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, acc[j], 0, 0, 0);
+        }
       }
+    }
+  }
+  if constexpr (KG > 1) {
+    __syncthreads();
+    double* red = reinterpret_cast<double*>(smem);
+    if (grp > 0) {
+      double* mine = red + ((size_t)(grp - 1) * 256 + tid) * 8;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mine[j * 4 + r] = acc[j][r];
+    }
+    __syncthreads();
+    if (grp > 0) return;
+#pragma unroll
+    for (int g = 1; g < KG; ++g) {
+      const double* o = red + ((size_t)(g - 1) * 256 + tid) * 8;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[j][r] += o[j * 4 + r];
     }
   }
 #pragma unroll
@@ -433,19 +503,25 @@ static int router_logits_sel(const moe_config& c, const void* x, const float* wr
     if (E <= 16 && (size_t)E * D * 4 <= 128 * 1024) {
       const FusedSelect fs = fsp ? *fsp : FusedSelect{nullptr, nullptr, nullptr, nullptr, 0, 0, 0};
       const char* name = fsp ? "route_fused" : "router_logits";
+      // one token pair per wave, but no more workgroups than fit on the chip
+      // at once (a staged W_r is loaded once per workgroup: with large tiles
+      // the waves loop over several pairs).  W_r up to 32 KB is read through
+      // the caches instead (no staging pass).
+      const bool stage = (size_t)E * D * 4 > 32 * 1024;
+      const size_t shm = stage ? (size_t)E * D * 4 : 0;
       const int waves_needed = (int)cdiv(T_, 2);
-      int grid = (int)std::min<int64_t>(cdiv(waves_needed, 4), 2048);
-      const size_t shm = (size_t)E * D * 4;
+      const int64_t per_cu = stage ? std::max<int64_t>(1, std::min<int64_t>(8, (160 * 1024) / (int64_t)shm)) : 8;
+      int grid = (int)std::min<int64_t>(cdiv(waves_needed, 4), 256 * per_cu);
       if (shm > 64 * 1024) {
         // W_r tiles above 64 KB need the kernels' dynamic-LDS limit raised:
         // once per process (outside any stream capture that comes later)
         static hipError_t lim = [] {
-          const void* fns[] = {(const void*)router_skinny_kernel<bf16_t, 4>,
-                               (const void*)router_skinny_kernel<bf16_t, 8>,
-                               (const void*)router_skinny_kernel<bf16_t, 16>,
-                               (const void*)router_skinny_kernel<float, 4>,
-                               (const void*)router_skinny_kernel<float, 8>,
-                               (const void*)router_skinny_kernel<float, 16>};
+          const void* fns[] = {(const void*)router_skinny_kernel<bf16_t, 4, true>,
+                               (const void*)router_skinny_kernel<bf16_t, 8, true>,
+                               (const void*)router_skinny_kernel<bf16_t, 16, true>,
+                               (const void*)router_skinny_kernel<float, 4, true>,
+                               (const void*)router_skinny_kernel<float, 8, true>,
+                               (const void*)router_skinny_kernel<float, 16, true>};
           for (const void* f : fns) {
             hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
                                                128 * 1024);
@@ -455,22 +531,35 @@ static int router_logits_sel(const moe_config& c, const void* x, const float* wr
         }();
         if (lim != hipSuccess) { set_error("router_logits (LDS limit)", lim); return MOE_ELAUNCH; }
       }
+#define SKINNY(TV, EMV, SV)                                                                 \
+  MOE_LAUNCH(name, (router_skinny_kernel<TV, EMV, SV>), dim3(grid), dim3(256), shm, st,     \
+             (const TV*)x, wr, rb, logits, T_, D, E, fs)
+#define SKINNY_E(TV, SV)              \
+  if (E <= 4) SKINNY(TV, 4, SV);      \
+  else if (E <= 8) SKINNY(TV, 8, SV); \
+  else SKINNY(TV, 16, SV);
       if (c.dtype == MOE_BF16) {
-        if (E <= 4) MOE_LAUNCH(name, (router_skinny_kernel<bf16_t, 4>), dim3(grid), dim3(256), shm, st, (const bf16_t*)x, wr, rb, logits, T_, D, E, fs);
-        else if (E <= 8) MOE_LAUNCH(name, (router_skinny_kernel<bf16_t, 8>), dim3(grid), dim3(256), shm, st, (const bf16_t*)x, wr, rb, logits, T_, D, E, fs);
-        else MOE_LAUNCH(name, (router_skinny_kernel<bf16_t, 16>), dim3(grid), dim3(256), shm, st, (const bf16_t*)x, wr, rb, logits, T_, D, E, fs);
+        if (stage) { SKINNY_E(bf16_t, true) } else { SKINNY_E(bf16_t, false) }
       } else {
-        if (E <= 4) MOE_LAUNCH(name, (router_skinny_kernel<float, 4>), dim3(grid), dim3(256), shm, st, (const float*)x, wr, rb, logits, T_, D, E, fs);
-        else if (E <= 8) MOE_LAUNCH(name, (router_skinny_kernel<float, 8>), dim3(grid), dim3(256), shm, st, (const float*)x, wr, rb, logits, T_, D, E, fs);
-        else MOE_LAUNCH(name, (router_skinny_kernel<float, 16>), dim3(grid), dim3(256), shm, st, (const float*)x, wr, rb, logits, T_, D, E, fs);
+        if (stage) { SKINNY_E(float, true) } else { SKINNY_E(float, false) }
       }
+#undef SKINNY_E
+#undef SKINNY
     } else {
       if (fsp) return 1;
+      // k-groups per workgroup: about 1024 four-wave groups on the chip
+      const int64_t tiles = cdiv(T_, kRtT) * cdiv(E, kRtE);
+      const int kg = tiles >= 1024 ? 1 : (tiles >= 512 ? 2 : 4);
       dim3 grid((unsigned)cdiv(T_, kRtT), (unsigned)cdiv(E, kRtE));
-      if (c.dtype == MOE_BF16)
-        MOE_LAUNCH("router_logits", (router_tiled_kernel<bf16_t>), grid, dim3(256), 0, st, (const bf16_t*)x, wr, rb, logits, T_, D, E);
-      else
-        MOE_LAUNCH("router_logits", (router_tiled_kernel<float>), grid, dim3(256), 0, st, (const float*)x, wr, rb, logits, T_, D, E);
+#define RT(TV, KGV)                                                                        \
+  MOE_LAUNCH("router_logits", (router_tiled_kernel<TV, KGV>), grid, dim3(256 * KGV), 0, st, \
+             (const TV*)x, wr, rb, logits, T_, D, E)
+      if (c.dtype == MOE_BF16) {
+        if (kg == 1) RT(bf16_t, 1); else if (kg == 2) RT(bf16_t, 2); else RT(bf16_t, 4);
+      } else {
+        if (kg == 1) RT(float, 1); else if (kg == 2) RT(float, 2); else RT(float, 4);
+      }
+#undef RT
     }
   }
   return MOE_OK;

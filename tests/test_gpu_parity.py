@@ -60,6 +60,52 @@ def test_route_given_logits_bit_exact(T, E, K, score, gating, ties):
     assert_close("lse", to_host(d_lse), lse, 1e-5)
 
 
+# router logits from x on the fp64 matrix cores (E > 16): 32 x 64 tiles with
+# 4, 2 or 1 k-groups per workgroup (fewer than 512, 512..1023, 1024+ tiles),
+# ragged tokens and experts, fewer k-slabs than k-groups (D = 64)
+ROUTER_TILED = [(200, 128, 64, S.BF16), (1000, 64, 100, S.F32), (16384, 128, 64, S.BF16),
+                (16000, 192, 100, S.BF16), (32768, 64, 64, S.F32)]
+
+
+# the few-expert router (E <= 16, logits and top-K in one kernel): W_r read
+# through the caches (<= 32 KB) or staged in LDS (waves then loop over several
+# token pairs), partial 4-vector chunks of D, a single token
+ROUTER_SKINNY = [(777, 768, 4, S.BF16), (4097, 2048, 16, S.BF16), (1000, 1088, 8, S.F32),
+                 (1, 64, 3, S.F32), (16384, 512, 16, S.BF16), (3001, 4096, 8, S.BF16)]
+
+
+@pytest.mark.parametrize("T,D,E,dt", ROUTER_TILED + ROUTER_SKINNY)
+def test_router_logits_tiled(T, D, E, dt):
+    from mixture_experts_layer_23_amd import _lib as L
+    note(f"router logits T={T} D={D} E={E} dtype={dt}")
+    rng = np.random.default_rng(T + 3 * D + 7 * E)
+    xf = rng.standard_normal((T, D)).astype(np.float32)
+    x = S.bf16_bits(xf) if dt == S.BF16 else xf
+    wr = (rng.standard_normal((E, D)) / np.sqrt(D)).astype(np.float32)
+    rb = rng.uniform(-0.5, 0.5, E).astype(np.float32)
+    K = min(4, E)
+    oc = O().Cfg(T=T, D=D, E=E, K=K, F=64)
+    lg = O().logits(oc, x, wr, rb)
+    idx, w, _, _ = O().route(oc, lg)
+    cfg = L.make_config(T, D, E, K, 64, dtype=L.MOE_BF16 if dt == S.BF16 else L.MOE_F32)
+    d_lg = torch.empty(T, E, dtype=torch.float32, device="cuda")
+    d_idx = torch.empty(T, K, dtype=torch.int32, device="cuda")
+    d_w = torch.empty(T, K, dtype=torch.float32, device="cuda")
+    L.moe_route(cfg, to_dev(x, torch), to_dev(wr, torch), to_dev(rb, torch), None, d_lg, d_idx,
+                d_w, None)
+    torch.cuda.synchronize()
+    g = to_host(d_lg)
+    # one rounding of an fp64 sum: equal to the oracle's unless the sum falls
+    # within fp64 rounding of a binary32 rounding boundary
+    nbad = int(np.sum(g != lg))
+    note(f"  logits differing: {nbad} of {g.size}")
+    assert nbad <= 2
+    assert_close("logits", g, lg, 1e-6)
+    if nbad == 0:
+        np.testing.assert_array_equal(to_host(d_idx), idx)
+    assert_close("topk_w", to_host(d_w), w, 1e-5)
+
+
 def test_sigmoid_key_bit_exact_on_a_sweep():
     """sig32 on the GPU equals the oracle's bit for bit: each row holds two
     adjacent binary32 logits, so the top-1 on sig32(s) depends on the last bit
@@ -306,6 +352,10 @@ EDGE = {
                                                                  lo=3, hi=3),
     "all_sentinel": S.WORKLOADS["olmoe_share"].with_(T=64, D=128, E=8, K=2, F=128, lo=8, hi=8),
     "tiny_capacity": S.WORKLOADS["mixtral_cap"].with_(T=100, D=128, F=128, cap=0.05),
+    # long batches: the un-permute takes 4 (K <= 2) or 2 (K <= 4) tokens per
+    # wave; ragged last wave
+    "unpermute_4_per_wave": S.WORKLOADS["minimind"].with_(T=16387, D=128, F=64, E=8, K=2),
+    "unpermute_2_per_wave": S.WORKLOADS["tiny_fp32"].with_(T=8195, D=192, F=64, E=6, K=3),
     "many_empty_experts": S.WORKLOADS["deepseek_v3"].with_(T=9, D=128, E=256, K=8, F=128),
 }
 
