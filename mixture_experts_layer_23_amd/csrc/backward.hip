@@ -27,8 +27,12 @@ int launch_unpermute(const moe_config& c, const void* dxp, const int32_t* slot_r
                      const int32_t* offsets, const float* ds, const float* wr, const float* dxr,
                      void* dx, hipStream_t st);
 
-// L lanes per token (L = min(64, pow2ceil(E))), EPL experts per lane
-template <int L, int EPL>
+// L lanes per token (L = min(64, pow2ceil(E))), EPL experts per lane.  With
+// KM > 0 (token choice, K <= KM) a token's slot data (weights, gradients,
+// indices, and the indexed logits) are loaded into registers up front, all
+// loads in flight together (indices clamped to the last slot, extra entries
+// never used); KM = 0 walks the slots in memory.  Same arithmetic and order.
+template <int L, int EPL, int KM>
 __global__ __launch_bounds__(256) void gating_bwd_kernel(
     const float* __restrict__ logits, const int32_t* __restrict__ idx,
     const float* __restrict__ gw, const float* __restrict__ dg, const float* __restrict__ dlx,
@@ -59,6 +63,83 @@ __global__ __launch_bounds__(256) void gating_bwd_kernel(
     for (int j = 0; j < EPL; ++j) {
       const int e = sub + L * j;
       if (e < E) out[j] = g[e] * (d[e] - G);
+    }
+  } else if constexpr (KM > 0) {
+    const int32_t* it = idx + (size_t)t * K;
+    float gk[KM], dk[KM], sk[KM];
+    int ik[KM];
+#pragma unroll
+    for (int k = 0; k < KM; ++k) {
+      const int kk = k < K ? k : K - 1;
+      gk[k] = g[kk];
+      dk[k] = d[kk];
+      ik[k] = it[kk];
+    }
+    float G = 0.f;
+#pragma unroll
+    for (int k = 0; k < KM; ++k)
+      if (k < K) G = fmaf(gk[k], dk[k], G);
+    if (score == 0 && gating == 0) {
+      float sv[EPL], m = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) {
+        const int e = sub + L * j;
+        const float v = s[e < E ? e : 0];
+        sv[j] = (e < E) ? v : -INFINITY;
+        m = fmaxf(m, sv[j]);
+      }
+#pragma unroll
+      for (int o = L / 2; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+      float z = 0.f;
+#pragma unroll
+      for (int j = 0; j < EPL; ++j)
+        if (sub + L * j < E) z += expf(sv[j] - m);
+#pragma unroll
+      for (int o = L / 2; o >= 1; o >>= 1) z += __shfl_xor(z, o, 64);
+      float dp[EPL];
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) dp[j] = 0.f;
+#pragma unroll
+      for (int k = 0; k < KM; ++k) {
+        const int e = ik[k];
+        if (k < K && (e % L) == sub) {
+          const int jj = e / L;
+#pragma unroll
+          for (int j = 0; j < EPL; ++j)
+            if (j == jj) dp[j] += dk[k];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < EPL; ++j)
+        if (sub + L * j < E) out[j] = (expf(sv[j] - m) / z) * (dp[j] - G);
+    } else {
+      if (score == 1) {
+#pragma unroll
+        for (int k = 0; k < KM; ++k) sk[k] = s[ik[k]];
+      }
+      float S = 0.f;
+      if (score == 1 && gating == 1) {
+#pragma unroll
+        for (int k = 0; k < KM; ++k)
+          if (k < K) S += 1.0f / (1.0f + expf(-sk[k]));
+      }
+#pragma unroll
+      for (int k = 0; k < KM; ++k) {
+        const int e = ik[k];
+        if (k >= K || (e % L) != sub) continue;
+        float v;
+        if (score == 0) {
+          v = gk[k] * (dk[k] - G);
+        } else {
+          const float sg = 1.0f / (1.0f + expf(-sk[k]));
+          const float dsig = sg * (1.0f - sg);
+          v = (gating == 0) ? dk[k] * dsig : ((dk[k] - G) / S) * dsig;
+        }
+        const int jj = e / L;
+#pragma unroll
+        for (int j = 0; j < EPL; ++j)
+          if (j == jj) out[j] = v;
+      }
     }
   } else {
     const int32_t* it = idx + (size_t)t * K;
@@ -135,8 +216,16 @@ static int launch_gating_bwd_t(const moe_config& c, const float* lg, const int32
                                const float* gw, const float* dg, const float* dlx,
                                const float* jit, float* ds, float* ds_copy, hipStream_t st) {
   const int grid = (int)cdiv((int64_t)c.T * L, 256);
-  MOE_LAUNCH("gating_bwd", (gating_bwd_kernel<L, EPL>), dim3(grid), dim3(256), 0, st, lg, idx,
-             gw, dg, dlx, jit, c.T, c.E, slot_width(c), c.score_fn, c.gating, ds, ds_copy);
+#define GBK(KMV)                                                                             \
+  MOE_LAUNCH("gating_bwd", (gating_bwd_kernel<L, EPL, KMV>), dim3(grid), dim3(256), 0, st, lg, \
+             idx, gw, dg, dlx, jit, c.T, c.E, slot_width(c), c.score_fn, c.gating, ds, ds_copy)
+  if (idx && c.K <= 2) GBK(2);
+  else if (idx && c.K <= 4) GBK(4);
+  else if (idx && c.K <= 8) GBK(8);
+#undef GBK
+  else
+    MOE_LAUNCH("gating_bwd", (gating_bwd_kernel<L, EPL, 0>), dim3(grid), dim3(256), 0, st, lg,
+               idx, gw, dg, dlx, jit, c.T, c.E, slot_width(c), c.score_fn, c.gating, ds, ds_copy);
   return MOE_OK;
 }
 
@@ -209,21 +298,30 @@ __global__ __launch_bounds__(256) void router_wgrad_skinny_kernel(
 #pragma unroll
     for (int i = 0; i < W; ++i) acc[e][i] = 0.f;
   }
-#pragma unroll 4
-  for (int t = t0 + wave; t < t1; t += 4) {
-    float xv[W];
-    if (dok) RowLoad<T, W>::f32(x + (size_t)t * D + d, xv);
-    else
+  // four of the wave's tokens per step, every load issued before the
+  // arithmetic: x unconditionally (lanes past D re-read column 0 and never
+  // store), ds as wave-uniform scalar loads (tokens past the chunk and
+  // experts past E get a zero weight); the sums run in token order
+  const int dl = dok ? d : 0;
+  for (int tb = t0 + wave; tb < t1; tb += 16) {
+    float xv[4][W], sv[4][EM];
 #pragma unroll
-      for (int i = 0; i < W; ++i) xv[i] = 0.f;
-    const float* dsr = ds + (size_t)t * E;
+    for (int u = 0; u < 4; ++u) {
+      const int t = __builtin_amdgcn_readfirstlane(min(tb + 4 * u, t1 - 1));
+      RowLoad<T, W>::f32(x + (size_t)t * D + dl, xv[u]);
+      const float* dsr = ds + (size_t)t * E;
 #pragma unroll
-    for (int e = 0; e < EM; ++e) {
-      if (e < E) {
-        const float s = dsr[e];
+      for (int e = 0; e < EM; ++e) sv[u][e] = dsr[e < E ? e : 0];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const bool tv = tb + 4 * u < t1;
+#pragma unroll
+      for (int e = 0; e < EM; ++e) {
+        const float s = (tv && e < E) ? sv[u][e] : 0.f;
         accb[e] += s;
 #pragma unroll
-        for (int i = 0; i < W; ++i) acc[e][i] = fmaf(s, xv[i], acc[e][i]);
+        for (int i = 0; i < W; ++i) acc[e][i] = fmaf(s, xv[u][i], acc[e][i]);
       }
     }
   }

@@ -126,6 +126,132 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const T* __restrict__ 
   }
 }
 
+// Few slots per token (slot width <= KM <= 8): the same combine with the
+// slot table read as wave-uniform scalars and, per 16-byte column chunk,
+// every kept slot's row load issued before any is added (an unused slot
+// re-reads row 0 and is not added); TPW consecutive tokens per wave.  Same
+// terms in the same order as combine_kernel.
+template <typename T, int KM, int TPW>
+__global__ __launch_bounds__(256) void combine_few_kernel(const T* __restrict__ o,
+                                                          const int32_t* __restrict__ slot_row,
+                                                          const float* __restrict__ topk_w,
+                                                          const int32_t* __restrict__ offsets,
+                                                          int EL, int n_shared, int T_, int K,
+                                                          int D, T* __restrict__ y) {
+  constexpr int VEC = Elem<T>::VEC;
+  const int lane = threadIdx.x & 63;
+  const int t0 = __builtin_amdgcn_readfirstlane((blockIdx.x * 4 + (threadIdx.x >> 6)) * TPW);
+  if (t0 >= T_) return;
+  int rows[TPW][KM];
+  float gk[TPW][KM];
+  int64_t srow[TPW];
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) {
+    const int t = t0 + j;
+    const bool tv = t < T_;
+#pragma unroll
+    for (int k = 0; k < KM; ++k) {
+      const bool ok = tv && k < K;
+      rows[j][k] = ok ? slot_row[(size_t)t * K + k] : -1;
+      gk[j][k] = ok ? topk_w[(size_t)t * K + k] : 0.f;
+    }
+    srow[j] = (tv && n_shared) ? (int64_t)offsets[EL] + t : -1;
+  }
+  for (int d0 = lane * VEC; d0 < D; d0 += 64 * VEC) {
+    Vec16<T> v[TPW][KM], vs[TPW];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+#pragma unroll
+      for (int k = 0; k < KM; ++k)
+        v[j][k].load(o + (size_t)(rows[j][k] >= 0 ? rows[j][k] : 0) * D + d0);
+      if (n_shared) vs[j].load(o + (size_t)(srow[j] >= 0 ? srow[j] : 0) * D + d0);
+    }
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+      if (t0 + j >= T_) continue;
+      float acc[VEC];
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
+#pragma unroll
+      for (int k = 0; k < KM; ++k)
+        if (rows[j][k] >= 0) {
+          float f[VEC];
+          v[j][k].to_f32(f);
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) acc[i] = fmaf(gk[j][k], f[i], acc[i]);
+        }
+      if (srow[j] >= 0) {
+        float f[VEC];
+        vs[j].to_f32(f);
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) acc[i] += f[i];
+      }
+      Vec16<T> out;
+      out.from_f32(acc);
+      out.store(y + (size_t)(t0 + j) * D + d0);
+    }
+  }
+}
+
+// Few slots per token: combine backward for all of a token's slots in one
+// pass over the row (dy read once per chunk, every slot's row load in flight
+// together), per-slot lane partials of the dot in the same order as
+// combine_bwd_kernel, then the same shuffle tree.
+template <typename T, int KM>
+__global__ __launch_bounds__(256) void combine_bwd_few_kernel(const T* __restrict__ o,
+                                                              const T* __restrict__ dy,
+                                                              const int32_t* __restrict__ slot_row,
+                                                              const float* __restrict__ topk_w,
+                                                              int T_, int K, int D,
+                                                              float* __restrict__ dg,
+                                                              T* __restrict__ d_o) {
+  constexpr int VEC = Elem<T>::VEC;
+  const int lane = threadIdx.x & 63;
+  const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+  if (t >= T_) return;
+  int rows[KM];
+  float gk[KM], dot[KM];
+#pragma unroll
+  for (int k = 0; k < KM; ++k) {
+    rows[k] = k < K ? slot_row[(size_t)t * K + k] : -1;
+    gk[k] = k < K ? topk_w[(size_t)t * K + k] : 0.f;
+    dot[k] = 0.f;
+  }
+  for (int d0 = lane * VEC; d0 < D; d0 += 64 * VEC) {
+    Vec16<T> vy, vo[KM];
+    vy.load(dy + (size_t)t * D + d0);
+#pragma unroll
+    for (int k = 0; k < KM; ++k) vo[k].load(o + (size_t)(rows[k] >= 0 ? rows[k] : 0) * D + d0);
+    float fy[VEC];
+    vy.to_f32(fy);
+#pragma unroll
+    for (int k = 0; k < KM; ++k) {
+      if (rows[k] < 0) continue;
+      float fo[VEC], fd[VEC];
+      vo[k].to_f32(fo);
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) {
+        dot[k] = fmaf(fy[i], fo[i], dot[k]);
+        fd[i] = gk[k] * fy[i];
+      }
+      Vec16<T> vd;
+      vd.from_f32(fd);
+      vd.store(d_o + (size_t)rows[k] * D + d0);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < KM; ++k) {
+    if (k >= K) break;
+    float v = 0.f;
+    if (rows[k] >= 0) {
+      v = dot[k];
+#pragma unroll
+      for (int mm = 32; mm >= 1; mm >>= 1) v += __shfl_xor(v, mm, 64);
+    }
+    if (lane == 0) dg[(size_t)t * K + k] = v;
+  }
+}
+
 // dx[t] = sum_k [row>=0] dx_perm[row] + dx_perm[shared row of t]
 //         + router part: sum_e ds[t,e] W_r[e,:] (inline for E <= EM) or dxr[t]
 // one wave per token, lanes stride over 16-byte vectors of the row; slots in
@@ -213,7 +339,8 @@ __global__ __launch_bounds__(256) void unpermute_few_kernel(
     T* __restrict__ dx) {
   constexpr int VEC = Elem<T>::VEC;
   const int lane = threadIdx.x & 63;
-  const int t0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * TPW;
+  // wave-uniform token index (scalar loads of the slot table and ds)
+  const int t0 = __builtin_amdgcn_readfirstlane((blockIdx.x * 4 + (threadIdx.x >> 6)) * TPW);
   if (t0 >= T_) return;
   int rows[TPW][KM];
   int64_t srow[TPW];
@@ -231,14 +358,32 @@ __global__ __launch_bounds__(256) void unpermute_few_kernel(
     }
   }
   for (int d0 = lane * VEC; d0 < D; d0 += 64 * VEC) {
+    // every load is issued (an unused slot re-reads row 0 of the row buffer
+    // and is not added), so that none waits for another; the router weights
+    // come in groups of four experts (experts past E re-read expert 0 and are
+    // not added), the first group together with the rows
+    float w[4][VEC];
+    auto load_w = [&](int e0) __attribute__((always_inline)) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = e0 + u;
+        const float4* wp = reinterpret_cast<const float4*>(wr + (size_t)(e < E ? e : 0) * D + d0);
+#pragma unroll
+        for (int q = 0; q < VEC / 4; ++q) {
+          const float4 f4 = wp[q];
+          w[u][4 * q] = f4.x; w[u][4 * q + 1] = f4.y; w[u][4 * q + 2] = f4.z; w[u][4 * q + 3] = f4.w;
+        }
+      }
+    };
     Vec16<T> v[TPW][KM], vs[TPW];
 #pragma unroll
     for (int j = 0; j < TPW; ++j) {
 #pragma unroll
       for (int k = 0; k < KM; ++k)
-        if (rows[j][k] >= 0) v[j][k].load(dxp + (size_t)rows[j][k] * D + d0);
-      if (srow[j] >= 0) vs[j].load(dxp + (size_t)srow[j] * D + d0);
+        v[j][k].load(dxp + (size_t)(rows[j][k] >= 0 ? rows[j][k] : 0) * D + d0);
+      if (n_shared) vs[j].load(dxp + (size_t)(srow[j] >= 0 ? srow[j] : 0) * D + d0);
     }
+    if constexpr (EM > 0) load_w(0);
     float acc[TPW][VEC];
 #pragma unroll
     for (int j = 0; j < TPW; ++j) {
@@ -261,19 +406,16 @@ __global__ __launch_bounds__(256) void unpermute_few_kernel(
     }
     if constexpr (EM > 0) {
 #pragma unroll
-      for (int e = 0; e < EM; ++e) {
-        if (e < E) {
-          float w[VEC];
-          const float4* wp = reinterpret_cast<const float4*>(wr + (size_t)e * D + d0);
+      for (int e0 = 0; e0 < EM; e0 += 4) {
+        if (e0 > 0) load_w(e0);
 #pragma unroll
-          for (int q = 0; q < VEC / 4; ++q) {
-            const float4 u = wp[q];
-            w[4 * q] = u.x; w[4 * q + 1] = u.y; w[4 * q + 2] = u.z; w[4 * q + 3] = u.w;
+        for (int u = 0; u < 4; ++u) {
+          if (e0 + u < E) {
+#pragma unroll
+            for (int j = 0; j < TPW; ++j)
+#pragma unroll
+              for (int i = 0; i < VEC; ++i) acc[j][i] = fmaf(s_e[j][e0 + u], w[u][i], acc[j][i]);
           }
-#pragma unroll
-          for (int j = 0; j < TPW; ++j)
-#pragma unroll
-            for (int i = 0; i < VEC; ++i) acc[j][i] = fmaf(s_e[j][e], w[i], acc[j][i]);
         }
       }
     } else {
@@ -295,8 +437,44 @@ __global__ __launch_bounds__(256) void unpermute_few_kernel(
   }
 }
 
+template <typename T>
+static int combine_few(const moe_config& c, const void* o_perm, const int32_t* offsets,
+                       const int32_t* slot_row, const float* topk_w, void* y, hipStream_t st) {
+  const int EL = c.expert_hi - c.expert_lo, W = slot_width(c);
+#define CF1(KMV, TPWV)                                                                     \
+  MOE_LAUNCH("combine", (combine_few_kernel<T, KMV, TPWV>), dim3((unsigned)cdiv(c.T, 4 * TPWV)), \
+             dim3(256), 0, st, (const T*)o_perm, slot_row, topk_w, offsets, EL, c.n_shared,    \
+             c.T, W, c.D, (T*)y)
+#define CF(KMV)                                                    \
+  if (KMV < 8 && c.T >= 4096 * (8 / KMV)) CF1(KMV, 8 / KMV);         \
+  else CF1(KMV, 1);
+  if (W <= 2) { CF(2) } else if (W <= 4) { CF(4) } else { CF(8) }
+#undef CF
+#undef CF1
+  return MOE_OK;
+}
+
+template <typename T>
+static int combine_bwd_few(const moe_config& c, const void* o_perm, const void* dy,
+                           const int32_t* slot_row, const float* topk_w, float* dg, void* d_o,
+                           hipStream_t st) {
+  const int W = slot_width(c);
+  const dim3 grid((unsigned)cdiv(c.T, 4));
+#define CB(KMV)                                                                               \
+  MOE_LAUNCH("combine_bwd", (combine_bwd_few_kernel<T, KMV>), grid, dim3(256), 0, st,         \
+             (const T*)o_perm, (const T*)dy, slot_row, topk_w, c.T, W, c.D, dg, (T*)d_o)
+  if (W <= 2) CB(2); else if (W <= 4) CB(4); else CB(8);
+#undef CB
+  return MOE_OK;
+}
+
 int launch_combine(const moe_config& c, const void* o_perm, const int32_t* offsets,
                    const int32_t* slot_row, const float* topk_w, void* y, hipStream_t st) {
+  if (slot_width(c) <= 8) {
+    if (c.dtype == MOE_BF16)
+      return combine_few<bf16_t>(c, o_perm, offsets, slot_row, topk_w, y, st);
+    return combine_few<float>(c, o_perm, offsets, slot_row, topk_w, y, st);
+  }
   const int EL = c.expert_hi - c.expert_lo;
   const int grid = (int)cdiv(c.T, 4);
   if (c.dtype == MOE_BF16)
@@ -313,6 +491,11 @@ int launch_combine(const moe_config& c, const void* o_perm, const int32_t* offse
 int launch_combine_bwd(const moe_config& c, const void* o_perm, const void* dy,
                        const int32_t* slot_row, const float* topk_w, float* dg, void* d_o,
                        hipStream_t st) {
+  if (slot_width(c) <= 8) {
+    if (c.dtype == MOE_BF16)
+      return combine_bwd_few<bf16_t>(c, o_perm, dy, slot_row, topk_w, dg, d_o, st);
+    return combine_bwd_few<float>(c, o_perm, dy, slot_row, topk_w, dg, d_o, st);
+  }
   const int grid = (int)cdiv(c.T, 4);
   if (c.dtype == MOE_BF16)
     MOE_LAUNCH("combine_bwd", combine_bwd_kernel<bf16_t>, dim3(grid), dim3(256), 0, st,

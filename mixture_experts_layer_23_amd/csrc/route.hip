@@ -84,21 +84,19 @@ __global__ __launch_bounds__(256) void router_skinny_kernel(const T* __restrict_
   const float* wsrc = wr;
   if constexpr (STAGE) {
     // staging in batches of eight 16-byte loads per thread, all in flight
-    // before the first LDS store
-    const int n4 = (E * D) >> 2;
-    for (int i0 = 0; i0 < n4; i0 += 256 * 8) {
+    // before the first LDS store (whole batches unconditional, so that the
+    // compiler does not sink each load into a guarded store); then the tail
+    const float4* w4 = reinterpret_cast<const float4*>(wr);
+    const int n4 = (E * D) >> 2, tid = (int)threadIdx.x;
+    int i0 = 0;
+    for (; i0 + 256 * 8 <= n4; i0 += 256 * 8) {
       float4 v[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i = i0 + u * 256 + (int)threadIdx.x;
-        if (i < n4) v[u] = reinterpret_cast<const float4*>(wr)[i];
-      }
+      for (int u = 0; u < 8; ++u) v[u] = w4[i0 + u * 256 + tid];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i = i0 + u * 256 + (int)threadIdx.x;
-        if (i < n4) sw4[i] = v[u];
-      }
+      for (int u = 0; u < 8; ++u) sw4[i0 + u * 256 + tid] = v[u];
     }
+    for (int i = i0 + tid; i < n4; i += 256) sw4[i] = w4[i];
     __syncthreads();
     wsrc = reinterpret_cast<const float*>(sw4);
   }
@@ -111,15 +109,19 @@ __global__ __launch_bounds__(256) void router_skinny_kernel(const T* __restrict_
     double acc0[EM], acc1[EM];
 #pragma unroll
     for (int e = 0; e < EM; ++e) { acc0[e] = 0.0; acc1[e] = 0.0; }
+    // every load is issued (past-the-end lanes re-read column 0, a lone
+    // last token re-reads itself; both are discarded below), so that no
+    // branch makes the compiler wait for one load before issuing the next
+    const T* xa_row = x + (size_t)t0 * D;
+    const T* xb_row = x + (size_t)(two ? t0 + 1 : t0) * D;
     for (int dc = 0; dc < D; dc += 64 * VEC * NV) {
       Vec16<T> va[NV], vb[NV];
 #pragma unroll
       for (int v = 0; v < NV; ++v) {
         const int d0 = dc + (v * 64 + lane) * VEC;
-        if (d0 < D) {
-          va[v].load(x + (size_t)t0 * D + d0);
-          if (two) vb[v].load(x + (size_t)(t0 + 1) * D + d0);
-        }
+        const int dl = d0 < D ? d0 : 0;
+        va[v].load(xa_row + dl);
+        vb[v].load(xb_row + dl);
       }
 #pragma unroll
       for (int v = 0; v < NV; ++v) {
@@ -397,11 +399,20 @@ __global__ __launch_bounds__(256) void route_select_kernel(
   float sv[EPL], key[EPL];
   bool used[EPL];
   float m = -INFINITY;
+  // all logit (and selection-bias) loads first, unconditional (index
+  // clamped), so that they are in flight together
+  float sl[EPL], bl[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const int e = sub + L * j;
+    sl[j] = s[e < E ? e : 0];
+    bl[j] = selb ? selb[e < E ? e : 0] : 0.0f;
+  }
 #pragma unroll
   for (int j = 0; j < EPL; ++j) {
     const int e = sub + L * j;
     const bool ok = e < E;
-    sv[j] = ok ? s[e] : -INFINITY;
+    sv[j] = ok ? sl[j] : -INFINITY;
     if (jit && ok) {
       sv[j] = sv[j] * jit[(size_t)t * E + e];
       s[e] = sv[j];
@@ -412,7 +423,7 @@ __global__ __launch_bounds__(256) void route_select_kernel(
         key[j] = (float)((double)sv[j] + (double)eps[(size_t)t * E + e] *
                                              softplus64((double)nlg[(size_t)t * E + e]));
     } else {
-      key[j] = ok ? (sig32(sv[j]) + (selb ? selb[e] : 0.0f)) : -INFINITY;
+      key[j] = ok ? (sig32(sv[j]) + bl[j]) : -INFINITY;
     }
     used[j] = !ok;
     m = fmaxf(m, sv[j]);

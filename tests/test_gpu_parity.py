@@ -352,6 +352,11 @@ EDGE = {
                                                                  lo=3, hi=3),
     "all_sentinel": S.WORKLOADS["olmoe_share"].with_(T=64, D=128, E=8, K=2, F=128, lo=8, hi=8),
     "tiny_capacity": S.WORKLOADS["mixtral_cap"].with_(T=100, D=128, F=128, cap=0.05),
+    # more than 8 slots per token: the generic slot loops of the combine, its
+    # backward, the gating backward and the un-permute
+    "K12_softmax_B": S.WORKLOADS["tiny_fp32"].with_(T=150, E=24, K=12, F=64),
+    "K10_sigmoid_A": S.WORKLOADS["deepseek_v3"].with_(T=120, D=128, E=32, K=10, F=64,
+                                                      gating=S.GATE_A),
     # long batches: the un-permute takes 4 (K <= 2) or 2 (K <= 4) tokens per
     # wave; ragged last wave
     "unpermute_4_per_wave": S.WORKLOADS["minimind"].with_(T=16387, D=128, F=64, E=8, K=2),
