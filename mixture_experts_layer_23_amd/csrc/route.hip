@@ -189,8 +189,15 @@ __global__ __launch_bounds__(256) void router_skinny_kernel(const T* __restrict_
       for (int e = 0; e < EM; ++e)
         if (e < E) z += expf(sv[e] - m);
       if (fs.lse) fs.lse[t] = m + logf(z);
-      float gsum = 0.f;
-      for (int k = 0; k < fs.K; ++k) {
+      // K <= E <= EM rounds; the weights stay in registers until the
+      // normaliser is known
+      float gsum = 0.f, gk[EM];
+      int ik[EM];
+#pragma unroll
+      for (int k = 0; k < EM; ++k) {
+        gk[k] = 0.f;
+        ik[k] = 0;
+        if (k >= fs.K) continue;
         float bk = -INFINITY, sc = -INFINITY;
         int bi = 0x7fffffff;
 #pragma unroll
@@ -202,14 +209,19 @@ __global__ __launch_bounds__(256) void router_skinny_kernel(const T* __restrict_
           if (e == bi) used[e] = true;
         const float g = fs.score == 0 ? expf(sc - m) : 1.0f / (1.0f + expf(-sc));
         gsum += g;
-        fs.idx[(size_t)t * fs.K + k] = bi;
-        fs.w[(size_t)t * fs.K + k] = g;
+        gk[k] = g;
+        ik[k] = bi;
       }
       float den = 1.f;
       if (fs.score == 0) den = (fs.gating == 0) ? z : gsum;
       else den = (fs.gating == 0) ? 1.f : gsum;
-      if (!(fs.score == 1 && fs.gating == 0))
-        for (int k = 0; k < fs.K; ++k) fs.w[(size_t)t * fs.K + k] = fs.w[(size_t)t * fs.K + k] / den;
+      const bool raw = fs.score == 1 && fs.gating == 0;
+#pragma unroll
+      for (int k = 0; k < EM; ++k) {
+        if (k >= fs.K) break;
+        fs.idx[(size_t)t * fs.K + k] = ik[k];
+        fs.w[(size_t)t * fs.K + k] = raw ? gk[k] : gk[k] / den;
+      }
     }
   }
 }
@@ -438,8 +450,10 @@ __global__ __launch_bounds__(256) void route_select_kernel(
   for (int o = L / 2; o >= 1; o >>= 1) z += __shfl_xor(z, o, 64);
   if (sub == 0 && lse_out) lse_out[t] = m + logf(z);
 
-  // K rounds of arg-max; the chosen raw scores are kept by lane sub==k%L
-  float gsum = 0.f;
+  // K rounds of arg-max (K <= L); lane sub == k keeps round k's expert and
+  // weight in registers and writes them once the normaliser is known
+  float gsum = 0.f, my_g = 0.f;
+  int my_i = 0;
   for (int k = 0; k < K; ++k) {
     float bk = -INFINITY;
     int bi = 0x7fffffff;
@@ -470,19 +484,16 @@ __global__ __launch_bounds__(256) void route_select_kernel(
     if (score == 0) g = expf(sc - m);                 // unnormalised softmax term
     else g = 1.0f / (1.0f + expf(-sc));               // raw sigmoid score
     gsum += g;
-    if (sub == 0) {
-      topk_idx[(size_t)t * K + k] = bi;
-      topk_w[(size_t)t * K + k] = g;
-    }
+    if (sub == k) { my_i = bi; my_g = g; }
   }
-  if (sub == 0) {
+  if (sub < K) {
     // normalise: softmax A divides by the full sum z; B by the selected sum;
     // sigmoid A keeps the raw score; sigmoid B divides by the selected sum.
     float den = 1.f;
     if (score == 0) den = (gating == 0) ? z : gsum;
     else den = (gating == 0) ? 1.f : gsum;
-    if (!(score == 1 && gating == 0))
-      for (int k = 0; k < K; ++k) topk_w[(size_t)t * K + k] = topk_w[(size_t)t * K + k] / den;
+    topk_idx[(size_t)t * K + sub] = my_i;
+    topk_w[(size_t)t * K + sub] = (score == 1 && gating == 0) ? my_g : my_g / den;
   }
 }
 
