@@ -597,15 +597,16 @@ int launch_backward(const moe_config& c, const void* x, const float* wr, const f
   float* dxr = (c.E > 16) ? reinterpret_cast<float*>(ws + L.dxr) : nullptr;
   int rc;
   if ((rc = launch_combine_bwd(c, o_perm, dy, slot_row, topk_w, dg, d_o, st))) return rc;
-  if ((rc = launch_gating_bwd(c, logits, idx, topk_w, dg, dlx, jit, ds, d_logits_out, st)))
-    return rc;
   // Independent parts overlap on two side streams:
   //   main:   down dgrad -> up dgrad -> (router) -> un-permute
   //   side 0: down wgrad -> (after down dgrad) up wgrad
-  //   side 1: router weight / bias gradient (and dgrad for many experts)
+  //   side 1: gating backward, then the router weight / bias gradient (and
+  //           dgrad for many experts); the un-permute waits for it
   hipStream_t s0 = side_stream(0), s1 = side_stream(1);
   if (!s0 || !s1) { set_error("side streams", hipErrorInvalidResourceHandle); return MOE_ELAUNCH; }
   if ((rc = fork_stream(st, s0)) || (rc = fork_stream(st, s1))) return rc;
+  if ((rc = launch_gating_bwd(c, logits, idx, topk_w, dg, dlx, jit, ds, d_logits_out, s1)))
+    return rc;
   if (c.dtype == MOE_BF16) {
     if ((rc = router_bwd_t<bf16_t>(c, x, wr, ds, dxr, dwr, drb, ws, L, s1))) return rc;
   } else {
