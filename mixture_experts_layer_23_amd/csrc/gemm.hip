@@ -1738,14 +1738,13 @@ static void tile_space(GemmParams& P, int grouping, int bm) {
 // 1 = 128-row tiles / 2 stages, 2 = 256-row tiles / 3 stages, 3 / 4 = 256 x
 // 256 / 256 x 128 large tiles on 4 waves, 5 / 6 = the same on 8 waves,
 // 7 / 8 = persistent 256 x 256 / 256 x 128 on 8 waves.
-// MOE_GEMM_CFG overrides the choice (measurement only): a number for every
-// GEMM, or "name=cfg" pairs separated by commas (e.g.
-// "gemm_down_dgrad=1,gemm_gate_up_fwd=5").
+// MOE_GEMM_CFG overrides the choice (measurement, and tests that run every
+// kernel variant): a number for every GEMM, or "name=cfg" pairs separated by
+// commas (e.g. "gemm_down_dgrad=1,gemm_gate_up_fwd=5").  Read at every
+// launch, so a process can change it between calls.
 static int cfg_override(const char* name) {
-  static const std::string spec = [] {
-    const char* e = getenv("MOE_GEMM_CFG");
-    return std::string(e ? e : "");
-  }();
+  const char* env = getenv("MOE_GEMM_CFG");
+  const std::string spec(env ? env : "");
   if (spec.empty()) return -1;
   if (spec.find('=') == std::string::npos) return atoi(spec.c_str());
   const std::string key = std::string(name) + "=";
