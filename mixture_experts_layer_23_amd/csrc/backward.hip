@@ -397,8 +397,10 @@ __global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restr
 }
 
 // ---------------------------------------------------------------------------
-// router GEMMs for many experts: SIMT fp32 tiles of 64 x 64, k-slabs of 16 in
-// LDS, 4 x 4 register micro-tile, optional split over k (partials).
+// router GEMMs for many experts when E is not a multiple of 4 (otherwise
+// router_gemm_kernel, on the matrix cores): SIMT fp32 tiles of 64 x 64,
+// k-slabs of 16 in LDS, 4 x 4 register micro-tile, optional split over k
+// (partials).
 //   C[split][m][n] = sum_{k in split} A(m,k) B(k,n)
 //   A(m,k) = AKC ? A[m*lda + k] : A[k*lda + m];  B(k,n) = B[k*ldb + n]
 // ---------------------------------------------------------------------------
