@@ -60,6 +60,9 @@ def parse():
     ap.add_argument("--graph", action="store_true",
                     help="also time the step replayed as one HIP graph (reported as ms_per_step_graph)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=None)
+    ap.add_argument("--no-isolated", action="store_true",
+                    help="skip the untimed pass that times every kernel alone "
+                         "(all kernels on one stream)")
     ap.add_argument("--json-out", default=None)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (for HBM counter scaling)")
@@ -237,6 +240,24 @@ def main():
         ms_graph = timed(sg.replay)
         del sg
 
+    # untimed pass with every kernel on the caller's stream (MOE_SERIAL_STREAMS):
+    # each kernel's duration alone, next to the overlapped ones of the step
+    kt_iso = None
+    if not args.no_isolated:
+        os.environ["MOE_SERIAL_STREAMS"] = "1"
+        try:
+            for _ in range(args.warmup):
+                step()
+            torch.cuda.synchronize()
+            L.timing_enable(True)
+            for _ in range(args.steps):
+                step()
+            torch.cuda.synchronize()
+            L.timing_enable(False)
+            kt_iso = L.timing_report()
+        finally:
+            del os.environ["MOE_SERIAL_STREAMS"]
+
     offsets = layer.offsets.cpu().numpy()
     counts = layer.counts.cpu().numpy()
     n_rows_local = int(offsets[wl.n_local]) if wl.n_local > 0 else 0
@@ -289,6 +310,31 @@ def main():
         if name in kernels:
             kernels[name]["gbs"] = b / (kernels[name]["avg_ms"] * 1e-3) / 1e9
             kernels[name]["hbm_frac"] = kernels[name]["gbs"] / HBM_PEAK_GBS
+    kernels_iso = None
+    gemm_iso = None
+    if kt_iso:
+        kernels_iso = {}
+        fl_iso = ms_iso = 0.0
+        for name, (n, tot) in kt_iso.items():
+            avg = tot / n
+            e = dict(avg_ms=avg)
+            if name in GEMM_FLOPS_PER_ROW:
+                fl = GEMM_FLOPS_PER_ROW[name] * wl.D * wl.F * rows
+                e["tflops"] = fl / (avg * 1e-3) / 1e12
+                e["frac_of_peak"] = e["tflops"] / (BF16_PEAK_TFLOPS if wl.dtype == S.BF16
+                                                   else F32_PEAK_TFLOPS)
+                fl_iso += fl * n
+                ms_iso += tot
+            if name in stage_bytes:
+                e["gbs"] = stage_bytes[name] / (avg * 1e-3) / 1e9
+                e["hbm_frac"] = e["gbs"] / HBM_PEAK_GBS
+            kernels_iso[name] = e
+        if ms_iso:
+            t_iso = fl_iso / (ms_iso * 1e-3) / 1e12
+            gemm_iso = {"tflops": t_iso,
+                        "frac_of_peak": t_iso / (BF16_PEAK_TFLOPS if wl.dtype == S.BF16
+                                                 else F32_PEAK_TFLOPS),
+                        "ms_per_step": ms_iso / max(args.steps, 1)}
     n_live, tot_live = kt_live[dom]
     dom_avg = tot_live / n_live
     peak_t = BF16_PEAK_TFLOPS if wl.dtype == S.BF16 else F32_PEAK_TFLOPS
@@ -345,6 +391,9 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": kernels,
+        # the same kernels timed alone (untimed pass, one stream)
+        "grouped_gemm_isolated": gemm_iso,
+        "kernels_isolated": kernels_iso,
     }
     line = json.dumps(out)
     print(line, flush=True)

@@ -15,6 +15,8 @@
 //   sigmoid B: ds_{i_k} = ((dg_k - G) / sum_j sig_{i_j}) sig(1 - sig)
 // The centred form keeps the exact zeros: K = 1 with B gives 1*(dg - dg) = 0.
 // Router backward: dx += ds W_r; dW_r = ds^T x; d r_b = sum_t ds_t.
+#include <cstdlib>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -604,8 +606,14 @@ int launch_backward(const moe_config& c, const void* x, const float* wr, const f
   //   side 0: down wgrad -> (after down dgrad) up wgrad
   //   side 1: gating backward, then the router weight / bias gradient (and
   //           dgrad for many experts); the un-permute waits for it
-  hipStream_t s0 = side_stream(0), s1 = side_stream(1);
-  if (!s0 || !s1) { set_error("side streams", hipErrorInvalidResourceHandle); return MOE_ELAUNCH; }
+  // MOE_SERIAL_STREAMS set (measurement): everything on the caller's stream,
+  // so that per-kernel timings are those of each kernel alone
+  const bool serial = getenv("MOE_SERIAL_STREAMS") != nullptr;
+  hipStream_t s0 = serial ? st : side_stream(0), s1 = serial ? st : side_stream(1);
+  if (!serial && (!s0 || !s1)) {
+    set_error("side streams", hipErrorInvalidResourceHandle);
+    return MOE_ELAUNCH;
+  }
   if ((rc = fork_stream(st, s0)) || (rc = fork_stream(st, s1))) return rc;
   if ((rc = launch_gating_bwd(c, logits, idx, topk_w, dg, dlx, jit, ds, d_logits_out, s1)))
     return rc;

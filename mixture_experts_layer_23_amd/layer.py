@@ -8,6 +8,7 @@ Backward: moe_backward (with the aux-loss logit gradient as d_logits_extra)
 """
 from __future__ import annotations
 
+import os
 from dataclasses import dataclass
 
 import torch
@@ -162,25 +163,27 @@ class MoELayer:
         bias_step = (self.spec.bias_gamma != 0 and self.sel_bias is not None
                      and not self.spec.expert_choice)
         side = self.use_aux or self.use_seq or bias_step
+        # MOE_SERIAL_STREAMS (measurement): the losses run on the main stream
+        side_stream = main if os.environ.get("MOE_SERIAL_STREAMS") else self._side
         if side:
             self._fork.record(main)
-            self._side.wait_event(self._fork)
+            side_stream.wait_event(self._fork)
             if self.use_aux:
                 L.aux_balance_loss(self.cfg, self.logits, self.counts, self.spec.alpha,
                                    self.spec.zlam, self.losses, self.dlogits_aux, self.ws,
-                                   stream=self._side)
+                                   stream=side_stream)
             if self.use_seq:
                 L.aux_seq_loss(self.cfg, self.logits, self.topk_idx, self.spec.seq_len,
                                self.spec.seq_alpha, self.seq_loss, self.dlogits_aux,
-                               self.use_aux, self.ws, stream=self._side)
+                               self.use_aux, self.ws, stream=side_stream)
             if bias_step:
                 L.moe_bias_update(self.cfg, self.counts, self.spec.bias_gamma, self.sel_bias,
-                                  stream=self._side)
+                                  stream=side_stream)
         L.moe_expert_ffn(self.cfg, x, self.x_perm, self.offsets, self.w_gate, self.w_up,
                          self.w_down, self.act, self.h, self.o_perm)
         L.moe_combine(self.cfg, self.o_perm, self.offsets, self.slot_row, self.topk_w, self.y)
         if side:
-            self._join.record(self._side)
+            self._join.record(side_stream)
             main.wait_event(self._join)
         return self.y
 
