@@ -298,6 +298,29 @@ MOE_DEV void gemm_epilogue(const GemmParams& P, f32x16_t (&acc)[2][2], char* reg
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, hi4 = (lane >> 5) * 4;
+  const int row_base = wm * 64;  // tile-relative first row of this wave
+  // SwiGLU backward: the activation chunks of this lane's eight items are
+  // loaded before the tile is staged, all in flight at once (items outside
+  // the valid rows / columns read the tile's first row and column and are not
+  // used), so one memory latency overlaps the staging
+  constexpr int NVV = sizeof(T) == 2 ? 1 : 2;  // 16-byte vectors per 8 values
+  constexpr int NPF = EPI == EPI_SWIGLU_BWD ? 8 : 1;
+  Vec16<T> pa[NPF][NVV], pb[NPF][NVV];
+  if constexpr (EPI == EPI_SWIGLU_BWD) {
+    const T* act = reinterpret_cast<const T*>(P.act);
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int item = lane + 64 * it;
+      const int row = item >> 3, col = wn * 64 + (item & 7) * 8;
+      const bool ok = row_base + row < rows_valid && col < cols_valid;
+      const T* src = act + (arow0 + m0 + (ok ? row_base + row : 0)) * 2 * P.F + n0 + (ok ? col : 0);
+#pragma unroll
+      for (int q = 0; q < NVV; ++q) {
+        pa[it][q].load(src + q * 4);
+        pb[it][q].load(src + P.F + q * 4);
+      }
+    }
+  }
   float* ep = reinterpret_cast<float*>(region);
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -329,21 +352,6 @@ MOE_DEV void gemm_epilogue(const GemmParams& P, f32x16_t (&acc)[2][2], char* reg
       o1.store(dst + 4);
     }
   };
-  auto load8 = [&](const T* src, float* v) {
-    if constexpr (sizeof(T) == 2) {
-      Vec16<T> o;
-      o.load(src);
-      o.to_f32(v);
-    } else {
-      Vec16<T> o0, o1;
-      o0.load(src);
-      o1.load(src + 4);
-      o0.to_f32(v);
-      o1.to_f32(v + 4);
-    }
-  };
-  const int row_base = wm * 64;  // tile-relative first row of this wave
-
   if constexpr (EPI == EPI_SWIGLU_FWD) {
     // LDS columns [0,32) hold a (gate), [32,64) hold b (up) of the same f's
     T* hout = reinterpret_cast<T*>(P.C1);
@@ -374,13 +382,15 @@ MOE_DEV void gemm_epilogue(const GemmParams& P, f32x16_t (&acc)[2][2], char* reg
       float v[8];
       read8(row, cg, v);
       if constexpr (EPI == EPI_SWIGLU_BWD) {
-        const T* act = reinterpret_cast<const T*>(P.act);
         T* dact = reinterpret_cast<T*>(P.C0);
         const int64_t grow = arow0 + m0 + row_base + row;
         const int f = n0 + col;
         float a[8], b[8], da[8], db[8];
-        load8(act + grow * 2 * P.F + f, a);
-        load8(act + grow * 2 * P.F + P.F + f, b);
+#pragma unroll
+        for (int q = 0; q < NVV; ++q) {
+          pa[it][q].to_f32(a + q * 4);
+          pb[it][q].to_f32(b + q * 4);
+        }
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
           const float sg = 1.0f / (1.0f + expf(-a[q]));
