@@ -82,19 +82,32 @@ __global__ __launch_bounds__(64) void rank_kernel(const int32_t* __restrict__ id
   int32_t* off = lds + E;   // [EL + 1] group offsets
   const int lane = threadIdx.x;
   const int EL = hi - lo;
+  // this lane's slot experts of every round, loaded up front (unconditional,
+  // index clamped; slots past TK are marked invalid below)
+  constexpr int R = kSlotTile / 64;
+  int ev[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t s = (int64_t)blockIdx.x * kSlotTile + r * 64 + lane;
+    ev[r] = idx[s < TK ? s : 0];
+  }
   for (int e = lane; e < E; e += 64) cnt[e] = 0;
   {
     // lane j owns local experts [j*per, (j+1)*per)
-    const int per = (EL + 63) / 64;
-    int kept = 0, drop = 0;
-    for (int i = 0; i < per; ++i) {
+    const int per = (EL + 63) / 64;  // <= 16 (E <= 1024)
+    int nk[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
       const int e = lane * per + i;
-      if (e < EL) {
-        const int n = counts_all[lo + e];
-        const int k = (capacity >= 0 && n > capacity) ? capacity : n;
-        kept += k;
-        drop += n - k;
-      }
+      nk[i] = (i < per && e < EL) ? counts_all[lo + e] : 0;
+    }
+    int kept = 0, drop = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int n = nk[i];
+      const int k = (capacity >= 0 && n > capacity) ? capacity : n;
+      kept += k;
+      drop += n - k;
     }
     int incl = kept;
 #pragma unroll
@@ -103,11 +116,12 @@ __global__ __launch_bounds__(64) void rank_kernel(const int32_t* __restrict__ id
       if (lane >= o) incl += u;
     }
     int run = incl - kept;
-    for (int i = 0; i < per; ++i) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
       const int e = lane * per + i;
-      if (e < EL) {
+      if (i < per && e < EL) {
         off[e] = run;
-        const int n = counts_all[lo + e];
+        const int n = nk[i];
         run += (capacity >= 0 && n > capacity) ? capacity : n;
       }
     }
@@ -122,10 +136,18 @@ __global__ __launch_bounds__(64) void rank_kernel(const int32_t* __restrict__ id
     }
   }
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int r = 0; r < kSlotTile / 64; ++r) {
+  // this tile's base position of each slot's expert, all loaded together
+  int tb[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t s = (int64_t)blockIdx.x * kSlotTile + r * 64 + lane;
+    tb[r] = tile_base[(size_t)blockIdx.x * E + (s < TK ? ev[r] : 0)];
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
     const int64_t s = (int64_t)blockIdx.x * kSlotTile + r * 64 + lane;
     const bool valid = s < TK;
-    const int e = valid ? idx[s] : 0;
+    const int e = valid ? ev[r] : 0;
     uint64_t peers = __ballot(valid);
     for (int b = 0; b < nbits; ++b) {
       const bool bit = (e >> b) & 1;
@@ -138,7 +160,7 @@ __global__ __launch_bounds__(64) void rank_kernel(const int32_t* __restrict__ id
     if (valid && (63 - __clzll(peers)) == lane) cnt[e] = base + __popcll(peers);
     __syncthreads();
     if (!valid) continue;
-    const int pos = tile_base[(size_t)blockIdx.x * E + e] + base + rank;
+    const int pos = tb[r] + base + rank;
     if (e < lo || e >= hi) {
       slot_row[s] = -2;
     } else if (capacity >= 0 && pos >= capacity) {
