@@ -360,6 +360,17 @@ int moe_route_expert_choice(const moe_config* cfg, const void* x, const float* w
 const char* moe_error_string(int code);
 
 /*
+ * Environment variables read at every call (measurement and tests only):
+ *   MOE_GEMM_CFG        forces the grouped-GEMM kernel variant: a number
+ *                       0..8 for every GEMM, or "name=cfg,..." pairs
+ *                       (gemm_gate_up_fwd, gemm_down_fwd, gemm_down_dgrad,
+ *                       gemm_down_wgrad, gemm_gate_up_dgrad, gemm_gate_up_wgrad).
+ *   MOE_SERIAL_STREAMS  when set, moe_backward runs every kernel on the
+ *                       caller's stream instead of overlapping independent
+ *                       parts on the library's side streams.
+ * MOE_SERIAL_STREAMS does not change any result; every MOE_GEMM_CFG variant
+ * meets the same tolerances (each is tested against the oracle).
+ *
  * Kernel timing for measurement: while enabled, every kernel the library
  * launches is bracketed by HIP events recorded on its own stream.
  * moe_timing_report() waits for those events and writes one line per kernel
