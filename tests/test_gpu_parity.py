@@ -352,6 +352,11 @@ EDGE = {
                                                                  lo=3, hi=3),
     "all_sentinel": S.WORKLOADS["olmoe_share"].with_(T=64, D=128, E=8, K=2, F=128, lo=8, hi=8),
     "tiny_capacity": S.WORKLOADS["mixtral_cap"].with_(T=100, D=128, F=128, cap=0.05),
+    "single_expert_K1": S.WORKLOADS["minimind"].with_(T=100, D=64, F=64, E=1, K=1),
+    "minimal_dims_sigmoid_A_shared": S.WORKLOADS["deepseek_v3"].with_(
+        T=50, D=64, F=64, E=16, K=4, gating=S.GATE_A),
+    "capacity_exactly_even": S.WORKLOADS["mixtral_cap"].with_(T=257, D=128, F=128, cap=1.0),
+    "K_equals_E_64": S.WORKLOADS["tiny_fp32"].with_(T=40, D=64, F=64, E=64, K=64),
     # more than 8 slots per token: the generic slot loops of the combine, its
     # backward, the gating backward and the un-permute
     "K12_softmax_B": S.WORKLOADS["tiny_fp32"].with_(T=150, E=24, K=12, F=64),
