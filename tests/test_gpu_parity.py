@@ -400,6 +400,20 @@ def test_all_tokens_to_one_expert_via_given_logits():
     assert_close("y", as_f64(to_host(layer.y)), y, TOL[wl.dtype])
 
 
+def test_serial_streams_give_identical_results(monkeypatch):
+    """The backward's side-stream overlap changes no result: with
+    MOE_SERIAL_STREAMS every kernel runs on the caller's stream, and all
+    outputs equal the overlapped run's bit for bit."""
+    wl = SMALL["deepseek_v3"]
+    _, a = run_layer(wl)
+    snap = {k: to_host(getattr(a, k)).copy() for k in
+            ("y", "dx", "dw_r", "dw_gate", "dw_up", "dw_down", "d_logits")}
+    monkeypatch.setenv("MOE_SERIAL_STREAMS", "1")
+    _, b = run_layer(wl)
+    for k, v in snap.items():
+        np.testing.assert_array_equal(to_host(getattr(b, k)), v, err_msg=k)
+
+
 def test_deterministic_across_runs():
     wl = SMALL["olmoe_share"]
     _, a = run_layer(wl)
