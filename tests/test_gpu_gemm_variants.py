@@ -21,6 +21,11 @@ CFGS = list(range(9))
 WORKLOADS = {
     "minimind_like": S.WORKLOADS["minimind"].with_(T=512, D=512, F=512, E=4, K=2),
     "shared_sigmoid": S.WORKLOADS["deepseek_v3"].with_(T=384, D=512, F=512, E=8, K=2),
+    # F = 576: reductions over F (and the gate / up split of the stacked
+    # reduction at k = F) take an odd number of 64-deep slabs, so the
+    # pipelines end on their other stage; the GEMMs whose N = F is not
+    # 128-divisible run on the register-staged kernel
+    "odd_reduction": S.WORKLOADS["minimind"].with_(T=512, D=512, F=576, E=4, K=2),
 }
 _ref = {}
 
