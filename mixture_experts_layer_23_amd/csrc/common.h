@@ -41,6 +41,8 @@ template <> struct Vec16<float> {
   float4 v;
   MOE_DEV void load(const float* p) { v = *reinterpret_cast<const float4*>(p); }
   MOE_DEV void store(float* p) const { *reinterpret_cast<float4*>(p) = v; }
+  MOE_DEV void store_nt(float* p) const { store(p); }
+  MOE_DEV void load_nt(const float* p) { load(p); }
   MOE_DEV float get(int i) const { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
   MOE_DEV void to_f32(float* o) const { o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w; }
   MOE_DEV void from_f32(const float* o) { v = make_float4(o[0], o[1], o[2], o[3]); }
@@ -49,6 +51,18 @@ template <> struct Vec16<bf16_t> {
   uint4 v;
   MOE_DEV void load(const bf16_t* p) { v = *reinterpret_cast<const uint4*>(p); }
   MOE_DEV void store(bf16_t* p) const { *reinterpret_cast<uint4*>(p) = v; }
+  // non-temporal (streaming) forms, for data read once much later or read
+  // once here: they do not displace the cached GEMM operand panels
+  MOE_DEV void store_nt(bf16_t* p) const {
+    typedef unsigned int nv4 __attribute__((ext_vector_type(4)));
+    const nv4 x = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(x, reinterpret_cast<nv4*>(p));
+  }
+  MOE_DEV void load_nt(const bf16_t* p) {
+    typedef unsigned int nv4 __attribute__((ext_vector_type(4)));
+    const nv4 x = __builtin_nontemporal_load(reinterpret_cast<const nv4*>(p));
+    v = make_uint4(x.x, x.y, x.z, x.w);
+  }
   MOE_DEV void to_f32(float* o) const {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll

@@ -302,7 +302,8 @@ MOE_DEV void gemm_epilogue(const GemmParams& P, f32x16_t (&acc)[2][2], char* reg
   // SwiGLU backward: the activation chunks of this lane's eight items are
   // loaded before the tile is staged, all in flight at once (items outside
   // the valid rows / columns read the tile's first row and column and are not
-  // used), so one memory latency overlaps the staging
+  // used), so one memory latency overlaps the staging; they are read once,
+  // non-temporally
   constexpr int NVV = sizeof(T) == 2 ? 1 : 2;  // 16-byte vectors per 8 values
   constexpr int NPF = EPI == EPI_SWIGLU_BWD ? 8 : 1;
   Vec16<T> pa[NPF][NVV], pb[NPF][NVV];
@@ -316,8 +317,8 @@ MOE_DEV void gemm_epilogue(const GemmParams& P, f32x16_t (&acc)[2][2], char* reg
       const T* src = act + (arow0 + m0 + (ok ? row_base + row : 0)) * 2 * P.F + n0 + (ok ? col : 0);
 #pragma unroll
       for (int q = 0; q < NVV; ++q) {
-        pa[it][q].load(src + q * 4);
-        pb[it][q].load(src + P.F + q * 4);
+        pa[it][q].load_nt(src + q * 4);
+        pb[it][q].load_nt(src + P.F + q * 4);
       }
     }
   }
@@ -339,17 +340,26 @@ MOE_DEV void gemm_epilogue(const GemmParams& P, f32x16_t (&acc)[2][2], char* reg
     v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
     v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
   };
-  auto store8 = [&](T* dst, const float* v) {
+  // NT: a non-temporal store (the SwiGLU activations and h, written once
+  // and read by a later kernel: measured 4-6 % faster for the gate/up
+  // forward than stores that allocate in the cache)
+  auto store8 = [&](T* dst, const float* v, bool nt = false) {
     if constexpr (sizeof(T) == 2) {
       Vec16<T> o;
       o.from_f32(v);
-      o.store(dst);
+      if (nt) o.store_nt(dst);
+      else o.store(dst);
     } else {
       Vec16<T> o0, o1;
       o0.from_f32(v);
       o1.from_f32(v + 4);
-      o0.store(dst);
-      o1.store(dst + 4);
+      if (nt) {
+        o0.store_nt(dst);
+        o1.store_nt(dst + 4);
+      } else {
+        o0.store(dst);
+        o1.store(dst + 4);
+      }
     }
   };
   if constexpr (EPI == EPI_SWIGLU_FWD) {
@@ -368,9 +378,9 @@ MOE_DEV void gemm_epilogue(const GemmParams& P, f32x16_t (&acc)[2][2], char* reg
       for (int q = 0; q < 8; ++q) h[q] = silu_f(a[q]) * b[q];
       const int64_t grow = arow0 + m0 + row_base + row;
       const int f = n0 / 2 + wn * 32 + fg;
-      store8(aout + grow * 2 * P.F + f, a);
-      store8(aout + grow * 2 * P.F + P.F + f, b);
-      store8(hout + grow * P.F + f, h);
+      store8(aout + grow * 2 * P.F + f, a, true);
+      store8(aout + grow * 2 * P.F + P.F + f, b, true);
+      store8(hout + grow * P.F + f, h, true);
     }
   } else {
 #pragma unroll
