@@ -286,7 +286,16 @@ MOE_DEV void mma_slab(const char* la, const char* lb, const int ra[2], const int
   }
 }
 
-MOE_DEV float silu_f(float a) { return a / (1.0f + expf(-a)); }
+// SwiGLU's logistic function in the GEMM epilogues from the hardware base-2
+// exponential (v_exp_f32) and reciprocal (v_rcp_f32), each within about one
+// ulp: a few instructions instead of the library exp and an IEEE division,
+// far below the bf16 rounding of a, b, h and the gradients that follows
+// (measured: gate/up forward -6 %, SwiGLU-backward GEMM -9 % on MiniMind).
+// Large |a| saturates correctly (exp2 -> inf or 0, rcp(inf) = 0).
+MOE_DEV float sigmoid_hw(float a) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(a * -1.4426950408889634f));
+}
+MOE_DEV float silu_f(float a) { return a * sigmoid_hw(a); }
 
 // Epilogue shared by both GEMM kernels: each wave's 64 x 64 fp32 tile goes
 // through its own 16 KB region of LDS (chunks of 4 floats
@@ -403,7 +412,7 @@ MOE_DEV void gemm_epilogue(const GemmParams& P, f32x16_t (&acc)[2][2], char* reg
         }
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-          const float sg = 1.0f / (1.0f + expf(-a[q]));
+          const float sg = sigmoid_hw(a[q]);
           da[q] = v[q] * b[q] * sg * (1.0f + a[q] * (1.0f - sg));
           db[q] = v[q] * a[q] * sg;
         }
@@ -1259,7 +1268,7 @@ __global__ __launch_bounds__(NW * 64) void grouped_gemm_big_kernel(GemmParams P)
         vb.to_f32(b);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float sg = 1.0f / (1.0f + expf(-a[e]));
+          const float sg = sigmoid_hw(a[e]);
           da[e] = v[e] * b[e] * sg * (1.0f + a[e] * (1.0f - sg));
           db[e] = v[e] * a[e] * sg;
         }
@@ -1680,7 +1689,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_persist_kernel(GemmParams P)
             vb.to_f32(b);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-              const float sg = 1.0f / (1.0f + expf(-a[e]));
+              const float sg = sigmoid_hw(a[e]);
               da[e] = v[e] * b[e] * sg * (1.0f + a[e] * (1.0f - sg));
               db[e] = v[e] * a[e] * sg;
             }
