@@ -16,11 +16,16 @@ typedef uint16_t bf16_t;  // bf16 storage: the upper 16 bits of an IEEE binary32
 MOE_DEV float bf16_to_f32(bf16_t v) { return __uint_as_float((uint32_t)v << 16); }
 
 // round to nearest even (inputs are finite)
-MOE_DEV bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
+// fp32 -> bf16, round to nearest even, two values per instruction
+// (v_cvt_pk_bf16_f32: the same bits as rounding the fp32 pattern by hand
+// for every finite value, in one instruction instead of about eight)
+MOE_DEV uint32_t pack_bf16x2(float a, float b) {
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  const f2 x = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf2));
 }
+MOE_DEV bf16_t f32_to_bf16(float f) { return (bf16_t)(pack_bf16x2(f, 0.0f) & 0xFFFFu); }
 
 template <typename T> struct Elem;
 template <> struct Elem<float> {
@@ -75,7 +80,7 @@ template <> struct Vec16<bf16_t> {
     uint32_t w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      w[i] = (uint32_t)f32_to_bf16(o[2 * i]) | ((uint32_t)f32_to_bf16(o[2 * i + 1]) << 16);
+      w[i] = pack_bf16x2(o[2 * i], o[2 * i + 1]);
     v = make_uint4(w[0], w[1], w[2], w[3]);
   }
 };

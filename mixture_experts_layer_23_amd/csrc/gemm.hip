@@ -921,8 +921,7 @@ __global__ __launch_bounds__(BMT * 2) void grouped_gemm_dma_kernel(GemmParams P)
 // row segments.
 // ---------------------------------------------------------------------------
 MOE_DEV uint2 pack_bf16x4(const float* v) {
-  return make_uint2((uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
-                    (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16));
+  return make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
 }
 
 template <int BN, int NW>
