@@ -77,6 +77,7 @@ struct GemmParams {
   const void* act;    // SwiGLU-backward input [rows][2F]
   void* act_out;      // SwiGLU forward a|b output [rows][2F]
   int F;
+  int xcd_xn;         // > 0: 2-D tile blocks per XCD (xcd_xn column groups)
 };
 
 MOE_DEV int swz(int row) { return (row ^ (row >> 3)) & 7; }
@@ -658,6 +659,19 @@ MOE_DEV uint4 frag_mc(char* tile, int rbase, int ks, int lane, int pitch) {
 // on all five layer shapes).
 constexpr int kSuperColsM = 2;  // row GEMMs (forward, data gradients)
 constexpr int kSuperColsK = 2;  // weight gradients
+// 2-D blocks of tiles per XCD (workgroup b runs on XCD b % 8): XCD
+// (xm, xn) takes m-tiles [xm mh, (xm + 1) mh) x n-tiles [xn ng, (xn + 1) ng)
+// row by row, so each row panel is fetched by xn_n XCDs and each weight
+// panel by 8 / xn_n, where contiguous super-columns per XCD make every XCD
+// stream all rows.  Needs mt_total % (8 / xn_n) == 0 and ntn % xn_n == 0.
+MOE_DEV void xcd_block_tile(int64_t b, int mt_total, int ntn, int xn_n, int& mt, int& nt) {
+  const int xm_n = 8 / xn_n;
+  const int x = (int)(b % 8), i = (int)(b / 8);
+  const int xn = x % xn_n, xm = x / xn_n;
+  const int ng = ntn / xn_n, mh = mt_total / xm_n;
+  mt = xm * mh + i / ng;
+  nt = xn * ng + i % ng;
+}
 template <int SC>
 MOE_DEV void supercol_tile(int64_t lin, int mt_total, int ntn, int& mt, int& nt) {
   const int full = ntn / SC, rem = ntn % SC;
@@ -708,7 +722,8 @@ __global__ __launch_bounds__(BMT * 2) void grouped_gemm_dma_kernel(GemmParams P)
   int nrows_g = 0;
   if constexpr (GROUPING == GROUP_M) {
     int mt, nt, mtl;
-    supercol_tile<kSuperColsM>(lin, P.mt_total, P.ntn, mt, nt);
+    if (P.xcd_xn > 0) xcd_block_tile(blockIdx.x, P.mt_total, P.ntn, P.xcd_xn, mt, nt);
+    else supercol_tile<kSuperColsM>(lin, P.mt_total, P.ntn, mt, nt);
     if (!find_group(P.offsets, P.G, mt, g, mtl, BMT)) return;
     g = __builtin_amdgcn_readfirstlane(g);
     mtl = __builtin_amdgcn_readfirstlane(mtl);
@@ -1785,6 +1800,18 @@ template <int AM, int BM_, int GR, int EPI, int BS, int BMT, int S>
 static int launch_dma(const char* name, GemmParams P, hipStream_t st) {
   tile_space(P, GR, BMT);
   if (P.nblocks <= 0) return MOE_OK;
+  if (GR == GROUP_M && BMT == 128 && EPI == EPI_SWIGLU_FWD && P.Kdim <= 1024) {
+    // the gate/up forward with short reductions takes 2-D tile blocks per
+    // XCD (measured on MiniMind: -4 to -7 % for this GEMM; with 2048-deep
+    // reductions, and for the other row GEMMs, slower); the extra m-tiles
+    // that round mt_total up find no group and exit
+    P.xcd_xn = (P.ntn % 4 == 0) ? 4 : (P.ntn % 2 == 0) ? 2 : 0;
+    if (P.xcd_xn) {
+      const int xm = 8 / P.xcd_xn;
+      P.mt_total = (P.mt_total + xm - 1) / xm * xm;
+      P.nblocks = (int64_t)P.mt_total * P.ntn;
+    }
+  }
   MOE_LAUNCH(name, (grouped_gemm_dma_kernel<AM, BM_, GR, EPI, BS, BMT, S>),
              dim3((unsigned)P.nblocks), dim3(BMT * 2), 0, st, P);
   return MOE_OK;
