@@ -36,8 +36,10 @@
  * depend on the thread count (each output element is summed in one fixed
  * order by one thread).
  */
+#define _GNU_SOURCE
 #include <math.h>
 #include <pthread.h>
+#include <sched.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -83,13 +85,18 @@ static void* pf_run(void* a_) {
   return NULL;
 }
 
+/* Default thread count: the CPUs this process may run on (its affinity
+ * mask), at most 64 (the parallel-for's limit); callers may set their own. */
 static int g_threads = 0;
 void orc_set_threads(int n) { g_threads = n; }
 int orc_get_threads(void) {
   if (g_threads > 0) return g_threads;
-  long n = sysconf(_SC_NPROCESSORS_ONLN);
+  long n = 0;
+  cpu_set_t set;
+  if (sched_getaffinity(0, sizeof set, &set) == 0) n = CPU_COUNT(&set);
+  if (n < 1) n = sysconf(_SC_NPROCESSORS_ONLN);
   if (n < 1) n = 1;
-  if (n > 16) n = 16;
+  if (n > 64) n = 64;
   return (int)n;
 }
 
@@ -930,4 +937,83 @@ void orc_backward(const orc_cfg* c, const void* x, int xdt, const double* wr, co
   if (dwg && dwu && dwd) parallel_for(G, wg_body, &w);
   if (dwr && drb) parallel_for(c->E, wr_body, &w);
   free(b.r_da); free(b.r_db); free(b.r_h); free(b.r_do);
+}
+
+/* ------------------------------------------------------------------------ */
+/* O10 restricted to F-columns, for one group, from every row of the group  */
+/* with a dense upstream gradient dy [T][D].                                 */
+/*   Column f of dW_gate / dW_up and row f of dW_down depend on a row only   */
+/*   through a_f = x W_gate[:,f], b_f = x W_up[:,f], h_f = silu(a_f) b_f and  */
+/*   dh_f = d_o . W_down[f,:] with d_o = g dy_t ([P5] 8.1 SwiGLU; 8.3 the    */
+/*   gate weight multiplies the expert output).  So a full-size check of     */
+/*   the weight gradients on sampled columns needs only these:               */
+/*     dW_gate[d][f] = sum_rows x_d da_f,  dW_up[d][f] = sum_rows x_d db_f,   */
+/*     dW_down[f][d] = sum_rows h_f (g dy_t)_d                               */
+/*   with da_f = dh_f b_f s(a_f)(1 + a_f(1 - s(a_f))), db_f = dh_f silu(a_f).  */
+/* Rows of routed group g (expert lo + g): the kept local slots t*K+k with    */
+/* that expert, in token order, weight g_{t,k}; shared group (g >= hi - lo): */
+/* every token, weight 1.  Outputs: dwg, dwu [D][nf], dwd [nf][D].           */
+/* Each thread owns one column (fixed summation order: tokens ascending).    */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+  ffn_w W; const int* idx; const double* gw; const int* slot_row; const double* dy;
+  int g; const int* fsel; int nf; double* dwg; double* dwu; double* dwd;
+} gwc_ctx;
+
+static void gwc_body(void* p, long j) {
+  gwc_ctx* a = (gwc_ctx*)p;
+  const orc_cfg* c = a->W.c;
+  const int D = c->D, F = c->F, K = c->K, EL = c->hi - c->lo, nf = a->nf;
+  const int f = a->fsel[j];
+  const size_t gd = (size_t)a->g * D * F;
+  for (int d = 0; d < D; ++d) {
+    a->dwg[(size_t)d * nf + j] = 0.0;
+    a->dwu[(size_t)d * nf + j] = 0.0;
+    a->dwd[(size_t)j * D + d] = 0.0;
+  }
+  for (long t = 0; t < c->T; ++t) {
+    /* weight of this token's row in group g, or skip */
+    double gk;
+    if (a->g >= EL) {
+      gk = 1.0;
+    } else {
+      int k;
+      for (k = 0; k < K; ++k) {
+        long s = t * K + k;
+        if (a->slot_row[s] >= 0 && a->idx[s] - c->lo == a->g) break;
+      }
+      if (k == K) continue;
+      gk = a->gw[t * K + k];
+    }
+    const double* dy = a->dy + (size_t)t * D;
+    double av = 0.0, bv = 0.0, dh = 0.0;
+    for (int d = 0; d < D; ++d) {
+      double xv = ld(a->W.x, (size_t)t * D + d, a->W.xdt);
+      av += xv * ld(a->W.wg, gd + (size_t)d * F + f, a->W.wdt);
+      bv += xv * ld(a->W.wu, gd + (size_t)d * F + f, a->W.wdt);
+      dh += gk * dy[d] * ld(a->W.wd, gd + (size_t)f * D + d, a->W.wdt);
+    }
+    const double sg = sigm(av);
+    const double h = silu(av) * bv;
+    const double da = dh * bv * sg * (1.0 + av * (1.0 - sg));
+    const double db = dh * silu(av);
+    for (int d = 0; d < D; ++d) {
+      double xv = ld(a->W.x, (size_t)t * D + d, a->W.xdt);
+      a->dwg[(size_t)d * nf + j] += xv * da;
+      a->dwu[(size_t)d * nf + j] += xv * db;
+      a->dwd[(size_t)j * D + d] += h * (gk * dy[d]);
+    }
+  }
+}
+
+void orc_group_wgrad_cols(const orc_cfg* c, const void* x, int xdt, const void* wg,
+                          const void* wu, const void* wd, int wdt, const int* idx,
+                          const double* gw, const int* slot_row, const double* dy, int g,
+                          const int* fsel, int nf, double* dwg, double* dwu, double* dwd) {
+  gwc_ctx a;
+  memset(&a, 0, sizeof a);
+  a.W.c = c; a.W.x = x; a.W.xdt = xdt; a.W.wg = wg; a.W.wu = wu; a.W.wd = wd; a.W.wdt = wdt;
+  a.idx = idx; a.gw = gw; a.slot_row = slot_row; a.dy = dy; a.g = g;
+  a.fsel = fsel; a.nf = nf; a.dwg = dwg; a.dwu = dwu; a.dwd = dwd;
+  parallel_for(nf, gwc_body, &a);
 }

@@ -107,6 +107,8 @@ def lib():
         L.orc_route_ec.restype = C.c_int
         L.orc_seq_aux.argtypes = [P, P, P, C.c_int, C.c_double, P, P]
         L.orc_seq_aux.restype = C.c_int
+        L.orc_group_wgrad_cols.argtypes = [P, P, C.c_int, P, P, P, C.c_int, P, P, P, P, C.c_int,
+                                           P, C.c_int, P, P, P]
         L.orc_backward.argtypes = [P, P, C.c_int, P, P, P, P, C.c_int, P, P, P, P, P, C.c_int,
                                    P, P, P, C.c_int, P, P, P, P, P, P, P, P]
         _lib = L
@@ -375,6 +377,29 @@ def backward(cfg: Cfg, x, wr, wg, wu, wd, lg, idx, w, slot_row, dy, tok=None, dl
                        _p(dy), _p(dlx), _p(fs), nf, _p(dx), _p(ds), _p(dwr), _p(drb),
                        _p(dwg), _p(dwu), _p(dwd), _p(jt))
     return dict(dx=dx, ds=ds, dwr=dwr, drb=drb, dwg=dwg, dwu=dwu, dwd=dwd)
+
+
+def group_wgrad_cols(cfg: Cfg, x, wg, wu, wd, idx, w, slot_row, dy, g: int, fsel):
+    """O10 on F-columns fsel for group g from every row of the group, with the
+    dense upstream gradient dy [T][D]: (dW_gate[g][:, fsel], dW_up[g][:, fsel],
+    dW_down[g][fsel, :]).  Routed group g is expert lo + g (kept local slots,
+    weight g_{t,k}); g >= n_local is the shared expert (every token, weight 1)."""
+    x, wg, wu, wd = _arr(x), _arr(wg), _arr(wu), _arr(wd)
+    assert wg.dtype == wu.dtype == wd.dtype
+    assert 0 <= g < cfg.groups
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    w = np.ascontiguousarray(w, dtype=np.float64)
+    slot_row = np.ascontiguousarray(slot_row, dtype=np.int32)
+    dy = np.ascontiguousarray(dy, dtype=np.float64)
+    assert dy.shape == (cfg.T, cfg.D)
+    fs = np.ascontiguousarray(fsel, dtype=np.int32)
+    nf = len(fs)
+    dwg = np.empty((cfg.D, nf)); dwu = np.empty((cfg.D, nf)); dwd = np.empty((nf, cfg.D))
+    c = cfg.c()
+    lib().orc_group_wgrad_cols(C.byref(c), _p(x), _DT[x.dtype], _p(wg), _p(wu), _p(wd),
+                               _DT[wg.dtype], _p(idx), _p(w), _p(slot_row), _p(dy), int(g),
+                               _p(fs), nf, _p(dwg), _p(dwu), _p(dwd))
+    return dwg, dwu, dwd
 
 
 def layer(cfg: Cfg, x, wr, wg, wu, wd, dy=None, rb=None, selb=None, alpha=0.0, zlam=0.0,

@@ -39,6 +39,29 @@ def assert_close(name, a, r, tol):
     return e
 
 
+def assert_rows_close(name, a, r, tol):
+    """Per-row form of the metric for outputs whose rows are independent
+    tokens (y, dx): every row i must have max|a_i - r_i| / max|r_i| <= tol,
+    and a row whose reference is all zeros must be exactly zero, so that a
+    token with small outputs cannot hide behind the tensor's largest row."""
+    a = np.asarray(a, np.float64)
+    r = np.asarray(r, np.float64)
+    assert a.shape == r.shape, (a.shape, r.shape)
+    if r.size == 0:
+        return 0.0
+    a2 = a.reshape(a.shape[0], -1)
+    r2 = r.reshape(r.shape[0], -1)
+    num = np.max(np.abs(a2 - r2), axis=1)
+    den = np.max(np.abs(r2), axis=1)
+    zero = den == 0.0
+    assert np.all(num[zero] == 0.0), f"{name}: rows {np.nonzero(zero & (num > 0))[0][:8]} " \
+                                     "must be exactly zero"
+    e = np.where(zero, 0.0, num / np.where(zero, 1.0, den))
+    worst = int(np.argmax(e))
+    assert e[worst] <= tol, f"{name}: row {worst} rel err {e[worst]:.3e} > {tol:.1e}"
+    return float(e[worst])
+
+
 def to_dev(arr, torch, dtype_code=None):
     """numpy (bf16 as uint16 bits / fp32) -> torch cuda tensor"""
     if arr is None:

@@ -201,6 +201,89 @@ def test_z_loss_definition_and_gradient(orc):
             assert abs(fd - dl[t, e]) < 1e-8
 
 
+def test_z_loss_equal_logits_closed_form(orc):
+    """Tutorial, ST-MoE (z-loss on the log-sum-exp of the router logits):
+    with all E logits of a token equal to c, lse = c + ln E, so the z-loss is
+    lambda (c + ln E)^2 and its logit gradient lambda (2/T) lse / E in every
+    entry (p = 1/E).  A dropped square, a missing ln E, a sum instead of a
+    mean over tokens or a wrong gradient factor fails here."""
+    T, lam = 7, 0.25
+    for E in (2, 5, 64):
+        for c in (-3.0, 0.0, 1.7):
+            cfg = orc.Cfg(T=T, D=1, E=E, K=1, F=8)
+            lg = np.full((T, E), c)
+            cnt = np.zeros(E, np.int32)
+            cnt[0] = T
+            losses, dl = orc.aux(cfg, lg, cnt, 0.0, lam)
+            want = (c + math.log(E)) ** 2
+            assert abs(losses[2] - want) <= 1e-13 * max(1.0, want)
+            assert abs(losses[1] - lam * want) <= 1e-13 * max(1.0, want)
+            np.testing.assert_allclose(dl, lam * (2.0 / T) * (c + math.log(E)) / E,
+                                       rtol=1e-12, atol=1e-15)
+
+
+def test_z_loss_hand_worked_example(orc):
+    """Two tokens whose exp-logits are small integers: the log-sum-exps are
+    exactly 2 ln 2 and 3 ln 2 (tests/golden/z_loss_example.json)."""
+    g = gold("z_loss_example.json")
+    ex = np.array(g["exp_logits"])
+    lg = np.log(ex)
+    T, E = ex.shape
+    cfg = orc.Cfg(T=T, D=1, E=E, K=1, F=8)
+    losses, dl = orc.aux(cfg, lg, np.array([T, 0, 0]), 0.0, g["lambda"])
+    assert abs(losses[2] - g["mean_lse2"]) < 1e-12
+    assert abs(losses[1] - g["z_loss"]) < 1e-15
+    lse = np.array([2.0, 3.0]) * math.log(2.0)
+    p = np.array([0.25, 0.25, 0.5])
+    np.testing.assert_allclose(dl, g["lambda"] * (2.0 / T) * lse[:, None] * p[None, :],
+                               rtol=1e-12)
+
+
+@pytest.mark.parametrize("K", [2, 4])
+def test_switch_loss_limits_top_k(orc, K):
+    """Course notes 8.5 state the balance loss's limits: alpha when load and
+    probability are uniform, alpha*E when everything collapses.  For K > 1
+    the uniform limit holds only with f_e normalised by the T*K slots (the
+    page warns the normaliser varies); with f normalised by T alone it would
+    read K*alpha.  Collapse onto K experts (every token picks the same K, the
+    probability split evenly over them) then gives alpha*E/K."""
+    E, T, alpha = 8, 64, 0.01
+    cfg = orc.Cfg(T=T, D=1, E=E, K=K, F=8)
+    losses, _ = orc.aux(cfg, np.zeros((T, E)), np.full(E, T * K // E), alpha, 0.0)
+    assert abs(losses[0] - alpha) < 1e-15
+    lg = np.full((T, E), -80.0)
+    lg[:, :K] = 0.0
+    cnt = np.zeros(E, np.int32)
+    cnt[:K] = T
+    losses, _ = orc.aux(cfg, lg, cnt, alpha, 0.0)
+    assert abs(losses[0] - alpha * E / K) < 1e-12
+    # the routing the oracle itself picks on these logits gives these counts
+    idx, _, _, _ = orc.route(cfg, lg)
+    assert np.array_equal(np.bincount(idx.ravel(), minlength=E), cnt)
+
+
+def test_group_wgrad_columns_equal_full_backward(orc):
+    """The column-restricted weight gradient of one group (used at full size,
+    where the full backward is too slow) equals the columns of the full
+    backward with a dense upstream gradient, for routed groups with drops and
+    sentinels around them and for the shared expert."""
+    rng = np.random.default_rng(17)
+    T, D, E, K, F = 40, 16, 6, 2, 24
+    cfg = orc.Cfg(T=T, D=D, E=E, K=K, F=F, lo=1, hi=5, n_shared=1, cap=0.9)
+    x, wr, wg, wu, wd, dy = tiny_inputs(rng, T, D, E, F, cfg.groups)
+    lg = orc.logits(cfg, x, wr)
+    idx, w, _, _ = orc.route(cfg, lg)
+    d = orc.dispatch(cfg, idx)
+    assert d["n_dropped"] > 0 and np.any(d["slot_row"] == -2)
+    fsel = np.array([0, 5, 11, 23])
+    full = orc.backward(cfg, x, wr, wg, wu, wd, lg, idx, w, d["slot_row"], dy, fsel=fsel)
+    for g in range(cfg.groups):
+        a, b, c = orc.group_wgrad_cols(cfg, x, wg, wu, wd, idx, w, d["slot_row"], dy, g, fsel)
+        np.testing.assert_allclose(a, full["dwg"][g], rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(b, full["dwu"][g], rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(c, full["dwd"][g], rtol=1e-12, atol=1e-14)
+
+
 # --------------------------------------------------------------------------
 # P5 capacity and drops (course lab printout) + P10 integer invariants
 # --------------------------------------------------------------------------
