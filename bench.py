@@ -4,20 +4,23 @@ python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--k K] [-
 
 A step is one pass of the whole layer over one batch of synthetic tokens:
 router GEMM, top-K gating, histogram/scan/permute, grouped SwiGLU expert
-GEMMs, weighted combine, Switch/z losses and the full backward (expert dgrad
+GEMMs, weighted combine, balance/z losses and the full backward (expert dgrad
 and wgrad, gating and router gradients).  Inputs and weights are resident in
 HBM before the timed region.  Prints one JSON line.
 
-The default workload is the MiniMind-like layer (T = 4096 tokens, D = 768,
-E = 4 experts, top-2, SwiGLU F = 2048, bf16 with an fp32 router, gating B,
-balance-loss coefficient 5e-4).
+The default workload is the largest layer configuration, the DeepSeek-V3-style
+layer (T = 8192 tokens, D = 7168, 256 routed experts, top-8 on sigmoid scores
+with a selection bias, one shared expert, SwiGLU F = 2048, bf16 with an fp32
+router).  The other layer configurations (tiny fp32, MiniMind-like,
+OLMoE-like expert share, Mixtral-like with capacity) are measured after it in
+a short pass each and reported under "configs".
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
-import platform
 import sys
 import time
 
@@ -27,11 +30,13 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
 F32_PEAK_TFLOPS = 157.3        # MI355X fp32 MFMA
+HOST_THREADS_MAX = 16          # the host CPU share of a one-GPU machine
 
 GEMM_FLOPS_PER_ROW = {          # in units of D*F per row
     "gemm_gate_up_fwd": 4, "gemm_down_fwd": 2, "gemm_down_dgrad": 2, "gemm_down_wgrad": 2,
     "gemm_gate_up_dgrad": 4, "gemm_gate_up_wgrad": 4,
 }
+OTHER_CONFIGS = ["tiny_fp32", "minimind", "olmoe_share", "mixtral_cap"]
 
 
 def parse():
@@ -39,7 +44,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="minimind")
+    ap.add_argument("--workload", default="deepseek_v3")
     ap.add_argument("--k", type=int, default=None, help="override top-K")
     ap.add_argument("--tokens", type=int, default=None,
                     help="override T (token sweeps of the routing / permute / combine kernels)")
@@ -63,6 +68,9 @@ def parse():
     ap.add_argument("--no-isolated", action="store_true",
                     help="skip the untimed pass that times every kernel alone "
                          "(all kernels on one stream)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the short passes over the other layer configurations")
+    ap.add_argument("--configs-steps", type=int, default=5)
     ap.add_argument("--json-out", default=None)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (for HBM counter scaling)")
@@ -99,6 +107,27 @@ def wl_name(wl):
     return s
 
 
+def gemm_work(name, wl, rows, groups_nonempty, esz):
+    """Algorithmic flop and HBM bytes of one launch of a grouped GEMM: every
+    operand row read once, the expert weights read once per expert that has
+    rows (forward and data gradients), every output written once (weight
+    gradients for every group, zeros for empty ones).  rows = routed kept
+    rows + shared rows."""
+    D, F, G = wl.D, wl.F, wl.groups
+    flop = GEMM_FLOPS_PER_ROW[name] * D * F * rows
+    w1 = D * F * esz                     # one weight matrix of one expert
+    act = rows * 2 * F * esz             # a|b or their gradients
+    byts = {
+        "gemm_gate_up_fwd": rows * D * esz + 2 * w1 * groups_nonempty + act + rows * F * esz,
+        "gemm_down_fwd": rows * F * esz + w1 * groups_nonempty + rows * D * esz,
+        "gemm_down_dgrad": rows * D * esz + w1 * groups_nonempty + 2 * act,
+        "gemm_gate_up_dgrad": act + 2 * w1 * groups_nonempty + rows * D * esz,
+        "gemm_down_wgrad": rows * F * esz + rows * D * esz + w1 * G,
+        "gemm_gate_up_wgrad": rows * D * esz + act + 2 * w1 * G,
+    }[name]
+    return flop, byts
+
+
 def measured_traffic(kernel, wl):
     """HBM bytes per launch of `kernel` from the committed counter record
     (FETCH_SIZE and WRITE_SIZE runs scaled by a copy kernel of known size);
@@ -116,14 +145,36 @@ def measured_traffic(kernel, wl):
     return None
 
 
+def host_info():
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except AttributeError:
+        aff = os.cpu_count()
+    return dict(nproc=os.cpu_count(), affinity=aff, model=model)
+
+
 def cpu_baseline(wl, host, n_tok, expert_choice=False):
     """The oracle as it stands, on a bounded sample of the same workload:
     routing of all T tokens (logits, top-K or expert choice, dispatch), then
     forward and the full backward (dx, dW_r and every expert-weight gradient
-    contribution) of the first n_tok tokens.  Reported in tokens/s."""
+    contribution) of the first n_tok tokens.  Reported in tokens/s of the
+    whole layer: per-token time = routing time / T + forward-backward time /
+    n_tok."""
     import numpy as np
     from oracle import oracle as O
 
+    hi = host_info()
+    threads = max(1, min(hi["affinity"] or 1, HOST_THREADS_MAX))
+    O.set_threads(threads)
     oc = O.Cfg(T=wl.T, D=wl.D, E=wl.E, K=wl.K, F=wl.F, lo=wl.lo, hi=wl.local_hi,
                n_shared=wl.n_shared, score=wl.score, gating=wl.gating, cap=wl.cap)
     x, wr, rb, selb, wg, wu, wd, dy = host
@@ -138,6 +189,7 @@ def cpu_baseline(wl, host, n_tok, expert_choice=False):
         idx, w, lse, _ = O.route(oc, lg, selb)
         d = O.dispatch(oc, idx)
         cw, slot_row, counts = oc, d["slot_row"], d["counts_all"]
+    t1 = time.perf_counter()
     O.forward(cw, x, wg, wu, wd, idx, w, slot_row, tok=tok)
     dl = None
     if wl.score == 0 and (wl.alpha or wl.zlam):
@@ -145,11 +197,196 @@ def cpu_baseline(wl, host, n_tok, expert_choice=False):
     dyt = dy[tok].astype(np.float64) if dy.dtype != np.uint16 else \
         ((dy[tok].astype(np.uint32) << 16).view(np.float32).astype(np.float64))
     O.backward(cw, x, wr, wg, wu, wd, lg, idx, w, slot_row, dyt, tok=tok, dlx=dl)
-    dt = time.perf_counter() - t0
-    return dict(value=n_tok / dt, unit="tokens/s", cores=O.threads(), kind="oracle",
-                sample=(f"routing of all {wl.T} tokens + forward and backward (dx, dW_r, all "
-                        f"expert-weight gradient rows) of {n_tok} of them; {dt:.1f} s on "
-                        f"{O.threads()} threads ({platform.processor() or platform.machine()})"))
+    t2 = time.perf_counter()
+    per_tok = (t1 - t0) / wl.T + (t2 - t1) / n_tok
+    return dict(value=1.0 / per_tok, unit="tokens/s", cores=threads, kind="oracle",
+                host_cpus=hi["nproc"], cpu_model=hi["model"],
+                sample=(f"routing (logits, top-K, dispatch) of all {wl.T} tokens in "
+                        f"{t1 - t0:.1f} s, then forward and backward (dx, dW_r, every "
+                        f"expert-weight gradient row) of {n_tok} of them in {t2 - t1:.1f} s; "
+                        f"fp64 oracle on {threads} threads of {hi['nproc']} host CPUs "
+                        f"({hi['model']}), thread pool capped at {HOST_THREADS_MAX}, the "
+                        "host share of a one-GPU box; value = 1 / (routing time per token + "
+                        "forward-backward time per sampled token)"))
+
+
+def device_facts(torch):
+    """Measured denominators next to the published peaks: a plain device copy
+    (torch copy_ of 2 GiB, read + write) timed with events, and the clocks
+    the HIP runtime reports (hipDeviceAttributeClockRate = 5,
+    MemoryClockRate = 60, MemoryBusWidth = 59 on this ROCm)."""
+    out = {}
+    n = (2 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    b.synchronize()
+    ms = a.elapsed_time(b) / reps
+    out["copy_gbs"] = 2 * n * 4 / (ms * 1e-3) / 1e9
+    out["copy_bytes"] = 2 * n * 4
+    del src, dst
+    torch.cuda.empty_cache()
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        v = ctypes.c_int()
+        vals = {}
+        for key, attr in (("sclk_max_khz", 5), ("mclk_max_khz", 60), ("mem_bus_bits", 59)):
+            if hip.hipDeviceGetAttribute(ctypes.byref(v), attr, 0) == 0:
+                vals[key] = v.value
+        out.update(vals)
+        if "sclk_max_khz" in vals:
+            out["bf16_peak_tflops_at_sclk"] = 256 * 4096 * vals["sclk_max_khz"] * 1e3 / 1e12
+    except OSError:
+        pass
+    return out
+
+
+def stage_bytes_of(wl, rows, n_rows_local, W, esz, use_aux):
+    """Algorithmic bytes per launch of the HBM-bound stages."""
+    Dsz = wl.D * esz
+    return {
+        "permute_gather": n_rows_local * Dsz * 2,
+        "combine": rows * Dsz + wl.T * Dsz + wl.T * W * 8,
+        "combine_bwd": n_rows_local * Dsz * 2 + wl.T * Dsz + wl.T * W * 8,
+        "unpermute_dx": rows * Dsz + wl.T * Dsz + wl.T * W * 4,
+        # logits read; p, keys of the local experts, sentinel columns written
+        "ec_token": wl.T * wl.E * 4 * 2 + wl.T * wl.n_local * 4
+                    + wl.T * (wl.E - wl.n_local) * 4,
+        # keys read by three digit passes and the compaction; the local
+        # columns of the slot table and two row maps written
+        "ec_select": wl.T * wl.n_local * 4 * 4 + wl.T * wl.n_local * 4 + n_rows_local * 8,
+        "route_select": wl.T * wl.E * 4 + wl.T * wl.K * 8 + wl.T * 4,
+        "router_logits": wl.T * Dsz + wl.E * wl.D * 4 + wl.T * wl.E * 4,
+        # x and W_r read; logits, top-K indices and weights, lse written
+        "route_fused": wl.T * Dsz + wl.E * wl.D * 4 + wl.T * wl.E * 4 + wl.T * wl.K * 8
+                       + wl.T * 4,
+        # slot experts read (twice for the tiled rank); slot rows and the
+        # two row maps written
+        "permute_small": wl.T * wl.K * 8 + n_rows_local * 8,
+        "permute_hist": wl.T * wl.K * 4,
+        "permute_rank": wl.T * wl.K * 8 + n_rows_local * 8,
+        "aux_single": wl.T * wl.E * 4 * (2 if wl.alpha or wl.zlam else 1),
+        "router_wgrad": wl.T * Dsz + wl.T * wl.E * 4,
+        "aux_partial": wl.T * wl.E * 4 * (2 if wl.alpha or wl.zlam else 1),
+        # logits read twice (probabilities, then the gradient), routing read,
+        # gradient written (read as well when accumulating)
+        "seq_aux": wl.T * wl.E * 4 * (4 if use_aux else 3) + wl.T * wl.K * 4,
+    }
+
+
+def serial_kernel_times(L, step, warmup, steps):
+    """Each kernel alone: every kernel on the caller's stream
+    (MOE_SERIAL_STREAMS), per-kernel durations from HIP events."""
+    import torch
+    os.environ["MOE_SERIAL_STREAMS"] = "1"
+    try:
+        for _ in range(max(warmup, 1)):
+            step()
+        torch.cuda.synchronize()
+        L.timing_enable(True)
+        for _ in range(max(steps, 1)):
+            step()
+        torch.cuda.synchronize()
+        L.timing_enable(False)
+        return L.timing_report()
+    finally:
+        del os.environ["MOE_SERIAL_STREAMS"]
+
+
+def summarize_kernels(kt, steps, wl, rows, groups_nonempty, esz, sbytes, peak_t):
+    """Per-kernel averages with GEMM TFLOP/s and stage GB/s; the GEMMs'
+    flop over the sum of their durations."""
+    out = {}
+    fl_all = ms_all = 0.0
+    for name, (n, tot) in kt.items():
+        avg = tot / n
+        e = dict(launches_per_step=n / max(steps, 1), avg_ms=avg)
+        if name in GEMM_FLOPS_PER_ROW:
+            fl, by = gemm_work(name, wl, rows, groups_nonempty, esz)
+            e["tflops"] = fl / (avg * 1e-3) / 1e12
+            e["frac_of_mfma_peak"] = e["tflops"] / peak_t
+            e["gbs"] = by / (avg * 1e-3) / 1e9
+            e["roofline_frac"] = max(fl / (peak_t * 1e12), by / (HBM_PEAK_GBS * 1e9)) / (avg * 1e-3)
+            fl_all += fl * n
+            ms_all += tot
+        if name in sbytes:
+            e["gbs"] = sbytes[name] / (avg * 1e-3) / 1e9
+            e["hbm_frac"] = e["gbs"] / HBM_PEAK_GBS
+        out[name] = e
+    gemm = None
+    if ms_all:
+        t = fl_all / (ms_all * 1e-3) / 1e12
+        gemm = {"tflops": t, "frac_of_peak": t / peak_t, "ms_per_step": ms_all / max(steps, 1)}
+    return out, gemm
+
+
+def measure_config(name, steps):
+    """A short pass over one more layer configuration: ms per step (kernels
+    overlapped as in the headline), each kernel alone (GEMM TFLOP/s, stage
+    GB/s), loads, drops and losses."""
+    import torch
+    from mixture_experts_layer_23_amd import _lib as L
+    from mixture_experts_layer_23_amd import synthetic as S
+    from mixture_experts_layer_23_amd.layer import LayerSpec, MoELayer
+
+    wl = S.WORKLOADS[name]
+    inp = S.device_inputs(wl, device="cuda")
+    layer = MoELayer(LayerSpec.from_workload(wl), inp["wr"], inp["wg"], inp["wu"], inp["wd"],
+                     inp["rb"], inp["selb"])
+    x, dy = inp["x"], inp["dy"]
+
+    def step():
+        layer.forward(x)
+        layer.backward(dy)
+
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1000.0 / steps
+    kt = serial_kernel_times(L, step, 1, min(steps, 3))
+    offsets = layer.offsets.cpu().numpy()
+    counts = layer.counts.cpu().numpy()
+    n_local_rows = int(offsets[wl.n_local]) if wl.n_local > 0 else 0
+    rows = n_local_rows + wl.n_shared * wl.T
+    esz = 2 if wl.dtype == S.BF16 else 4
+    peak_t = BF16_PEAK_TFLOPS if wl.dtype == S.BF16 else F32_PEAK_TFLOPS
+    ne = int((offsets[1:] - offsets[:-1] > 0).sum())
+    sb = stage_bytes_of(wl, rows, n_local_rows, wl.K, esz, layer.use_aux)
+    kern, gemm = summarize_kernels(kt, min(steps, 3), wl, rows, ne, esz, sb, peak_t)
+    out = {"workload": wl_name(wl), "ms_per_step": ms, "tokens_per_s": wl.T / (ms * 1e-3),
+           "dtype": "bf16" if wl.dtype == S.BF16 else "f32",
+           "local_rows": n_local_rows, "shared_rows": wl.n_shared * wl.T,
+           "grouped_gemm_isolated": gemm,
+           "stages_isolated": {k: {"avg_ms": v["avg_ms"], "gbs": v.get("gbs"),
+                                   "hbm_frac": v.get("hbm_frac")}
+                               for k, v in kern.items() if k in sb},
+           "gemms_isolated": {k: {"avg_ms": v["avg_ms"], "tflops": v["tflops"],
+                                  "frac_of_mfma_peak": v["frac_of_mfma_peak"]}
+                              for k, v in kern.items() if k in GEMM_FLOPS_PER_ROW}}
+    if wl.E <= 16:
+        out["expert_load"] = counts.tolist()
+    out["dropped"] = int(layer.n_dropped.cpu().numpy()[0])
+    if layer.use_aux:
+        ls = layer.losses.cpu().numpy()
+        out["losses"] = {"balance": float(ls[0]), "z_loss": float(ls[1]),
+                         "mean_lse_sq": float(ls[2]), "alpha": wl.alpha, "z_lambda": wl.zlam}
+    if wl.cap > 0:
+        out["capacity"] = L.capacity(layer.cfg)
+    del layer, inp, x, dy
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -167,6 +404,8 @@ def main():
 
     assert torch.cuda.is_available(), "needs a GPU"
     L.lib()
+    print(f"bench: workload {args.workload}, {args.warmup} warm-up + {args.steps} timed steps",
+          file=sys.stderr, flush=True)
     if args.copy_calibration_mib:
         # one elementwise kernel that reads and writes exactly this many bytes:
         # the HBM counters of this launch calibrate FETCH_SIZE / WRITE_SIZE
@@ -213,22 +452,12 @@ def main():
         return (time.perf_counter() - t0) * 1000.0 / max(args.steps, 1)
 
     # the kernel the roofline line is about: the largest total duration with
-    # every kernel alone on the caller's stream (MOE_SERIAL_STREAMS, a short
-    # untimed pass); beside other kernels on the side streams a duration also
-    # counts the time the kernel shares the GPU
-    os.environ["MOE_SERIAL_STREAMS"] = "1"
-    try:
-        for _ in range(max(args.warmup, 1)):
-            step()
-        torch.cuda.synchronize()
-        L.timing_enable(True)
-        for _ in range(max(min(args.steps, 5), 1)):
-            step()
-        torch.cuda.synchronize()
-        L.timing_enable(False)
-        dom = max(L.timing_report().items(), key=lambda kv: kv[1][1])[0]
-    finally:
-        del os.environ["MOE_SERIAL_STREAMS"]
+    # every kernel alone on the caller's stream (a short untimed pass); beside
+    # other kernels on the side streams a duration also counts the time the
+    # kernel shares the GPU
+    sel = serial_kernel_times(L, step, args.warmup, min(args.steps, 5))
+    dom = max(sel.items(), key=lambda kv: kv[1][1])[0]
+    print(f"bench: dominant kernel {dom}", file=sys.stderr, flush=True)
 
     # untimed pass: per-kernel durations of every launch from HIP events the
     # library records on the stream each kernel runs on
@@ -249,6 +478,7 @@ def main():
     L.timing_enable(False)
     L.timing_select(None)
     kt_live = L.timing_report()
+    print(f"bench: {ms:.3f} ms per step", file=sys.stderr, flush=True)
     ms_graph = None
     if args.graph:
         from mixture_experts_layer_23_amd.layer import StepGraph
@@ -256,118 +486,64 @@ def main():
         ms_graph = timed(sg.replay)
         del sg
 
-    # untimed pass with every kernel on the caller's stream (MOE_SERIAL_STREAMS):
-    # each kernel's duration alone, next to the overlapped ones of the step
-    kt_iso = None
-    if not args.no_isolated:
-        os.environ["MOE_SERIAL_STREAMS"] = "1"
-        try:
-            for _ in range(args.warmup):
-                step()
-            torch.cuda.synchronize()
-            L.timing_enable(True)
-            for _ in range(args.steps):
-                step()
-            torch.cuda.synchronize()
-            L.timing_enable(False)
-            kt_iso = L.timing_report()
-        finally:
-            del os.environ["MOE_SERIAL_STREAMS"]
+    # untimed pass with every kernel on the caller's stream: each kernel's
+    # duration alone, next to the overlapped ones of the step
+    kt_iso = None if args.no_isolated else serial_kernel_times(L, step, args.warmup, args.steps)
 
     offsets = layer.offsets.cpu().numpy()
     counts = layer.counts.cpu().numpy()
     n_rows_local = int(offsets[wl.n_local]) if wl.n_local > 0 else 0
     rows = n_rows_local + wl.n_shared * wl.T
+    groups_nonempty = int((offsets[1:] - offsets[:-1] > 0).sum())
     n_dropped = None if ec else int(layer.n_dropped.cpu().numpy()[0])
     W = spec.width  # slots per token: K, or E under expert choice
     esz = 2 if wl.dtype == S.BF16 else 4
-    kernels = {}
-    gemm_flops = gemm_ms = 0.0
-    for name, (n, tot) in kt.items():
-        avg = tot / n
-        e = dict(launches_per_step=n / max(args.steps, 1), avg_ms=avg)
-        if name in GEMM_FLOPS_PER_ROW:
-            fl = GEMM_FLOPS_PER_ROW[name] * wl.D * wl.F * rows
-            e["tflops"] = fl / (avg * 1e-3) / 1e12
-            gemm_flops += fl * n
-            gemm_ms += tot
-        kernels[name] = e
-    # algorithmic bytes of the HBM-bound stages (per launch)
-    Dsz = wl.D * esz
-    stage_bytes = {
-        "permute_gather": n_rows_local * Dsz * 2,
-        "combine": rows * Dsz + wl.T * Dsz + wl.T * W * 8,
-        "combine_bwd": n_rows_local * Dsz * 2 + wl.T * Dsz + wl.T * W * 8,
-        "unpermute_dx": rows * Dsz + wl.T * Dsz + wl.T * W * 4,
-        # logits read; p, keys of the local experts, sentinel columns written
-        "ec_token": wl.T * wl.E * 4 * 2 + wl.T * wl.n_local * 4
-                    + wl.T * (wl.E - wl.n_local) * 4,
-        # keys read by three digit passes and the compaction; the local
-        # columns of the slot table and two row maps written
-        "ec_select": wl.T * wl.n_local * 4 * 4 + wl.T * wl.n_local * 4 + n_rows_local * 8,
-        "route_select": wl.T * wl.E * 4 + wl.T * wl.K * 8 + wl.T * 4,
-        "router_logits": wl.T * Dsz + wl.E * wl.D * 4 + wl.T * wl.E * 4,
-        # x and W_r read; logits, top-K indices and weights, lse written
-        "route_fused": wl.T * Dsz + wl.E * wl.D * 4 + wl.T * wl.E * 4 + wl.T * wl.K * 8
-                       + wl.T * 4,
-        # slot experts read (twice for the tiled rank); slot rows and the
-        # two row maps written
-        "permute_small": wl.T * wl.K * 8 + n_rows_local * 8,
-        "permute_hist": wl.T * wl.K * 4,
-        "permute_rank": wl.T * wl.K * 8 + n_rows_local * 8,
-        "aux_single": wl.T * wl.E * 4 * (2 if wl.alpha or wl.zlam else 1),
-        "router_wgrad": wl.T * Dsz + wl.T * wl.E * 4,
-        "aux_partial": wl.T * wl.E * 4 * (2 if wl.alpha or wl.zlam else 1),
-        # logits read twice (probabilities, then the gradient), routing read,
-        # gradient written (read as well when accumulating)
-        "seq_aux": wl.T * wl.E * 4 * (4 if layer.use_aux else 3) + wl.T * wl.K * 4,
-    }
-    for name, b in stage_bytes.items():
-        if name in kernels:
-            kernels[name]["gbs"] = b / (kernels[name]["avg_ms"] * 1e-3) / 1e9
-            kernels[name]["hbm_frac"] = kernels[name]["gbs"] / HBM_PEAK_GBS
-    kernels_iso = None
-    gemm_iso = None
+    peak_t = BF16_PEAK_TFLOPS if wl.dtype == S.BF16 else F32_PEAK_TFLOPS
+    sbytes = stage_bytes_of(wl, rows, n_rows_local, W, esz, layer.use_aux)
+    kernels, gemm_step = summarize_kernels(kt, args.steps, wl, rows, groups_nonempty, esz,
+                                           sbytes, peak_t)
+    kernels_iso = gemm_iso = None
     if kt_iso:
-        kernels_iso = {}
-        fl_iso = ms_iso = 0.0
-        for name, (n, tot) in kt_iso.items():
-            avg = tot / n
-            e = dict(avg_ms=avg)
-            if name in GEMM_FLOPS_PER_ROW:
-                fl = GEMM_FLOPS_PER_ROW[name] * wl.D * wl.F * rows
-                e["tflops"] = fl / (avg * 1e-3) / 1e12
-                e["frac_of_peak"] = e["tflops"] / (BF16_PEAK_TFLOPS if wl.dtype == S.BF16
-                                                   else F32_PEAK_TFLOPS)
-                fl_iso += fl * n
-                ms_iso += tot
-            if name in stage_bytes:
-                e["gbs"] = stage_bytes[name] / (avg * 1e-3) / 1e9
-                e["hbm_frac"] = e["gbs"] / HBM_PEAK_GBS
-            kernels_iso[name] = e
-        if ms_iso:
-            t_iso = fl_iso / (ms_iso * 1e-3) / 1e12
-            gemm_iso = {"tflops": t_iso,
-                        "frac_of_peak": t_iso / (BF16_PEAK_TFLOPS if wl.dtype == S.BF16
-                                                 else F32_PEAK_TFLOPS),
-                        "ms_per_step": ms_iso / max(args.steps, 1)}
+        kernels_iso, gemm_iso = summarize_kernels(kt_iso, args.steps, wl, rows, groups_nonempty,
+                                                  esz, sbytes, peak_t)
+
     n_live, tot_live = kt_live[dom]
     dom_avg = tot_live / n_live
-    peak_t = BF16_PEAK_TFLOPS if wl.dtype == S.BF16 else F32_PEAK_TFLOPS
     if dom in GEMM_FLOPS_PER_ROW:
-        ach = GEMM_FLOPS_PER_ROW[dom] * wl.D * wl.F * rows / (dom_avg * 1e-3) / 1e12
-        roof = dict(kernel=dom, bound="mfma", achieved=ach, peak=peak_t, unit="TFLOP/s",
-                    frac=ach / peak_t, traffic=measured_traffic(dom, wl),
-                    per_launch=f"{GEMM_FLOPS_PER_ROW[dom]}*D*F flop x {rows} rows",
-                    launches_timed=n_live)
+        # a grouped GEMM is bounded by the larger of its matrix-core time and
+        # its HBM time (the DeepSeek-V3-like layer sits at the ridge point:
+        # the weight gradients write 15 GB of bf16 dW for 4.3 TFLOP)
+        fl, by = gemm_work(dom, wl, rows, groups_nonempty, esz)
+        t_mfma = fl / (peak_t * 1e12)
+        t_hbm = by / (HBM_PEAK_GBS * 1e9)
+        tf = fl / (dom_avg * 1e-3) / 1e12
+        gbs = by / (dom_avg * 1e-3) / 1e9
+        mfma = dict(achieved=tf, peak=peak_t, unit="TFLOP/s", frac=tf / peak_t)
+        hbm = dict(achieved=gbs, peak=HBM_PEAK_GBS, unit="GB/s", frac=gbs / HBM_PEAK_GBS)
+        roof = dict(kernel=dom, bound="hbm" if t_hbm > t_mfma else "mfma",
+                    **(hbm if t_hbm > t_mfma else mfma),
+                    traffic=measured_traffic(dom, wl),
+                    per_launch=(f"{GEMM_FLOPS_PER_ROW[dom]}*D*F flop x {rows} rows = "
+                                f"{fl / 1e12:.3f} TFLOP; {by / 1e9:.3f} GB algorithmic HBM "
+                                f"bytes ({groups_nonempty} of {wl.groups} groups with rows)"),
+                    time_at_roof_ms=max(t_mfma, t_hbm) * 1e3, avg_ms=dom_avg,
+                    mfma=mfma, hbm=hbm, launches_timed=n_live)
     else:
-        b = stage_bytes.get(dom, 0)
+        b = sbytes.get(dom, 0)
         ach = b / (dom_avg * 1e-3) / 1e9
         roof = dict(kernel=dom, bound="hbm", achieved=ach, peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=ach / HBM_PEAK_GBS, traffic=None, launches_timed=n_live)
+                    frac=ach / HBM_PEAK_GBS, traffic=None, avg_ms=dom_avg,
+                    launches_timed=n_live)
+
+    ec_capacity = L.capacity(layer.cfg) if ec else None
+    losses = None
+    if layer.use_aux:
+        ls = layer.losses.cpu().numpy()
+        losses = {"balance": float(ls[0]), "z_loss": float(ls[1]), "mean_lse_sq": float(ls[2])}
 
     cpu = None
     if not args.no_cpu_baseline:
+        print("bench: cpu baseline", file=sys.stderr, flush=True)
         host = (S.bf16_bits(inp["x"].float().cpu().numpy()) if wl.dtype == S.BF16
                 else inp["x"].cpu().numpy(),
                 inp["wr"].cpu().numpy(),
@@ -375,8 +551,23 @@ def main():
                 None if inp["selb"] is None else inp["selb"].cpu().numpy(),
                 *[t.cpu().view(torch.int16).numpy().view(np.uint16) if wl.dtype == S.BF16
                   else t.cpu().numpy() for t in (inp["wg"], inp["wu"], inp["wd"], inp["dy"])])
-        n_tok = args.cpu_sample_tokens or min(wl.T, 4096)
+        n_tok = args.cpu_sample_tokens or min(wl.T, 128 if wl.D * wl.F > 4e6 else 4096)
         cpu = cpu_baseline(wl, host, n_tok, expert_choice=ec)
+        del host
+
+    config_lines = None
+    facts = None
+    if not args.no_configs:
+        del layer, inp, x, dy
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        facts = device_facts(torch)
+        config_lines = {}
+        for name in OTHER_CONFIGS:
+            if name == args.workload:
+                continue
+            print(f"bench: config {name}", file=sys.stderr, flush=True)
+            config_lines[name] = measure_config(name, args.configs_steps)
 
     out = {
         "metric": "MoE layer fwd+bwd tokens/s",
@@ -396,20 +587,24 @@ def main():
                    "tokens": wl.T, "local_rows": n_rows_local,
                    "shared_rows": wl.n_shared * wl.T, "dropped": n_dropped,
                    "expert_load": counts.tolist() if wl.E <= 16 else None,
+                   "expert_load_min_max": [int(counts.min()), int(counts.max())],
                    "seq_len": args.seq_len or None, "bias_gamma": args.bias_gamma or None,
                    "jitter": args.jitter or None, "noise": args.noise or None,
                    "routing": "expert choice" if ec else "token choice",
-                   "expert_capacity": L.capacity(layer.cfg) if ec else None},
-        "grouped_gemm": {"tflops": gemm_flops / (gemm_ms * 1e-3) / 1e12 if gemm_ms else None,
-                         "frac_of_peak": (gemm_flops / (gemm_ms * 1e-3) / 1e12 / peak_t)
-                         if gemm_ms else None,
-                         "ms_per_step": gemm_ms / max(args.steps, 1)},
+                   "expert_capacity": ec_capacity},
         "roofline": roof,
         "cpu_baseline": cpu,
+        # each kernel alone (untimed pass, one stream): the six GEMMs' flop
+        # over the sum of their durations
+        "grouped_gemm": gemm_iso,
+        # the same from the durations inside the overlapped step (kernels on
+        # the side streams share the GPU, so these durations overlap)
+        "grouped_gemm_in_step": gemm_step,
+        "losses": losses,
+        "device": facts,
         "kernels": kernels,
-        # the same kernels timed alone (untimed pass, one stream)
-        "grouped_gemm_isolated": gemm_iso,
         "kernels_isolated": kernels_iso,
+        "configs": config_lines,
     }
     line = json.dumps(out)
     print(line, flush=True)

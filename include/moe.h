@@ -45,7 +45,8 @@
  *    sets the per-expert capacity C; moe_expert_ffn, moe_combine,
  *    aux_balance_loss and moe_backward take the same [T][E] tables.
  *  - Pointers must be 16-byte aligned device pointers (MOE_EALIGN).
- *  - Requirements: T >= 0; D and F positive multiples of 64; 1 <= K <= E;
+ *  - Requirements: T >= 0; D and F positive multiples of 64, at most 2^20
+ *    (row buffers of any total size are supported); 1 <= K <= E;
  *    K <= 64 for token choice; E <= 1024; 0 <= expert_lo <= expert_hi <= E;
  *    n_shared in {0,1}; expert choice needs softmax scoring and
  *    MOE_GATE_TRUNCATED (MOE_EINVAL).  T == 0 is a successful no-op.
@@ -125,9 +126,10 @@ int moe_workspace_size(const moe_config* cfg, size_t* bytes);
  *                                            equal keys -> lower index first
  *   topk_w   [T][K] fp32               out  gate weights (A or B)
  *   lse      [T] fp32                  out  log-sum-exp of the logits
- * The logits are the binary32 rounding of a double-precision accumulation of
- * the products, so a top-K decision on them does not depend on the summation
- * order.  Selection key: softmax -> the logit; sigmoid -> sig32(s) + b, a
+ * The logits are the binary32 rounding of a double-precision sum of the
+ * exact products: another summation order changes a logit only when its
+ * double sum lies within double rounding error of a binary32 rounding
+ * boundary.  Given identical logits the top-K is bit-exact.  Selection key: softmax -> the logit; sigmoid -> sig32(s) + b, a
  * fixed binary32 sequence (range reduction by ln2 split in two parts, degree-7
  * Taylor polynomial with fma, scaling by 2^n, IEEE division).
  * Token choice only (MOE_EINVAL under expert choice).

@@ -67,6 +67,10 @@ static int check_cfg(const moe_config* c) {
   if (!c) return MOE_EINVAL;
   if (c->T < 0 || c->D <= 0 || c->F <= 0 || c->E < 1 || c->E > 1024) return MOE_EINVAL;
   if (c->D % 64 || c->F % 64) return MOE_EINVAL;
+  // the grouped GEMMs address one tile's rows of D or 2F elements with 32-bit
+  // byte offsets inside a descriptor based at the tile: D and F up to 2^20
+  // keep 256 rows of 2F bf16 under 2^31 bytes
+  if (c->D > kMaxDim || c->F > kMaxDim) return MOE_EINVAL;
   if (c->routing != MOE_TOKEN_CHOICE && c->routing != MOE_EXPERT_CHOICE) return MOE_EINVAL;
   if (c->K < 1 || c->K > c->E) return MOE_EINVAL;
   if (c->routing == MOE_TOKEN_CHOICE && c->K > 64) return MOE_EINVAL;

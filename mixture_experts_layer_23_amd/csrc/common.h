@@ -10,6 +10,10 @@
 
 typedef uint16_t bf16_t;  // bf16 storage: the upper 16 bits of an IEEE binary32
 
+// largest D and F: a grouped-GEMM tile addresses its 256 rows of up to 2F
+// bf16 elements with 32-bit byte offsets inside a descriptor based at the tile
+constexpr int kMaxDim = 1 << 20;
+
 // ---------------------------------------------------------------------------
 // element conversion
 // ---------------------------------------------------------------------------

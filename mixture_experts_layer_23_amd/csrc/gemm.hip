@@ -78,6 +78,7 @@ struct GemmParams {
   void* act_out;      // SwiGLU forward a|b output [rows][2F]
   int F;
   int xcd_xn;         // > 0: 2-D tile blocks per XCD (xcd_xn column groups)
+  int a_cap, b_cap;   // rows of lda / ldb bf16 elements in 2^31 - 1 bytes
 };
 
 MOE_DEV int swz(int row) { return (row ^ (row >> 3)) & 7; }
@@ -591,23 +592,71 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int kBufDword3 = 0x00020000;  // raw buffer descriptor word 3 (CDNA)
 
-MOE_DEV __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  const int nb = bytes > 0x7fffffffLL ? 0x7fffffff : (int)bytes;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nb, kBufDword3);
+// A raw buffer descriptor (base, stride 0, num_records, word 3) in four
+// scalar registers: every dword goes through readfirstlane, so the DMA
+// instructions take it from SGPRs (the values are wave-uniform by
+// construction).
+typedef int rsrc_t __attribute__((ext_vector_type(4)));
+MOE_DEV rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int nb = bytes > 0x7fffffffLL ? 0x7fffffff : bytes < 0 ? 0 : (int)bytes;
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  rsrc_t r;
+  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  r.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(b >> 32) & 0xFFFFu));
+  r.z = __builtin_amdgcn_readfirstlane(nb);
+  r.w = kBufDword3;
+  return r;
+}
+
+// Descriptor over rows [r0, rows) of a row-major bf16 operand with rows of ld
+// elements, based at row r0.  Every DMA of a tile (rows r0 .. r0 + 255, row
+// operand) or of a k-slab (rows r0 .. r0 + 63, k-major operand) then has an
+// offset below 256 * ld * 2 bytes, which the host keeps under 2^31 (D and F
+// at most 2^20), however large the whole tensor is; rows at or past `rows`
+// read zeros.  The range is capped at cap = floor((2^31 - 1) / (2 ld)) rows
+// (from the host), which always covers the rows one tile or slab reads, so an
+// offset of 2^31 is always out of range (the padding slabs use that).  All
+// 32-bit scalar arithmetic: this runs once per slab.
+MOE_DEV rsrc_t rows_rsrc(const bf16_t* base, int r0, int rows, int ld, int cap) {
+  const int rem = min(max(rows - r0, 0), cap);
+  const uint64_t b = (uint64_t)(uintptr_t)(base + (int64_t)r0 * ld);
+  rsrc_t r;
+  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  r.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(b >> 32) & 0xFFFFu));
+  r.z = __builtin_amdgcn_readfirstlane(rem * ld * 2);
+  r.w = kBufDword3;
+  return r;
 }
 
 MOE_DEV lds_void_t* to_lds(char* p) {
   return (lds_void_t*)(__attribute__((address_space(3))) char*)(p);
 }
 
-// 16-byte LDS-DMA loads.  Plain (non-template) device functions: the host
-// pass does not check the gfx950-only operand size inside them.
+// 16-byte LDS-DMA loads (global_load_lds_dwordx4 / buffer_load_dwordx4 ...
+// lds, LDS destination in M0), issued as inline assembly.  The kernels order
+// every slab themselves -- an explicit vmcnt wait for their own DMA, then a
+// workgroup barrier, before any wave reads the slab or overwrites a stage --
+// so the compiler's own tracking of LDS-DMA is not needed; left to it, the
+// tracking loses the destination object of some fragment reads and then
+// waits for the DMA just issued (for the slab after next) before reading the
+// current slab, which serialises the pipeline (measured on the DeepSeek-V3-
+// like weight gradients: 8.7 -> 10.3 ms after an unrelated change moved such
+// a wait into the main loop).  The instructions write no register (data goes
+// to LDS) and read their operands at issue; "memory" keeps every LDS access
+// on its side.  M0 is written here and read by nothing else in these kernels.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 MOE_DEV void dma16_global(const void* src, lds_void_t* dst) {
-  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+  const uint32_t m = (uint32_t)(uintptr_t)dst;
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(m), "v"(src) : "memory", "m0");
 }
-MOE_DEV void dma16_buffer(__amdgpu_buffer_rsrc_t rs, lds_void_t* dst, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, voff, 0, 0, 0);
+MOE_DEV void dma16_buffer(rsrc_t rs, lds_void_t* dst, uint32_t voff) {
+  const uint32_t m = (uint32_t)(uintptr_t)dst;
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(m), "v"(voff), "s"(rs) : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // vmcnt wait with expcnt / lgkmcnt left open (gfx9 s_waitcnt encoding)
 template <int N>
@@ -631,10 +680,14 @@ MOE_DEV void mc_slot(int t, int lane, int& krow, int& lc) {
 }
 
 // fragment reads: 8 bf16 of one 32x32x16 MFMA operand for block rows rbase
+// Chunk ch = 2 ks + (lane >> 5) sits at (ch ^ swz(r)) << 4 in its 128-byte
+// row; since 2 ks has no low bit, that is ((((lane >> 5) ^ swz(r)) << 4) ^
+// (32 ks)): one per-lane offset for all four k-steps, XORed with a uniform
+// constant, instead of a separate address register per k-step and stage.
 MOE_DEV uint4 frag_kc(const char* tile, int rbase, int ks, int lane) {
   const int r = rbase + (lane & 31);
-  const int ch = ks * 2 + (lane >> 5);
-  return *reinterpret_cast<const uint4*>(tile + r * 128 + ((ch ^ swz(r)) << 4));
+  const int off = (r * 128 + (((lane >> 5) ^ swz(r)) << 4)) ^ (ks << 5);
+  return *reinterpret_cast<const uint4*>(tile + off);
 }
 MOE_DEV uint4 frag_mc(char* tile, int rbase, int ks, int lane, int pitch) {
   const int gi = lane >> 4, a = lane & 15, j = a >> 2, q = a & 3;
@@ -691,7 +744,8 @@ MOE_DEV void supercol_tile(int64_t lin, int mt_total, int ntn, int& mt, int& nt)
 // BMT x 128 tiles, NW = BMT / 32 waves (a (BMT/64) x 2 grid of 64 x 64 wave
 // tiles), S LDS stages.
 template <int AMODE, int BMODE, int GROUPING, int EPI, int BSPL, int BMT, int S>
-__global__ __launch_bounds__(BMT * 2) void grouped_gemm_dma_kernel(GemmParams P) {
+__global__ __launch_bounds__(BMT * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void grouped_gemm_dma_kernel(GemmParams P) {
   typedef bf16_t T;
   constexpr int BK = 64;
   constexpr int NW = BMT / 32;
@@ -746,18 +800,22 @@ __global__ __launch_bounds__(BMT * 2) void grouped_gemm_dma_kernel(GemmParams P)
   }
   const int cols_valid = kBN;
 
-  // ---- A source: buffer over this group's rows
+  // ---- A source: the group's rows.  Row-major A (the row GEMMs): one
+  // descriptor based at the tile's first row.  k-major A (the weight
+  // gradients, k = the group's rows): a descriptor per k-slab, based at the
+  // slab's first row.
+  static_assert((GROUPING == GROUP_M) == (AMODE == KC), "A is row-major exactly for GROUP_M");
   const T* a_base = (g < P.EL_A) ? reinterpret_cast<const T*>(P.A) + arow0 * P.lda
                                  : reinterpret_cast<const T*>(P.A_sh);
   const int64_t a_rows = (GROUPING == GROUP_M) ? nrows_g : kdim;
-  const __amdgpu_buffer_rsrc_t a_rs = make_rsrc(a_base, a_rows * P.lda * 2);
+  const rsrc_t a_rs_tile = rows_rsrc(a_base, (AMODE == KC) ? m0 : 0, a_rows, P.lda, P.a_cap);
   uint32_t a_off[A_PER_WAVE];
 #pragma unroll
   for (int u = 0; u < A_PER_WAVE; ++u) {
     const int P_ = 64 * (wave * A_PER_WAVE + u) + lane;  // 16-byte chunk of the slab
     if constexpr (AMODE == KC) {
       const int r = P_ >> 3, lc = (P_ & 7) ^ swz(r);
-      a_off[u] = (uint32_t)(((int64_t)(m0 + r) * P.lda + 8 * lc) * 2);
+      a_off[u] = (uint32_t)(((int64_t)r * P.lda + 8 * lc) * 2);
     } else {
       constexpr int CPR = BMT / 8;  // chunks per k-row
       const int kr = P_ / CPR, lc = (P_ % CPR) ^ ((kr & 3) << 2);
@@ -768,7 +826,7 @@ __global__ __launch_bounds__(BMT * 2) void grouped_gemm_dma_kernel(GemmParams P)
   // GROUP_K: activations (k = rows of the group), buffer over the group rows.
   const T* b_ptr[B_PER_WAVE];
   uint32_t b_off[B_PER_WAVE];
-  __amdgpu_buffer_rsrc_t b_rs;
+  const T* b_base = nullptr;  // GROUP_K: the group's activation rows (k-major)
   const T* Bw0 = reinterpret_cast<const T*>(P.B0) + (int64_t)g * P.strideB;
   const T* Bw1 = (BSPL != BS_NONE) ? reinterpret_cast<const T*>(P.B1) + (int64_t)g * P.strideB
                                    : nullptr;
@@ -790,11 +848,9 @@ __global__ __launch_bounds__(BMT * 2) void grouped_gemm_dma_kernel(GemmParams P)
         }
       }
     }
-    b_rs = make_rsrc(Bw0, 16);
   } else {
-    const T* b_base = (g < P.EL_B) ? reinterpret_cast<const T*>(P.B0) + arow0 * P.ldb
-                                   : reinterpret_cast<const T*>(P.B1);
-    b_rs = make_rsrc(b_base, (int64_t)kdim * P.ldb * 2);
+    b_base = (g < P.EL_B) ? reinterpret_cast<const T*>(P.B0) + arow0 * P.ldb
+                          : reinterpret_cast<const T*>(P.B1);
 #pragma unroll
     for (int u = 0; u < B_PER_WAVE; ++u) {
       const int P_ = 64 * (wave * B_PER_WAVE + u) + lane;
@@ -806,10 +862,16 @@ __global__ __launch_bounds__(BMT * 2) void grouped_gemm_dma_kernel(GemmParams P)
   // issue this wave's DMA instructions for slab kt into (la, lb)
   auto issue = [&](int kt, char* la, char* lb) {
     const int k0 = kt * BK;
-    const uint32_t kadd = (AMODE == KC) ? (uint32_t)(k0 * 2) : (uint32_t)((int64_t)k0 * P.lda * 2);
+    // row-major A: the k offset inside the tile's rows; k-major A: a
+    // descriptor based at the slab's first row
+    const rsrc_t a_rs =
+        (AMODE == KC) ? a_rs_tile : rows_rsrc(a_base, k0, a_rows, P.lda, P.a_cap);
+    const uint32_t kadd = (AMODE == KC) ? (uint32_t)(k0 * 2) : 0u;
 #pragma unroll
     for (int u = 0; u < A_PER_WAVE; ++u)
       dma16_buffer(a_rs, to_lds(la + (wave * A_PER_WAVE + u) * 1024), a_off[u] + kadd);
+    rsrc_t b_rs = {0, 0, 0, 0};  // GROUP_K only: the slab's activation rows
+    if constexpr (GROUPING == GROUP_K) b_rs = rows_rsrc(b_base, k0, kdim, P.ldb, P.b_cap);
 #pragma unroll
     for (int u = 0; u < B_PER_WAVE; ++u) {
       char* dst = lb + (wave * B_PER_WAVE + u) * 1024;
@@ -827,7 +889,7 @@ __global__ __launch_bounds__(BMT * 2) void grouped_gemm_dma_kernel(GemmParams P)
         }
         dma16_global(src, to_lds(dst));
       } else {
-        dma16_buffer(b_rs, to_lds(dst), b_off[u] + (uint32_t)((int64_t)k0 * P.ldb * 2));
+        dma16_buffer(b_rs, to_lds(dst), b_off[u]);
       }
     }
   };
@@ -851,64 +913,82 @@ __global__ __launch_bounds__(BMT * 2) void grouped_gemm_dma_kernel(GemmParams P)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // fragments of k-step ks + 1 are read while the MFMAs of k-step ks run
-  auto mma = [&](char* la, char* lb) {
-    uint4 fa[2][2], fb[2][2];
-    auto frags = [&](int ks, uint4* a, uint4* b) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        a[i] = (AMODE == KC) ? frag_kc(la, ra[i], ks, lane) : frag_mc(la, ra[i], ks, lane, BMT * 2);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        b[j] = (BMODE == KC) ? frag_kc(lb, rb[j], ks, lane) : frag_mc(lb, rb[j], ks, lane, 256);
-    };
-    frags(0, fa[0], fb[0]);
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const int cur = ks & 1;
-      if (ks + 1 < BK / 16) frags(ks + 1, fa[cur ^ 1], fb[cur ^ 1]);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8_t, fa[cur][i]), __builtin_bit_cast(bf16x8_t, fb[cur][j]),
-              acc[i][j], 0, 0, 0);
-    }
-  };
   const int nk = (kdim + BK - 1) / BK;
   constexpr int PER_SLAB = A_PER_WAVE + B_PER_WAVE;  // DMA instructions per slab
-  // one pipeline step: slab kt is in (la, lb); slab kt + S - 1 goes to (na, nb)
-  auto step = [&](int kt, char* la, char* lb, char* na, char* nb) {
-    // slab kt has landed once at most the next slab's loads are outstanding
-    if (S == 3 && kt + 1 < nk) wait_vmcnt<PER_SLAB>();
-    else wait_vmcnt<0>();
-    __syncthreads();
-    if (kt + S - 1 < nk) issue(kt + S - 1, na, nb);
-    // keep the DMA at the head of this slab's MFMAs (the compiler would
-    // otherwise sink it towards the next wait)
-    __builtin_amdgcn_sched_barrier(0);
-    mma(la, lb);
+  // The pipeline for NB active 32-row blocks of this wave's 64 rows: a
+  // ragged group's last tile multiplies (and reads A fragments for) only the
+  // blocks that hold rows of the group; every wave still issues its DMA share
+  // and joins every barrier.
+  auto pipeline = [&](auto nb_c) __attribute__((always_inline)) {
+    constexpr int NB = decltype(nb_c)::value;
+    // fragments of k-step ks + 1 are read while the MFMAs of k-step ks run
+    auto mma = [&](char* la, char* lb) {
+      uint4 fa[2][2], fb[2][2];
+      auto frags = [&](int ks, uint4* a, uint4* b) {
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+          a[i] = (AMODE == KC) ? frag_kc(la, ra[i], ks, lane) : frag_mc(la, ra[i], ks, lane, BMT * 2);
+        if constexpr (NB > 0) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            b[j] = (BMODE == KC) ? frag_kc(lb, rb[j], ks, lane) : frag_mc(lb, rb[j], ks, lane, 256);
+        }
+      };
+      frags(0, fa[0], fb[0]);
+#pragma unroll
+      for (int ks = 0; ks < BK / 16; ++ks) {
+        const int cur = ks & 1;
+        if (ks + 1 < BK / 16) frags(ks + 1, fa[cur ^ 1], fb[cur ^ 1]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8_t, fa[cur][i]), __builtin_bit_cast(bf16x8_t, fb[cur][j]),
+                acc[i][j], 0, 0, 0);
+      }
+    };
+    // one pipeline step: slab kt is in (la, lb); slab kt + S - 1 goes to (na, nb)
+    auto step = [&](int kt, char* la, char* lb, char* na, char* nb) {
+      // slab kt has landed once at most the next slab's loads are outstanding
+      if (S == 3 && kt + 1 < nk) wait_vmcnt<PER_SLAB>();
+      else wait_vmcnt<0>();
+      __syncthreads();
+      if (kt + S - 1 < nk) issue(kt + S - 1, na, nb);
+      // keep the DMA at the head of this slab's MFMAs (the compiler would
+      // otherwise sink it towards the next wait)
+      __builtin_amdgcn_sched_barrier(0);
+      mma(la, lb);
+    };
+    if (nk > 0) issue(0, sA0, sB0);
+    if (S == 3 && nk > 1) issue(1, sA1, sB1);
+    if constexpr (S == 2) {
+      int kt = 0;
+      for (; kt + 1 < nk; kt += 2) {
+        step(kt, sA0, sB0, sA1, sB1);
+        step(kt + 1, sA1, sB1, sA0, sB0);
+      }
+      if (kt < nk) step(kt, sA0, sB0, sA1, sB1);
+    } else {
+      int kt = 0;
+      for (; kt + 2 < nk; kt += 3) {
+        step(kt, sA0, sB0, sA2, sB2);
+        step(kt + 1, sA1, sB1, sA0, sB0);
+        step(kt + 2, sA2, sB2, sA1, sB1);
+      }
+      if (kt < nk) step(kt, sA0, sB0, sA2, sB2);
+      if (kt + 1 < nk) step(kt + 1, sA1, sB1, sA0, sB0);
+    }
   };
-  if (nk > 0) issue(0, sA0, sB0);
-  if (S == 3 && nk > 1) issue(1, sA1, sB1);
-  if constexpr (S == 2) {
-    int kt = 0;
-    for (; kt + 1 < nk; kt += 2) {
-      step(kt, sA0, sB0, sA1, sB1);
-      step(kt + 1, sA1, sB1, sA0, sB0);
-    }
-    if (kt < nk) step(kt, sA0, sB0, sA1, sB1);
+  if constexpr (GROUPING == GROUP_M) {
+    // 32-row blocks of this wave's 64 rows that hold group rows (uniform)
+    const int nb = __builtin_amdgcn_readfirstlane(max(0, min(2, (rows_valid - wm * 64 + 31) / 32)));
+    if (nb == 2) pipeline(std::integral_constant<int, 2>{});
+    else if (nb == 1) pipeline(std::integral_constant<int, 1>{});
+    else pipeline(std::integral_constant<int, 0>{});
   } else {
-    int kt = 0;
-    for (; kt + 2 < nk; kt += 3) {
-      step(kt, sA0, sB0, sA2, sB2);
-      step(kt + 1, sA1, sB1, sA0, sB0);
-      step(kt + 2, sA2, sB2, sA1, sB1);
-    }
-    if (kt < nk) step(kt, sA0, sB0, sA2, sB2);
-    if (kt + 1 < nk) step(kt + 1, sA1, sB1, sA0, sB0);
+    pipeline(std::integral_constant<int, 2>{});
   }
   __syncthreads();
   // 16 KB of LDS per wave for the epilogue, carved from the stage arrays
@@ -997,18 +1077,20 @@ __global__ __launch_bounds__(NW * 64) void grouped_gemm_big_kernel(GemmParams P)
     arow0 = P.offsets[g];
   }
 
-  // ---- A source: buffer over this group's rows (rows past the end read 0)
+  // ---- A source: the group's rows (rows past the end read 0); descriptor
+  // based at the tile's first row (row-major A) or per k-slab (k-major A)
+  static_assert((GROUPING == GROUP_M) == (AMODE == KC), "A is row-major exactly for GROUP_M");
   const T* a_base = (g < P.EL_A) ? reinterpret_cast<const T*>(P.A) + arow0 * P.lda
                                  : reinterpret_cast<const T*>(P.A_sh);
   const int64_t a_rows = (GROUPING == GROUP_M) ? nrows_g : kdim;
-  const __amdgpu_buffer_rsrc_t a_rs = make_rsrc(a_base, a_rows * P.lda * 2);
+  const rsrc_t a_rs_tile = rows_rsrc(a_base, (AMODE == KC) ? m0 : 0, a_rows, P.lda, P.a_cap);
   uint32_t a_off[A_PER_WAVE];
 #pragma unroll
   for (int u = 0; u < A_PER_WAVE; ++u) {
     const int P_ = 64 * (wave * A_PER_WAVE + u) + lane;
     if constexpr (AMODE == KC) {
       const int r = P_ >> 3, lc = (P_ & 7) ^ swz(r);
-      a_off[u] = (uint32_t)(((int64_t)(m0 + r) * P.lda + 8 * lc) * 2);
+      a_off[u] = (uint32_t)(((int64_t)r * P.lda + 8 * lc) * 2);
     } else {
       const int kr = P_ / 32, lc = (P_ % 32) ^ ((kr & 3) << 2);
       a_off[u] = (uint32_t)(((int64_t)kr * P.lda + m0 + 8 * lc) * 2);
@@ -1018,7 +1100,7 @@ __global__ __launch_bounds__(NW * 64) void grouped_gemm_big_kernel(GemmParams P)
   // activation rows of the group through a buffer)
   const T* b_ptr[B_PER_WAVE];
   uint32_t b_off[B_PER_WAVE];
-  __amdgpu_buffer_rsrc_t b_rs;
+  const T* b_base = nullptr;  // GROUP_K: the group's activation rows (k-major)
   const T* Bw0 = reinterpret_cast<const T*>(P.B0) + (int64_t)g * P.strideB;
   const T* Bw1 = (BSPL != BS_NONE) ? reinterpret_cast<const T*>(P.B1) + (int64_t)g * P.strideB
                                    : nullptr;
@@ -1040,11 +1122,9 @@ __global__ __launch_bounds__(NW * 64) void grouped_gemm_big_kernel(GemmParams P)
         }
       }
     }
-    b_rs = make_rsrc(Bw0, 16);
   } else {
-    const T* b_base = (g < P.EL_B) ? reinterpret_cast<const T*>(P.B0) + arow0 * P.ldb
-                                   : reinterpret_cast<const T*>(P.B1);
-    b_rs = make_rsrc(b_base, (int64_t)kdim * P.ldb * 2);
+    b_base = (g < P.EL_B) ? reinterpret_cast<const T*>(P.B0) + arow0 * P.ldb
+                          : reinterpret_cast<const T*>(P.B1);
 #pragma unroll
     for (int u = 0; u < B_PER_WAVE; ++u) {
       const int P_ = 64 * (wave * B_PER_WAVE + u) + lane;
@@ -1062,7 +1142,13 @@ __global__ __launch_bounds__(NW * 64) void grouped_gemm_big_kernel(GemmParams P)
   auto issue = [&](int kt, char* la, char* lb) __attribute__((always_inline)) {
     const bool pad = kt >= nk;
     const int k0 = (GROUPING == GROUP_M && pad) ? (nk - 1) * BK : kt * BK;
-    const uint32_t kadd = (AMODE == KC) ? (uint32_t)(k0 * 2) : (uint32_t)((int64_t)k0 * P.lda * 2);
+    // k-major operands: descriptors based at the slab's first row (a slab
+    // past the group's rows gets an empty range and reads zeros)
+    const rsrc_t a_rs =
+        (AMODE == KC) ? a_rs_tile : rows_rsrc(a_base, k0, a_rows, P.lda, P.a_cap);
+    rsrc_t b_rs = {0, 0, 0, 0};  // GROUP_K only: the slab's activation rows
+    if constexpr (GROUPING == GROUP_K) b_rs = rows_rsrc(b_base, k0, kdim, P.ldb, P.b_cap);
+    const uint32_t kadd = (AMODE == KC) ? (uint32_t)(k0 * 2) : 0u;
 #pragma unroll
     for (int u = 0; u < A_PER_WAVE; ++u)
       dma16_buffer(a_rs, to_lds(la + (wave * A_PER_WAVE + u) * 1024),
@@ -1083,7 +1169,7 @@ __global__ __launch_bounds__(NW * 64) void grouped_gemm_big_kernel(GemmParams P)
         }
         dma16_global(src, to_lds(dst));
       } else {
-        dma16_buffer(b_rs, to_lds(dst), b_off[u] + (uint32_t)((int64_t)k0 * P.ldb * 2));
+        dma16_buffer(b_rs, to_lds(dst), b_off[u]);
       }
     }
   };
@@ -1117,57 +1203,80 @@ __global__ __launch_bounds__(NW * 64) void grouped_gemm_big_kernel(GemmParams P)
   // cores busy.  Scheduling barriers keep the compiler from moving the
   // reads and the DMA behind the MFMAs.
   uint4 fa[2][NI], fb[2][NJ];
-  auto frags = [&](const char* la, const char* lb, int ks, int slot) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < NI; ++i)
-      fa[slot][i] = (AMODE == KC) ? frag_kc(la, wm * WTM + i * 32, ks, lane)
-                                  : frag_mc(const_cast<char*>(la), wm * WTM + i * 32, ks, lane, BM * 2);
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      fb[slot][j] = (BMODE == KC) ? frag_kc(lb, rb[j], ks, lane)
-                                  : frag_mc(const_cast<char*>(lb), rb[j], ks, lane, BN * 2);
-  };
-  auto mfmas = [&](int slot) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < NI; ++i)
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(bf16x8_t, fb[slot][j]), __builtin_bit_cast(bf16x8_t, fa[slot][i]),
-            acc[i][j], 0, 0, 0);
-  };
   constexpr int PER_SLAB = A_PER_WAVE + B_PER_WAVE;  // DMA instructions per slab
-  // Slab kt is in (la, lb) with its k-step 0 fragments in register slot 0;
-  // slab kt + 1 is landing in (na, nb).  The body is branch-free: the slab
-  // count is padded to even and the DMA runs on past the end (see issue).
-  auto step = [&](int kt, char* la, char* lb, char* na, char* nb) __attribute__((always_inline)) {
-    frags(la, lb, 1, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas(0);
-    frags(la, lb, 2, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas(1);
-    frags(la, lb, 3, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas(0);
-    wait_vmcnt<0>();
-    __syncthreads();
-    issue(kt + 2, la, lb);
-    frags(na, nb, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas(1);
-  };
   const int nkp = nk + (nk & 1);
-  if (nkp > 0) {
-    issue(0, sA0, sB0);
-    issue(1, sA1, sB1);
-    wait_vmcnt<PER_SLAB>();
-    __syncthreads();
-    frags(sA0, sB0, 0, 0);
-  }
-  for (int kt = 0; kt < nkp; kt += 2) {
-    step(kt, sA0, sB0, sA1, sB1);
-    step(kt + 1, sA1, sB1, sA0, sB0);
+  // The main loop for NB active 32-row blocks of the wave tile: a ragged
+  // group's last tile computes (and reads A fragments for) only the blocks
+  // that hold rows of the group; a wave with none still issues its DMA share
+  // and joins every barrier.
+  auto main_loop = [&](auto nb_c) __attribute__((always_inline)) {
+    constexpr int NB = decltype(nb_c)::value;
+    auto frags = [&](const char* la, const char* lb, int ks, int slot) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+        fa[slot][i] = (AMODE == KC) ? frag_kc(la, wm * WTM + i * 32, ks, lane)
+                                    : frag_mc(const_cast<char*>(la), wm * WTM + i * 32, ks, lane, BM * 2);
+      if constexpr (NB > 0) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          fb[slot][j] = (BMODE == KC) ? frag_kc(lb, rb[j], ks, lane)
+                                      : frag_mc(const_cast<char*>(lb), rb[j], ks, lane, BN * 2);
+      }
+    };
+    auto mfmas = [&](int slot) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8_t, fb[slot][j]), __builtin_bit_cast(bf16x8_t, fa[slot][i]),
+              acc[i][j], 0, 0, 0);
+    };
+    // Slab kt is in (la, lb) with its k-step 0 fragments in register slot 0;
+    // slab kt + 1 is landing in (na, nb).  The body is branch-free: the slab
+    // count is padded to even and the DMA runs on past the end (see issue).
+    auto step = [&](int kt, char* la, char* lb, char* na, char* nb) __attribute__((always_inline)) {
+      frags(la, lb, 1, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(0);
+      frags(la, lb, 2, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(1);
+      frags(la, lb, 3, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(0);
+      wait_vmcnt<0>();
+      __syncthreads();
+      issue(kt + 2, la, lb);
+      frags(na, nb, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(1);
+    };
+    if (nkp > 0) {
+      issue(0, sA0, sB0);
+      issue(1, sA1, sB1);
+      wait_vmcnt<PER_SLAB>();
+      __syncthreads();
+      frags(sA0, sB0, 0, 0);
+    }
+    for (int kt = 0; kt < nkp; kt += 2) {
+      step(kt, sA0, sB0, sA1, sB1);
+      step(kt + 1, sA1, sB1, sA0, sB0);
+    }
+  };
+  if constexpr (GROUPING == GROUP_M) {
+    // 32-row blocks of this wave's rows that hold group rows (uniform)
+    const int nb = __builtin_amdgcn_readfirstlane(
+        max(0, min(NI, (rows_valid - wm * WTM + 31) / 32)));
+    if (nb >= NI) main_loop(std::integral_constant<int, NI>{});
+    else if (nb == 0) main_loop(std::integral_constant<int, 0>{});
+    else if (nb == 1) main_loop(std::integral_constant<int, 1>{});
+    else if constexpr (NI > 2) {
+      if (nb == 2) main_loop(std::integral_constant<int, 2>{});
+      else main_loop(std::integral_constant<int, (NI > 3 ? 3 : NI)>{});
+    }
+  } else {
+    main_loop(std::integral_constant<int, NI>{});
   }
   // the run-ahead DMA must land, and every wave be done with the slabs,
   // before the stage buffers are reused for the epilogue
@@ -1419,10 +1528,12 @@ __global__ __launch_bounds__(512) void grouped_gemm_persist_kernel(GemmParams P)
 
   // ---- tile state (uniform)
   struct Tile {
-    int g, m0, n0, rows_valid, nk;
-    int64_t arow0;
+    int g, m0, n0, rows_valid, nk, kdim;
+    int64_t arow0, a_rows;
     bool real;
-    __amdgpu_buffer_rsrc_t a_rs, b_rs;
+    const T* a_base;               // the group's A rows
+    const T* b_base;               // GROUP_K: the group's B rows
+    rsrc_t a_rs;   // row-major A: based at the tile's first row
   };
   auto decode = [&](int64_t j, bool real) __attribute__((always_inline)) {
     Tile t;
@@ -1451,19 +1562,17 @@ __global__ __launch_bounds__(512) void grouped_gemm_persist_kernel(GemmParams P)
       kdim = P.offsets[t.g + 1] - P.offsets[t.g];
     }
     t.arow0 = P.offsets[t.g];
+    t.kdim = kdim;
     t.nk = max(2, (kdim + BK - 1) / BK);
     t.nk += t.nk & 1;  // even: the next tile's slab 0 always lands in stage 0
-    const T* a_base = (t.g < P.EL_A) ? reinterpret_cast<const T*>(P.A) + t.arow0 * P.lda
-                                     : reinterpret_cast<const T*>(P.A_sh);
-    const int64_t a_rows = (GROUPING == GROUP_M) ? nrows_g : kdim;
-    t.a_rs = make_rsrc(a_base, a_rows * P.lda * 2);
-    if constexpr (GROUPING == GROUP_K) {
-      const T* b_base = (t.g < P.EL_B) ? reinterpret_cast<const T*>(P.B0) + t.arow0 * P.ldb
-                                       : reinterpret_cast<const T*>(P.B1);
-      t.b_rs = make_rsrc(b_base, (int64_t)kdim * P.ldb * 2);
-    } else {
-      t.b_rs = make_rsrc(P.B0, 16);
-    }
+    t.a_base = (t.g < P.EL_A) ? reinterpret_cast<const T*>(P.A) + t.arow0 * P.lda
+                              : reinterpret_cast<const T*>(P.A_sh);
+    t.a_rows = (GROUPING == GROUP_M) ? nrows_g : kdim;
+    t.a_rs = rows_rsrc(t.a_base, (AMODE == KC) ? t.m0 : 0, t.a_rows, P.lda, P.a_cap);
+    t.b_base = nullptr;
+    if constexpr (GROUPING == GROUP_K)
+      t.b_base = (t.g < P.EL_B) ? reinterpret_cast<const T*>(P.B0) + t.arow0 * P.ldb
+                                : reinterpret_cast<const T*>(P.B1);
     // slabs holding real data: the rest of the (padded) slab count reads 0
     t.rows_valid = real ? t.rows_valid : 0;
     return t;
@@ -1480,11 +1589,17 @@ __global__ __launch_bounds__(512) void grouped_gemm_persist_kernel(GemmParams P)
   auto issue = [&](const Tile& t, int nreal, int s, char* la, char* lb) __attribute__((always_inline)) {
     const bool pad = !t.real || s >= nreal;
     const int k0 = (GROUPING == GROUP_M && pad) ? max(nreal - 1, 0) * BK : s * BK;
-    const uint32_t tbase = (AMODE == KC) ? (uint32_t)((int64_t)t.m0 * P.lda * 2) : (uint32_t)(t.m0 * 2);
-    const uint32_t kadd = (AMODE == KC) ? (uint32_t)(k0 * 2) : (uint32_t)((int64_t)k0 * P.lda * 2);
+    // row-major A: tile-based descriptor plus the k offset; k-major A: a
+    // descriptor based at the slab's first row plus the tile's m offset
+    const rsrc_t a_rs =
+        (AMODE == KC) ? t.a_rs : rows_rsrc(t.a_base, k0, t.a_rows, P.lda, P.a_cap);
+    const uint32_t tbase = (AMODE == KC) ? 0u : (uint32_t)(t.m0 * 2);
+    const uint32_t kadd = (AMODE == KC) ? (uint32_t)(k0 * 2) : 0u;
+    rsrc_t b_rs = {0, 0, 0, 0};  // GROUP_K only: the slab's activation rows
+    if constexpr (GROUPING == GROUP_K) b_rs = rows_rsrc(t.b_base, k0, t.kdim, P.ldb, P.b_cap);
 #pragma unroll
     for (int u = 0; u < A_PER_WAVE; ++u)
-      dma16_buffer(t.a_rs, to_lds(la + (wave * A_PER_WAVE + u) * 1024),
+      dma16_buffer(a_rs, to_lds(la + (wave * A_PER_WAVE + u) * 1024),
                    pad ? 0x80000000u : tbase + a_lane[u] + kadd);
 #pragma unroll
     for (int u = 0; u < B_PER_WAVE; ++u) {
@@ -1510,9 +1625,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_persist_kernel(GemmParams P)
         }
         dma16_global(src, to_lds(dst));
       } else {
-        dma16_buffer(t.b_rs, to_lds(dst),
-                     pad ? 0x80000000u
-                         : (uint32_t)(t.n0 * 2 + b_lane[u] + (int64_t)k0 * P.ldb * 2));
+        dma16_buffer(b_rs, to_lds(dst), pad ? 0x80000000u : (uint32_t)(t.n0 * 2 + b_lane[u]));
       }
     }
   };
@@ -1800,11 +1913,15 @@ template <int AM, int BM_, int GR, int EPI, int BS, int BMT, int S>
 static int launch_dma(const char* name, GemmParams P, hipStream_t st) {
   tile_space(P, GR, BMT);
   if (P.nblocks <= 0) return MOE_OK;
-  if (GR == GROUP_M && BMT == 128 && EPI == EPI_SWIGLU_FWD && P.Kdim <= 1024) {
+  if (GR == GROUP_M && BMT == 128 && EPI == EPI_SWIGLU_FWD && P.Kdim <= 1024 &&
+      (int64_t)P.n_routed * 16 <= P.mt_total) {
     // the gate/up forward with short reductions takes 2-D tile blocks per
     // XCD (measured on MiniMind: -4 to -7 % for this GEMM; with 2048-deep
     // reductions, and for the other row GEMMs, slower); the extra m-tiles
-    // that round mt_total up find no group and exit
+    // that round mt_total up find no group and exit.  The m-tile bound
+    // exceeds the real m-tiles by up to one per routed group, and those
+    // surplus tiles all fall to the XCDs of the last row block: with few
+    // groups next to the m-tiles that imbalance stays small
     P.xcd_xn = (P.ntn % 4 == 0) ? 4 : (P.ntn % 2 == 0) ? 2 : 0;
     if (P.xcd_xn) {
       const int xm = 8 / P.xcd_xn;
@@ -1845,6 +1962,8 @@ static int launch_persist(const char* name, GemmParams P, hipStream_t st) {
 
 template <typename T, int AM, int BM_, int GR, int EPI, int BS>
 static int run_gemm(const char* name, GemmParams& P, hipStream_t st) {
+  P.a_cap = (int)(INT32_MAX / (std::max<int64_t>(P.lda, 1) * 2));
+  P.b_cap = (int)(INT32_MAX / (std::max<int64_t>(P.ldb, 1) * 2));
   if constexpr (sizeof(T) == 2) {
     const bool full128 = (P.N % kBN == 0) && (GR == GROUP_M ? P.Kdim % 64 == 0 : P.Mfix % 128 == 0);
     const bool full256 = full128 && (GR == GROUP_M || P.Mfix % 256 == 0);

@@ -39,11 +39,21 @@ def assert_close(name, a, r, tol):
     return e
 
 
-def assert_rows_close(name, a, r, tol):
+ROW_FLOOR = 1e-3  # rows below this fraction of the largest row: absolute bound
+
+
+def assert_rows_close(name, a, r, tol, zero_rows_exact=False):
     """Per-row form of the metric for outputs whose rows are independent
-    tokens (y, dx): every row i must have max|a_i - r_i| / max|r_i| <= tol,
-    and a row whose reference is all zeros must be exactly zero, so that a
-    token with small outputs cannot hide behind the tensor's largest row."""
+    tokens (y, dx), so that a token with small outputs cannot hide behind the
+    tensor's largest row: every row i must have
+
+        max|a_i - r_i| <= tol * max(max|r_i|, ROW_FLOOR * max|r|).
+
+    The floor covers rows that are (near) zero only by cancellation, e.g. the
+    router part of dx for a token no expert took, whose logit gradient sums to
+    ~1e-17 in fp64 and ~1e-9 in fp32.  zero_rows_exact additionally demands
+    exact zeros where the reference row is exactly zero by structure (y of a
+    token with no kept slot)."""
     a = np.asarray(a, np.float64)
     r = np.asarray(r, np.float64)
     assert a.shape == r.shape, (a.shape, r.shape)
@@ -53,12 +63,17 @@ def assert_rows_close(name, a, r, tol):
     r2 = r.reshape(r.shape[0], -1)
     num = np.max(np.abs(a2 - r2), axis=1)
     den = np.max(np.abs(r2), axis=1)
-    zero = den == 0.0
-    assert np.all(num[zero] == 0.0), f"{name}: rows {np.nonzero(zero & (num > 0))[0][:8]} " \
-                                     "must be exactly zero"
-    e = np.where(zero, 0.0, num / np.where(zero, 1.0, den))
+    if zero_rows_exact:
+        bad = np.nonzero((den == 0.0) & (num > 0))[0]
+        assert len(bad) == 0, f"{name}: rows {bad[:8]} must be exactly zero"
+    scale = float(np.max(den))
+    if scale == 0.0:
+        assert np.all(num == 0.0), f"{name}: reference all zero, output not"
+        return 0.0
+    e = num / np.maximum(den, ROW_FLOOR * scale)
     worst = int(np.argmax(e))
-    assert e[worst] <= tol, f"{name}: row {worst} rel err {e[worst]:.3e} > {tol:.1e}"
+    assert e[worst] <= tol, (f"{name}: row {worst} err {e[worst]:.3e} > {tol:.1e} "
+                             f"(row max {den[worst]:.3e}, tensor max {scale:.3e})")
     return float(e[worst])
 
 

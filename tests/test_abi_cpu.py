@@ -54,7 +54,7 @@ def test_rows_and_workspace():
     assert L.workspace_size(cfg(T=0)) >= 0
 
 
-BAD = [dict(D=100), dict(F=96), dict(K=0), dict(K=9), dict(E=0), dict(E=2000, K=2),
+BAD = [dict(D=100), dict(F=96), dict(D=(1 << 20) + 64), dict(F=(1 << 20) + 64), dict(K=0), dict(K=9), dict(E=0), dict(E=2000, K=2),
        dict(expert_lo=5, expert_hi=3), dict(expert_hi=9), dict(n_shared=2), dict(score_fn=3),
        dict(gating=2), dict(T=-1), dict(K=65, E=100), dict(capacity_factor=float("inf"))]
 
@@ -64,6 +64,19 @@ def test_invalid_config_rejected(bad):
     c = cfg(**bad)
     v = C.c_size_t()
     assert L.lib().moe_workspace_size(C.byref(c), C.byref(v)) == L.MOE_EINVAL
+
+
+def test_groups_over_2gib_accepted():
+    """Row buffers beyond 2^31 bytes are supported (the grouped GEMMs base
+    their buffer descriptors at each tile's or slab's first row): one expert
+    of 40000 rows with 2F = 65536 bf16 activations per row (5.2 GB) is a valid
+    configuration; only D or F above 2^20 is refused."""
+    c = cfg(T=40000, D=256, E=1, K=1, F=32768)
+    v = C.c_size_t()
+    assert L.lib().moe_workspace_size(C.byref(c), C.byref(v)) == L.MOE_OK
+    assert v.value > 40000 * 65536 * 2
+    c = cfg(D=1 << 20, F=1 << 20)
+    assert L.lib().moe_workspace_size(C.byref(c), C.byref(v)) == L.MOE_OK
 
 
 def test_bad_dtype_rejected():

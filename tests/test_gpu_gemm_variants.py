@@ -26,6 +26,9 @@ WORKLOADS = {
     # pipelines end on their other stage; the GEMMs whose N = F is not
     # 128-divisible run on the register-staged kernel
     "odd_reduction": S.WORKLOADS["minimind"].with_(T=512, D=512, F=576, E=4, K=2),
+    # F = 640: the gate/up forward has 2F / 128 = 10 column tiles, so its
+    # 2-D tile blocks per XCD split the columns in two (not four)
+    "xcd_two_column_groups": S.WORKLOADS["minimind"].with_(T=512, D=512, F=640, E=4, K=2),
 }
 _ref = {}
 
