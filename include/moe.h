@@ -166,6 +166,26 @@ int moe_permute(const moe_config* cfg, const int32_t* topk_idx, const void* x,
                 moe_stream_t stream);
 
 /*
+ * moe_permute_noalloc -- moe_permute without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  Same arguments,
+ * results and errors as moe_permute, bit for bit.  Its scratch (the tiled
+ * permute's per-tile expert histograms and bases, 2 * ceil(T*K/256) * E
+ * int32) lives in a static device array of 8 MiB that every GPU the library
+ * runs on holds until the process ends; T*K*E up to about 2^28 fits.  Larger
+ * configurations return MOE_EWORKSPACE before any device call.  The call
+ * allocates nothing.  It runs on the current device; the first call on a
+ * device looks up that device's copy of the array (MOE_ELAUNCH if that
+ * fails).  All calls on one GPU share the array: calls that overlap in time
+ * on one GPU (on different streams, or from several host threads) race, so
+ * order them on one stream.
+ */
+int moe_permute_noalloc(const moe_config* cfg, const int32_t* topk_idx, const void* x,
+                        int32_t* counts_all, int32_t* offsets, int32_t* slot_row,
+                        int32_t* row_token, int32_t* row_slot, int32_t* n_dropped, void* x_perm,
+                        moe_stream_t stream);
+
+/*
  * moe_expert_ffn -- grouped SwiGLU experts on the permuted rows.
  * [P5] 8.1 (SwiGLU expert, ~3DF parameters), 8.7 (shared expert, weight 1),
  * 8.8 (grouped GEMM instead of a per-expert loop); [P3] efficient inference.

@@ -24,7 +24,7 @@ EXPORTS = ["moe_capacity", "moe_rows_max", "moe_workspace_size", "moe_route", "m
            "moe_expert_ffn", "moe_combine", "aux_balance_loss", "moe_backward",
            "moe_error_string", "moe_timing_enable", "moe_timing_report",
            "moe_timing_select", "moe_bias_update", "aux_seq_loss", "moe_route_ex",
-           "moe_backward_ex", "moe_route_expert_choice"]
+           "moe_backward_ex", "moe_route_expert_choice", "moe_permute_noalloc"]
 
 
 class MoeConfig(C.Structure):
@@ -60,6 +60,7 @@ def lib():
             "moe_workspace_size": [cfg, C.POINTER(C.c_size_t)],
             "moe_route": [cfg, P, P, P, P, P, P, P, P, I, P],
             "moe_permute": [cfg, P, P, P, P, P, P, P, P, P, P, S, P],
+            "moe_permute_noalloc": [cfg, P, P, P, P, P, P, P, P, P, P],
             "moe_expert_ffn": [cfg, P, P, P, P, P, P, P, P, P, P],
             "moe_combine": [cfg, P, P, P, P, P, P],
             "aux_balance_loss": [cfg, P, P, C.c_float, C.c_float, P, P, P, S, P],
@@ -146,6 +147,14 @@ def moe_permute(cfg, topk_idx, x, counts_all, offsets, slot_row, row_token, row_
                            ptr(x_perm), ptr(ws), ws.numel() * ws.element_size(),
                            stream_handle(stream))
     _check("moe_permute", rc)
+
+
+def moe_permute_noalloc(cfg, topk_idx, x, counts_all, offsets, slot_row, row_token, row_slot,
+                        n_dropped, x_perm, stream=None):
+    rc = lib().moe_permute_noalloc(C.byref(cfg), ptr(topk_idx), ptr(x), ptr(counts_all),
+                                   ptr(offsets), ptr(slot_row), ptr(row_token), ptr(row_slot),
+                                   ptr(n_dropped), ptr(x_perm), stream_handle(stream))
+    _check("moe_permute_noalloc", rc)
 
 
 def moe_expert_ffn(cfg, x, x_perm, offsets, w_gate, w_up, w_down, act, h, o_perm, stream=None):

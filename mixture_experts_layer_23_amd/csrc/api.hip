@@ -4,6 +4,7 @@
 #include <cstdio>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -160,6 +161,50 @@ Workspace workspace_layout(const moe_config& c) {
   return L;
 }
 
+// --- allocation-free permute ----------------------------------------------
+// The tiled permute's per-tile expert histograms and bases (2 * ntiles * E
+// int32, ntiles = ceil(T*K / 256)) live in this static device array for
+// moe_permute_noalloc.  Every GPU the library runs on holds its own copy for
+// the life of the process; each call on a GPU reuses it (nothing in it must
+// start at zero: the histogram kernel writes every entry it later reads).
+constexpr size_t kScratchBytes = 8u << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+// Host code may not pass `scratch` itself to a kernel (on the host that name
+// is a stand-in, not the device address): the address is looked up once per
+// device, with that device current, and kept.
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices] = {};
+
+static int scratch_on_current_device(char** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    set_error("hipGetDevice", e);
+    return MOE_ELAUNCH;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return MOE_EINVAL;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      set_error("hipGetSymbolAddress(scratch)", e);
+      return MOE_ELAUNCH;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = static_cast<char*>(g_scratch_ptr[dev]);
+  return MOE_OK;
+}
+
+// scratch bytes the permute needs: the tile histograms and, after them, the
+// tile bases (the first two regions of the workspace layout)
+static size_t permute_scratch_bytes(const moe_config& c, const Workspace& L) {
+  return L.tile_base + al((size_t)L.ntiles * c.E * 4);
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -260,6 +305,24 @@ int moe_permute(const moe_config* cfg, const int32_t* topk_idx, const void* x,
   if (cfg->T == 0) return MOE_OK;
   return launch_permute(*cfg, capacity_of(*cfg), topk_idx, x, counts_all, offsets, slot_row,
                         row_token, row_slot, n_dropped, x_perm, (char*)ws, L, (hipStream_t)stream);
+}
+
+int moe_permute_noalloc(const moe_config* cfg, const int32_t* topk_idx, const void* x,
+                        int32_t* counts_all, int32_t* offsets, int32_t* slot_row,
+                        int32_t* row_token, int32_t* row_slot, int32_t* n_dropped, void* x_perm,
+                        moe_stream_t stream) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (cfg->routing != MOE_TOKEN_CHOICE) return MOE_EINVAL;
+  REQ(topk_idx); REQ(x); REQ(counts_all); REQ(offsets); REQ(slot_row); REQ(row_token);
+  REQ(row_slot); REQ(n_dropped); REQ(x_perm);
+  const Workspace L = workspace_layout(*cfg);
+  if (permute_scratch_bytes(*cfg, L) > kScratchBytes) return MOE_EWORKSPACE;
+  if (cfg->T == 0) return MOE_OK;
+  char* ws = nullptr;
+  if ((rc = scratch_on_current_device(&ws))) return rc;
+  return launch_permute(*cfg, capacity_of(*cfg), topk_idx, x, counts_all, offsets, slot_row,
+                        row_token, row_slot, n_dropped, x_perm, ws, L, (hipStream_t)stream);
 }
 
 int moe_expert_ffn(const moe_config* cfg, const void* x, const void* x_perm, const int32_t* offsets,

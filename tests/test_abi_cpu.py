@@ -79,6 +79,21 @@ def test_groups_over_2gib_accepted():
     assert L.lib().moe_workspace_size(C.byref(c), C.byref(v)) == L.MOE_OK
 
 
+def test_permute_noalloc_refuses_oversized_scratch_on_host():
+    """moe_permute_noalloc keeps the tile histograms in a fixed 8 MiB device
+    array: a configuration that needs more is refused before any device call
+    (this runs without a GPU), and argument errors match moe_permute's."""
+    lib = L.lib()
+    big = cfg(T=8192, E=1024, K=64, D=128, F=128)   # 2048 tiles x 1024 experts x 8 B
+    args = [FAKE] * 9 + [None]
+    assert lib.moe_permute_noalloc(C.byref(big), *args) == L.MOE_EWORKSPACE
+    c = cfg()
+    assert lib.moe_permute_noalloc(C.byref(c), None, *([FAKE] * 8), None) == L.MOE_EINVAL
+    assert lib.moe_permute_noalloc(C.byref(c), FAKE + 8, *([FAKE] * 8), None) == L.MOE_EALIGN
+    ec = cfg(routing=L.MOE_EXPERT_CHOICE, gating=L.MOE_GATE_TRUNCATED)
+    assert lib.moe_permute_noalloc(C.byref(ec), *args) == L.MOE_EINVAL
+
+
 def test_bad_dtype_rejected():
     c = cfg(dtype=7)
     v = C.c_size_t()
