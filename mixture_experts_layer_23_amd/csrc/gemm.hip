@@ -79,6 +79,7 @@ struct GemmParams {
   int F;
   int xcd_xn;         // > 0: 2-D tile blocks per XCD (xcd_xn column groups)
   int a_cap, b_cap;   // rows of lda / ldb bf16 elements in 2^31 - 1 bytes
+  int xcd_m;          // GROUP_M: each XCD takes a block of the real m-tiles
 };
 
 MOE_DEV int swz(int row) { return (row ^ (row >> 3)) & 7; }
@@ -89,6 +90,25 @@ MOE_DEV int64_t remap_xcd(int64_t b, int64_t n) {
   const int64_t q = n / 8, r = n % 8;
   const int64_t x = b % 8, i = b / 8;
   return (x < r) ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
+}
+
+// Weight-gradient (GROUP_K) tile order for launch (or work) index b of n
+// tiles: the shared expert's tiles -- each a reduction over all T rows, much
+// longer than a routed expert's -- come first, so they are spread over the
+// CUs and finish early instead of forming the tail (each XCD takes a
+// contiguous block of them); the routed experts' tiles follow, XCD-blocked.
+// The shared expert is the last group.  g: group, tl: tile within the group.
+MOE_DEV void groupk_tile(int64_t b, int64_t n, int64_t per, bool shared, int G, int& g,
+                         int64_t& tl) {
+  const int64_t sh = shared ? per : 0;
+  if (b < sh) {
+    g = G - 1;
+    tl = remap_xcd(b, sh);
+  } else {
+    const int64_t l = remap_xcd(b - sh, n - sh);
+    g = (int)(l / per);
+    tl = l - (int64_t)g * per;
+  }
 }
 
 // wave-parallel search of the group holding global m-tile mt (GROUP_M) for
@@ -126,6 +146,37 @@ MOE_DEV bool find_group(const int32_t* offsets, int G, int mt, int& g_out, int& 
   g_out = __shfl(gsel, owner, 64);
   mt_local = mt - __shfl(base, owner, 64);
   return true;
+}
+
+// Total m-tiles of bm rows over all groups (uniform).
+MOE_DEV int total_mtiles(const int32_t* offsets, int G, int bm) {
+  const int lane = threadIdx.x & 63;
+  const int gpl = (G + 63) / 64;
+  int mine = 0;
+  for (int j = 0; j < gpl; ++j) {
+    const int g = lane * gpl + j;
+    if (g < G) mine += (offsets[g + 1] - offsets[g] + bm - 1) / bm;
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mine += __shfl_xor(mine, o, 64);
+  return __builtin_amdgcn_readfirstlane(mine);
+}
+
+// Row-GEMM tile order for layers with many small groups: XCD x (workgroup b
+// runs on XCD b % 8) takes the real m-tiles [x mh, (x + 1) mh), mh =
+// ceil(mt_real / 8), each with all its column tiles, column fastest.  A row
+// panel is then fetched by one XCD for all its column tiles, and a group's
+// weights by the one or two XCDs holding its few m-tiles, where giving each
+// XCD a column band makes every XCD fetch every row panel.  The grid holds 8
+// ceil(mt_total / 8) ntn blocks (mt_total bounds mt_real); blocks past an
+// XCD's share return false.
+MOE_DEV bool xcd_mblock_tile(int64_t b, int mt_real, int ntn, int& mt, int& nt) {
+  const int x = (int)(b % 8);
+  const int64_t i = b / 8;
+  const int mh = (mt_real + 7) / 8;
+  mt = x * mh + (int)(i / ntn);
+  nt = (int)(i % ntn);
+  return mt < min((x + 1) * mh, mt_real);
 }
 
 template <typename T>
@@ -789,9 +840,10 @@ void grouped_gemm_dma_kernel(GemmParams P) {
     arow0 = P.offsets[g];
   } else {
     const int64_t per = (int64_t)P.ntm * P.ntn;
-    g = (int)(lin / per);
+    int64_t tl;
+    groupk_tile(blockIdx.x, P.nblocks, per, P.shared_rows > 0, P.G, g, tl);
     int mt, nt;
-    supercol_tile<kSuperColsK>(lin - (int64_t)g * per, P.ntm, P.ntn, mt, nt);
+    supercol_tile<kSuperColsK>(tl, P.ntm, P.ntn, mt, nt);
     m0 = mt * BMT;
     n0 = nt * kBN;
     rows_valid = BMT;
@@ -1055,7 +1107,11 @@ __global__ __launch_bounds__(NW * 64) void grouped_gemm_big_kernel(GemmParams P)
   int nrows_g = 0;
   if constexpr (GROUPING == GROUP_M) {
     int mt, nt, mtl;
-    supercol_tile<kSuperColsM>(lin, P.mt_total, P.ntn, mt, nt);
+    if (P.xcd_m) {
+      if (!xcd_mblock_tile(blockIdx.x, total_mtiles(P.offsets, P.G, BM), P.ntn, mt, nt)) return;
+    } else {
+      supercol_tile<kSuperColsM>(lin, P.mt_total, P.ntn, mt, nt);
+    }
     if (!find_group(P.offsets, P.G, mt, g, mtl, BM)) return;
     g = __builtin_amdgcn_readfirstlane(g);
     mtl = __builtin_amdgcn_readfirstlane(mtl);
@@ -1067,9 +1123,10 @@ __global__ __launch_bounds__(NW * 64) void grouped_gemm_big_kernel(GemmParams P)
     arow0 = P.offsets[g];
   } else {
     const int64_t per = (int64_t)P.ntm * P.ntn;
-    g = (int)(lin / per);
+    int64_t tl;
+    groupk_tile(blockIdx.x, P.nblocks, per, P.shared_rows > 0, P.G, g, tl);
     int mt, nt;
-    supercol_tile<kSuperColsK>(lin - (int64_t)g * per, P.ntm, P.ntn, mt, nt);
+    supercol_tile<kSuperColsK>(tl, P.ntm, P.ntn, mt, nt);
     m0 = mt * BM;
     n0 = nt * BN;
     rows_valid = BM;
@@ -1553,9 +1610,10 @@ __global__ __launch_bounds__(512) void grouped_gemm_persist_kernel(GemmParams P)
       kdim = P.Kdim;
     } else {
       const int64_t per = (int64_t)P.ntm * P.ntn;
-      t.g = (int)(lin / per);
+      int64_t tl;
+      groupk_tile(j, n_tiles, per, P.shared_rows > 0, P.G, t.g, tl);
       int mt, nt;
-      supercol_tile<kSuperColsK>(lin - (int64_t)t.g * per, P.ntm, P.ntn, mt, nt);
+      supercol_tile<kSuperColsK>(tl, P.ntm, P.ntn, mt, nt);
       t.m0 = mt * BM;
       t.n0 = nt * BN;
       t.rows_valid = BM;
@@ -1943,6 +2001,14 @@ static int launch_big(const char* name, GemmParams P, hipStream_t st) {
   P.ntn = P.N / BN;
   tile_space(P, GR, 256);
   if (P.nblocks <= 0) return MOE_OK;
+  if (GR == GROUP_M && EPI == EPI_STORE && P.n_routed >= 64) {
+    // many small groups: XCD blocks of the real m-tiles (rounded grid).
+    // Measured on the DeepSeek-V3-like layer: down projection 3.08 -> 2.83
+    // ms, gate/up input gradient 5.79 -> 5.67 ms; not for the SwiGLU
+    // forward (5.15 -> 5.33 ms)
+    P.xcd_m = 1;
+    P.nblocks = (int64_t)cdiv(P.mt_total, 8) * 8 * P.ntn;
+  }
   MOE_LAUNCH(name, (grouped_gemm_big_kernel<AM, BM_, GR, EPI, BS, BN, NW>),
              dim3((unsigned)P.nblocks), dim3(NW * 64), 0, st, P);
   return MOE_OK;
@@ -1969,13 +2035,25 @@ static int run_gemm(const char* name, GemmParams& P, hipStream_t st) {
     const bool full256 = full128 && (GR == GROUP_M || P.Mfix % 256 == 0);
     const bool wide = full256 && P.N % 256 == 0;
     int cfg = cfg_override(name);
-    if (cfg < 0 && (EPI == EPI_SWIGLU_BWD || (GR == GROUP_M && P.Kdim <= 2048))) {
+    // 256 x 256 tiles of a row GEMM: the m-tile bound times the column tiles
+    int64_t tiles256 = 0;
+    if (GR == GROUP_M && EPI == EPI_STORE && wide) {
+      GemmParams Q = P;
+      Q.ntn = P.N / 256;
+      tile_space(Q, GR, 256);
+      tiles256 = Q.nblocks;
+    }
+    if (cfg < 0 && (EPI == EPI_SWIGLU_BWD ||
+                    (GR == GROUP_M && (P.Kdim < 2048 || (P.Kdim == 2048 && tiles256 < 1024))))) {
       // 128 x 128 tiles run two workgroups per CU, so one's epilogue and
       // first-slab wait overlap the other's main loop.  That wins for the
       // row GEMMs with short reductions (K <= 2048: a tile's main loop is
       // then not much longer than its prologue and epilogue) and for the
       // SwiGLU-backward epilogue (activations read, two gradients written)
-      // at every measured shape; long reductions favour the 256-wide tiles.
+      // at every measured shape; long reductions, and the plain-store row
+      // GEMM at K = 2048 with many tiles (DeepSeek-V3-like down projection:
+      // 3.04 vs 3.33 ms; the SwiGLU forward at OLMoE-like K = 2048 is not:
+      // 0.53 vs 0.38 ms), favour the 256-wide tiles.
       cfg = 1;
     }
     if (cfg < 0) {
@@ -1988,10 +2066,10 @@ static int run_gemm(const char* name, GemmParams& P, hipStream_t st) {
         tile_space(Q, GR, 256);
       }
       if (wide && Q.nblocks >= (GR == GROUP_K ? 192 : 384)) {
-        // the plain-store row GEMM (down projection forward) runs persistent:
-        // measured 10-30 % faster there; the fused epilogues and the weight
-        // gradients are not (register pressure, store waits at tile change)
-        cfg = (GR == GROUP_M && EPI == EPI_STORE && BS == BS_NONE) ? 7 : 5;
+        // 256 x 256 tiles on 8 waves (the persistent variant spills
+        // registers and was measured no faster: Mixtral-like down projection
+        // 2.79 vs 2.83 ms)
+        cfg = 5;
       } else {
         Q = P;
         tile_space(Q, GR, 256);

@@ -29,6 +29,9 @@ WORKLOADS = {
     # F = 640: the gate/up forward has 2F / 128 = 10 column tiles, so its
     # 2-D tile blocks per XCD split the columns in two (not four)
     "xcd_two_column_groups": S.WORKLOADS["minimind"].with_(T=512, D=512, F=640, E=4, K=2),
+    # 64 routed experts (+ a shared one): the 256-row kernels give each XCD a
+    # block of the real m-tiles in the plain-store row GEMMs
+    "many_experts": S.WORKLOADS["deepseek_v3"].with_(T=512, D=1024, F=256, E=64, K=8),
 }
 _ref = {}
 
