@@ -627,7 +627,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmParams P) {
 //  * K-contiguous operand: LDS tile [128 rows][64 k] (128-byte rows, 16-byte
 //    chunks XOR-swizzled by swz(row)); MFMA fragments by ds_read_b128.
 //  * M/N-contiguous operand: LDS tile [64 k][128 m|n] as stored in memory
-//    (256-byte rows, chunk swizzle (k & 3) << 2); MFMA fragments by
+//    (256-byte rows, chunk swizzle mcswz(k)); MFMA fragments by
 //    ds_read_b64_tr_b16, which hands lane l of each 16-lane group element l%4
 //    of the 8-byte chunk addressed by lane 4j + l/4 (j = 0..3): with lane
 //    4j + q pointing at (k0 + j, n0 + 4q), lane l receives column n0 + l for
@@ -702,10 +702,33 @@ MOE_DEV void dma16_global(const void* src, lds_void_t* dst) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
                :: "s"(m), "v"(src) : "memory", "m0");
 }
+// The descriptor operand must sit in SGPRs: a descriptor kept across a
+// loop of tiles can end up in VGPRs (as the compiler sees fit for a value it
+// knows is uniform), which the assembler rejects, so each dword goes through
+// readfirstlane here (a plain move when it already is scalar).
+MOE_DEV rsrc_t sgpr_rsrc(rsrc_t r) {
+  rsrc_t o;
+  o.x = __builtin_amdgcn_readfirstlane(r.x);
+  o.y = __builtin_amdgcn_readfirstlane(r.y);
+  o.z = __builtin_amdgcn_readfirstlane(r.z);
+  o.w = __builtin_amdgcn_readfirstlane(r.w);
+  return o;
+}
 MOE_DEV void dma16_buffer(rsrc_t rs, lds_void_t* dst, uint32_t voff) {
   const uint32_t m = (uint32_t)(uintptr_t)dst;
+  rs = sgpr_rsrc(rs);
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :: "s"(m), "v"(voff), "s"(rs) : "memory", "m0");
+}
+// as dma16_buffer, with a wave-uniform byte offset in soffset (added to the
+// address; the layouts here keep it inside one row of the range, so the
+// row-validity of the range check is decided by voff either way)
+MOE_DEV void dma16_buffer_so(rsrc_t rs, lds_void_t* dst, uint32_t voff, uint32_t soff) {
+  const uint32_t m = (uint32_t)(uintptr_t)dst;
+  rs = sgpr_rsrc(rs);
+  soff = __builtin_amdgcn_readfirstlane(soff);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(m), "v"(voff), "s"(rs), "s"(soff) : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
@@ -716,6 +739,26 @@ MOE_DEV void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// Wave-uniform read of a group offset through the constant address space,
+// so it compiles to a scalar load (waited for on lgkmcnt): a vector load
+// would be waited for on vmcnt, and with LDS-DMA in flight that wait would
+// also wait for every DMA issued before it.  The offsets are written by an
+// earlier kernel and only read here.
+MOE_DEV int group_offset(const int32_t* offsets, int g) {
+  typedef const __attribute__((address_space(4))) int32_t* cptr_t;
+  return ((cptr_t)offsets)[g];
+}
+
+// Workgroup barrier for LDS hand-overs without a memory fence: this wave's
+// LDS reads and writes are complete (lgkmcnt 0), then s_barrier.  The fence
+// of __syncthreads() would also wait for every global store in flight (on
+// CDNA one counter covers vector loads and stores), which a pipeline that
+// stores one tile while loading the next must not do.  The "memory" clobber
+// keeps the compiler from moving memory accesses across it.
+MOE_DEV void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // per-lane source of one DMA instruction (u = 0..3) of this wave
 // KC tile: chunk P = 64*t + lane, row = P/8, logical chunk = (P%8) ^ swz(row)
 MOE_DEV void kc_slot(int t, int lane, int& row, int& lc) {
@@ -723,11 +766,17 @@ MOE_DEV void kc_slot(int t, int lane, int& row, int& lc) {
   row = P >> 3;
   lc = (P & 7) ^ swz(row);
 }
-// MC tile: chunk P = 64*t + lane, k row = P/16, logical chunk = (P%16) ^ ((k&3)<<2)
+// Chunk swizzle of the M/N-contiguous tiles: 16-byte chunk c of k-row k is
+// stored at c ^ mcswz(k).  A transposing fragment read has each 16-lane group
+// read 32 bytes from each of four consecutive k-rows (two such groups 32
+// bytes apart in the same rows per 32 lanes); rows one tile pitch apart fall
+// on the same banks, so the four rows are spread over the banks.
+MOE_DEV int mcswz(int k) { return (k & 3) << 2; }
+// MC tile: chunk P = 64*t + lane, k row = P/16, logical chunk = (P%16) ^ mcswz(k)
 MOE_DEV void mc_slot(int t, int lane, int& krow, int& lc) {
   const int P = 64 * t + lane;
   krow = P >> 4;
-  lc = (P & 15) ^ ((krow & 3) << 2);
+  lc = (P & 15) ^ mcswz(krow);
 }
 
 // fragment reads: 8 bf16 of one 32x32x16 MFMA operand for block rows rbase
@@ -748,7 +797,7 @@ MOE_DEV uint4 frag_mc(char* tile, int rbase, int ks, int lane, int pitch) {
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int krow = ks * 16 + (gi >> 1) * 8 + 4 * h + j;
-    char* p = tile + krow * pitch + ((lc ^ ((krow & 3) << 2)) << 4) + (half << 3);
+    char* p = tile + krow * pitch + ((lc ^ mcswz(krow)) << 4) + (half << 3);
     const v4s_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)(__attribute__((address_space(3))) char*)p);
     w[2 * h] = (uint32_t)(uint16_t)v[0] | ((uint32_t)(uint16_t)v[1] << 16);
     w[2 * h + 1] = (uint32_t)(uint16_t)v[2] | ((uint32_t)(uint16_t)v[3] << 16);
@@ -870,7 +919,7 @@ void grouped_gemm_dma_kernel(GemmParams P) {
       a_off[u] = (uint32_t)(((int64_t)r * P.lda + 8 * lc) * 2);
     } else {
       constexpr int CPR = BMT / 8;  // chunks per k-row
-      const int kr = P_ / CPR, lc = (P_ % CPR) ^ ((kr & 3) << 2);
+      const int kr = P_ / CPR, lc = (P_ % CPR) ^ mcswz(kr);
       a_off[u] = (uint32_t)(((int64_t)kr * P.lda + m0 + 8 * lc) * 2);
     }
   }
@@ -890,7 +939,7 @@ void grouped_gemm_dma_kernel(GemmParams P) {
         const int r = P_ >> 3, lc = (P_ & 7) ^ swz(r);
         b_ptr[u] = Bw0 + (int64_t)(n0 + r) * P.ldb + 8 * lc;  // + k0 per slab
       } else {
-        const int kr = P_ >> 4, lc = (P_ & 15) ^ ((kr & 3) << 2);
+        const int kr = P_ >> 4, lc = (P_ & 15) ^ mcswz(kr);
         if constexpr (BSPL == BS_N) {
           const int col0 = n0 / 2;
           b_ptr[u] = (lc < 8) ? Bw0 + (int64_t)kr * P.ldb + col0 + 8 * lc
@@ -906,7 +955,7 @@ void grouped_gemm_dma_kernel(GemmParams P) {
 #pragma unroll
     for (int u = 0; u < B_PER_WAVE; ++u) {
       const int P_ = 64 * (wave * B_PER_WAVE + u) + lane;
-      const int kr = P_ >> 4, lc = (P_ & 15) ^ ((kr & 3) << 2);
+      const int kr = P_ >> 4, lc = (P_ & 15) ^ mcswz(kr);
       b_off[u] = (uint32_t)(((int64_t)kr * P.ldb + n0 + 8 * lc) * 2);
     }
   }
@@ -1149,7 +1198,7 @@ __global__ __launch_bounds__(NW * 64) void grouped_gemm_big_kernel(GemmParams P)
       const int r = P_ >> 3, lc = (P_ & 7) ^ swz(r);
       a_off[u] = (uint32_t)(((int64_t)r * P.lda + 8 * lc) * 2);
     } else {
-      const int kr = P_ / 32, lc = (P_ % 32) ^ ((kr & 3) << 2);
+      const int kr = P_ / 32, lc = (P_ % 32) ^ mcswz(kr);
       a_off[u] = (uint32_t)(((int64_t)kr * P.lda + m0 + 8 * lc) * 2);
     }
   }
@@ -1169,7 +1218,7 @@ __global__ __launch_bounds__(NW * 64) void grouped_gemm_big_kernel(GemmParams P)
         const int r = P_ >> 3, lc = (P_ & 7) ^ swz(r);
         b_ptr[u] = Bw0 + (int64_t)(n0 + r) * P.ldb + 8 * lc;
       } else {
-        const int kr = P_ / CPRB, lc = (P_ % CPRB) ^ ((kr & 3) << 2);
+        const int kr = P_ / CPRB, lc = (P_ % CPRB) ^ mcswz(kr);
         if constexpr (BSPL == BS_N) {
           const int col0 = n0 / 2;
           b_ptr[u] = (lc < CPRB / 2) ? Bw0 + (int64_t)kr * P.ldb + col0 + 8 * lc
@@ -1185,7 +1234,7 @@ __global__ __launch_bounds__(NW * 64) void grouped_gemm_big_kernel(GemmParams P)
 #pragma unroll
     for (int u = 0; u < B_PER_WAVE; ++u) {
       const int P_ = 64 * (wave * B_PER_WAVE + u) + lane;
-      const int kr = P_ / CPRB, lc = (P_ % CPRB) ^ ((kr & 3) << 2);
+      const int kr = P_ / CPRB, lc = (P_ % CPRB) ^ mcswz(kr);
       b_off[u] = (uint32_t)(((int64_t)kr * P.ldb + n0 + 8 * lc) * 2);
     }
   }
@@ -1516,11 +1565,15 @@ __global__ __launch_bounds__(512) void grouped_gemm_persist_kernel(GemmParams P)
   constexpr int CPRB = BN / 8;
   constexpr int EREG = 4096;  // epilogue staging bytes per wave
   static_assert(WTN == 64, "epilogue staging sized for 64-column wave tiles");
-  __shared__ __attribute__((aligned(1024))) char sA0[ATILE];
-  __shared__ __attribute__((aligned(1024))) char sB0[BTILE];
-  __shared__ __attribute__((aligned(1024))) char sA1[ATILE];
-  __shared__ __attribute__((aligned(1024))) char sB1[BTILE];
-  __shared__ __attribute__((aligned(1024))) char sE[NW * EREG];
+  // one LDS object: the two A stages side by side, then the two B stages, so
+  // a stage-1 fragment address is the stage-0 one plus an offset that fits
+  // the ds_read immediate (no second address register per fragment)
+  __shared__ __attribute__((aligned(1024))) char smem[2 * ATILE + 2 * BTILE + NW * EREG];
+  char* const sA0 = smem;
+  char* const sA1 = smem + ATILE;
+  char* const sB0 = smem + 2 * ATILE;
+  char* const sB1 = smem + 2 * ATILE + BTILE;
+  char* const sE = smem + 2 * ATILE + 2 * BTILE;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int wm = wave / S::WNW, wn = wave % S::WNW;
@@ -1554,11 +1607,11 @@ __global__ __launch_bounds__(512) void grouped_gemm_persist_kernel(GemmParams P)
       const int r = P_ >> 3, lc = (P_ & 7) ^ swz(r);
       a_lane[u] = (uint32_t)(((int64_t)r * P.lda + 8 * lc) * 2);
     } else {
-      const int kr = P_ / 32, lc = (P_ % 32) ^ ((kr & 3) << 2);
+      const int kr = P_ / 32, lc = (P_ % 32) ^ mcswz(kr);
       a_lane[u] = (uint32_t)(((int64_t)kr * P.lda + 8 * lc) * 2);
     }
   }
-  int64_t b_lane[B_PER_WAVE];  // elements (GROUP_M) or bytes (GROUP_K)
+  int32_t b_lane[B_PER_WAVE];  // elements (GROUP_M) or bytes (GROUP_K)
   bool b_hi[B_PER_WAVE];       // BS_N: chunk from the second (up) matrix
 #pragma unroll
   for (int u = 0; u < B_PER_WAVE; ++u) {
@@ -1567,19 +1620,19 @@ __global__ __launch_bounds__(512) void grouped_gemm_persist_kernel(GemmParams P)
     if constexpr (GROUPING == GROUP_M) {
       if constexpr (BMODE == KC) {
         const int r = P_ >> 3, lc = (P_ & 7) ^ swz(r);
-        b_lane[u] = (int64_t)r * P.ldb + 8 * lc;
+        b_lane[u] = r * P.ldb + 8 * lc;
       } else {
-        const int kr = P_ / CPRB, lc = (P_ % CPRB) ^ ((kr & 3) << 2);
+        const int kr = P_ / CPRB, lc = (P_ % CPRB) ^ mcswz(kr);
         if constexpr (BSPL == BS_N) {
           b_hi[u] = lc >= CPRB / 2;
-          b_lane[u] = (int64_t)kr * P.ldb + 8 * (lc % (CPRB / 2));
+          b_lane[u] = kr * P.ldb + 8 * (lc % (CPRB / 2));
         } else {
-          b_lane[u] = (int64_t)kr * P.ldb + 8 * lc;
+          b_lane[u] = kr * P.ldb + 8 * lc;
         }
       }
     } else {
-      const int kr = P_ / CPRB, lc = (P_ % CPRB) ^ ((kr & 3) << 2);
-      b_lane[u] = ((int64_t)kr * P.ldb + 8 * lc) * 2;
+      const int kr = P_ / CPRB, lc = (P_ % CPRB) ^ mcswz(kr);
+      b_lane[u] = (kr * P.ldb + 8 * lc) * 2;
     }
   }
 
@@ -1603,7 +1656,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_persist_kernel(GemmParams P)
       find_group(P.offsets, P.G, mt, g, mtl, BM);
       t.g = __builtin_amdgcn_readfirstlane(g);
       mtl = __builtin_amdgcn_readfirstlane(mtl);
-      nrows_g = P.offsets[t.g + 1] - P.offsets[t.g];
+      nrows_g = group_offset(P.offsets, t.g + 1) - group_offset(P.offsets, t.g);
       t.m0 = mtl * BM;
       t.n0 = nt * BN;
       t.rows_valid = min(BM, nrows_g - t.m0);
@@ -1617,9 +1670,9 @@ __global__ __launch_bounds__(512) void grouped_gemm_persist_kernel(GemmParams P)
       t.m0 = mt * BM;
       t.n0 = nt * BN;
       t.rows_valid = BM;
-      kdim = P.offsets[t.g + 1] - P.offsets[t.g];
+      kdim = group_offset(P.offsets, t.g + 1) - group_offset(P.offsets, t.g);
     }
-    t.arow0 = P.offsets[t.g];
+    t.arow0 = group_offset(P.offsets, t.g);
     t.kdim = kdim;
     t.nk = max(2, (kdim + BK - 1) / BK);
     t.nk += t.nk & 1;  // even: the next tile's slab 0 always lands in stage 0
@@ -1638,13 +1691,31 @@ __global__ __launch_bounds__(512) void grouped_gemm_persist_kernel(GemmParams P)
   // real k-slabs of a tile (for GROUP_M: Kdim / BK; GROUP_K: the group rows)
   auto real_slabs = [&](const Tile& t) __attribute__((always_inline)) {
     if constexpr (GROUPING == GROUP_M) return (P.Kdim + BK - 1) / BK;
-    else return (P.offsets[t.g + 1] - P.offsets[t.g] + BK - 1) / BK;
+    else return (t.kdim + BK - 1) / BK;
   };
 
   // DMA of slab s of tile t into (la, lb); slabs past the real ones read
   // zeros for A (offset past the buffer range; GROUP_K: B too) and, for
   // GROUP_M, re-read the tile's last weight slab (times a zero A: nothing)
   auto issue = [&](const Tile& t, int nreal, int s, char* la, char* lb) __attribute__((always_inline)) {
+    if constexpr (GROUPING == GROUP_K) {
+      // both operands k-major: descriptors based at the slab's first row, the
+      // tile's column offset in soffset, the per-lane offsets fixed for the
+      // kernel; a slab past the group's rows, and every slab of the padding
+      // tile, gets an empty range and reads zeros
+      const int rows = t.real ? t.kdim : 0;
+      const rsrc_t a_rs = rows_rsrc(t.a_base, s * BK, rows, P.lda, P.a_cap);
+      const rsrc_t b_rs = rows_rsrc(t.b_base, s * BK, rows, P.ldb, P.b_cap);
+      const uint32_t a_so = __builtin_amdgcn_readfirstlane(t.m0 * 2);
+      const uint32_t b_so = __builtin_amdgcn_readfirstlane(t.n0 * 2);
+#pragma unroll
+      for (int u = 0; u < A_PER_WAVE; ++u)
+        dma16_buffer_so(a_rs, to_lds(la + (wave * A_PER_WAVE + u) * 1024), a_lane[u], a_so);
+#pragma unroll
+      for (int u = 0; u < B_PER_WAVE; ++u)
+        dma16_buffer_so(b_rs, to_lds(lb + (wave * B_PER_WAVE + u) * 1024), (uint32_t)b_lane[u], b_so);
+      return;
+    }
     const bool pad = !t.real || s >= nreal;
     const int k0 = (GROUPING == GROUP_M && pad) ? max(nreal - 1, 0) * BK : s * BK;
     // row-major A: tile-based descriptor plus the k offset; k-major A: a
@@ -1726,22 +1797,28 @@ __global__ __launch_bounds__(512) void grouped_gemm_persist_kernel(GemmParams P)
             acc[i][j], 0, 0, 0);
   };
   constexpr int PER_SLAB = A_PER_WAVE + B_PER_WAVE;
+  // vector-memory instructions each wave issues in a tile's epilogue (a
+  // lower bound): the weight gradients store every row of the tile, four
+  // 16-byte chunks per lane and 32-row block; the row GEMMs skip rows past
+  // the group's end, so nothing is counted for them
+  constexpr int EPI_VM = (GROUPING == GROUP_K && EPI == EPI_STORE) ? NI * 4 : 0;
 
   int64_t j = blockIdx.x;
   Tile cur = decode(j, true);
   int cur_real = real_slabs(cur);
-  Tile nxt = (j + nwg < n_tiles) ? decode(j + nwg, true) : decode(j, false);
-  int nxt_real = real_slabs(nxt);
+  Tile nxt;
+  int nxt_real = 0;
   issue(cur, cur_real, 0, sA0, sB0);
   issue(cur, cur_real, 1, sA1, sB1);
   wait_vmcnt<PER_SLAB>();
-  __syncthreads();
+  lds_barrier();
   frags(sA0, sB0, 0, 0);
   zero_acc();
+  bool after_epi = false;  // this tile follows an epilogue of the workgroup
 
-  // one pipeline step (see grouped_gemm_big_kernel); the DMA two slabs ahead
-  // belongs to the next tile once the current one runs out
-  auto step = [&](int kt, char* la, char* lb, char* na, char* nb) __attribute__((always_inline)) {
+  // k-steps 1..3 of the slab in (la, lb), the fragments one k-step ahead of
+  // the MFMAs (see grouped_gemm_big_kernel)
+  auto body = [&](char* la, char* lb) __attribute__((always_inline)) {
     frags(la, lb, 1, 1);
     __builtin_amdgcn_sched_barrier(0);
     mfmas(0);
@@ -1751,8 +1828,17 @@ __global__ __launch_bounds__(512) void grouped_gemm_persist_kernel(GemmParams P)
     frags(la, lb, 3, 1);
     __builtin_amdgcn_sched_barrier(0);
     mfmas(0);
-    wait_vmcnt<0>();
-    __syncthreads();
+  };
+  // hand-over from slab kt (in la, lb) to slab kt + 1 (in na, nb): wait for
+  // slab kt + 1 -- at the first hand-over after an epilogue, the epilogue's
+  // stores were issued after it and may stay in flight -- then barrier, DMA
+  // slab kt + 2 (the next tile's slab 0 once the current one runs out) into
+  // the stage just released, first fragments of slab kt + 1
+  auto hand = [&](int kt, bool first, char* la, char* lb, char* na, char* nb)
+                  __attribute__((always_inline)) {
+    if (first) wait_vmcnt<EPI_VM>();
+    else wait_vmcnt<0>();
+    lds_barrier();
     if (kt + 2 < cur.nk) issue(cur, cur_real, kt + 2, la, lb);
     else issue(nxt, nxt_real, kt + 2 - cur.nk, la, lb);
     frags(na, nb, 0, 0);
@@ -1774,16 +1860,34 @@ __global__ __launch_bounds__(512) void grouped_gemm_persist_kernel(GemmParams P)
   };
 
   for (;;) {
-    for (int kt = 0; kt < cur.nk; kt += 2) {
-      step(kt, sA0, sB0, sA1, sB1);
-      step(kt + 1, sA1, sB1, sA0, sB0);
+    // slab pairs of cur (nk is even); the last pair is peeled
+    int kt = 0;
+    for (; kt + 2 < cur.nk; kt += 2) {
+      body(sA0, sB0);
+      hand(kt, after_epi && kt == 0, sA0, sB0, sA1, sB1);
+      body(sA1, sB1);
+      hand(kt + 1, false, sA1, sB1, sA0, sB0);
     }
-    // ---- epilogue of cur (its own LDS region; the next tile's first slabs
+    // last pair: the next tile (or, past the list, a padding tile that
+    // reads zeros) is decoded; its slab 0 goes into stage 0 at the first
+    // hand-over, its slab 1 into stage 1 as soon as every wave has read the
+    // last slab -- no wait for it: the epilogue comes first
+    const bool more = j + nwg < n_tiles;
+    nxt = more ? decode(j + nwg, true) : decode(j, false);
+    nxt_real = real_slabs(nxt);
+    body(sA0, sB0);
+    hand(kt, after_epi && kt == 0, sA0, sB0, sA1, sB1);
+    body(sA1, sB1);
+    lds_barrier();
+    issue(nxt, nxt_real, 1, sA1, sB1);
+    mfmas(1);
+  // ---- epilogue of cur (its own LDS region; the next tile's first slabs
     // are landing meanwhile)
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int row_t0 = wm * WTM + i * 32;
-      if (row_t0 >= cur.rows_valid) break;
+      // (a weight-gradient tile stores all its rows: its stores are counted)
+      if (GROUPING == GROUP_M && row_t0 >= cur.rows_valid) break;
       const int64_t grow0 = cur.arow0 + cur.m0 + row_t0;
       if constexpr (EPI == EPI_SWIGLU_FWD) {
         constexpr int W = WTN / 2;  // 32 f columns
@@ -1902,7 +2006,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_persist_kernel(GemmParams P)
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
           const int row = it * 8 + (lane >> 3);
-          if (row_t0 + row >= cur.rows_valid) continue;
+          if (GROUPING == GROUP_M && row_t0 + row >= cur.rows_valid) continue;
           const uint4 v = get16(reg, WTN, row, ch);
           if constexpr (GROUPING == GROUP_M) {
             *reinterpret_cast<uint4*>(reinterpret_cast<T*>(P.C0) + (grow0 + row) * P.ldc + col) = v;
@@ -1917,13 +2021,17 @@ __global__ __launch_bounds__(512) void grouped_gemm_persist_kernel(GemmParams P)
         }
       }
     }
-    zero_acc();
-    if (!nxt.real) break;
+    if (!more) break;
     j += nwg;
     cur = nxt;
     cur_real = nxt_real;
-    nxt = (j + nwg < n_tiles) ? decode(j + nwg, true) : decode(j, false);
-    nxt_real = real_slabs(nxt);
+    // the next tile's slab 0 has landed once at most its slab 1 and the
+    // epilogue's stores (issued after it) are outstanding
+    wait_vmcnt<PER_SLAB + EPI_VM>();
+    lds_barrier();
+    frags(sA0, sB0, 0, 0);
+    zero_acc();
+    after_epi = true;
   }
   // the run-ahead DMA (padding) must land before the LDS is released
   wait_vmcnt<0>();
