@@ -69,160 +69,247 @@ struct FusedSelect {
 // implementation.
 // ---------------------------------------------------------------------------
 
-// Skinny router (E <= 16): each wave takes two tokens at a time, lanes stride
-// over D in 16-byte vectors (coalesced), four vectors per lane in flight at
-// once; fp64 partials are reduced across the wave.  W_r (E*D fp32, at most
-// 128 KB) is read straight from the caches when small (STAGE false) or staged
-// in LDS once per workgroup.
-template <typename T, int EM, bool STAGE>
-__global__ __launch_bounds__(256) void router_skinny_kernel(const T* __restrict__ x,
-                                                            const float* __restrict__ wr,
-                                                            const float* __restrict__ rb,
-                                                            float* __restrict__ logits, int T_,
-                                                            int D, int E, FusedSelect fs) {
-  extern __shared__ float4 sw4[];
-  const float* wsrc = wr;
-  if constexpr (STAGE) {
-    // staging in batches of eight 16-byte loads per thread, all in flight
-    // before the first LDS store (whole batches unconditional, so that the
-    // compiler does not sink each load into a guarded store); then the tail
-    const float4* w4 = reinterpret_cast<const float4*>(wr);
-    const int n4 = (E * D) >> 2, tid = (int)threadIdx.x;
-    int i0 = 0;
-    for (; i0 + 256 * 8 <= n4; i0 += 256 * 8) {
-      float4 v[8];
+// Few-expert router (E <= 16).  LPT lanes per token (8, or 16 for short
+// batches): lane p of a token reads 16-byte vectors p, p + LPT, ... of each
+// slab of the token's row (LPT lanes read 16 LPT contiguous bytes of a row
+// per load instruction), so a lane's fp64 partial sums need only a
+// reduction over its LPT lanes (DPP steps, no LDS traffic) instead of one
+// over the whole wave.  Each lane works on TPL tokens (the same columns of
+// TPL rows).  W_r goes through LDS in slabs of kFewSlab columns, widened to
+// double once when staged and zero past E and D, so the products run over
+// whole slabs and all EM experts without a branch (a branch per expert kept
+// the compiler from issuing the next expert's LDS reads early: 81 -> 69 us
+// on the Mixtral-like layer without it); double-buffered, one barrier per
+// slab.  W_r is read from L2 once per workgroup, any D works, and the
+// stripes of a wave read distinct 16-byte LDS words per instruction
+// (few_swz spreads them over the banks).  The x vectors of slab s + 1 and
+// the W_r values of slab s + 2 are loaded while slab s is multiplied, into
+// registers that alternate between even and odd slabs, so no slab waits for
+// a load it issued itself (with register copies at the end of each slab,
+// every slab waited for them).  Workgroups start at different slabs.  Lane
+// 0 of each token takes the top-K when fs.idx is set.
+constexpr int kFewSlab = 256;  // columns per W_r slab
+
+// sum over the eight lanes of a token (lanes 8j .. 8j + 7): pairs, quads,
+// then the two quads of the half-row; every lane ends with the same bits
+template <int CTRL>
+MOE_DEV double dpp_d(double v) {
+  const int2 u = __builtin_bit_cast(int2, v);
+  int2 r;
+  r.x = __builtin_amdgcn_update_dpp(0, u.x, CTRL, 0xF, 0xF, false);
+  r.y = __builtin_amdgcn_update_dpp(0, u.y, CTRL, 0xF, 0xF, false);
+  return __builtin_bit_cast(double, r);
+}
+template <int LPT>
+MOE_DEV double sum_lanes(double v) {
+  v += dpp_d<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_d<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_d<0x141>(v);  // row_half_mirror
+  if constexpr (LPT == 16) v += dpp_d<0x140>(v);  // row_mirror
+  return v;
+}
+// LDS slot of double pair L of a staged slab: the stripes read pairs 4 apart
+// (bf16 rows), so stripes p, p + 4, p + 8, p + 12 would share banks;
+// permuting the four pairs of a stripe by (L >> 4) & 3 separates them
+MOE_DEV int few_swz(int L) { return L ^ ((L >> 4) & 3); }
+
+// logits, then (fs.idx set, lane 0 of the token) top-K, weights and lse of
+// token t from its fp64 sums
+template <int EM, int LPT>
+MOE_DEV void few_finish(const double* acc, int t, int p, int E, const float* __restrict__ rb,
+                        float* __restrict__ logits, const FusedSelect& fs) {
+  // logits: lane p stores experts p, p + LPT, ...
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = w4[i0 + u * 256 + tid];
+  for (int h = 0; h < EM; h += LPT) {
+    const int e = h + p;
+    if (e < E) {
+      double a = 0.0;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) sw4[i0 + u * 256 + tid] = v[u];
+      for (int f = 0; f < EM; ++f)
+        if (f == e) a = acc[f];
+      logits[(size_t)t * E + e] = (float)(a + (rb ? (double)rb[e] : 0.0));
     }
-    for (int i = i0 + tid; i < n4; i += 256) sw4[i] = w4[i];
-    __syncthreads();
-    wsrc = reinterpret_cast<const float*>(sw4);
   }
-  constexpr int VEC = Elem<T>::VEC, NV = 4;
-  const int lane = threadIdx.x & 63;
-  const int wave = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  const int nwave = gridDim.x * (blockDim.x >> 6);
-  for (int t0 = wave * 2; t0 < T_; t0 += nwave * 2) {
-    const bool two = (t0 + 1) < T_;
-    double acc0[EM], acc1[EM];
+  if (!fs.idx || p != 0) return;
+  float sv[EM], key[EM];
+  bool used[EM];
+  float m = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < EM; ++e) { acc0[e] = 0.0; acc1[e] = 0.0; }
-    // every load is issued (past-the-end lanes re-read column 0, a lone
-    // last token re-reads itself; both are discarded below), so that no
-    // branch makes the compiler wait for one load before issuing the next
-    const T* xa_row = x + (size_t)t0 * D;
-    const T* xb_row = x + (size_t)(two ? t0 + 1 : t0) * D;
-    for (int dc = 0; dc < D; dc += 64 * VEC * NV) {
-      Vec16<T> va[NV], vb[NV];
+  for (int e = 0; e < EM; ++e) {
+    const bool ok = e < E;
+    sv[e] = ok ? (float)(acc[e] + (rb ? (double)rb[e] : 0.0)) : -INFINITY;
+    key[e] = fs.score == 0 ? sv[e]
+                           : (ok ? sig32(sv[e]) + (fs.selb ? fs.selb[e] : 0.0f) : -INFINITY);
+    used[e] = !ok;
+    m = fmaxf(m, sv[e]);
+  }
+  float z = 0.f;
 #pragma unroll
-      for (int v = 0; v < NV; ++v) {
-        const int d0 = dc + (v * 64 + lane) * VEC;
-        const int dl = d0 < D ? d0 : 0;
-        va[v].load(xa_row + dl);
-        vb[v].load(xb_row + dl);
+  for (int e = 0; e < EM; ++e)
+    if (e < E) z += expf(sv[e] - m);
+  if (fs.lse) fs.lse[t] = m + logf(z);
+  // K <= E <= EM rounds; the weights stay in registers until the normaliser
+  // is known
+  float gsum = 0.f, gk[EM];
+  int ik[EM];
+#pragma unroll
+  for (int k = 0; k < EM; ++k) {
+    gk[k] = 0.f;
+    ik[k] = 0;
+    if (k >= fs.K) continue;
+    float bk = -INFINITY, sc = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int e = 0; e < EM; ++e)
+      if (!used[e] && better(key[e], e, bk, bi)) { bk = key[e]; bi = e; sc = sv[e]; }
+    bi = bi < E ? bi : 0;  // only reachable with non-finite logits (outside the contract)
+#pragma unroll
+    for (int e = 0; e < EM; ++e)
+      if (e == bi) used[e] = true;
+    const float g = fs.score == 0 ? expf(sc - m) : 1.0f / (1.0f + expf(-sc));
+    gsum += g;
+    gk[k] = g;
+    ik[k] = bi;
+  }
+  float den = 1.f;
+  if (fs.score == 0) den = (fs.gating == 0) ? z : gsum;
+  else den = (fs.gating == 0) ? 1.f : gsum;
+  const bool raw = fs.score == 1 && fs.gating == 0;
+#pragma unroll
+  for (int k = 0; k < EM; ++k) {
+    if (k >= fs.K) break;
+    fs.idx[(size_t)t * fs.K + k] = ik[k];
+    fs.w[(size_t)t * fs.K + k] = raw ? gk[k] : gk[k] / den;
+  }
+}
+
+template <typename T, int EM, int TPL, int LPT>
+__global__ __launch_bounds__(256) void router_few_kernel(const T* __restrict__ x,
+                                                         const float* __restrict__ wr,
+                                                         const float* __restrict__ rb,
+                                                         float* __restrict__ logits, int T_,
+                                                         int D, int E, FusedSelect fs) {
+  constexpr int VEC = Elem<T>::VEC;            // elements per 16-byte vector
+  constexpr int NJ = kFewSlab / (LPT * VEC);   // vectors per lane and row per full slab
+  constexpr int TPW = 256 / LPT;               // tokens per workgroup and TPL step
+  constexpr int WQ = EM * kFewSlab / 4 / 256;  // float4 of a W_r slab per thread
+  constexpr int QR = kFewSlab / 4;             // float4 per expert row of a slab
+  __shared__ double2 sw[2][EM * kFewSlab / 2];  // [e][column pair], few_swz order
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int p = lane & (LPT - 1);
+  // token i of this lane: block base + TPW i + tid / LPT
+  const int t0 = blockIdx.x * (TPW * TPL) + tid / LPT;
+  const T* xrow[TPL];
+#pragma unroll
+  for (int i = 0; i < TPL; ++i) {
+    const int t = t0 + TPW * i;
+    // rows past the end re-read the last row (discarded): no load is guarded
+    xrow[i] = x + (size_t)(t < T_ ? t : T_ - 1) * D;
+  }
+  const int nslab = (D + kFewSlab - 1) / kFewSlab;
+  // workgroups start at different slabs (pass k covers slab (k + rot) mod
+  // nslab), so the column ranges read at one time differ across the chip
+  const int rot = blockIdx.x % nslab;
+  auto phys = [&](int k) __attribute__((always_inline)) {
+    const int q = k + rot;
+    return q >= nslab ? q - nslab : q;
+  };
+
+  // W_r slab s -> registers: float4 q of the slab is expert q / QR, columns
+  // 4 (q % QR) .. +3; experts past E and columns past D are zero (the load
+  // reads row 0 and is discarded), so the products run over all EM experts
+  // and whole slabs without a branch: a zero W_r times a finite x adds
+  // nothing, and the unused sums are never read
+  auto load_w = [&](int k, float4* wv) __attribute__((always_inline)) {
+    const int s = phys(k);
+#pragma unroll
+    for (int u = 0; u < WQ; ++u) {
+      const int q = u * 256 + tid, e = q / QR, c = s * kFewSlab + 4 * (q % QR);
+      const bool ok = e < E && c < D;
+      const float4 v = *reinterpret_cast<const float4*>(wr + (ok ? (size_t)e * D + c : 0));
+      wv[u] = ok ? v : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  auto store_w = [&](int buf, const float4* wv) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < WQ; ++u) {
+      const int q = u * 256 + tid;
+      sw[buf][few_swz(2 * q)] = make_double2((double)wv[u].x, (double)wv[u].y);
+      sw[buf][few_swz(2 * q + 1)] = make_double2((double)wv[u].z, (double)wv[u].w);
+    }
+  };
+  // x vectors of slab s (columns past D re-read column 0: their W_r is zero)
+  auto load_x = [&](int k, Vec16<T> (*xv)[NJ]) __attribute__((always_inline)) {
+    const int s = phys(k);
+#pragma unroll
+    for (int i = 0; i < TPL; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int c = s * kFewSlab + (j * LPT + p) * VEC;
+        xv[i][j].load(xrow[i] + (c < D ? c : 0));
       }
+  };
+
+  double acc[TPL][EM];
 #pragma unroll
-      for (int v = 0; v < NV; ++v) {
-        const int d0 = dc + (v * 64 + lane) * VEC;
-        if (d0 >= D) break;
-        float xa[VEC], xb[VEC];
-        va[v].to_f32(xa);
-        if (two) {
-          vb[v].to_f32(xb);
-        } else {
+  for (int i = 0; i < TPL; ++i)
 #pragma unroll
-          for (int i = 0; i < VEC; ++i) xb[i] = 0.f;
-        }
+    for (int e = 0; e < EM; ++e) acc[i][e] = 0.0;
+  // Register buffers alternate between even and odd slabs (the loop runs
+  // two slabs per pass), so no register copy waits for a load in flight.
+  float4 w0[WQ], w1[WQ];
+  Vec16<T> x0[TPL][NJ], x1[TPL][NJ];
+  load_w(0, w0);
+  load_x(0, x0);
+  if (nslab > 1) load_w(1, w1);
+  store_w(0, w0);
+  // slab s: its x vectors in xc (loaded one slab earlier), W_r slab s + 1 in
+  // wst (loaded two slabs earlier); x of slab s + 1 goes into xn and W_r of
+  // slab s + 2 into wld
+  auto slab = [&](int s, Vec16<T> (*xc)[NJ], Vec16<T> (*xn)[NJ], const float4* wst, float4* wld)
+                  __attribute__((always_inline)) {
+    // W_r slab s is in sw[s & 1]; every wave is done with slab s - 1
+    __syncthreads();
+    if (s + 1 < nslab) load_x(s + 1, xn);
+    if (s + 2 < nslab) load_w(s + 2, wld);
+    const double2* w2 = sw[s & 1];
 #pragma unroll
-        for (int e = 0; e < EM; ++e) {
-          if (e < E) {
-            const float* w = wsrc + e * D + d0;
+    for (int j = 0; j < NJ; ++j) {
+      double xd[TPL][VEC];
 #pragma unroll
-            for (int i = 0; i < VEC; ++i) {
-              acc0[e] = fma((double)xa[i], (double)w[i], acc0[e]);
-              acc1[e] = fma((double)xb[i], (double)w[i], acc1[e]);
-            }
+      for (int i = 0; i < TPL; ++i) {
+        float xf[VEC];
+        xc[i][j].to_f32(xf);
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) xd[i][v] = (double)xf[v];
+      }
+      const int c = (j * LPT + p) * VEC;  // column within the slab
+#pragma unroll
+      for (int e = 0; e < EM; ++e) {
+#pragma unroll
+        for (int h = 0; h < VEC / 2; ++h) {
+          const double2 w = w2[few_swz((e * kFewSlab + c) / 2 + h)];
+#pragma unroll
+          for (int i = 0; i < TPL; ++i) {
+            acc[i][e] = fma(xd[i][2 * h], w.x, acc[i][e]);
+            acc[i][e] = fma(xd[i][2 * h + 1], w.y, acc[i][e]);
           }
         }
       }
     }
+    // slab s + 1 into the slot of slab s - 1
+    if (s + 1 < nslab) store_w((s + 1) & 1, wst);
+  };
+  for (int s = 0; s < nslab; s += 2) {
+    slab(s, x0, x1, w1, w0);
+    if (s + 1 < nslab) slab(s + 1, x1, x0, w0, w1);
+  }
 #pragma unroll
-    for (int e = 0; e < EM; ++e) {
-      if (e < E) {
+  for (int i = 0; i < TPL; ++i) {
 #pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) {
-          acc0[e] += shfl_xor_d(acc0[e], m);
-          acc1[e] += shfl_xor_d(acc1[e], m);
-        }
-      }
-    }
-    if (lane < E) {
-      double a0 = 0.0, a1 = 0.0;
-#pragma unroll
-      for (int e = 0; e < EM; ++e)
-        if (e == lane) { a0 = acc0[e]; a1 = acc1[e]; }
-      const double b = rb ? (double)rb[lane] : 0.0;
-      logits[(size_t)t0 * E + lane] = (float)(a0 + b);
-      if (two) logits[(size_t)(t0 + 1) * E + lane] = (float)(a1 + b);
-    }
-    if (fs.idx && (lane == 0 || (lane == 1 && two))) {
-      // lane 0 selects for token t0, lane 1 for t0 + 1; every lane holds
-      // all E sums after the reduction
-      const int t = t0 + lane;
-      float sv[EM], key[EM];
-      bool used[EM];
-      float m = -INFINITY;
-#pragma unroll
-      for (int e = 0; e < EM; ++e) {
-        const bool ok = e < E;
-        const double a = lane == 0 ? acc0[e] : acc1[e];
-        sv[e] = ok ? (float)(a + (rb ? (double)rb[e] : 0.0)) : -INFINITY;
-        key[e] = fs.score == 0 ? sv[e]
-                               : (ok ? sig32(sv[e]) + (fs.selb ? fs.selb[e] : 0.0f) : -INFINITY);
-        used[e] = !ok;
-        m = fmaxf(m, sv[e]);
-      }
-      float z = 0.f;
-#pragma unroll
-      for (int e = 0; e < EM; ++e)
-        if (e < E) z += expf(sv[e] - m);
-      if (fs.lse) fs.lse[t] = m + logf(z);
-      // K <= E <= EM rounds; the weights stay in registers until the
-      // normaliser is known
-      float gsum = 0.f, gk[EM];
-      int ik[EM];
-#pragma unroll
-      for (int k = 0; k < EM; ++k) {
-        gk[k] = 0.f;
-        ik[k] = 0;
-        if (k >= fs.K) continue;
-        float bk = -INFINITY, sc = -INFINITY;
-        int bi = 0x7fffffff;
-#pragma unroll
-        for (int e = 0; e < EM; ++e)
-          if (!used[e] && better(key[e], e, bk, bi)) { bk = key[e]; bi = e; sc = sv[e]; }
-        bi = bi < E ? bi : 0;  // only reachable with non-finite logits (outside the contract)
-#pragma unroll
-        for (int e = 0; e < EM; ++e)
-          if (e == bi) used[e] = true;
-        const float g = fs.score == 0 ? expf(sc - m) : 1.0f / (1.0f + expf(-sc));
-        gsum += g;
-        gk[k] = g;
-        ik[k] = bi;
-      }
-      float den = 1.f;
-      if (fs.score == 0) den = (fs.gating == 0) ? z : gsum;
-      else den = (fs.gating == 0) ? 1.f : gsum;
-      const bool raw = fs.score == 1 && fs.gating == 0;
-#pragma unroll
-      for (int k = 0; k < EM; ++k) {
-        if (k >= fs.K) break;
-        fs.idx[(size_t)t * fs.K + k] = ik[k];
-        fs.w[(size_t)t * fs.K + k] = raw ? gk[k] : gk[k] / den;
-      }
-    }
+    for (int e = 0; e < EM; ++e) acc[i][e] = sum_lanes<LPT>(acc[i][e]);
+    const int t = t0 + TPW * i;
+    if (t < T_) few_finish<EM, LPT>(acc[i], t, p, E, rb, logits, fs);
   }
 }
 
@@ -522,51 +609,29 @@ static int router_logits_sel(const moe_config& c, const void* x, const float* wr
                              hipStream_t st) {
   const int T_ = c.T, D = c.D, E = c.E;
   {
-    if (E <= 16 && (size_t)E * D * 4 <= 128 * 1024) {
+    if (E <= 16) {
       const FusedSelect fs = fsp ? *fsp : FusedSelect{nullptr, nullptr, nullptr, nullptr, 0, 0, 0};
       const char* name = fsp ? "route_fused" : "router_logits";
-      // one token pair per wave, but no more workgroups than fit on the chip
-      // at once (a staged W_r is loaded once per workgroup: with large tiles
-      // the waves loop over several pairs).  W_r up to 32 KB is read through
-      // the caches instead (no staging pass).
-      const bool stage = (size_t)E * D * 4 > 32 * 1024;
-      const size_t shm = stage ? (size_t)E * D * 4 : 0;
-      const int waves_needed = (int)cdiv(T_, 2);
-      const int64_t per_cu = stage ? std::max<int64_t>(1, std::min<int64_t>(8, (160 * 1024) / (int64_t)shm)) : 8;
-      int grid = (int)std::min<int64_t>(cdiv(waves_needed, 4), 256 * per_cu);
-      if (shm > 64 * 1024) {
-        // W_r tiles above 64 KB need the kernels' dynamic-LDS limit raised:
-        // once per process (outside any stream capture that comes later)
-        static hipError_t lim = [] {
-          const void* fns[] = {(const void*)router_skinny_kernel<bf16_t, 4, true>,
-                               (const void*)router_skinny_kernel<bf16_t, 8, true>,
-                               (const void*)router_skinny_kernel<bf16_t, 16, true>,
-                               (const void*)router_skinny_kernel<float, 4, true>,
-                               (const void*)router_skinny_kernel<float, 8, true>,
-                               (const void*)router_skinny_kernel<float, 16, true>};
-          for (const void* f : fns) {
-            hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               128 * 1024);
-            if (e != hipSuccess) return e;
-          }
-          return hipSuccess;
-        }();
-        if (lim != hipSuccess) { set_error("router_logits (LDS limit)", lim); return MOE_ELAUNCH; }
-      }
-#define SKINNY(TV, EMV, SV)                                                                 \
-  MOE_LAUNCH(name, (router_skinny_kernel<TV, EMV, SV>), dim3(grid), dim3(256), shm, st,     \
-             (const TV*)x, wr, rb, logits, T_, D, E, fs)
-#define SKINNY_E(TV, SV)              \
-  if (E <= 4) SKINNY(TV, 4, SV);      \
-  else if (E <= 8) SKINNY(TV, 8, SV); \
-  else SKINNY(TV, 16, SV);
-      if (c.dtype == MOE_BF16) {
-        if (stage) { SKINNY_E(bf16_t, true) } else { SKINNY_E(bf16_t, false) }
-      } else {
-        if (stage) { SKINNY_E(float, true) } else { SKINNY_E(float, false) }
-      }
-#undef SKINNY_E
-#undef SKINNY
+      // One token per lane (two halved the workgroups and measured slower on
+      // the Mixtral-like layer and MiniMind); eight lanes per token, or
+      // sixteen (16 tokens per workgroup) when eight would leave fewer than
+      // two workgroups per CU: MiniMind 14.6 -> 11.1 us, while the
+      // Mixtral-like layer is faster with eight (72 against 86 us).
+      const bool wide = cdiv(T_, 32) < 512;
+#define FEW(TV, EMV, LPTV)                                                                  \
+  MOE_LAUNCH(name, (router_few_kernel<TV, EMV, 1, LPTV>), dim3((unsigned)cdiv(T_, 256 / LPTV)), \
+             dim3(256), 0, st, (const TV*)x, wr, rb, logits, T_, D, E, fs)
+#define FEW_L(TV, EMV)            \
+  if (wide) FEW(TV, EMV, 16);     \
+  else FEW(TV, EMV, 8);
+#define FEW_E(TV)                 \
+  if (E <= 4) { FEW_L(TV, 4) }    \
+  else if (E <= 8) { FEW_L(TV, 8) } \
+  else { FEW_L(TV, 16) }
+      if (c.dtype == MOE_BF16) { FEW_E(bf16_t) } else { FEW_E(float) }
+#undef FEW_E
+#undef FEW_L
+#undef FEW
     } else {
       if (fsp) return 1;
       // k-groups per workgroup: about 1024 four-wave groups on the chip
