@@ -107,8 +107,8 @@ int moe_capacity(const moe_config* cfg, int32_t* capacity);
  * n_shared*T (expert choice, C from moe_capacity).  Host-only. */
 int moe_rows_max(const moe_config* cfg, int64_t* rows);
 
-/* Bytes of device workspace needed by moe_permute, aux_balance_loss and
- * moe_backward for this configuration.  Host-only. */
+/* Bytes of device workspace needed by moe_permute, moe_route_permute,
+ * aux_balance_loss and moe_backward for this configuration.  Host-only. */
 int moe_workspace_size(const moe_config* cfg, size_t* bytes);
 
 /*
@@ -164,6 +164,28 @@ int moe_permute(const moe_config* cfg, const int32_t* topk_idx, const void* x,
                 int32_t* counts_all, int32_t* offsets, int32_t* slot_row, int32_t* row_token,
                 int32_t* row_slot, int32_t* n_dropped, void* x_perm, void* ws, size_t ws_bytes,
                 moe_stream_t stream);
+
+/*
+ * moe_route_permute -- moe_route (plain routing: no given logits, jitter or
+ * noise) followed by moe_permute, in fewer launches: with at most 16 experts
+ * and up to 32768 slots the router also ranks every slot among its
+ * workgroup's slots of the same expert, and one more kernel forms the
+ * offsets, assigns the rows and gathers the token rows (two launches where
+ * the separate calls take three); otherwise the two calls' kernels run in
+ * sequence.  [P3] Router/Gating Network, efficient inference (group
+ * the tokens by expert); [P5] 8.5 (capacity), 8.8.
+ *   Arguments and outputs: those of moe_route (flags 0) and moe_permute, with
+ *   the same layouts; every output is identical, bit for bit, to the two
+ *   separate calls.
+ *   ws: the workspace of moe_workspace_size (no initial contents needed).
+ * Errors: those of moe_route and moe_permute.
+ */
+int moe_route_permute(const moe_config* cfg, const void* x, const float* w_r,
+                      const float* r_bias, const float* sel_bias, float* logits,
+                      int32_t* topk_idx, float* topk_w, float* lse, int32_t* counts_all,
+                      int32_t* offsets, int32_t* slot_row, int32_t* row_token, int32_t* row_slot,
+                      int32_t* n_dropped, void* x_perm, void* ws, size_t ws_bytes,
+                      moe_stream_t stream);
 
 /*
  * moe_permute_noalloc -- moe_permute without a workspace argument, for

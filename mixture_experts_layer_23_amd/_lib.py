@@ -24,7 +24,8 @@ EXPORTS = ["moe_capacity", "moe_rows_max", "moe_workspace_size", "moe_route", "m
            "moe_expert_ffn", "moe_combine", "aux_balance_loss", "moe_backward",
            "moe_error_string", "moe_timing_enable", "moe_timing_report",
            "moe_timing_select", "moe_bias_update", "aux_seq_loss", "moe_route_ex",
-           "moe_backward_ex", "moe_route_expert_choice", "moe_permute_noalloc"]
+           "moe_backward_ex", "moe_route_expert_choice", "moe_permute_noalloc",
+           "moe_route_permute"]
 
 
 class MoeConfig(C.Structure):
@@ -74,6 +75,9 @@ def lib():
             "moe_backward_ex": [cfg] + [P] * 25 + [S, P],
             "aux_seq_loss": [cfg, P, P, I, C.c_float, P, P, I, P, S, P],
             "moe_route_expert_choice": [cfg] + [P] * 12 + [I, P, S, P],
+            # x, w_r, r_bias, sel_bias, logits, idx, w, lse, counts_all,
+            # offsets, slot_row, row_token, row_slot, n_dropped, x_perm, ws
+            "moe_route_permute": [cfg] + [P] * 16 + [S, P],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -147,6 +151,16 @@ def moe_permute(cfg, topk_idx, x, counts_all, offsets, slot_row, row_token, row_
                            ptr(x_perm), ptr(ws), ws.numel() * ws.element_size(),
                            stream_handle(stream))
     _check("moe_permute", rc)
+
+
+def moe_route_permute(cfg, x, w_r, r_bias, sel_bias, logits, topk_idx, topk_w, lse, counts_all,
+                      offsets, slot_row, row_token, row_slot, n_dropped, x_perm, ws, stream=None):
+    rc = lib().moe_route_permute(C.byref(cfg), ptr(x), ptr(w_r), ptr(r_bias), ptr(sel_bias),
+                                 ptr(logits), ptr(topk_idx), ptr(topk_w), ptr(lse),
+                                 ptr(counts_all), ptr(offsets), ptr(slot_row), ptr(row_token),
+                                 ptr(row_slot), ptr(n_dropped), ptr(x_perm), ptr(ws),
+                                 ws.numel() * ws.element_size(), stream_handle(stream))
+    _check("moe_route_permute", rc)
 
 
 def moe_permute_noalloc(cfg, topk_idx, x, counts_all, offsets, slot_row, row_token, row_slot,

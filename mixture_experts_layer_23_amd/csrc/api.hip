@@ -157,6 +157,11 @@ Workspace workspace_layout(const moe_config& c) {
   L.seq_blk_n = o;   o += al((size_t)std::max(c.T, 1) * c.E * 4);
   L.seq_blk_p = o;   o += al((size_t)std::max(c.T, 1) * c.E * 4);
   L.ec_keys = o;     o += ec ? al((size_t)(c.expert_hi - c.expert_lo) * std::max(c.T, 1) * 4) : 0;
+  {
+    const bool fold = !ec && c.E <= 16;
+    L.fold_counts = o; o += fold ? al((size_t)cdiv(std::max(c.T, 1), 16) * c.E * 4) : 0;
+    L.fold_rank = o;   o += fold ? al((size_t)std::max<int64_t>(TK, 1) * 4) : 0;
+  }
   L.total = o;
   return L;
 }
@@ -268,6 +273,27 @@ int moe_route(const moe_config* cfg, const void* x, const float* w_r, const floa
               int32_t flags, moe_stream_t stream) {
   return moe_route_ex(cfg, x, w_r, r_bias, sel_bias, nullptr, nullptr, nullptr, nullptr, logits,
                       topk_idx, topk_w, lse, flags, stream);
+}
+
+int moe_route_permute(const moe_config* cfg, const void* x, const float* w_r,
+                      const float* r_bias, const float* sel_bias, float* logits,
+                      int32_t* topk_idx, float* topk_w, float* lse, int32_t* counts_all,
+                      int32_t* offsets, int32_t* slot_row, int32_t* row_token, int32_t* row_slot,
+                      int32_t* n_dropped, void* x_perm, void* ws, size_t ws_bytes,
+                      moe_stream_t stream) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (cfg->routing != MOE_TOKEN_CHOICE) return MOE_EINVAL;
+  REQ(x); REQ(w_r); OPT(r_bias); OPT(sel_bias);
+  REQ(logits); REQ(topk_idx); REQ(topk_w); OPT(lse);
+  REQ(counts_all); REQ(offsets); REQ(slot_row); REQ(row_token); REQ(row_slot); REQ(n_dropped);
+  REQ(x_perm); REQ(ws);
+  const Workspace L = workspace_layout(*cfg);
+  if (ws_bytes < L.total) return MOE_EWORKSPACE;
+  if (cfg->T == 0) return MOE_OK;
+  return launch_route_permute(*cfg, x, w_r, r_bias, sel_bias, logits, topk_idx, topk_w, lse,
+                              capacity_of(*cfg), counts_all, offsets, slot_row, row_token,
+                              row_slot, n_dropped, x_perm, (char*)ws, L, (hipStream_t)stream);
 }
 
 int moe_route_expert_choice(const moe_config* cfg, const void* x, const float* w_r,

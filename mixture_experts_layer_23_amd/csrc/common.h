@@ -98,6 +98,19 @@ template <typename V> MOE_DEV V shfl_xor(V v, int m) { return __shfl_xor(v, m, 6
 
 MOE_DEV double shfl_xor_d(double v, int m) { return __shfl_xor(v, m, 64); }
 
+// lanes of the wave whose (valid) expert index equals this lane's, from one
+// ballot per index bit (nbits bits cover the expert indices); 0 for an
+// invalid lane
+MOE_DEV uint64_t same_expert_peers(bool valid, int e, int nbits) {
+  uint64_t peers = __ballot(valid);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t bb = __ballot(bit);
+    peers &= bit ? bb : ~bb;
+  }
+  return valid ? peers : 0ull;
+}
+
 // ---------------------------------------------------------------------------
 // host side: launch bookkeeping (errors, optional per-kernel timing)
 // ---------------------------------------------------------------------------

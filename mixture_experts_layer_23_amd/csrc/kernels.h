@@ -21,6 +21,7 @@ struct Workspace {
   size_t seq_part;                 // float [T] per-sequence balance-loss partials
   size_t seq_blk_n, seq_blk_p;     // int32 / float [T][E] per-token-block partials
   size_t ec_keys;                  // uint32 [EL][T] expert-choice selection keys
+  size_t fold_counts, fold_rank;   // int32 [ceil(T/16)][E], [T*K] (permute folded into the router)
   size_t total;
   int ntiles, aux_blocks, dwr_splits, rb_splits;
 };
@@ -58,6 +59,14 @@ int launch_route(const moe_config& c, const void* x, const float* wr, const floa
                  const float* selb, const float* jit, const float* wn, const float* eps,
                  float* nlg, float* logits, int32_t* idx, float* w, float* lse, bool logits_given,
                  hipStream_t st);
+
+// moe_route followed by moe_permute, with the permute's counting, scan and
+// row assignment folded into the few-expert router when it fits (route.hip)
+int launch_route_permute(const moe_config& c, const void* x, const float* wr, const float* rb,
+                         const float* selb, float* logits, int32_t* idx, float* w, float* lse,
+                         int capacity, int32_t* counts_all, int32_t* offsets, int32_t* slot_row,
+                         int32_t* row_token, int32_t* row_slot, int32_t* n_dropped,
+                         void* x_perm, char* ws, const Workspace& L, hipStream_t st);
 
 int launch_route_ec(const moe_config& c, const void* x, const float* wr, const float* rb,
                     float* logits, float* w, float* lse, int32_t* counts_all, int32_t* offsets,

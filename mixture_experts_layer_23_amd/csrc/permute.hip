@@ -188,16 +188,6 @@ constexpr int kSmallWaves = kSmallThreads / 64;
 constexpr int64_t kSmallSlots = 32768;  // up to 32 groups of 64 slots per wave
 constexpr int kSmallExperts = 256;      // LDS: (17 E + EL + 1) int32
 
-MOE_DEV uint64_t same_expert_peers(bool valid, int e, int nbits) {
-  uint64_t peers = __ballot(valid);
-  for (int b = 0; b < nbits; ++b) {
-    const bool bit = (e >> b) & 1;
-    const uint64_t bb = __ballot(bit);
-    peers &= bit ? bb : ~bb;
-  }
-  return valid ? peers : 0ull;
-}
-
 template <int R>  // groups of 64 slots per wave, held in registers (16 * 64 * R >= TK)
 __global__ __launch_bounds__(kSmallThreads) void permute_small_kernel(
     const int32_t* __restrict__ idx, int TK, int K, int E, int lo, int hi, int capacity,

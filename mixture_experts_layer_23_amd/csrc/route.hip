@@ -117,7 +117,7 @@ MOE_DEV int few_swz(int L) { return L ^ ((L >> 4) & 3); }
 // token t from its fp64 sums
 template <int EM, int LPT>
 MOE_DEV void few_finish(const double* acc, int t, int p, int E, const float* __restrict__ rb,
-                        float* __restrict__ logits, const FusedSelect& fs) {
+                        float* __restrict__ logits, const FusedSelect& fs, int32_t* s_pick) {
   // logits: lane p stores experts p, p + LPT, ...
 #pragma unroll
   for (int h = 0; h < EM; h += LPT) {
@@ -180,6 +180,152 @@ MOE_DEV void few_finish(const double* acc, int t, int p, int E, const float* __r
     if (k >= fs.K) break;
     fs.idx[(size_t)t * fs.K + k] = ik[k];
     fs.w[(size_t)t * fs.K + k] = raw ? gk[k] : gk[k] / den;
+    if (s_pick) s_pick[k] = ik[k];
+  }
+}
+
+// The permute of the same slots folded into the few-expert router (fewer
+// launches; [P3] efficient inference: group the tokens by expert; [P5] 8.5
+// capacity).  Every router workgroup ranks its own slots per expert in slot
+// order (ballots per 64-slot group, then the groups before it) and stores
+// its per-expert counts; scatter_slots_kernel, the next launch, adds the
+// counts of the router workgroups before a slot's own to its rank, forms
+// the capacity-limited group offsets from all counts, gives every slot its
+// row and moves its token's row of x.  The positions are the stable
+// in-expert ranks of moe_permute, so every output is identical.  (Letting
+// the router's last workgroup -- found by an atomic counter -- do the scan
+// put a device-scope fence in every workgroup and a serial tail on the
+// router: MiniMind 26 us against 17 us without it.)
+struct FusedPermute {
+  int32_t* wg_counts;   // [router workgroups][E] slots per expert
+  int32_t* local_rank;  // [T K] rank of a slot among its workgroup's slots of its expert
+  int K, nbits;
+};
+constexpr int kFoldWgs = 1024;  // router workgroups the folded permute takes
+
+// the router workgroup's slots: tokens blockIdx.x TPW ..., K each, their
+// experts in s_pick
+MOE_DEV void fold_permute(const FusedPermute& fp, const int32_t* s_pick, int TPW, int T_,
+                          int E) {
+  __shared__ int32_t gcnt[4][16];  // slots per expert of each 64-slot group
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, K = fp.K;
+  if (tid < 64) gcnt[tid >> 4][tid & 15] = 0;
+  __syncthreads();
+  const int tb = blockIdx.x * TPW;
+  const int nslots = min(TPW, T_ - tb) * K;  // <= 256
+  const bool v = tid < nslots;
+  const int e = v ? s_pick[tid] : 0;
+  const uint64_t peers = same_expert_peers(v, e, fp.nbits);
+  const uint64_t lt = lane ? (~0ull >> (64 - lane)) : 0ull;
+  if (v && (63 - __clzll(peers)) == lane) gcnt[wave][e] = __popcll(peers);
+  __syncthreads();
+  if (v) {
+    int r = __popcll(peers & lt);
+    for (int w = 0; w < wave; ++w) r += gcnt[w][e];
+    fp.local_rank[(size_t)tb * K + tid] = r;
+  }
+  if (tid < E) fp.wg_counts[(size_t)blockIdx.x * E + tid] =
+      gcnt[0][tid] + gcnt[1][tid] + gcnt[2][tid] + gcnt[3][tid];
+}
+
+// The rows of the folded permute.  A workgroup takes kScatterSlots
+// consecutive slots (all of one router workgroup g): it sums the counts of
+// the router workgroups before g (the slots' bases) and of all of them (the
+// totals, hence the group offsets) per expert, then every wave takes a slot
+// at a time: slot_row -2 for an expert outside [lo, hi), -1 past its
+// expert's capacity, else row = offset + base + rank, with the token's row
+// of x moved to x_perm.  Workgroup 0 also writes counts_all, offsets and
+// n_dropped.  tpw: tokens per router workgroup.
+constexpr int kScatterSlots = 16;
+template <typename T>
+__global__ __launch_bounds__(256) void scatter_slots_kernel(
+    const T* __restrict__ x, const int32_t* __restrict__ idx,
+    const int32_t* __restrict__ wg_counts, const int32_t* __restrict__ local_rank, int nwg,
+    int tpw, int TK, int K, int E, int lo, int hi, int capacity, int n_shared, int T_, int D,
+    int32_t* __restrict__ counts_all, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ n_dropped, int32_t* __restrict__ slot_row,
+    int32_t* __restrict__ row_token, int32_t* __restrict__ row_slot, T* __restrict__ x_perm) {
+  constexpr int VEC = Elem<T>::VEC;
+  __shared__ int32_t part[4][2][16];
+  __shared__ int32_t base[16], off[17];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int s0 = blockIdx.x * kScatterSlots;
+  const int g = (s0 / K) / tpw;
+  // per expert: counts of the router workgroups before g, and of all
+  int pre[16], tot[16];
+#pragma unroll
+  for (int x2 = 0; x2 < 16; ++x2) { pre[x2] = 0; tot[x2] = 0; }
+  for (int h = tid; h < nwg; h += 256) {
+#pragma unroll
+    for (int x2 = 0; x2 < 16; ++x2) {
+      if (x2 < E) {
+        const int c = wg_counts[(size_t)h * E + x2];
+        tot[x2] += c;
+        pre[x2] += h < g ? c : 0;
+      }
+    }
+  }
+#pragma unroll
+  for (int x2 = 0; x2 < 16; ++x2) {
+    if (x2 < E) {
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        pre[x2] += __shfl_xor(pre[x2], o, 64);
+        tot[x2] += __shfl_xor(tot[x2], o, 64);
+      }
+      if (lane == 0) { part[wave][0][x2] = pre[x2]; part[wave][1][x2] = tot[x2]; }
+    }
+  }
+  __syncthreads();
+  if (tid < E) base[tid] = part[0][0][tid] + part[1][0][tid] + part[2][0][tid] + part[3][0][tid];
+  if (tid == 0) {
+    const int EL = hi - lo;
+    int r = 0, drop = 0;
+    for (int x2 = 0; x2 < E; ++x2) {
+      const int n = part[0][1][x2] + part[1][1][x2] + part[2][1][x2] + part[3][1][x2];
+      if (blockIdx.x == 0) counts_all[x2] = n;
+      if (x2 >= lo && x2 < hi) {
+        const int k = (capacity >= 0 && n > capacity) ? capacity : n;
+        off[x2 - lo] = r;
+        r += k;
+        drop += n - k;
+      }
+    }
+    off[EL] = r;
+    if (blockIdx.x == 0) {
+      for (int x2 = 0; x2 <= EL; ++x2) offsets[x2] = off[x2];
+      for (int sh = 0; sh < n_shared; ++sh) offsets[EL + 1 + sh] = r + (sh + 1) * T_;
+      *n_dropped = drop;
+    }
+  }
+  __syncthreads();
+  for (int i = wave; i < kScatterSlots; i += 4) {
+    const int s = s0 + i;
+    if (s >= TK) break;
+    const int e = idx[s];
+    const int tok = s / K;
+    const int pos = base[e] + local_rank[s];
+    int row = -1;
+    if (e < lo || e >= hi) {
+      if (lane == 0) slot_row[s] = -2;
+    } else if (capacity >= 0 && pos >= capacity) {
+      if (lane == 0) slot_row[s] = -1;
+    } else {
+      row = off[e - lo] + pos;
+      if (lane == 0) {
+        slot_row[s] = row;
+        row_token[row] = tok;
+        row_slot[row] = s;
+      }
+    }
+    if (row < 0) continue;
+    const T* src = x + (size_t)tok * D;
+    T* dst = x_perm + (size_t)row * D;
+    for (int d0 = lane * VEC; d0 < D; d0 += 64 * VEC) {
+      Vec16<T> v;
+      v.load(src + d0);
+      v.store(dst + d0);
+    }
   }
 }
 
@@ -188,13 +334,16 @@ __global__ __launch_bounds__(256) void router_few_kernel(const T* __restrict__ x
                                                          const float* __restrict__ wr,
                                                          const float* __restrict__ rb,
                                                          float* __restrict__ logits, int T_,
-                                                         int D, int E, FusedSelect fs) {
+                                                         int D, int E, FusedSelect fs,
+                                                         FusedPermute fp) {
+  static_assert(TPL == 1, "the folded permute takes one token per lane");
   constexpr int VEC = Elem<T>::VEC;            // elements per 16-byte vector
   constexpr int NJ = kFewSlab / (LPT * VEC);   // vectors per lane and row per full slab
   constexpr int TPW = 256 / LPT;               // tokens per workgroup and TPL step
   constexpr int WQ = EM * kFewSlab / 4 / 256;  // float4 of a W_r slab per thread
   constexpr int QR = kFewSlab / 4;             // float4 per expert row of a slab
   __shared__ double2 sw[2][EM * kFewSlab / 2];  // [e][column pair], few_swz order
+  __shared__ int32_t s_pick[256];                 // folded permute: the slots' experts
   const int tid = threadIdx.x, lane = tid & 63;
   const int p = lane & (LPT - 1);
   // token i of this lane: block base + TPW i + tid / LPT
@@ -309,7 +458,13 @@ __global__ __launch_bounds__(256) void router_few_kernel(const T* __restrict__ x
 #pragma unroll
     for (int e = 0; e < EM; ++e) acc[i][e] = sum_lanes<LPT>(acc[i][e]);
     const int t = t0 + TPW * i;
-    if (t < T_) few_finish<EM, LPT>(acc[i], t, p, E, rb, logits, fs);
+    if (t < T_)
+      few_finish<EM, LPT>(acc[i], t, p, E, rb, logits, fs,
+                          fp.wg_counts ? s_pick + (tid / LPT) * fp.K : nullptr);
+  }
+  if (fp.wg_counts) {
+    __syncthreads();
+    fold_permute(fp, s_pick, TPW, T_, E);
   }
 }
 
@@ -604,23 +759,28 @@ static int launch_select(float* lg, const float* selb, const SelectExtras& x, in
 // router logits out[T][E] = fl32(x W^T + b), fp64 accumulation
 // the few-expert router can take the selection as well (fsp != nullptr);
 // returns 1 (nothing launched) when it cannot, so the caller selects apart
+// tokens per workgroup of the few-expert router (8 or 16 lanes per token)
+static int few_tokens_per_wg(int T_) { return cdiv(T_, 32) < 512 ? 16 : 32; }
+
 static int router_logits_sel(const moe_config& c, const void* x, const float* wr,
                              const float* rb, float* logits, const FusedSelect* fsp,
-                             hipStream_t st) {
+                             const FusedPermute* fpp, hipStream_t st) {
   const int T_ = c.T, D = c.D, E = c.E;
   {
     if (E <= 16) {
       const FusedSelect fs = fsp ? *fsp : FusedSelect{nullptr, nullptr, nullptr, nullptr, 0, 0, 0};
+      FusedPermute fp = {};
+      if (fpp) fp = *fpp;
       const char* name = fsp ? "route_fused" : "router_logits";
       // One token per lane (two halved the workgroups and measured slower on
       // the Mixtral-like layer and MiniMind); eight lanes per token, or
       // sixteen (16 tokens per workgroup) when eight would leave fewer than
       // two workgroups per CU: MiniMind 14.6 -> 11.1 us, while the
       // Mixtral-like layer is faster with eight (72 against 86 us).
-      const bool wide = cdiv(T_, 32) < 512;
+      const bool wide = few_tokens_per_wg(T_) == 16;
 #define FEW(TV, EMV, LPTV)                                                                  \
   MOE_LAUNCH(name, (router_few_kernel<TV, EMV, 1, LPTV>), dim3((unsigned)cdiv(T_, 256 / LPTV)), \
-             dim3(256), 0, st, (const TV*)x, wr, rb, logits, T_, D, E, fs)
+             dim3(256), 0, st, (const TV*)x, wr, rb, logits, T_, D, E, fs, fp)
 #define FEW_L(TV, EMV)            \
   if (wide) FEW(TV, EMV, 16);     \
   else FEW(TV, EMV, 8);
@@ -654,7 +814,7 @@ static int router_logits_sel(const moe_config& c, const void* x, const float* wr
 
 int router_logits(const moe_config& c, const void* x, const float* wr, const float* rb,
                   float* logits, hipStream_t st) {
-  return router_logits_sel(c, x, wr, rb, logits, nullptr, st);
+  return router_logits_sel(c, x, wr, rb, logits, nullptr, nullptr, st);
 }
 
 int launch_route(const moe_config& c, const void* x, const float* wr, const float* rb,
@@ -668,7 +828,7 @@ int launch_route(const moe_config& c, const void* x, const float* wr, const floa
   if (!logits_given && !jit && !wn) {
     // plain routing: the few-expert router selects in the same kernel
     const FusedSelect fs = {sb, idx, w, lse, K, sc, ga};
-    rc = router_logits_sel(c, x, wr, rb, logits, &fs, st);
+    rc = router_logits_sel(c, x, wr, rb, logits, &fs, nullptr, st);
     if (rc <= 0) return rc;
   }
   if (!logits_given && (rc = router_logits(c, x, wr, rb, logits, st))) return rc;
@@ -687,6 +847,47 @@ int launch_route(const moe_config& c, const void* x, const float* wr, const floa
   if (E <= 512) SEL(64, 8);
   SEL(64, 16);
 #undef SEL
+}
+
+int launch_route_permute(const moe_config& c, const void* x, const float* wr, const float* rb,
+                         const float* selb, float* logits, int32_t* idx, float* w, float* lse,
+                         int capacity, int32_t* counts_all, int32_t* offsets, int32_t* slot_row,
+                         int32_t* row_token, int32_t* row_slot, int32_t* n_dropped,
+                         void* x_perm, char* ws, const Workspace& L, hipStream_t st) {
+  const int E = c.E, K = c.K;
+  const int64_t TK = (int64_t)c.T * K;
+  // the fold needs the few-expert router (its last workgroup does the
+  // scan), at most 256 slots per workgroup, and a batch whose slots one
+  // workgroup assigns quickly (the one-workgroup permute's range)
+  const int tpw = few_tokens_per_wg(c.T);
+  const bool fold = E <= 16 && tpw * K <= 256 && TK <= 32768 && cdiv(c.T, tpw) <= kFoldWgs;
+  if (!fold) {
+    int rc = launch_route(c, x, wr, rb, selb, nullptr, nullptr, nullptr, nullptr, logits, idx,
+                          w, lse, false, st);
+    if (rc) return rc;
+    return launch_permute(c, capacity, idx, x, counts_all, offsets, slot_row, row_token,
+                          row_slot, n_dropped, x_perm, ws, L, st);
+  }
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  const float* sb = (c.score_fn == MOE_SCORE_SIGMOID) ? selb : nullptr;
+  const FusedSelect fs = {sb, idx, w, lse, K, c.score_fn, c.gating};
+  int32_t* wg_counts = reinterpret_cast<int32_t*>(ws + L.fold_counts);
+  int32_t* local_rank = reinterpret_cast<int32_t*>(ws + L.fold_rank);
+  const FusedPermute fp = {wg_counts, local_rank, K, nbits};
+  int rc = router_logits_sel(c, x, wr, rb, logits, &fs, &fp, st);
+  if (rc) return rc;
+  const int nwg = (int)cdiv(c.T, tpw);
+  const dim3 grid((unsigned)cdiv(TK, kScatterSlots));
+#define SCATTER(TV)                                                                           \
+  MOE_LAUNCH("permute_scatter", scatter_slots_kernel<TV>, grid, dim3(256), 0, st, (const TV*)x, \
+             idx, wg_counts, local_rank, nwg, tpw, (int)TK, K, E, c.expert_lo, c.expert_hi,   \
+             capacity, c.n_shared, c.T, c.D, counts_all, offsets, n_dropped, slot_row,         \
+             row_token, row_slot, (TV*)x_perm)
+  if (c.dtype == MOE_BF16) SCATTER(bf16_t);
+  else SCATTER(float);
+#undef SCATTER
+  return launch_shared_rows(c, offsets, row_token, row_slot, st);
 }
 
 }  // namespace moe

@@ -1,7 +1,8 @@
 """A MoE layer driven through the C ABI: buffers come from torch (device memory
 only), every computation is a call into ``libmoe_mi355x.so``.
 
-Forward:  moe_route -> moe_permute -> moe_expert_ffn -> moe_combine
+Forward:  moe_route_permute (plain routing; else moe_route -> moe_permute)
+          -> moe_expert_ffn -> moe_combine
           (+ aux_balance_loss when a balance or z-loss coefficient is set);
           expert choice: moe_route_expert_choice -> moe_expert_ffn -> moe_combine
 Backward: moe_backward (with the aux-loss logit gradient as d_logits_extra)
@@ -155,6 +156,13 @@ class MoELayer:
                                       self.topk_w, self.lse, self.counts, self.offsets,
                                       self.slot_row, self.row_token, self.row_slot, self.x_perm,
                                       self.ws, L.MOE_ROUTE_LOGITS_GIVEN if logits_given else 0)
+        elif not logits_given and jitter is None and self.w_noise is None:
+            # plain routing: route and permute in one call (fewer launches)
+            self.jitter = None
+            L.moe_route_permute(self.cfg, x, self.w_r, self.r_bias, self.sel_bias, self.logits,
+                                self.topk_idx, self.topk_w, self.lse, self.counts, self.offsets,
+                                self.slot_row, self.row_token, self.row_slot, self.n_dropped,
+                                self.x_perm, self.ws)
         else:
             self.route(x, logits_given, jitter, noise_eps)
             L.moe_permute(self.cfg, self.topk_idx, x, self.counts, self.offsets, self.slot_row,
