@@ -148,6 +148,66 @@ MOE_DEV bool find_group(const int32_t* offsets, int G, int mt, int& g_out, int& 
   return true;
 }
 
+// Cost-balanced XCD ranges of the weight-gradient tiles (persistent kernel).
+// Expert loads are skewed, so equal tile counts per XCD give some XCDs far
+// more slabs than others (per-tile timestamps: 0.78 of the chip busy, the
+// last XCD 2.7 ms behind on the DeepSeek-V3-like gate/up gradient).  Each
+// XCD x takes an eighth of the shared expert's tiles (its reductions run over
+// all T rows: on one XCD they made that XCD the straggler) and the routed
+// tiles, in group order, whose cumulative cost starts in [x C / 8,
+// (x + 1) C / 8): a tile of group g costs its padded slab count plus
+// kTileOverhead slab-times (epilogue and hand-over), C is the routed total.
+// Wave-uniform; every wave computes the same ranges.
+constexpr int kTileOverhead = 2;
+MOE_DEV int groupk_slabs(const int32_t* offsets, int g) {
+  const int n = offsets[g + 1] - offsets[g];
+  int nk = max(2, (n + 63) / 64);
+  return nk + (nk & 1);
+}
+// routed tiles [begin, end) of XCD x (tile r = group r / per, tile r % per)
+MOE_DEV void groupk_xcd_range(const int32_t* offsets, int Gr, int64_t per, int x,
+                              int64_t& begin, int64_t& end) {
+  const int lane = threadIdx.x & 63;
+  const int L = (Gr + 63) / 64;  // groups per lane
+  int64_t sum = 0;
+  for (int i = 0; i < L; ++i) {
+    const int q = lane * L + i;
+    if (q < Gr) sum += per * (groupk_slabs(offsets, q) + kTileOverhead);
+  }
+  int64_t incl = sum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int64_t u = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += u;
+  }
+  const int64_t total = __shfl(incl, 63, 64);
+  const int64_t excl = incl - sum;
+  // first tile whose cumulative cost start is >= B (B = k C / 8)
+  auto tile_at = [&](int k) -> int64_t {
+    const int64_t B = total * k / 8;
+    const uint64_t who = __ballot(B >= excl && B < incl);
+    if (k >= 8 || who == 0) return (int64_t)Gr * per;
+    const int owner = __ffsll((long long)who) - 1;
+    int64_t t = 0;
+    if (lane == owner) {
+      int64_t c = excl;
+      for (int i = 0; i < L; ++i) {
+        const int q = lane * L + i;
+        if (q >= Gr) break;
+        const int64_t ct = groupk_slabs(offsets, q) + kTileOverhead;
+        if (B < c + per * ct) {
+          t = (int64_t)q * per + (B - c + ct - 1) / ct;
+          break;
+        }
+        c += per * ct;
+      }
+    }
+    return __shfl(t, owner, 64);
+  };
+  begin = tile_at(x);
+  end = tile_at(x + 1);
+}
+
 // Total m-tiles of bm rows over all groups (uniform).
 MOE_DEV int total_mtiles(const int32_t* offsets, int G, int bm) {
   const int lane = threadIdx.x & 63;
@@ -1595,8 +1655,31 @@ __global__ __launch_bounds__(512) void grouped_gemm_persist_kernel(GemmParams P)
   } else {
     n_tiles = (int64_t)P.G * P.ntm * P.ntn;
   }
-  const int64_t nwg = gridDim.x;
-  if ((int64_t)blockIdx.x >= n_tiles) return;
+  // GROUP_M: tiles blockIdx.x, + gridDim.x, ... (XCD-remapped).  GROUP_K:
+  // the cost-balanced range of this workgroup's XCD, tiles w, w + nw, ... of
+  // it (w = blockIdx.x / 8 of the nw = gridDim.x / 8 workgroups on the XCD)
+  // GROUP_K: virtual tiles 0 .. nsh + (rt1 - rt0) of this workgroup's XCD --
+  // its share [sh0, sh0 + nsh) of the shared expert's tiles, then its
+  // routed range [rt0, rt1) -- tiles w, w + nw, ... of them (w =
+  // blockIdx.x / 8 of the nw = gridDim.x / 8 workgroups on the XCD)
+  int64_t nwg = gridDim.x, j_end = n_tiles;
+  int64_t j = blockIdx.x;
+  int64_t sh0 = 0, nsh = 0, rt0 = 0;
+  if constexpr (GROUPING == GROUP_K) {
+    const int64_t per = (int64_t)P.ntm * P.ntn;
+    const int x = (int)(blockIdx.x % 8);
+    const bool shared = P.shared_rows > 0;
+    if (shared) {
+      sh0 = per * x / 8;
+      nsh = per * (x + 1) / 8 - sh0;
+    }
+    int64_t rt1;
+    groupk_xcd_range(P.offsets, P.G - (shared ? 1 : 0), per, x, rt0, rt1);
+    nwg = gridDim.x / 8;
+    j = blockIdx.x / 8;
+    j_end = nsh + (rt1 - rt0);
+  }
+  if (j >= j_end) return;
 
   // ---- per-lane DMA offsets, fixed for the kernel
   uint32_t a_lane[A_PER_WAVE];
@@ -1648,7 +1731,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_persist_kernel(GemmParams P)
   auto decode = [&](int64_t j, bool real) __attribute__((always_inline)) {
     Tile t;
     t.real = real;
-    const int64_t lin = remap_xcd(j, n_tiles);
+    const int64_t lin = (GROUPING == GROUP_M) ? remap_xcd(j, n_tiles) : j;
     int kdim, nrows_g = 0;
     if constexpr (GROUPING == GROUP_M) {
       int mt, nt, mtl, g;
@@ -1664,7 +1747,14 @@ __global__ __launch_bounds__(512) void grouped_gemm_persist_kernel(GemmParams P)
     } else {
       const int64_t per = (int64_t)P.ntm * P.ntn;
       int64_t tl;
-      groupk_tile(j, n_tiles, per, P.shared_rows > 0, P.G, t.g, tl);
+      if (j < nsh) {
+        t.g = P.G - 1;
+        tl = sh0 + j;
+      } else {
+        const int64_t r = rt0 + (j - nsh);
+        t.g = (int)(r / per);
+        tl = r - (int64_t)t.g * per;
+      }
       int mt, nt;
       supercol_tile<kSuperColsK>(tl, P.ntm, P.ntn, mt, nt);
       t.m0 = mt * BM;
@@ -1803,7 +1893,6 @@ __global__ __launch_bounds__(512) void grouped_gemm_persist_kernel(GemmParams P)
   // the group's end, so nothing is counted for them
   constexpr int EPI_VM = (GROUPING == GROUP_K && EPI == EPI_STORE) ? NI * 4 : 0;
 
-  int64_t j = blockIdx.x;
   Tile cur = decode(j, true);
   int cur_real = real_slabs(cur);
   Tile nxt;
@@ -1872,7 +1961,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_persist_kernel(GemmParams P)
     // reads zeros) is decoded; its slab 0 goes into stage 0 at the first
     // hand-over, its slab 1 into stage 1 as soon as every wave has read the
     // last slab -- no wait for it: the epilogue comes first
-    const bool more = j + nwg < n_tiles;
+    const bool more = j + nwg < j_end;
     nxt = more ? decode(j + nwg, true) : decode(j, false);
     nxt_real = real_slabs(nxt);
     body(sA0, sB0);
@@ -2128,7 +2217,8 @@ static int launch_persist(const char* name, GemmParams P, hipStream_t st) {
   P.ntn = P.N / BN;
   tile_space(P, GR, 256);
   if (P.nblocks <= 0) return MOE_OK;
-  const int64_t grid = std::min<int64_t>(P.nblocks, 256);
+  // GROUP_K: 32 workgroups per XCD, each XCD its cost-balanced tile range
+  const int64_t grid = (GR == GROUP_K) ? 256 : std::min<int64_t>(P.nblocks, 256);
   MOE_LAUNCH(name, (grouped_gemm_persist_kernel<AM, BM_, GR, EPI, BS, BN>), dim3((unsigned)grid),
              dim3(512), 0, st, P);
   return MOE_OK;
@@ -2173,10 +2263,19 @@ static int run_gemm(const char* name, GemmParams& P, hipStream_t st) {
         Q.ntn = P.N / 256;
         tile_space(Q, GR, 256);
       }
-      if (wide && Q.nblocks >= (GR == GROUP_K ? 192 : 384)) {
-        // 256 x 256 tiles on 8 waves (the persistent variant spills
-        // registers and was measured no faster: Mixtral-like down projection
-        // 2.79 vs 2.83 ms)
+      if (wide && GR == GROUP_K && EPI == EPI_STORE && P.n_routed > 0 &&
+          P.routed_rows_max / P.n_routed >= 2048 && Q.nblocks >= 4096) {
+        // weight gradients with long reductions and many tiles: persistent
+        // 256 x 256 tiles, each XCD a cost-balanced tile range (Mixtral-like
+        // gate/up 7.35 -> 5.50 ms, down 3.71 -> 2.74 ms).  With short
+        // reductions the per-tile hand-over costs more than the overlapped
+        // prologue saves (DeepSeek-V3-like gate/up 7.8 against 8.5 ms) and
+        // with few tiles the split is coarse (OLMoE-like 0.28 against 0.32)
+        cfg = 7;
+      } else if (wide && Q.nblocks >= (GR == GROUP_K ? 192 : 384)) {
+        // 256 x 256 tiles on 8 waves (the persistent variant was measured no
+        // faster for the row GEMMs: Mixtral-like down projection 2.79 vs
+        // 2.83 ms)
         cfg = 5;
       } else {
         Q = P;
