@@ -92,22 +92,30 @@ MOE_DEV int64_t remap_xcd(int64_t b, int64_t n) {
   return (x < r) ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
 }
 
-// Weight-gradient (GROUP_K) tile order for launch (or work) index b of n
-// tiles: the shared expert's tiles -- each a reduction over all T rows, much
-// longer than a routed expert's -- come first, so they are spread over the
-// CUs and finish early instead of forming the tail (each XCD takes a
-// contiguous block of them); the routed experts' tiles follow, XCD-blocked.
-// The shared expert is the last group.  g: group, tl: tile within the group.
-MOE_DEV void groupk_tile(int64_t b, int64_t n, int64_t per, bool shared, int G, int& g,
-                         int64_t& tl) {
+// Weight-gradient (GROUP_K) tile order for launch index b of n tiles: the
+// shared expert's tiles -- each a reduction over all T rows, much longer
+// than a routed expert's -- come first, so they are spread over the CUs and
+// finish early instead of forming the tail; the routed experts' tiles
+// follow in group order (the shared expert is the last group).  Launch
+// order is tile order, so the hardware's
+// round-robin placement (workgroup b on XCD b % 8) hands every XCD every
+// eighth tile of each group: the XCDs carry equal shares of every group's
+// slabs however skewed the expert loads are, and all of them stream the
+// same group's operands at about the same time.  Contiguous per-XCD tile
+// ranges (better L2 reuse in principle) left the XCD with the heaviest
+// experts 1.8 ms behind the lightest on the DeepSeek-V3-like gate/up
+// gradient (60 k against 99 k slabs per XCD); the round-robin order
+// measured gate/up 7.73 -> 6.78 ms, down 4.32 -> 3.47 ms there and 7.44 ->
+// 4.82, 3.70 -> 2.36 ms on the Mixtral-like layer (chunks of 4 or 16
+// consecutive tiles per XCD were no better).  g: group, tl: tile within it.
+MOE_DEV void groupk_tile(int64_t b, int64_t per, bool shared, int G, int& g, int64_t& tl) {
   const int64_t sh = shared ? per : 0;
   if (b < sh) {
     g = G - 1;
-    tl = remap_xcd(b, sh);
+    tl = b;
   } else {
-    const int64_t l = remap_xcd(b - sh, n - sh);
-    g = (int)(l / per);
-    tl = l - (int64_t)g * per;
+    g = (int)((b - sh) / per);
+    tl = (b - sh) - (int64_t)g * per;
   }
 }
 
@@ -950,7 +958,7 @@ void grouped_gemm_dma_kernel(GemmParams P) {
   } else {
     const int64_t per = (int64_t)P.ntm * P.ntn;
     int64_t tl;
-    groupk_tile(blockIdx.x, P.nblocks, per, P.shared_rows > 0, P.G, g, tl);
+    groupk_tile(blockIdx.x, per, P.shared_rows > 0, P.G, g, tl);
     int mt, nt;
     supercol_tile<kSuperColsK>(tl, P.ntm, P.ntn, mt, nt);
     m0 = mt * BMT;
@@ -1233,7 +1241,7 @@ __global__ __launch_bounds__(NW * 64) void grouped_gemm_big_kernel(GemmParams P)
   } else {
     const int64_t per = (int64_t)P.ntm * P.ntn;
     int64_t tl;
-    groupk_tile(blockIdx.x, P.nblocks, per, P.shared_rows > 0, P.G, g, tl);
+    groupk_tile(blockIdx.x, per, P.shared_rows > 0, P.G, g, tl);
     int mt, nt;
     supercol_tile<kSuperColsK>(tl, P.ntm, P.ntn, mt, nt);
     m0 = mt * BM;
@@ -2263,19 +2271,11 @@ static int run_gemm(const char* name, GemmParams& P, hipStream_t st) {
         Q.ntn = P.N / 256;
         tile_space(Q, GR, 256);
       }
-      if (wide && GR == GROUP_K && EPI == EPI_STORE && P.n_routed > 0 &&
-          P.routed_rows_max / P.n_routed >= 2048 && Q.nblocks >= 4096) {
-        // weight gradients with long reductions and many tiles: persistent
-        // 256 x 256 tiles, each XCD a cost-balanced tile range (Mixtral-like
-        // gate/up 7.35 -> 5.50 ms, down 3.71 -> 2.74 ms).  With short
-        // reductions the per-tile hand-over costs more than the overlapped
-        // prologue saves (DeepSeek-V3-like gate/up 7.8 against 8.5 ms) and
-        // with few tiles the split is coarse (OLMoE-like 0.28 against 0.32)
-        cfg = 7;
-      } else if (wide && Q.nblocks >= (GR == GROUP_K ? 192 : 384)) {
-        // 256 x 256 tiles on 8 waves (the persistent variant was measured no
-        // faster for the row GEMMs: Mixtral-like down projection 2.79 vs
-        // 2.83 ms)
+      if (wide && Q.nblocks >= (GR == GROUP_K ? 192 : 384)) {
+        // 256 x 256 tiles on 8 waves.  The persistent variant was measured
+        // no faster: Mixtral-like down projection 2.79 vs 2.83 ms; weight
+        // gradients with cost-balanced XCD ranges, Mixtral-like gate/up 5.51
+        // against 4.82 ms, DeepSeek-V3-like 8.55 against 6.78 ms.
         cfg = 5;
       } else {
         Q = P;
