@@ -232,19 +232,40 @@ MOE_DEV int total_mtiles(const int32_t* offsets, int G, int bm) {
 
 // Row-GEMM tile order for layers with many small groups: XCD x (workgroup b
 // runs on XCD b % 8) takes the real m-tiles [x mh, (x + 1) mh), mh =
-// ceil(mt_real / 8), each with all its column tiles, column fastest.  A row
-// panel is then fetched by one XCD for all its column tiles, and a group's
-// weights by the one or two XCDs holding its few m-tiles, where giving each
-// XCD a column band makes every XCD fetch every row panel.  The grid holds 8
-// ceil(mt_total / 8) ntn blocks (mt_total bounds mt_real); blocks past an
-// XCD's share return false.
-MOE_DEV bool xcd_mblock_tile(int64_t b, int mt_real, int ntn, int& mt, int& nt) {
+// ceil(mt_real / 8), with all their column tiles.  A row panel is then
+// fetched by one XCD, and a group's weights by the one or two XCDs holding
+// its few m-tiles, where giving each XCD a column band makes every XCD fetch
+// every row panel.  Inside the block, each group's share runs column by
+// column with the group's m-tiles innermost, so the workgroups that read
+// one weight panel run side by side on the XCD and share it through its L2
+// (with the column fastest, a group's second m-tile came a full round of
+// column tiles later and fetched the weights again: DeepSeek-V3-like gate/up
+// input gradient 5.71 -> 5.12 ms).  The grid holds 8 ceil(mt_total / 8) ntn
+// blocks (mt_total bounds mt_real); blocks past an XCD's share return
+// false.  Out: the tile (mt, nt), its group g and m-tile mtl within it.
+MOE_DEV bool xcd_mblock_tile(int64_t b, const int32_t* offsets, int G, int bm, int ntn, int& mt,
+                             int& nt, int& g, int& mtl) {
+  const int mt_real = total_mtiles(offsets, G, bm);
   const int x = (int)(b % 8);
   const int64_t i = b / 8;
   const int mh = (mt_real + 7) / 8;
-  mt = x * mh + (int)(i / ntn);
-  nt = (int)(i % ntn);
-  return mt < min((x + 1) * mh, mt_real);
+  const int hi = min((x + 1) * mh, mt_real);
+  const int row = x * mh + (int)(i / ntn);  // the m-tile in column-fastest order
+  if (row >= hi) return false;
+  // the group segment holding that m-tile, clipped to the XCD's block: the
+  // same segment holds this block index in the group-column order
+  int ml;
+  if (!find_group(offsets, G, row, g, ml, bm)) return false;
+  g = __builtin_amdgcn_readfirstlane(g);
+  ml = __builtin_amdgcn_readfirstlane(ml);
+  const int sg = row - ml;
+  const int eg = sg + (offsets[g + 1] - offsets[g] + bm - 1) / bm;
+  const int a = max(sg, x * mh), len = min(eg, hi) - a;
+  const int64_t j = i - (int64_t)(a - x * mh) * ntn;
+  nt = (int)(j / len);
+  mt = a + (int)(j % len);
+  mtl = mt - sg;
+  return true;
 }
 
 template <typename T>
@@ -1225,11 +1246,11 @@ __global__ __launch_bounds__(NW * 64) void grouped_gemm_big_kernel(GemmParams P)
   if constexpr (GROUPING == GROUP_M) {
     int mt, nt, mtl;
     if (P.xcd_m) {
-      if (!xcd_mblock_tile(blockIdx.x, total_mtiles(P.offsets, P.G, BM), P.ntn, mt, nt)) return;
+      if (!xcd_mblock_tile(blockIdx.x, P.offsets, P.G, BM, P.ntn, mt, nt, g, mtl)) return;
     } else {
       supercol_tile<kSuperColsM>(lin, P.mt_total, P.ntn, mt, nt);
+      if (!find_group(P.offsets, P.G, mt, g, mtl, BM)) return;
     }
-    if (!find_group(P.offsets, P.G, mt, g, mtl, BM)) return;
     g = __builtin_amdgcn_readfirstlane(g);
     mtl = __builtin_amdgcn_readfirstlane(mtl);
     nrows_g = P.offsets[g + 1] - P.offsets[g];
@@ -2209,8 +2230,9 @@ static int launch_big(const char* name, GemmParams P, hipStream_t st) {
   if (GR == GROUP_M && EPI == EPI_STORE && P.n_routed >= 64) {
     // many small groups: XCD blocks of the real m-tiles (rounded grid).
     // Measured on the DeepSeek-V3-like layer: down projection 3.08 -> 2.83
-    // ms, gate/up input gradient 5.79 -> 5.67 ms; not for the SwiGLU
-    // forward (5.15 -> 5.33 ms)
+    // ms, gate/up input gradient 5.79 -> 5.67 ms (5.12 with the group-column
+    // order inside the blocks); not for the SwiGLU forward (5.15 -> 5.33 ms,
+    // and 5.02 -> 5.16 ms with the group-column order)
     P.xcd_m = 1;
     P.nblocks = (int64_t)cdiv(P.mt_total, 8) * 8 * P.ntn;
   }
