@@ -2271,8 +2271,16 @@ static int run_gemm(const char* name, GemmParams& P, hipStream_t st) {
       tile_space(Q, GR, 256);
       tiles256 = Q.nblocks;
     }
-    if (cfg < 0 && (EPI == EPI_SWIGLU_BWD ||
-                    (GR == GROUP_M && (P.Kdim < 2048 || (P.Kdim == 2048 && tiles256 < 1024))))) {
+    // the SwiGLU-backward GEMM on large groups with long reductions takes the
+    // 256 x 256 tiles below: Mixtral-like 3.43 -> 3.10 ms, OLMoE-like 0.371
+    // -> 0.356 ms; on small groups (DeepSeek-V3-like, ~256 rows: 2.98 against
+    // 3.36 ms) or short reductions (MiniMind, K = 768: 58 against 77 us) the
+    // 128 x 128 tiles stay
+    const bool bwd_big = EPI == EPI_SWIGLU_BWD && wide && P.Kdim >= 2048 && P.n_routed > 0 &&
+                         P.routed_rows_max / P.n_routed >= 1024;
+    if (cfg < 0 && ((EPI == EPI_SWIGLU_BWD && !bwd_big) ||
+                    (GR == GROUP_M && EPI != EPI_SWIGLU_BWD &&
+                     (P.Kdim < 2048 || (P.Kdim == 2048 && tiles256 < 1024))))) {
       // 128 x 128 tiles run two workgroups per CU, so one's epilogue and
       // first-slab wait overlap the other's main loop.  That wins for the
       // row GEMMs with short reductions (K <= 2048: a tile's main loop is
