@@ -2280,16 +2280,21 @@ static int run_gemm(const char* name, GemmParams& P, hipStream_t st) {
                          P.routed_rows_max / P.n_routed >= 1024;
     if (cfg < 0 && ((EPI == EPI_SWIGLU_BWD && !bwd_big) ||
                     (GR == GROUP_M && EPI != EPI_SWIGLU_BWD &&
-                     (P.Kdim < 2048 || (P.Kdim == 2048 && tiles256 < 1024))))) {
+                     (P.Kdim < 2048 ||
+                      (P.Kdim == 2048 && !(EPI == EPI_STORE && P.n_routed >= 64 &&
+                                           tiles256 >= 1024)))))) {
       // 128 x 128 tiles run two workgroups per CU, so one's epilogue and
       // first-slab wait overlap the other's main loop.  That wins for the
       // row GEMMs with short reductions (K <= 2048: a tile's main loop is
       // then not much longer than its prologue and epilogue) and for the
       // SwiGLU-backward epilogue (activations read, two gradients written)
-      // at every measured shape; long reductions, and the plain-store row
-      // GEMM at K = 2048 with many tiles (DeepSeek-V3-like down projection:
-      // 3.04 vs 3.33 ms; the SwiGLU forward at OLMoE-like K = 2048 is not:
-      // 0.53 vs 0.38 ms), favour the 256-wide tiles.
+      // on small groups or short reductions; long reductions, and the
+      // plain-store row GEMM at K = 2048 on many small groups with many
+      // tiles (DeepSeek-V3-like down projection: 3.04 vs 3.33 ms, with the
+      // XCD m-tile blocks of launch_big), favour the 256-wide tiles.  Not
+      // the SwiGLU forward at OLMoE-like K = 2048 (0.53 vs 0.38 ms), nor the
+      // gate/up input gradient there (32 local experts of ~1000 rows: 0.506
+      // vs 0.348 ms).
       cfg = 1;
     }
     if (cfg < 0) {
