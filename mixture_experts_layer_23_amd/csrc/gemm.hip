@@ -1217,14 +1217,23 @@ struct BigShape {
   static constexpr int NI = WTM / 32, NJ = WTN / 32;           // 32 x 32 blocks
 };
 
-template <int AMODE, int BMODE, int GROUPING, int EPI, int BSPL, int BN, int NW>
+// BK: reduction depth of one LDS slab.  64 everywhere except the weight-
+// gradient variant on 256 x 128 tiles with 4 waves, which takes 32-deep slabs
+// (48 KB of LDS for two stages) so that two workgroups share a CU: the
+// reductions of a weight gradient run only over one group's rows, so each
+// tile is short and its prologue and epilogue stores are a large part of it;
+// with two workgroups per CU they overlap the other workgroup's main loop.
+template <int AMODE, int BMODE, int GROUPING, int EPI, int BSPL, int BN, int NW, int BK = 64>
 __global__ __launch_bounds__(NW * 64) void grouped_gemm_big_kernel(GemmParams P) {
   typedef bf16_t T;
   typedef BigShape<BN, NW> S;
-  constexpr int BM = 256, BK = 64;
+  constexpr int BM = 256;
+  static_assert(BK == 64 || (BK == 32 && GROUPING == GROUP_K && AMODE == MC && BMODE == MC),
+                "32-deep slabs only for the weight gradients (both operands k-major)");
+  constexpr int KS = BK / 16;        // 16-deep MFMA k-steps per slab
   constexpr int NI = S::NI, NJ = S::NJ, WTM = S::WTM, WTN = S::WTN;
-  constexpr int ATILE = BM * 128;    // bytes of the A slab
-  constexpr int BTILE = BN * 128;    // bytes of the B slab
+  constexpr int ATILE = BM * BK * 2;  // bytes of the A slab
+  constexpr int BTILE = BN * BK * 2;  // bytes of the B slab
   constexpr int A_PER_WAVE = ATILE / 1024 / NW;
   constexpr int B_PER_WAVE = BTILE / 1024 / NW;
   constexpr int CPRB = BN / 8;       // 16-byte chunks per k-row of an MC B slab
@@ -1431,21 +1440,18 @@ __global__ __launch_bounds__(NW * 64) void grouped_gemm_big_kernel(GemmParams P)
     // slab kt + 1 is landing in (na, nb).  The body is branch-free: the slab
     // count is padded to even and the DMA runs on past the end (see issue).
     auto step = [&](int kt, char* la, char* lb, char* na, char* nb) __attribute__((always_inline)) {
-      frags(la, lb, 1, 1);
-      __builtin_amdgcn_sched_barrier(0);
-      mfmas(0);
-      frags(la, lb, 2, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      mfmas(1);
-      frags(la, lb, 3, 1);
-      __builtin_amdgcn_sched_barrier(0);
-      mfmas(0);
+#pragma unroll
+      for (int ks = 1; ks < KS; ++ks) {
+        frags(la, lb, ks, ks & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas((ks - 1) & 1);
+      }
       wait_vmcnt<0>();
       __syncthreads();
       issue(kt + 2, la, lb);
       frags(na, nb, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
-      mfmas(1);
+      mfmas((KS - 1) & 1);
     };
     if (nkp > 0) {
       issue(0, sA0, sB0);
@@ -1618,12 +1624,20 @@ __global__ __launch_bounds__(NW * 64) void grouped_gemm_big_kernel(GemmParams P)
         if constexpr (GROUPING == GROUP_M) {
           *reinterpret_cast<uint4*>(reinterpret_cast<T*>(P.C0) + (grow0 + row) * P.ldc + col) = v;
         } else {
+          // weight gradients: streaming stores.  dW is written once and not
+          // read again by this layer; cached stores displaced the operand
+          // slabs the other tiles of the group re-read from L2 (DeepSeek-V3-
+          // like layer: operand fetches 5.9 GB per launch without the dW
+          // stores, 8.1 GB with them; gate/up weight gradient 6.81 -> 6.60
+          // ms, down 3.45 -> 3.31 ms)
           const int64_t mrow = m0 + row_t0 + row;
           T* C = (col < P.csplit)
                      ? reinterpret_cast<T*>(P.C0) + (int64_t)g * P.strideC + mrow * P.ldc + col
                      : reinterpret_cast<T*>(P.C1) + (int64_t)g * P.strideC + mrow * P.ldc +
                            (col - P.csplit);
-          *reinterpret_cast<uint4*>(C) = v;
+          Vec16<T> o;
+          o.v = v;
+          o.store_nt(C);
         }
       }
     }
@@ -2177,7 +2191,9 @@ static void tile_space(GemmParams& P, int grouping, int bm) {
 // GEMM configuration of the LDS-DMA kernels: 0 = register-staged kernel,
 // 1 = 128-row tiles / 2 stages, 2 = 256-row tiles / 3 stages, 3 / 4 = 256 x
 // 256 / 256 x 128 large tiles on 4 waves, 5 / 6 = the same on 8 waves,
-// 7 / 8 = persistent 256 x 256 / 256 x 128 on 8 waves.
+// 7 / 8 = persistent 256 x 256 / 256 x 128 on 8 waves, 9 = 256 x 128 on 4
+// waves with 32-deep slabs, two workgroups per CU (weight gradients; the row
+// GEMMs then take 1).
 // MOE_GEMM_CFG overrides the choice (measurement, and tests that run every
 // kernel variant): a number for every GEMM, or "name=cfg" pairs separated by
 // commas (e.g. "gemm_down_dgrad=1,gemm_gate_up_fwd=5").  Read at every
@@ -2222,21 +2238,24 @@ static int launch_dma(const char* name, GemmParams P, hipStream_t st) {
 // tiles runs on the LDS-DMA kernel -- 256-row tiles when that still gives at
 // least two workgroups per CU, else 128-row tiles; fp32 and ragged shapes
 // run on the register-staged kernel.
-template <int AM, int BM_, int GR, int EPI, int BS, int BN, int NW>
+template <int AM, int BM_, int GR, int EPI, int BS, int BN, int NW, int BK = 64>
 static int launch_big(const char* name, GemmParams P, hipStream_t st) {
   P.ntn = P.N / BN;
   tile_space(P, GR, 256);
   if (P.nblocks <= 0) return MOE_OK;
-  if (GR == GROUP_M && EPI == EPI_STORE && P.n_routed >= 64) {
+  if (GR == GROUP_M && (EPI == EPI_STORE || EPI == EPI_SWIGLU_BWD) && P.n_routed >= 64) {
     // many small groups: XCD blocks of the real m-tiles (rounded grid).
     // Measured on the DeepSeek-V3-like layer: down projection 3.08 -> 2.83
     // ms, gate/up input gradient 5.79 -> 5.67 ms (5.12 with the group-column
-    // order inside the blocks); not for the SwiGLU forward (5.15 -> 5.33 ms,
-    // and 5.02 -> 5.16 ms with the group-column order)
+    // order inside the blocks), SwiGLU-backward GEMM 3.33 -> 2.76 ms (against
+    // 2.94 ms on the 128 x 128 tiles, whose column bands per XCD made every
+    // XCD stream all of d_o: 19.3 GB fetched per launch); not for the SwiGLU
+    // forward (5.15 -> 5.33 ms, and 5.02 -> 5.16 ms with the group-column
+    // order)
     P.xcd_m = 1;
     P.nblocks = (int64_t)cdiv(P.mt_total, 8) * 8 * P.ntn;
   }
-  MOE_LAUNCH(name, (grouped_gemm_big_kernel<AM, BM_, GR, EPI, BS, BN, NW>),
+  MOE_LAUNCH(name, (grouped_gemm_big_kernel<AM, BM_, GR, EPI, BS, BN, NW, BK>),
              dim3((unsigned)P.nblocks), dim3(NW * 64), 0, st, P);
   return MOE_OK;
 }
@@ -2271,13 +2290,15 @@ static int run_gemm(const char* name, GemmParams& P, hipStream_t st) {
       tile_space(Q, GR, 256);
       tiles256 = Q.nblocks;
     }
-    // the SwiGLU-backward GEMM on large groups with long reductions takes the
-    // 256 x 256 tiles below: Mixtral-like 3.43 -> 3.10 ms, OLMoE-like 0.371
-    // -> 0.356 ms; on small groups (DeepSeek-V3-like, ~256 rows: 2.98 against
-    // 3.36 ms) or short reductions (MiniMind, K = 768: 58 against 77 us) the
+    // the SwiGLU-backward GEMM with long reductions takes the 256 x 256
+    // tiles below on large groups (Mixtral-like 3.43 -> 3.10 ms, OLMoE-like
+    // 0.371 -> 0.356 ms) and on many small groups, where each XCD then takes
+    // a block of the real m-tiles (DeepSeek-V3-like, ~256 rows per expert:
+    // 2.94 -> 2.76 ms; 3.33 ms in the column-band order); on a few small
+    // groups or short reductions (MiniMind, K = 768: 58 against 77 us) the
     // 128 x 128 tiles stay
     const bool bwd_big = EPI == EPI_SWIGLU_BWD && wide && P.Kdim >= 2048 && P.n_routed > 0 &&
-                         P.routed_rows_max / P.n_routed >= 1024;
+                         (P.routed_rows_max / P.n_routed >= 1024 || P.n_routed >= 64);
     if (cfg < 0 && ((EPI == EPI_SWIGLU_BWD && !bwd_big) ||
                     (GR == GROUP_M && EPI != EPI_SWIGLU_BWD &&
                      (P.Kdim < 2048 ||
@@ -2324,6 +2345,8 @@ static int run_gemm(const char* name, GemmParams& P, hipStream_t st) {
     if (cfg == 7 && wide) return launch_persist<AM, BM_, GR, EPI, BS, 256>(name, P, st);
     if (cfg == 8 && full256) return launch_persist<AM, BM_, GR, EPI, BS, 128>(name, P, st);
     if (cfg == 6 && full256) return launch_big<AM, BM_, GR, EPI, BS, 128, 8>(name, P, st);
+    if constexpr (GR == GROUP_K && AM == MC && BM_ == MC)
+      if (cfg == 9 && full256) return launch_big<AM, BM_, GR, EPI, BS, 128, 4, 32>(name, P, st);
     if (cfg == 2 && full256) return launch_dma<AM, BM_, GR, EPI, BS, 256, 3>(name, P, st);
     if (cfg >= 1 && full128) return launch_dma<AM, BM_, GR, EPI, BS, 128, 2>(name, P, st);
   }
