@@ -2243,15 +2243,16 @@ static int launch_big(const char* name, GemmParams P, hipStream_t st) {
   P.ntn = P.N / BN;
   tile_space(P, GR, 256);
   if (P.nblocks <= 0) return MOE_OK;
-  if (GR == GROUP_M && (EPI == EPI_STORE || EPI == EPI_SWIGLU_BWD) && P.n_routed >= 64) {
+  if (GR == GROUP_M && P.n_routed >= 64) {
     // many small groups: XCD blocks of the real m-tiles (rounded grid).
     // Measured on the DeepSeek-V3-like layer: down projection 3.08 -> 2.83
     // ms, gate/up input gradient 5.79 -> 5.67 ms (5.12 with the group-column
     // order inside the blocks), SwiGLU-backward GEMM 3.33 -> 2.76 ms (against
     // 2.94 ms on the 128 x 128 tiles, whose column bands per XCD made every
-    // XCD stream all of d_o: 19.3 GB fetched per launch); not for the SwiGLU
-    // forward (5.15 -> 5.33 ms, and 5.02 -> 5.16 ms with the group-column
-    // order)
+    // XCD stream all of d_o: 19.3 GB fetched per launch).  The SwiGLU
+    // forward takes the same time either way (5.11 / 5.16 against 5.16 /
+    // 5.17 ms, alternating runs on one box: its main loop bounds it) but
+    // fetches 19.9 instead of 27.6 GB per launch
     P.xcd_m = 1;
     P.nblocks = (int64_t)cdiv(P.mt_total, 8) * 8 * P.ntn;
   }
