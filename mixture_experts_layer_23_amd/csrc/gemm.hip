@@ -80,7 +80,22 @@ struct GemmParams {
   int xcd_xn;         // > 0: 2-D tile blocks per XCD (xcd_xn column groups)
   int a_cap, b_cap;   // rows of lda / ldb bf16 elements in 2^31 - 1 bytes
   int xcd_m;          // GROUP_M: each XCD takes a block of the real m-tiles
+  // weight-gradient loop kernel: multipliers for n / per and n / (2 ntm)
+  // (ceil(2^32 / d), UINT32_MAX for d = 1; see udiv_magic)
+  uint32_t per_magic, span_magic;
 };
+
+// n / d for n < 2^31 from m = ceil(2^32 / d) (UINT32_MAX for d = 1): the
+// multiply-high estimate is floor(n / d) or one above (one below for d = 1),
+// and one correction each way makes it exact.  Uniform operands compile to
+// scalar multiplies, where a division would keep a reciprocal in vector
+// registers for the whole kernel.
+MOE_DEV uint32_t udiv_magic(uint32_t n, uint32_t d, uint32_t m) {
+  uint32_t q = __umulhi(n, m);
+  if (q * d > n) --q;
+  if ((q + 1) * d <= n) ++q;
+  return q;
+}
 
 MOE_DEV int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
@@ -2170,6 +2185,255 @@ __global__ __launch_bounds__(512) void grouped_gemm_persist_kernel(GemmParams P)
 }
 
 // ---------------------------------------------------------------------------
+// Weight gradients (both operands k-major) on 256 x 256 tiles with the next
+// tile's first slabs fetched during the current tile's epilogue.  One
+// workgroup per CU takes tiles w, w + W, w + 2 W, ... of the round-robin
+// weight-gradient order (W = gridDim.x, a multiple of 8, so tile t still
+// runs on XCD t mod 8 and every XCD keeps an equal share of every group).
+// The main loop is grouped_gemm_big_kernel's; its run-ahead DMA (the two
+// slabs past a tile's end) loads slabs 0 and 1 of the workgroup's next
+// tile, so the next tile starts with slab 0 in LDS instead of paying a full
+// DMA round trip (each tile of a routed expert runs only four or five
+// slabs).  The epilogue stages through a 32 KB LDS region of its own (4 KB of
+// bf16 per wave), not the stage buffers.  Per-lane DMA offsets are fixed for
+// the kernel and a tile's column offsets go in soffset, so the hand-over
+// needs no vector registers: the tile state is scalar.  Tiles of an empty
+// group store zeros directly.  Ordering: vector loads and stores retire in
+// issue order on one counter; a tile that waits for its own slab 0 issued
+// it after the previous epilogue's stores, so that wait also covers them.
+// ---------------------------------------------------------------------------
+struct WgTile {
+  int g, m0, n0, kdim, nkp;
+  const bf16_t* a;  // the group's k-major A rows
+  const bf16_t* b;  // the group's k-major B rows
+};
+
+__global__ __launch_bounds__(512) void grouped_gemm_wgrad_loop_kernel(GemmParams P) {
+  typedef bf16_t T;
+  typedef BigShape<256, 8> S;
+  constexpr int BM = 256, BN = 256, BK = 64, NW = 8;
+  constexpr int NI = S::NI, NJ = S::NJ, WTM = S::WTM, WTN = S::WTN;
+  constexpr int ATILE = BM * BK * 2, BTILE = BN * BK * 2;
+  constexpr int A_PER_WAVE = ATILE / 1024 / NW, B_PER_WAVE = BTILE / 1024 / NW;
+  constexpr int PER_SLAB = A_PER_WAVE + B_PER_WAVE;
+  constexpr int CPRB = BN / 8;
+  constexpr int EWAVE = 32 * WTN * 2;  // epilogue staging bytes per wave
+  static_assert(4 * (ATILE) + NW * EWAVE <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(1024))) char sA0[ATILE];
+  __shared__ __attribute__((aligned(1024))) char sB0[BTILE];
+  __shared__ __attribute__((aligned(1024))) char sA1[ATILE];
+  __shared__ __attribute__((aligned(1024))) char sB1[BTILE];
+  __shared__ __attribute__((aligned(1024))) char sE[NW * EWAVE];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int wm = wave / S::WNW, wn = wave % S::WNW;
+  const int64_t per = (int64_t)P.ntm * P.ntn;
+  const int64_t n_tiles = (int64_t)P.G * per;
+  const bool shared = P.shared_rows > 0;
+  int64_t t = blockIdx.x;
+  if (t >= n_tiles) return;
+
+  // per-lane DMA offsets (bytes) within a slab, tile-independent
+  uint32_t a_lane[A_PER_WAVE], b_lane[B_PER_WAVE];
+#pragma unroll
+  for (int u = 0; u < A_PER_WAVE; ++u) {
+    const int P_ = 64 * (wave * A_PER_WAVE + u) + lane;
+    const int kr = P_ / 32, lc = (P_ % 32) ^ mcswz(kr);
+    a_lane[u] = (uint32_t)(((int64_t)kr * P.lda + 8 * lc) * 2);
+  }
+#pragma unroll
+  for (int u = 0; u < B_PER_WAVE; ++u) {
+    const int P_ = 64 * (wave * B_PER_WAVE + u) + lane;
+    const int kr = P_ / CPRB, lc = (P_ % CPRB) ^ mcswz(kr);
+    b_lane[u] = (uint32_t)(((int64_t)kr * P.ldb + 8 * lc) * 2);
+  }
+  // tile tt of the order of groupk_tile + supercol_tile<2>, in 32-bit
+  // scalar arithmetic (the host keeps n_tiles below 2^31)
+  static_assert(kSuperColsK == 2, "two-column super-columns");
+  const uint32_t uper = (uint32_t)per, span = 2u * (uint32_t)P.ntm;
+  const uint32_t full = (uint32_t)P.ntn / 2;
+  auto tile_of = [&](int64_t tt, WgTile& w) __attribute__((always_inline)) {
+    const uint32_t b = (uint32_t)tt, sh = shared ? uper : 0u;
+    uint32_t g, tl;
+    if (b < sh) {
+      g = (uint32_t)P.G - 1;
+      tl = b;
+    } else {
+      g = udiv_magic(b - sh, uper, P.per_magic);
+      tl = b - sh - g * uper;
+    }
+    const uint32_t sc = udiv_magic(tl, span, P.span_magic);
+    uint32_t mt, nt;
+    if (sc < full) {
+      const uint32_t q = tl - sc * span;
+      mt = q >> 1;
+      nt = sc * 2 + (q & 1);
+    } else {  // the last, single column (odd ntn)
+      mt = tl - full * span;
+      nt = full * 2;
+    }
+    w.g = __builtin_amdgcn_readfirstlane((int)g);
+    w.m0 = __builtin_amdgcn_readfirstlane((int)mt * BM);
+    w.n0 = __builtin_amdgcn_readfirstlane((int)nt * BN);
+    const int r0 = group_offset(P.offsets, w.g), r1 = group_offset(P.offsets, w.g + 1);
+    w.kdim = r1 - r0;
+    const int nk = (w.kdim + BK - 1) / BK;
+    w.nkp = nk + (nk & 1);
+    w.a = (w.g < P.EL_A) ? reinterpret_cast<const T*>(P.A) + (int64_t)r0 * P.lda
+                         : reinterpret_cast<const T*>(P.A_sh);
+    w.b = (w.g < P.EL_B) ? reinterpret_cast<const T*>(P.B0) + (int64_t)r0 * P.ldb
+                         : reinterpret_cast<const T*>(P.B1);
+  };
+  // slab kt of tile w (rows at or past its k extent read zeros)
+  auto issue = [&](int kt, const WgTile& w, char* la, char* lb) __attribute__((always_inline)) {
+    const int k0 = kt * BK;
+    const rsrc_t a_rs = rows_rsrc(w.a, k0, w.kdim, P.lda, P.a_cap);
+    const rsrc_t b_rs = rows_rsrc(w.b, k0, w.kdim, P.ldb, P.b_cap);
+#pragma unroll
+    for (int u = 0; u < A_PER_WAVE; ++u)
+      dma16_buffer_so(a_rs, to_lds(la + (wave * A_PER_WAVE + u) * 1024), a_lane[u],
+                      (uint32_t)(w.m0 * 2));
+#pragma unroll
+    for (int u = 0; u < B_PER_WAVE; ++u)
+      dma16_buffer_so(b_rs, to_lds(lb + (wave * B_PER_WAVE + u) * 1024), b_lane[u],
+                      (uint32_t)(w.n0 * 2));
+  };
+  auto out_ptr = [&](const WgTile& w, int64_t mrow, int col) __attribute__((always_inline)) {
+    return (col < P.csplit)
+               ? reinterpret_cast<T*>(P.C0) + (int64_t)w.g * P.strideC + mrow * P.ldc + col
+               : reinterpret_cast<T*>(P.C1) + (int64_t)w.g * P.strideC + mrow * P.ldc +
+                     (col - P.csplit);
+  };
+
+  int rb[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) rb[j] = wn * WTN + j * 32;
+  uint4 fa[2][NI], fb[2][NJ];
+  f32x16_t acc[NI][NJ];
+  auto frags = [&](const char* la, const char* lb, int ks, int slot) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      fa[slot][i] = frag_mc(const_cast<char*>(la), wm * WTM + i * 32, ks, lane, BM * 2);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      fb[slot][j] = frag_mc(const_cast<char*>(lb), rb[j], ks, lane, BN * 2);
+  };
+  auto mfmas = [&](int slot) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8_t, fb[slot][j]), __builtin_bit_cast(bf16x8_t, fa[slot][i]),
+            acc[i][j], 0, 0, 0);
+  };
+
+  WgTile cur, nxt;
+  tile_of(t, cur);
+  issue(0, cur, sA0, sB0);
+  issue(1, cur, sA1, sB1);
+  bool ready = false;  // slab 0 of cur has landed and every wave has passed a barrier since
+  const int lrow = lane & 31, lcol = (lane >> 5) * 4;
+  char* reg = sE + wave * EWAVE;
+  for (;;) {
+    const int64_t tn = t + gridDim.x;
+    const bool has_next = tn < n_tiles;
+    if (has_next) tile_of(tn, nxt);
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    if (cur.nkp > 0) {
+      if (!ready) {
+        wait_vmcnt<PER_SLAB>();
+        lds_barrier();
+      }
+      frags(sA0, sB0, 0, 0);
+      const int nkp = cur.nkp;
+      // slab kt + 2 of this tile, or slab kt + 2 - nkp of the next one
+      auto run_ahead = [&](int kt, char* la, char* lb) __attribute__((always_inline)) {
+        const int q = kt + 2;
+        if (q < nkp || !has_next) issue(q, cur, la, lb);
+        else issue(q - nkp, nxt, la, lb);
+      };
+      auto step = [&](int kt, char* la, char* lb, char* na, char* nb) __attribute__((always_inline)) {
+        frags(la, lb, 1, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(0);
+        frags(la, lb, 2, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(1);
+        frags(la, lb, 3, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(0);
+        wait_vmcnt<0>();
+        lds_barrier();
+        run_ahead(kt, la, lb);
+        frags(na, nb, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(1);
+      };
+      for (int kt = 0; kt < nkp; kt += 2) {
+        step(kt, sA0, sB0, sA1, sB1);
+        step(kt + 1, sA1, sB1, sA0, sB0);
+      }
+    }
+    // (an empty group's tile, nkp = 0, stores the zeros)
+    {
+      // epilogue: each 32-row block of the wave through its LDS region
+      // (bf16, 16-byte chunks XOR-swizzled within the row), 16-byte row
+      // segments out, streaming (dW is not read again by this layer)
+      constexpr int CPR = WTN / 8, RPI = 64 / CPR, MSK = (CPR < 8 ? CPR : 8) - 1;
+      const int ch = lane % CPR;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
+            const int col = j * 32 + q * 8 + lcol;
+            const int c8 = col >> 3, half = (col >> 2) & 1;
+            *reinterpret_cast<uint2*>(reg + lrow * WTN * 2 + ((c8 ^ (lrow & MSK)) << 4) + (half << 3)) =
+                pack_bf16x4(v);
+          }
+#pragma unroll
+        for (int it = 0; it < 32 / RPI; ++it) {
+          const int row = it * RPI + lane / CPR;
+          Vec16<T> o;
+          o.v = *reinterpret_cast<const uint4*>(reg + row * WTN * 2 + ((ch ^ (row & MSK)) << 4));
+          o.store_nt(out_ptr(cur, cur.m0 + wm * WTM + i * 32 + row, cur.n0 + wn * WTN + ch * 8));
+        }
+      }
+    }
+    if (cur.nkp > 0) {
+      // the last step waited for the next tile's slab 0 (issued by the
+      // run-ahead) and every wave has passed its barrier since; slab 1 is
+      // in flight
+      ready = has_next;
+    } else {
+      // the next tile's first slabs, issued after this tile's stores so that
+      // its wait for slab 0 also covers them
+      if (has_next) {
+        issue(0, nxt, sA0, sB0);
+        issue(1, nxt, sA1, sB1);
+      }
+      ready = false;
+    }
+    if (!has_next) break;
+    t = tn;
+    cur = nxt;
+  }
+  // the run-ahead DMA (zeros past the last tile) must land before the LDS is
+  // released
+  wait_vmcnt<0>();
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 static int groups_of(const moe_config& c) { return (c.expert_hi - c.expert_lo) + c.n_shared; }
@@ -2192,8 +2456,9 @@ static void tile_space(GemmParams& P, int grouping, int bm) {
 // 1 = 128-row tiles / 2 stages, 2 = 256-row tiles / 3 stages, 3 / 4 = 256 x
 // 256 / 256 x 128 large tiles on 4 waves, 5 / 6 = the same on 8 waves,
 // 7 / 8 = persistent 256 x 256 / 256 x 128 on 8 waves, 9 = 256 x 128 on 4
-// waves with 32-deep slabs, two workgroups per CU (weight gradients; the row
-// GEMMs then take 1).
+// waves with 32-deep slabs, two workgroups per CU, 10 = 256 x 256 tile loop
+// with the next tile's first slabs fetched during the epilogue (9 and 10:
+// weight gradients; the row GEMMs then take 1).
 // MOE_GEMM_CFG overrides the choice (measurement, and tests that run every
 // kernel variant): a number for every GEMM, or "name=cfg" pairs separated by
 // commas (e.g. "gemm_down_dgrad=1,gemm_gate_up_fwd=5").  Read at every
@@ -2274,6 +2539,20 @@ static int launch_persist(const char* name, GemmParams P, hipStream_t st) {
   return MOE_OK;
 }
 
+// weight gradients on 256 x 256 tiles, one workgroup per CU walking its tiles
+// with the next tile's first slabs fetched during the epilogue
+static int launch_wgrad_loop(const char* name, GemmParams P, hipStream_t st) {
+  P.ntn = P.N / 256;
+  tile_space(P, GROUP_K, 256);
+  if (P.nblocks <= 0) return MOE_OK;
+  const uint64_t per = (uint64_t)P.ntm * P.ntn, span = 2ull * (uint64_t)P.ntm;
+  P.per_magic = (per == 1) ? UINT32_MAX : (uint32_t)(((1ull << 32) + per - 1) / per);
+  P.span_magic = (uint32_t)(((1ull << 32) + span - 1) / span);
+  MOE_LAUNCH(name, grouped_gemm_wgrad_loop_kernel,
+             dim3((unsigned)std::min<int64_t>(P.nblocks, 256)), dim3(512), 0, st, P);
+  return MOE_OK;
+}
+
 template <typename T, int AM, int BM_, int GR, int EPI, int BS>
 static int run_gemm(const char* name, GemmParams& P, hipStream_t st) {
   P.a_cap = (int)(INT32_MAX / (std::max<int64_t>(P.lda, 1) * 2));
@@ -2319,6 +2598,18 @@ static int run_gemm(const char* name, GemmParams& P, hipStream_t st) {
       // vs 0.348 ms).
       cfg = 1;
     }
+    if (cfg < 0 && GR == GROUP_K && wide && P.n_routed > 0 &&
+        P.routed_rows_max / P.n_routed <= 512 && (int64_t)(P.Mfix / 256) * (P.N / 256) >= 256) {
+      // weight gradients with short reductions (a few hundred rows per
+      // expert: each tile runs four or five slabs and its first-slab wait is
+      // a large part of it) and at least one tile per CU in every group: the
+      // tile loop that fetches the next tile's first slabs during the
+      // epilogue.  Measured alone, cfg 10 against 5: DeepSeek-V3-like gate/up
+      // weight gradient 6.03 / 6.05 against 6.42 / 6.43 ms; slower on its down
+      // weight gradient (224 tiles per group: 3.58 against 3.27 ms) and on the
+      // long-reduction layers (Mixtral-like gate/up 5.05 against 4.80 ms)
+      cfg = 10;
+    }
     if (cfg < 0) {
       // 256 x 256 tiles on 8 waves when they give enough tiles (a weight
       // gradient, with its long reduction over the group rows, needs fewer);
@@ -2346,8 +2637,14 @@ static int run_gemm(const char* name, GemmParams& P, hipStream_t st) {
     if (cfg == 7 && wide) return launch_persist<AM, BM_, GR, EPI, BS, 256>(name, P, st);
     if (cfg == 8 && full256) return launch_persist<AM, BM_, GR, EPI, BS, 128>(name, P, st);
     if (cfg == 6 && full256) return launch_big<AM, BM_, GR, EPI, BS, 128, 8>(name, P, st);
-    if constexpr (GR == GROUP_K && AM == MC && BM_ == MC)
+    if constexpr (GR == GROUP_K && AM == MC && BM_ == MC) {
       if (cfg == 9 && full256) return launch_big<AM, BM_, GR, EPI, BS, 128, 4, 32>(name, P, st);
+      if constexpr (EPI == EPI_STORE && BS == BS_NONE) {
+        // (tile indices in 32 bits)
+        if (cfg == 10 && wide && (int64_t)P.G * (P.Mfix / 256) * (P.N / 256) < INT32_MAX)
+          return launch_wgrad_loop(name, P, st);
+      }
+    }
     if (cfg == 2 && full256) return launch_dma<AM, BM_, GR, EPI, BS, 256, 3>(name, P, st);
     if (cfg >= 1 && full128) return launch_dma<AM, BM_, GR, EPI, BS, 128, 2>(name, P, st);
   }
