@@ -406,7 +406,9 @@ const char* moe_error_string(int code);
 /*
  * Environment variables read at every call (measurement and tests only):
  *   MOE_GEMM_CFG        forces the grouped-GEMM kernel variant: a number
- *                       0..8 for every GEMM, or "name=cfg,..." pairs
+ *                       0..11 for every GEMM (9 to 11 are weight-gradient
+ *                       kernels; the other GEMMs then take 1), or
+ *                       "name=cfg,..." pairs
  *                       (gemm_gate_up_fwd, gemm_down_fwd, gemm_down_dgrad,
  *                       gemm_down_wgrad, gemm_gate_up_dgrad, gemm_gate_up_wgrad).
  *   MOE_SERIAL_STREAMS  when set, moe_backward runs every kernel on the

@@ -2188,8 +2188,9 @@ __global__ __launch_bounds__(512) void grouped_gemm_persist_kernel(GemmParams P)
 // Weight gradients (both operands k-major) on 256 x 256 tiles with the next
 // tile's first slabs fetched during the current tile's epilogue.  One
 // workgroup per CU takes tiles w, w + W, w + 2 W, ... of the round-robin
-// weight-gradient order (W = gridDim.x, a multiple of 8, so tile t still
-// runs on XCD t mod 8 and every XCD keeps an equal share of every group).
+// weight-gradient order (W = gridDim.x = 256 whenever there are that many
+// tiles, a multiple of 8, so tile t still runs on XCD t mod 8 and every XCD
+// keeps an equal share of every group; placement only, not correctness).
 // The main loop is grouped_gemm_big_kernel's; its run-ahead DMA (the two
 // slabs past a tile's end) loads slabs 0 and 1 of the workgroup's next
 // tile, so the next tile starts with slab 0 in LDS instead of paying a full
@@ -2197,10 +2198,12 @@ __global__ __launch_bounds__(512) void grouped_gemm_persist_kernel(GemmParams P)
 // slabs).  The epilogue stages through a 32 KB LDS region of its own (4 KB of
 // bf16 per wave), not the stage buffers.  Per-lane DMA offsets are fixed for
 // the kernel and a tile's column offsets go in soffset, so the hand-over
-// needs no vector registers: the tile state is scalar.  Tiles of an empty
-// group store zeros directly.  Ordering: vector loads and stores retire in
-// issue order on one counter; a tile that waits for its own slab 0 issued
-// it after the previous epilogue's stores, so that wait also covers them.
+// needs no vector registers: the tile state is scalar.  A tile of an empty
+// group runs no main loop: it stores its zero accumulators through the same
+// epilogue and then issues the next tile's first slabs.  Ordering: vector
+// loads and stores retire in issue order on one counter; a tile that waits
+// for its own slab 0 issued it after the previous epilogue's stores, so that
+// wait also covers them.
 // ---------------------------------------------------------------------------
 struct WgTile {
   int g, m0, n0, kdim, nkp;
@@ -2208,21 +2211,24 @@ struct WgTile {
   const bf16_t* b;  // the group's k-major B rows
 };
 
+// BK-deep slabs through NS stages (64 x 2 or 32 x 4: 128 KB either way).
+template <int BK, int NS>
 __global__ __launch_bounds__(512) void grouped_gemm_wgrad_loop_kernel(GemmParams P) {
   typedef bf16_t T;
   typedef BigShape<256, 8> S;
-  constexpr int BM = 256, BN = 256, BK = 64, NW = 8;
+  constexpr int BM = 256, BN = 256, NW = 8, KS = BK / 16;
+  static_assert((BK == 64 && NS == 2) || (BK == 32 && NS == 4), "stages");
   constexpr int NI = S::NI, NJ = S::NJ, WTM = S::WTM, WTN = S::WTN;
   constexpr int ATILE = BM * BK * 2, BTILE = BN * BK * 2;
   constexpr int A_PER_WAVE = ATILE / 1024 / NW, B_PER_WAVE = BTILE / 1024 / NW;
-  constexpr int PER_SLAB = A_PER_WAVE + B_PER_WAVE;
+  constexpr int PER_SLAB = A_PER_WAVE + B_PER_WAVE;  // DMA instructions per slab and wave
   constexpr int CPRB = BN / 8;
   constexpr int EWAVE = 32 * WTN * 2;  // epilogue staging bytes per wave
-  static_assert(4 * (ATILE) + NW * EWAVE <= 160 * 1024, "LDS");
-  __shared__ __attribute__((aligned(1024))) char sA0[ATILE];
-  __shared__ __attribute__((aligned(1024))) char sB0[BTILE];
-  __shared__ __attribute__((aligned(1024))) char sA1[ATILE];
-  __shared__ __attribute__((aligned(1024))) char sB1[BTILE];
+  constexpr int NSTORE = NI * 4;       // epilogue store instructions per wave
+  static_assert(NS * (ATILE + BTILE) + NW * EWAVE <= 160 * 1024, "LDS");
+  static_assert((NS - 2) * PER_SLAB + NSTORE < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) char sA[NS][ATILE];
+  __shared__ __attribute__((aligned(1024))) char sB[NS][BTILE];
   __shared__ __attribute__((aligned(1024))) char sE[NW * EWAVE];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -2278,7 +2284,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_wgrad_loop_kernel(GemmParams
     const int r0 = group_offset(P.offsets, w.g), r1 = group_offset(P.offsets, w.g + 1);
     w.kdim = r1 - r0;
     const int nk = (w.kdim + BK - 1) / BK;
-    w.nkp = nk + (nk & 1);
+    w.nkp = (nk + NS - 1) / NS * NS;
     w.a = (w.g < P.EL_A) ? reinterpret_cast<const T*>(P.A) + (int64_t)r0 * P.lda
                          : reinterpret_cast<const T*>(P.A_sh);
     w.b = (w.g < P.EL_B) ? reinterpret_cast<const T*>(P.B0) + (int64_t)r0 * P.ldb
@@ -2330,9 +2336,12 @@ __global__ __launch_bounds__(512) void grouped_gemm_wgrad_loop_kernel(GemmParams
 
   WgTile cur, nxt;
   tile_of(t, cur);
-  issue(0, cur, sA0, sB0);
-  issue(1, cur, sA1, sB1);
-  bool ready = false;  // slab 0 of cur has landed and every wave has passed a barrier since
+#pragma unroll
+  for (int q = 0; q < NS; ++q) issue(q, cur, sA[q], sB[q]);
+  // ready: slab 0 of cur has landed and every wave has passed a barrier
+  // since; its slabs 1 .. NS-1 were issued before the previous tile's
+  // epilogue stores (the run-ahead), so those stores are younger than them
+  bool ready = false;
   const int lrow = lane & 31, lcol = (lane >> 5) * 4;
   char* reg = sE + wave * EWAVE;
   for (;;) {
@@ -2346,38 +2355,49 @@ __global__ __launch_bounds__(512) void grouped_gemm_wgrad_loop_kernel(GemmParams
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
     if (cur.nkp > 0) {
+      const bool after_stores = ready;
       if (!ready) {
-        wait_vmcnt<PER_SLAB>();
+        // slabs 1 .. NS-1 (issued after slab 0) may still be in flight
+        wait_vmcnt<(NS - 1) * PER_SLAB>();
         lds_barrier();
       }
-      frags(sA0, sB0, 0, 0);
+      frags(sA[0], sB[0], 0, 0);
       const int nkp = cur.nkp;
-      // slab kt + 2 of this tile, or slab kt + 2 - nkp of the next one
+      // slab kt + NS of this tile, or slab kt + NS - nkp of the next one
       auto run_ahead = [&](int kt, char* la, char* lb) __attribute__((always_inline)) {
-        const int q = kt + 2;
+        const int q = kt + NS;
         if (q < nkp || !has_next) issue(q, cur, la, lb);
         else issue(q - nkp, nxt, la, lb);
       };
-      auto step = [&](int kt, char* la, char* lb, char* na, char* nb) __attribute__((always_inline)) {
-        frags(la, lb, 1, 1);
-        __builtin_amdgcn_sched_barrier(0);
-        mfmas(0);
-        frags(la, lb, 2, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        mfmas(1);
-        frags(la, lb, 3, 1);
-        __builtin_amdgcn_sched_barrier(0);
-        mfmas(0);
-        wait_vmcnt<0>();
+      // Slab kt (stage s = kt mod NS) is computed while slabs kt + 1 ..
+      // kt + NS - 1 are in flight; at its end the wait is for slab kt + 1
+      // only: the NS - 2 slabs issued after it may stay in flight, and in
+      // the first NS - 1 slabs of a tile that follows a computed tile so may
+      // that tile's NSTORE epilogue stores (issued after slab kt + 1).
+      auto step = [&](int kt, auto sc, bool first) __attribute__((always_inline)) {
+        constexpr int s = decltype(sc)::value, sn = (s + 1) % NS;
+#pragma unroll
+        for (int ks = 1; ks < KS; ++ks) {
+          frags(sA[s], sB[s], ks, ks & 1);
+          __builtin_amdgcn_sched_barrier(0);
+          mfmas((ks - 1) & 1);
+        }
+        if (s <= NS - 2 && first && after_stores) wait_vmcnt<(NS - 2) * PER_SLAB + NSTORE>();
+        else wait_vmcnt<(NS - 2) * PER_SLAB>();
         lds_barrier();
-        run_ahead(kt, la, lb);
-        frags(na, nb, 0, 0);
+        run_ahead(kt, sA[s], sB[s]);
+        frags(sA[sn], sB[sn], 0, 0);
         __builtin_amdgcn_sched_barrier(0);
-        mfmas(1);
+        mfmas((KS - 1) & 1);
       };
-      for (int kt = 0; kt < nkp; kt += 2) {
-        step(kt, sA0, sB0, sA1, sB1);
-        step(kt + 1, sA1, sB1, sA0, sB0);
+      for (int kt = 0; kt < nkp; kt += NS) {
+        const bool first = kt == 0;
+        step(kt, std::integral_constant<int, 0>{}, first);
+        step(kt + 1, std::integral_constant<int, 1>{}, first);
+        if constexpr (NS == 4) {
+          step(kt + 2, std::integral_constant<int, NS == 4 ? 2 : 0>{}, first);
+          step(kt + 3, std::integral_constant<int, NS == 4 ? 3 : 0>{}, first);
+        }
       }
     }
     // (an empty group's tile, nkp = 0, stores the zeros)
@@ -2419,8 +2439,8 @@ __global__ __launch_bounds__(512) void grouped_gemm_wgrad_loop_kernel(GemmParams
       // the next tile's first slabs, issued after this tile's stores so that
       // its wait for slab 0 also covers them
       if (has_next) {
-        issue(0, nxt, sA0, sB0);
-        issue(1, nxt, sA1, sB1);
+#pragma unroll
+        for (int q = 0; q < NS; ++q) issue(q, nxt, sA[q], sB[q]);
       }
       ready = false;
     }
@@ -2456,9 +2476,10 @@ static void tile_space(GemmParams& P, int grouping, int bm) {
 // 1 = 128-row tiles / 2 stages, 2 = 256-row tiles / 3 stages, 3 / 4 = 256 x
 // 256 / 256 x 128 large tiles on 4 waves, 5 / 6 = the same on 8 waves,
 // 7 / 8 = persistent 256 x 256 / 256 x 128 on 8 waves, 9 = 256 x 128 on 4
-// waves with 32-deep slabs, two workgroups per CU, 10 = 256 x 256 tile loop
-// with the next tile's first slabs fetched during the epilogue (9 and 10:
-// weight gradients; the row GEMMs then take 1).
+// waves with 32-deep slabs, two workgroups per CU, 10 / 11 = 256 x 256 tile
+// loop with the next tile's first slabs fetched during the epilogue, two
+// 64-deep / four 32-deep stages (9-11: weight gradients; the row GEMMs then
+// take 1).
 // MOE_GEMM_CFG overrides the choice (measurement, and tests that run every
 // kernel variant): a number for every GEMM, or "name=cfg" pairs separated by
 // commas (e.g. "gemm_down_dgrad=1,gemm_gate_up_fwd=5").  Read at every
@@ -2541,6 +2562,7 @@ static int launch_persist(const char* name, GemmParams P, hipStream_t st) {
 
 // weight gradients on 256 x 256 tiles, one workgroup per CU walking its tiles
 // with the next tile's first slabs fetched during the epilogue
+template <int BK, int NS>
 static int launch_wgrad_loop(const char* name, GemmParams P, hipStream_t st) {
   P.ntn = P.N / 256;
   tile_space(P, GROUP_K, 256);
@@ -2548,7 +2570,7 @@ static int launch_wgrad_loop(const char* name, GemmParams P, hipStream_t st) {
   const uint64_t per = (uint64_t)P.ntm * P.ntn, span = 2ull * (uint64_t)P.ntm;
   P.per_magic = (per == 1) ? UINT32_MAX : (uint32_t)(((1ull << 32) + per - 1) / per);
   P.span_magic = (uint32_t)(((1ull << 32) + span - 1) / span);
-  MOE_LAUNCH(name, grouped_gemm_wgrad_loop_kernel,
+  MOE_LAUNCH(name, (grouped_gemm_wgrad_loop_kernel<BK, NS>),
              dim3((unsigned)std::min<int64_t>(P.nblocks, 256)), dim3(512), 0, st, P);
   return MOE_OK;
 }
@@ -2604,11 +2626,15 @@ static int run_gemm(const char* name, GemmParams& P, hipStream_t st) {
       // expert: each tile runs four or five slabs and its first-slab wait is
       // a large part of it) and at least one tile per CU in every group: the
       // tile loop that fetches the next tile's first slabs during the
-      // epilogue.  Measured alone, cfg 10 against 5: DeepSeek-V3-like gate/up
-      // weight gradient 6.03 / 6.05 against 6.42 / 6.43 ms; slower on its down
-      // weight gradient (224 tiles per group: 3.58 against 3.27 ms) and on the
-      // long-reduction layers (Mixtral-like gate/up 5.05 against 4.80 ms)
-      cfg = 10;
+      // epilogue, on four 32-deep stages (three slabs in flight).  Measured
+      // alone against the 256 x 256 kernel (cfg 5), DeepSeek-V3-like gate/up
+      // weight gradient: cfg 11 5.64 / 5.65 ms, cfg 10 (two 64-deep stages)
+      // 5.92 / 5.94, cfg 5 6.36 (step 27.6 -> 26.7 ms).  Its down weight
+      // gradient (224 tiles per group) and the long-reduction layers tie
+      // alone (Mixtral-like gate/up 4.77 both) but lose in the overlapped
+      // step (Mixtral-like 23.9 -> 24.4 ms): one workgroup holding a CU's
+      // whole LDS leaves no room for the data-gradient GEMM beside it
+      cfg = 11;
     }
     if (cfg < 0) {
       // 256 x 256 tiles on 8 waves when they give enough tiles (a weight
@@ -2641,8 +2667,9 @@ static int run_gemm(const char* name, GemmParams& P, hipStream_t st) {
       if (cfg == 9 && full256) return launch_big<AM, BM_, GR, EPI, BS, 128, 4, 32>(name, P, st);
       if constexpr (EPI == EPI_STORE && BS == BS_NONE) {
         // (tile indices in 32 bits)
-        if (cfg == 10 && wide && (int64_t)P.G * (P.Mfix / 256) * (P.N / 256) < INT32_MAX)
-          return launch_wgrad_loop(name, P, st);
+        const bool fits = wide && (int64_t)P.G * (P.Mfix / 256) * (P.N / 256) < INT32_MAX;
+        if (cfg == 10 && fits) return launch_wgrad_loop<64, 2>(name, P, st);
+        if (cfg == 11 && fits) return launch_wgrad_loop<32, 4>(name, P, st);
       }
     }
     if (cfg == 2 && full256) return launch_dma<AM, BM_, GR, EPI, BS, 256, 3>(name, P, st);

@@ -17,10 +17,10 @@ torch = pytest.importorskip("torch")
 # 0 register-staged; 1 128x128 DMA, 2 stages; 2 256x128 DMA, 3 stages;
 # 3 / 4 256x256 / 256x128 on 4 waves; 5 / 6 the same on 8 waves;
 # 7 / 8 persistent 256x256 / 256x128; 9 256x128 on 4 waves with 32-deep
-# slabs, two workgroups per CU; 10 256x256 tile loop with the next tile's
-# first slabs fetched during the epilogue (9 and 10 are weight-gradient
-# kernels: the row GEMMs take 1)
-CFGS = list(range(11))
+# slabs, two workgroups per CU; 10 / 11 256x256 tile loop with the next
+# tile's first slabs fetched during the epilogue, two 64-deep / four 32-deep
+# stages (9-11 are weight-gradient kernels: the row GEMMs take 1)
+CFGS = list(range(12))
 WORKLOADS = {
     "minimind_like": S.WORKLOADS["minimind"].with_(T=512, D=512, F=512, E=4, K=2),
     "shared_sigmoid": S.WORKLOADS["deepseek_v3"].with_(T=384, D=512, F=512, E=8, K=2),
