@@ -35,6 +35,11 @@ WORKLOADS = {
     # 64 routed experts (+ a shared one): the 256-row kernels give each XCD a
     # block of the real m-tiles in the plain-store row GEMMs
     "many_experts": S.WORKLOADS["deepseek_v3"].with_(T=512, D=1024, F=256, E=64, K=8),
+    # 128 slots over 256 experts: most groups are empty, so the weight-gradient
+    # tile loops run long runs of empty tiles (zero stores, then the next
+    # tile's slabs issued by hand) between the shared expert's and the few
+    # routed experts' tiles
+    "mostly_empty": S.WORKLOADS["deepseek_v3"].with_(T=64, D=512, F=256, E=256, K=2),
 }
 _ref = {}
 
