@@ -87,6 +87,9 @@ def workload(args):
     if args.gating is not None:
         wl = wl.with_(gating=S.GATE_A if args.gating == "A" else S.GATE_B)
     if args.routing == "expert":
+        if wl.score != S.SOFTMAX:
+            sys.exit(f"bench.py: expert-choice routing needs softmax scoring; the {args.workload} "
+                     "layer scores with sigmoid")
         wl = wl.with_(gating=S.GATE_A)  # a pair is weighted by its softmax probability
     return wl
 
